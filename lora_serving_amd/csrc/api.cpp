@@ -1,0 +1,304 @@
+// C ABI of libmlora: argument checks, workspace layout and kernel dispatch.
+// Declarations and the contract of every entry point are in include/mlora.h.
+#include "mlora.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace mlora;
+
+namespace {
+
+constexpr int64_t DECODE_MAX_T = 128;   // batches up to this size take the decode path
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Checks an mlora_slots and fills the kernels' geometry (slice table normalised).
+mlora_status check_slots(const mlora_slots *s, int64_t n_out, bool need_data, SlotGeom *g)
+{
+    if (s == nullptr)
+        return MLORA_ERR_ARG;
+    if (s->S < 1 || s->S > MLORA_MAX_SLOTS)
+        return MLORA_ERR_UNSUPPORTED;
+    if (s->R < 8 || s->R > MLORA_MAX_RANK || !is_pow2(s->R))
+        return MLORA_ERR_UNSUPPORTED;
+    if (s->n_slices < 1 || s->n_slices > MLORA_MAX_SLICES)
+        return MLORA_ERR_UNSUPPORTED;
+    std::memset(g, 0, sizeof *g);
+    g->S = s->S;
+    g->R = s->R;
+    g->n_slices = s->n_slices;
+    bool all_zero = true;
+    for (int i = 0; i <= s->n_slices; ++i)
+        all_zero &= s->slice_start[i] == 0;
+    if (s->n_slices == 1 && all_zero) {
+        g->slice_start[0] = 0;
+        g->slice_start[1] = (int32_t)n_out;
+    } else {
+        if (s->slice_start[0] != 0 || s->slice_start[s->n_slices] != n_out)
+            return MLORA_ERR_SHAPE;
+        for (int i = 0; i < s->n_slices; ++i)
+            if (s->slice_start[i + 1] <= s->slice_start[i])
+                return MLORA_ERR_SHAPE;
+        for (int i = 0; i <= s->n_slices; ++i)
+            g->slice_start[i] = s->slice_start[i];
+    }
+    for (int i = s->n_slices + 1; i < 5; ++i)
+        g->slice_start[i] = g->slice_start[s->n_slices];
+    if (need_data) {
+        if (s->A == nullptr || s->B == nullptr || s->factor == nullptr)
+            return MLORA_ERR_ARG;
+        if (!aligned16(s->A) || !aligned16(s->B))
+            return MLORA_ERR_ARG;
+    }
+    g->A = (const uint16_t *)s->A;
+    g->B = (const uint16_t *)s->B;
+    g->factor = s->factor;
+    return MLORA_OK;
+}
+
+// Workspace layout of one call; every region 256-byte aligned.
+struct Layout {
+    size_t sort_cnt = 0;   // counting-sort scratch (plan)
+    size_t v = 0;          // fp32 [K][Tc][n_slices*R] shrink output (decode path)
+    size_t part = 0;       // fp32 partial sums of the decode GEMM
+    size_t total = 0;
+    size_t off_sort = 0, off_v = 0, off_part = 0;
+};
+
+Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t wd)
+{
+    Layout L;
+    L.sort_cnt = align_up(sort_workspace_bytes(T * K, S));
+    const int64_t Tc = std::min<int64_t>(T, DECODE_MAX_T);
+    L.v = align_up((size_t)K * Tc * wd * sizeof(float));
+    L.part = Tc > 0 ? align_up(decode_partial_bytes(Tc, n_in, n_out)) : 0;
+    L.off_sort = 0;
+    L.off_v = L.off_sort + L.sort_cnt;
+    L.off_part = L.off_v + L.v;
+    L.total = L.off_part + L.part;
+    return L;
+}
+
+thread_local char g_last_error[256] = "";
+
+mlora_status hip_status(hipError_t e, const char *where = "launch")
+{
+    if (e == hipSuccess)
+        return MLORA_OK;
+    std::snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", where, hipGetErrorString(e),
+                  (int)e);
+    return MLORA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mlora_last_error(void) { return g_last_error; }
+
+const char *mlora_status_string(mlora_status status)
+{
+    switch (status) {
+    case MLORA_OK: return "ok";
+    case MLORA_ERR_ARG: return "invalid argument (null, negative or misaligned)";
+    case MLORA_ERR_SHAPE: return "inconsistent shapes";
+    case MLORA_ERR_RANK: return "adapter rank outside [1, R]";
+    case MLORA_ERR_INDEX: return "slot index outside [-1, S)";
+    case MLORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLORA_ERR_HIP: return "HIP error";
+    case MLORA_ERR_UNSUPPORTED: return "outside the supported limits";
+    }
+    return "unknown status";
+}
+
+float mlora_factor(float alpha, int32_t r, int32_t use_rslora)
+{
+    if (r < 1)
+        return NAN;
+    const double a = (double)alpha;
+    return (float)(use_rslora ? a / std::sqrt((double)r) : a / (double)r);
+}
+
+int64_t mlora_slot_bytes(int32_t S, int32_t R, int64_t n_in, int64_t n_out, int32_t n_slices)
+{
+    if (S < 0 || R < 0 || n_in < 0 || n_out < 0 || n_slices < 0)
+        return -1;
+    return (int64_t)S * ((int64_t)n_slices * R * n_in + n_out * (int64_t)R) * 2;
+}
+
+size_t mlora_workspace_size(int64_t T, int32_t K, int64_t n_in, int64_t n_out,
+                            const mlora_slots *slots)
+{
+    if (T < 0 || K < 1 || K > MLORA_MAX_K || n_in <= 0 || n_out <= 0 || slots == nullptr)
+        return 0;
+    SlotGeom g;
+    if (check_slots(slots, n_out, false, &g) != MLORA_OK)
+        return 0;
+    return make_layout(T, K, n_in, n_out, g.S, g.n_slices * g.R).total + 256;
+}
+
+mlora_status mlora_validate(const int32_t *idx, int64_t T, int32_t K, const mlora_slots *slots,
+                            const int32_t *rank, int64_t *bad_value, hipStream_t stream)
+{
+    if (T < 0 || K < 1 || K > MLORA_MAX_K || slots == nullptr || (T > 0 && idx == nullptr))
+        return MLORA_ERR_ARG;
+    if (rank != nullptr)
+        for (int32_t a = 0; a < slots->S; ++a)
+            if (rank[a] < 1 || rank[a] > slots->R) {
+                if (bad_value)
+                    *bad_value = rank[a];
+                return MLORA_ERR_RANK;
+            }
+    if (T == 0)
+        return MLORA_OK;
+    std::vector<int32_t> h((size_t)(T * K));
+    if (hipMemcpyAsync(h.data(), idx, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                       stream) != hipSuccess)
+        return hip_status(hipGetLastError(), "copy of idx");
+    if (hipError_t e = hipStreamSynchronize(stream); e != hipSuccess)
+        return hip_status(e, "stream synchronize");
+    for (int32_t v : h)
+        if (v < -1 || v >= slots->S) {
+            if (bad_value)
+                *bad_value = v;
+            return MLORA_ERR_INDEX;
+        }
+    return MLORA_OK;
+}
+
+mlora_status mlora_plan(const int32_t *idx, int64_t T, int32_t K, int32_t S, int32_t *perm,
+                        int32_t *seg_slot, int32_t *seg_start, int32_t *seg_len,
+                        int32_t *counts, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (T < 0 || K < 1 || K > MLORA_MAX_K || S < 1 || S > MLORA_MAX_SLOTS)
+        return T < 0 || K < 1 ? MLORA_ERR_ARG : MLORA_ERR_UNSUPPORTED;
+    if (counts == nullptr || seg_slot == nullptr || seg_start == nullptr || seg_len == nullptr)
+        return MLORA_ERR_ARG;
+    if (T > 0 && (idx == nullptr || perm == nullptr))
+        return MLORA_ERR_ARG;
+    if ((int64_t)T * K > INT32_MAX)
+        return MLORA_ERR_UNSUPPORTED;
+    const size_t need = sort_workspace_bytes(T * K, S);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return MLORA_ERR_WORKSPACE;
+    return hip_status(launch_stable_sort(idx, T * K, S, perm, seg_slot, seg_start, seg_len,
+                                         counts, (int32_t *)ws, stream));
+}
+
+mlora_status mlora_shrink(const void *x, int64_t T, int64_t n_in, const mlora_slots *slots,
+                          const int32_t *idx, int32_t K, const float *scale, float *v, void *ws,
+                          size_t ws_bytes, hipStream_t stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    if (T < 0 || n_in <= 0 || K < 1 || K > MLORA_MAX_K)
+        return MLORA_ERR_ARG;
+    if (n_in % 8 != 0)
+        return MLORA_ERR_SHAPE;
+    if (slots == nullptr)
+        return MLORA_ERR_ARG;
+    SlotGeom g;
+    // the slice table is irrelevant to shrink: take a view with one output row per slice
+    mlora_slots s1 = *slots;
+    std::memset(s1.slice_start, 0, sizeof s1.slice_start);
+    for (int i = 1; i <= s1.n_slices && i <= MLORA_MAX_SLICES; ++i)
+        s1.slice_start[i] = i;
+    mlora_status st = check_slots(&s1, s1.n_slices, true, &g);
+    if (st != MLORA_OK)
+        return st;
+    if (T == 0)
+        return MLORA_OK;
+    if (x == nullptr || idx == nullptr || v == nullptr || !aligned16(x) || !aligned16(v))
+        return MLORA_ERR_ARG;
+    return hip_status(launch_shrink_pairs((const uint16_t *)x, T, n_in, g, idx, K, scale, v,
+                                          stream));
+}
+
+mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_slots *slots,
+                          const int32_t *idx, int32_t K, void *y, hipStream_t stream)
+{
+    if (T < 0 || n_out <= 0 || K < 1 || K > MLORA_MAX_K)
+        return MLORA_ERR_ARG;
+    SlotGeom g;
+    mlora_status st = check_slots(slots, n_out, true, &g);
+    if (st != MLORA_OK)
+        return st;
+    if (T == 0)
+        return MLORA_OK;
+    if (v == nullptr || idx == nullptr || y == nullptr || !aligned16(v) || !aligned16(y))
+        return MLORA_ERR_ARG;
+    return hip_status(launch_expand_tokens(v, T, n_out, g, idx, K, nullptr, 0, (uint16_t *)y,
+                                           stream));
+}
+
+mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in, int64_t n_out,
+                          const mlora_slots *slots, const int32_t *idx, int32_t K,
+                          const float *scale, void *y, uint32_t flags, void *ws, size_t ws_bytes,
+                          hipStream_t stream)
+{
+    if (T < 0 || n_in <= 0 || n_out <= 0 || K < 1 || K > MLORA_MAX_K)
+        return MLORA_ERR_ARG;
+    if (n_in % 8 != 0)
+        return MLORA_ERR_SHAPE;
+    if (n_in > INT32_MAX / 2 || n_out > INT32_MAX / 2)
+        return MLORA_ERR_UNSUPPORTED;
+    const bool lora = (flags & MLORA_NO_ADAPTERS) == 0;
+    SlotGeom g;
+    std::memset(&g, 0, sizeof g);
+    int32_t S = 1, wd = 8;
+    if (lora || slots != nullptr) {
+        mlora_status st = check_slots(slots, n_out, lora, &g);
+        if (st != MLORA_OK)
+            return st;
+        S = g.S;
+        wd = g.n_slices * g.R;
+    }
+    if (T == 0)
+        return MLORA_OK;
+    if (x == nullptr || W == nullptr || y == nullptr || !aligned16(x) || !aligned16(W) ||
+        !aligned16(y))
+        return MLORA_ERR_ARG;
+    if (lora && idx == nullptr)
+        return MLORA_ERR_ARG;
+    const Layout L = make_layout(T, K, n_in, n_out, S, wd);
+    if (ws == nullptr || ws_bytes < L.total)
+        return MLORA_ERR_WORKSPACE;
+    uint8_t *wsb = (uint8_t *)ws;
+    if (!aligned16(wsb))
+        return MLORA_ERR_ARG;
+    float *v = (float *)(wsb + L.off_v);
+    float *part = (float *)(wsb + L.off_part);
+    const uint16_t *xb = (const uint16_t *)x;
+    uint16_t *yb = (uint16_t *)y;
+    // Token chunks of at most DECODE_MAX_T go through the decode kernels.
+    for (int64_t t0 = 0; t0 < T; t0 += DECODE_MAX_T) {
+        const int64_t Tc = std::min<int64_t>(DECODE_MAX_T, T - t0);
+        const DecodeCfg cfg = decode_config(Tc, n_in, n_out);
+        const int32_t *idx_c = lora ? idx + t0 * K : nullptr;
+        const float *scale_c = (lora && scale) ? scale + t0 * K : nullptr;
+        hipError_t e = launch_decode_gemm(xb + t0 * n_in, (const uint16_t *)W, Tc, n_in, n_out,
+                                          part, cfg, lora ? &g : nullptr, idx_c, K, scale_c,
+                                          lora ? v : nullptr, stream);
+        if (e != hipSuccess)
+            return hip_status(e, "decode gemm launch");
+        e = launch_expand_tokens(v, Tc, n_out, g, idx_c, lora ? K : 0, part, cfg.sk,
+                                 yb + t0 * n_out, stream);
+        if (e != hipSuccess)
+            return hip_status(e, "expand launch");
+    }
+    return MLORA_OK;
+}
+
+}  // extern "C"

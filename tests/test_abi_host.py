@@ -1,0 +1,141 @@
+"""The C-ABI library on the host: it loads, exports every function include/mlora.h declares,
+its host helpers agree with the pages' numbers, and argument checks return their status codes
+before any HIP call (nothing here touches a GPU)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    from lora_serving_amd import mlora
+    return mlora
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "mlora.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mlora_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(m):
+    names = header_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(m._lib, name), name
+    assert set(names) == set(m.EXPORTS)
+
+
+def test_factor_matches_page_values(m):
+    with open(os.path.join(ROOT, "tests", "golden", "rslora.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        assert m.mlora_factor(c["alpha"], c["r"], c["rslora"]) == c["factor"]
+    assert m.mlora_factor(16, 0, 0) != m.mlora_factor(16, 0, 0)  # NaN for r < 1
+
+
+def test_slot_bytes_matches_page_sizing(m):
+    with open(os.path.join(ROOT, "tests", "golden", "sizing.json")) as fh:
+        g = json.load(fh)
+    mods = g["model"]["modules"]
+
+    def adapter(rank, slots=1):
+        return g["model"]["layers"] * sum(m.mlora_slot_bytes(slots, rank, i, o, 1)
+                                          for i, o in mods.values())
+
+    for r, mib in g["printed"]["adapter_MiB_0dp"].items():
+        assert round(adapter(int(r)) / 2 ** 20) == mib
+    for slots, rank, gib in g["printed"]["slots_GiB_2dp"]:
+        assert round(adapter(rank, slots) / 2 ** 30, 2) == gib
+    assert m.mlora_slot_bytes(-1, 16, 1, 1, 1) == -1
+
+
+def slots_struct(m, S=4, R=16, n_slices=1, starts=None, A=0x1000, B=0x2000, f=0x3000):
+    st = (ctypes.c_int32 * 5)(*(starts or [0, 0, 0, 0, 0]))
+    return m.mlora_slots(A, B, f, S, R, n_slices, st)
+
+
+def test_workspace_size(m):
+    s = slots_struct(m)
+    assert m._lib.mlora_workspace_size(64, 1, 4096, 4096, ctypes.byref(s)) > 0
+    assert m._lib.mlora_workspace_size(-1, 1, 4096, 4096, ctypes.byref(s)) == 0
+    assert m._lib.mlora_workspace_size(64, 0, 4096, 4096, ctypes.byref(s)) == 0
+    bad = slots_struct(m, R=24)
+    assert m._lib.mlora_workspace_size(64, 1, 4096, 4096, ctypes.byref(bad)) == 0
+
+
+def call_linear(m, slots, T=8, n_in=64, n_out=32, K=1, x=0x10000, W=0x20000, y=0x30000,
+                idx=0x40000, ws=None, ws_bytes=0, flags=0):
+    sp = None if slots is None else ctypes.byref(slots)
+    return m._lib.mlora_linear(x, W, T, n_in, n_out, sp, idx, K, None, y, flags, ws, ws_bytes,
+                               None)
+
+
+def test_linear_argument_checks(m):
+    s = slots_struct(m)
+    assert call_linear(m, s, T=-1) == m.MLORA_ERR_ARG
+    assert call_linear(m, s, K=0) == m.MLORA_ERR_ARG
+    assert call_linear(m, s, K=9) == m.MLORA_ERR_ARG
+    assert call_linear(m, s, n_in=60) == m.MLORA_ERR_SHAPE
+    assert call_linear(m, None) == m.MLORA_ERR_ARG
+    assert call_linear(m, slots_struct(m, R=24)) == m.MLORA_ERR_UNSUPPORTED
+    assert call_linear(m, slots_struct(m, R=1024)) == m.MLORA_ERR_UNSUPPORTED
+    assert call_linear(m, slots_struct(m, S=0)) == m.MLORA_ERR_UNSUPPORTED
+    assert call_linear(m, slots_struct(m, n_slices=5)) == m.MLORA_ERR_UNSUPPORTED
+    assert call_linear(m, slots_struct(m, n_slices=2, starts=[0, 40, 32, 0, 0])) == \
+        m.MLORA_ERR_SHAPE
+    assert call_linear(m, slots_struct(m, n_slices=2, starts=[0, 16, 31, 0, 0])) == \
+        m.MLORA_ERR_SHAPE
+    assert call_linear(m, slots_struct(m, A=0)) == m.MLORA_ERR_ARG
+    assert call_linear(m, slots_struct(m, A=0x1008)) == m.MLORA_ERR_ARG   # misaligned
+    assert call_linear(m, s, x=0) == m.MLORA_ERR_ARG
+    assert call_linear(m, s, y=0x30002) == m.MLORA_ERR_ARG
+    assert call_linear(m, s, idx=0) == m.MLORA_ERR_ARG
+    assert call_linear(m, s) == m.MLORA_ERR_WORKSPACE          # no workspace
+    assert call_linear(m, s, ws=0x50000, ws_bytes=16) == m.MLORA_ERR_WORKSPACE
+    assert call_linear(m, s, T=0) == m.MLORA_OK                # T = 0 is a no-op
+    # base-only hint needs no slots and no index map, but still a workspace
+    assert call_linear(m, None, idx=0, flags=m.MLORA_NO_ADAPTERS) == m.MLORA_ERR_WORKSPACE
+
+
+def test_other_entry_points_argument_checks(m):
+    s = slots_struct(m)
+    L = m._lib
+    assert L.mlora_shrink(0x1000, -1, 64, ctypes.byref(s), 0x2000, 1, None, 0x3000, None, 0,
+                          None) == m.MLORA_ERR_ARG
+    assert L.mlora_shrink(0x1000, 4, 60, ctypes.byref(s), 0x2000, 1, None, 0x3000, None, 0,
+                          None) == m.MLORA_ERR_SHAPE
+    assert L.mlora_shrink(0x1000, 4, 64, None, 0x2000, 1, None, 0x3000, None, 0, None) == \
+        m.MLORA_ERR_ARG
+    assert L.mlora_shrink(0, 4, 64, ctypes.byref(s), 0x2000, 1, None, 0x3000, None, 0, None) == \
+        m.MLORA_ERR_ARG
+    assert L.mlora_expand(0x1000, 4, 32, ctypes.byref(s), 0x2000, 0, 0x3000, None) == \
+        m.MLORA_ERR_ARG
+    assert L.mlora_expand(0, 4, 32, ctypes.byref(s), 0x2000, 1, 0x3000, None) == m.MLORA_ERR_ARG
+    assert L.mlora_plan(0x1000, 4, 1, 0, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, 1 << 20,
+                        None) == m.MLORA_ERR_UNSUPPORTED
+    assert L.mlora_plan(0x1000, 4, 1, 4, 0x2000, 0x3000, 0x4000, 0x5000, None, 0x7000, 1 << 20,
+                        None) == m.MLORA_ERR_ARG
+    assert L.mlora_plan(0x1000, 4, 1, 4, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None, 0,
+                        None) == m.MLORA_ERR_WORKSPACE
+    bad = ctypes.c_int64(0)
+    rk = (ctypes.c_int32 * 4)(8, 16, 17, 4)
+    assert L.mlora_validate(0x1000, 0, 1, ctypes.byref(s), rk, ctypes.byref(bad), None) == \
+        m.MLORA_ERR_RANK
+    assert bad.value == 17
+    rk0 = (ctypes.c_int32 * 4)(8, 0, 16, 4)
+    assert L.mlora_validate(0x1000, 0, 1, ctypes.byref(s), rk0, ctypes.byref(bad), None) == \
+        m.MLORA_ERR_RANK
+    ok = (ctypes.c_int32 * 4)(8, 16, 16, 4)
+    assert L.mlora_validate(0x1000, 0, 1, ctypes.byref(s), ok, None, None) == m.MLORA_OK
+
+
+def test_status_strings(m):
+    for code in range(8):
+        assert m.mlora_status_string(code)
+    assert m.mlora_status_string(99) == "unknown status"

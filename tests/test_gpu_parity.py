@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs.
+
+Acceptance (floating point): |y - y_ref| <= 2e-2 (1 + |y_ref|) elementwise, on the whole layer
+and on the LoRA delta alone (shrink, then expand into a zero y), so a wrong delta cannot hide
+under a large W x.  The mapping plan must match bit-exactly.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from lora_serving_amd import synth
+from tests.gpu_util import DevLayer, from_dev_bf16, tol_ok, worst
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lora_serving_amd import mlora  # noqa: F401  (fails loudly if the library is missing)
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_linear(oracle_mod, L, tokens=None, label=""):
+    say(f"[linear] {label} T={L.T} n_in={L.n_in} n_out={L.n_out} K={L.K} S={L.S} R={L.R} "
+        f"slices={L.n_slices}")
+    D = DevLayer(L)
+    y = from_dev_bf16(D.linear())
+    if tokens is None:
+        y_ref = oracle_mod.linear(L)
+        yy = y
+    else:
+        y_ref = oracle_mod.linear(L, tokens=tokens)
+        yy = y[tokens]
+    ok = tol_ok(yy, y_ref)
+    assert ok.all(), f"{label}: worst {worst(yy, y_ref):.3e}, {np.sum(~ok)} elements out"
+    return D, y
+
+
+def check_delta(oracle_mod, L, D=None, tokens=None, label=""):
+    say(f"[delta] {label} T={L.T} K={L.K}")
+    D = D or DevLayer(L)
+    d = from_dev_bf16(D.delta())
+    d_ref = oracle_mod.linear(L, tokens=tokens, with_base=False)
+    dd = d if tokens is None else d[tokens]
+    ok = tol_ok(dd, d_ref)
+    assert ok.all(), f"{label}: delta worst {worst(dd, d_ref):.3e}"
+    assert np.any(d_ref != 0) == np.any(dd != 0)
+    return d
+
+
+# ------------------------------------------------------------------------------------------
+SMALL = [
+    # seed, T, n_in, n_out, S, R, K, slices
+    (1, 1, 64, 48, 3, 8, 1, None),
+    (2, 17, 256, 200, 5, 16, 2, None),
+    (3, 64, 512, 520, 7, 16, 3, [260, 130, 130]),
+    (4, 100, 392, 136, 4, 64, 1, [64, 72]),
+    (5, 128, 1024, 1000, 9, 32, 2, None),
+    (6, 129, 320, 264, 6, 16, 3, [200, 32, 32]),
+    (7, 300, 2056, 136, 11, 8, 1, None),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{c[0]}" for c in SMALL])
+def test_linear_and_delta_small(oracle_mod, case):
+    seed, T, n_in, n_out, S, R, K, slices = case
+    L = synth.random_layer(seed, T=T, n_in=n_in, n_out=n_out, S=S, R=R, K=K, slice_sizes=slices,
+                           p_sentinel=0.25)
+    D, _ = check_linear(oracle_mod, L, label=f"small{seed}")
+    check_delta(oracle_mod, L, D, label=f"small{seed}")
+
+
+def test_shrink_matches_oracle(oracle_mod):
+    L = synth.random_layer(21, T=33, n_in=1024, n_out=96, S=6, R=16, K=3,
+                           slice_sizes=[32, 32, 32], p_sentinel=0.3)
+    D = DevLayer(L)
+    v = D.shrink().cpu().numpy().astype(np.float64)
+    v_ref = oracle_mod.shrink(L)
+    scale = np.abs(v_ref).max()
+    assert np.all(np.abs(v - v_ref) <= 1e-4 * (scale + np.abs(v_ref)))
+    # pairs holding -1 are exactly zero
+    for t in range(L.T):
+        for j in range(L.K):
+            if L.idx[t, j] == -1:
+                assert np.all(v[j, t] == 0)
+
+
+def test_tiny_workload(oracle_mod):
+    L = synth.workload_tiny()
+    D, _ = check_linear(oracle_mod, L, label="tiny")
+    check_delta(oracle_mod, L, D, label="tiny")
+
+
+def test_decode_workload_full(oracle_mod):
+    L = synth.workload_decode()
+    D, _ = check_linear(oracle_mod, L, label="decode")
+    check_delta(oracle_mod, L, D, label="decode")
+
+
+def _sample_tokens(L, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    edges = set()
+    for first, length in L.segments:
+        edges.add(first)
+        edges.add(first + length - 1)
+    edges = sorted(edges)
+    extra = rng.choice(L.T, size=min(n, L.T), replace=False)
+    toks = sorted(set(edges[:: max(1, len(edges) // n)]) | set(int(e) for e in extra)
+                  | {0, L.T - 1})
+    return np.array(toks, np.int64)
+
+
+@pytest.mark.parametrize("which", ["prefill", "mixed_qkv", "compose"])
+def test_large_workloads_sampled(oracle_mod, which):
+    layers = synth.WORKLOADS[which]()
+    if not isinstance(layers, list):
+        layers = [layers]
+    for L in layers:
+        toks = _sample_tokens(L)
+        check_linear(oracle_mod, L, tokens=toks, label=f"{which}:{L.name}")
+
+
+# ------------------------------------------------------------------------------------------
+# invariants
+# ------------------------------------------------------------------------------------------
+def test_sentinel_rows_equal_base_only_run():
+    L = synth.random_layer(31, T=90, n_in=512, n_out=384, S=5, R=16, K=2, p_sentinel=0.3)
+    L.idx[::3] = -1
+    D = DevLayer(L)
+    y = D.linear()
+    y0 = D.linear(flags=1)
+    rows = np.where(np.all(L.idx == -1, axis=1))[0]
+    assert len(rows) > 0
+    a = from_dev_bf16(y)[rows]
+    b = from_dev_bf16(y0)[rows]
+    assert np.array_equal(a, b)
+
+
+def test_all_sentinel_batch_equals_no_adapters_flag():
+    L = synth.random_layer(32, T=64, n_in=256, n_out=256, S=3, R=8, K=1)
+    L.idx[:] = -1
+    D = DevLayer(L)
+    assert np.array_equal(from_dev_bf16(D.linear()), from_dev_bf16(D.linear(flags=1)))
+
+
+def test_k3_with_sentinels_equals_k1():
+    L1 = synth.random_layer(33, T=70, n_in=512, n_out=320, S=6, R=16, K=1, p_sentinel=0.2)
+    y1 = from_dev_bf16(DevLayer(L1).linear())
+    for pos in range(3):
+        L3 = synth.random_layer(33, T=70, n_in=512, n_out=320, S=6, R=16, K=1, p_sentinel=0.2)
+        idx = np.full((L1.T, 3), -1, np.int32)
+        idx[:, pos] = L1.idx[:, 0]
+        sc = np.ones((L1.T, 3), np.float32)
+        sc[:, pos] = L1.scale[:, 0]
+        L3.idx, L3.scale, L3.K = idx, sc, 3
+        assert np.array_equal(from_dev_bf16(DevLayer(L3).linear()), y1), pos
+
+
+def test_run_to_run_bits_identical():
+    import torch
+    L = synth.workload_decode(seed=77)
+    D = DevLayer(L)
+    a = D.linear().view(torch.int16).cpu().numpy()
+    b = D.linear().view(torch.int16).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+def test_t_zero_is_noop():
+    import torch
+    from lora_serving_amd import mlora
+    L = synth.random_layer(34, T=4, n_in=64, n_out=32, S=2, R=8, K=1)
+    D = DevLayer(L)
+    y = torch.full((0, 32), 1.0, dtype=torch.bfloat16, device="cuda")
+    mlora.mlora_linear(D.x[:0], D.W, D.slots, D.idx[:0], None, y, ws=D.ws)
+
+
+# ------------------------------------------------------------------------------------------
+# plan
+# ------------------------------------------------------------------------------------------
+PLAN_CASES = [(0, 1, 1, 1), (1, 6, 1, 4), (2, 64, 1, 100), (3, 1000, 3, 7), (4, 16384, 1, 100),
+              (5, 8192, 3, 32), (6, 3000, 2, 16384), (7, 0, 1, 5), (8, 5000, 8, 1)]
+
+
+@pytest.mark.parametrize("case", PLAN_CASES, ids=[f"p{c[0]}" for c in PLAN_CASES])
+def test_plan_bit_exact(oracle_mod, case):
+    import torch
+    from lora_serving_amd import mlora
+    seed, T, K, S = case
+    say(f"[plan] seed={seed} T={T} K={K} S={S}")
+    rng = np.random.default_rng(seed)
+    if seed == 1:
+        idx = np.array([2, 0, -1, 2, 3, 0], np.int32)[:, None]
+    elif seed == 4:
+        idx = synth.workload_prefill().idx
+    else:
+        idx = rng.integers(-1, S, size=(T, K)).astype(np.int32)
+    perm_r, ss_r, st_r, sl_r = oracle_mod.plan(idx, S)
+    dev = lambda n: torch.full((max(n, 1),), -7, dtype=torch.int32, device="cuda")
+    perm, ss, st, sl, cnt = dev(T * K), dev(S), dev(S), dev(S), dev(2)
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx)).cuda()
+    ws = torch.empty(max(1, T * K * S // 256 + 4 * S + 4096) * 4, dtype=torch.uint8, device="cuda")
+    mlora.mlora_plan(idx_d, S, perm, ss, st, sl, cnt, ws)
+    cnt = cnt.cpu().numpy()
+    g, n = int(cnt[0]), int(cnt[1])
+    assert n == len(perm_r) and g == len(ss_r)
+    assert np.array_equal(perm.cpu().numpy()[:n], perm_r)
+    assert np.array_equal(ss.cpu().numpy()[:g], ss_r)
+    assert np.array_equal(st.cpu().numpy()[:g], st_r)
+    assert np.array_equal(sl.cpu().numpy()[:g], sl_r)
+
+
+def test_validate_rejects_bad_index_and_rank():
+    import torch
+    from lora_serving_amd import mlora
+    L = synth.random_layer(35, T=10, n_in=64, n_out=32, S=4, R=16, K=2)
+    D = DevLayer(L)
+    code, _ = mlora.mlora_validate(D.idx, D.slots, rank=L.rank)
+    assert code == mlora.MLORA_OK
+    bad = D.idx.clone()
+    bad[3, 1] = 4
+    code, val = mlora.mlora_validate(bad, D.slots)
+    assert code == mlora.MLORA_ERR_INDEX and val == 4
+    rk = L.rank.copy()
+    rk[2] = 32
+    code, val = mlora.mlora_validate(D.idx, D.slots, rank=rk)
+    assert code == mlora.MLORA_ERR_RANK and val == 32
+    del torch
