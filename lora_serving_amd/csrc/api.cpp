@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -16,7 +17,7 @@ using namespace mlora;
 
 namespace {
 
-constexpr int64_t DECODE_MAX_T = 128;   // batches up to this size take the decode path
+constexpr int64_t DECODE_MAX_T = 64;    // token chunk of the decode kernels
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -68,28 +69,39 @@ mlora_status check_slots(const mlora_slots *s, int64_t n_out, bool need_data, Sl
     return MLORA_OK;
 }
 
-// Workspace layout of one call; every region 256-byte aligned.
+// Workspace layout of one call; every region 256-byte aligned.  The counter words at the
+// start must be zero before the first call (mlora_workspace_init); every call leaves them zero.
 struct Layout {
+    size_t sync = 0;       // uint32 counters of the fused decode kernel
     size_t sort_cnt = 0;   // counting-sort scratch (plan)
-    size_t v = 0;          // fp32 [K][Tc][n_slices*R] shrink output (decode path)
+    size_t v = 0;          // fp32 [sk][K][Tc][n_slices*R] shrink partials (decode path)
     size_t part = 0;       // fp32 partial sums of the decode GEMM
     size_t total = 0;
-    size_t off_sort = 0, off_v = 0, off_part = 0;
+    size_t off_sync = 0, off_sort = 0, off_v = 0, off_part = 0;
 };
+
+constexpr size_t SYNC_BYTES = 64 * 1024;   // fixed, so mlora_workspace_init knows its size
 
 Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t wd)
 {
     Layout L;
+    L.sync = SYNC_BYTES;
     L.sort_cnt = align_up(sort_workspace_bytes(T * K, S));
     const int64_t Tc = std::min<int64_t>(T, DECODE_MAX_T);
-    L.v = align_up((size_t)K * Tc * wd * sizeof(float));
+    const int64_t sk = Tc > 0 ? decode_config(Tc, n_in, n_out).sk : 0;
+    L.v = align_up((size_t)sk * K * Tc * wd * sizeof(float));
     L.part = Tc > 0 ? align_up(decode_partial_bytes(Tc, n_in, n_out)) : 0;
-    L.off_sort = 0;
+    L.off_sync = 0;
+    L.off_sort = L.off_sync + L.sync;
     L.off_v = L.off_sort + L.sort_cnt;
     L.off_part = L.off_v + L.v;
     L.total = L.off_part + L.part;
     return L;
 }
+
+// The fused decode kernel needs every workgroup resident at once (cooperative launch); when
+// the grid does not fit, the two-kernel path runs instead.  Off switch for comparisons.
+bool g_fused_decode_enabled = std::getenv("MLORA_DECODE_TWO_KERNELS") == nullptr;
 
 thread_local char g_last_error[256] = "";
 
@@ -121,6 +133,14 @@ const char *mlora_status_string(mlora_status status)
     case MLORA_ERR_UNSUPPORTED: return "outside the supported limits";
     }
     return "unknown status";
+}
+
+mlora_status mlora_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (ws == nullptr || ws_bytes < SYNC_BYTES || !aligned16(ws))
+        return MLORA_ERR_ARG;
+    return hip_status(launch_zero_words((uint32_t *)ws, SYNC_BYTES / sizeof(uint32_t), stream),
+                      "workspace init");
 }
 
 float mlora_factor(float alpha, int32_t r, int32_t use_rslora)
@@ -239,8 +259,8 @@ mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_
         return MLORA_OK;
     if (v == nullptr || idx == nullptr || y == nullptr || !aligned16(v) || !aligned16(y))
         return MLORA_ERR_ARG;
-    return hip_status(launch_expand_tokens(v, T, n_out, g, idx, K, nullptr, 0, (uint16_t *)y,
-                                           stream));
+    return hip_status(launch_expand_tokens(v, 1, 0, nullptr, T, n_out, g, idx, K, nullptr, 0,
+                                           (uint16_t *)y, stream));
 }
 
 mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in, int64_t n_out,
@@ -278,8 +298,9 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
     uint8_t *wsb = (uint8_t *)ws;
     if (!aligned16(wsb))
         return MLORA_ERR_ARG;
-    float *v = (float *)(wsb + L.off_v);
+    float *upart = (float *)(wsb + L.off_v);
     float *part = (float *)(wsb + L.off_part);
+    uint32_t *sync = (uint32_t *)(wsb + L.off_sync);
     const uint16_t *xb = (const uint16_t *)x;
     uint16_t *yb = (uint16_t *)y;
     // Token chunks of at most DECODE_MAX_T go through the decode kernels.
@@ -288,13 +309,26 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
         const DecodeCfg cfg = decode_config(Tc, n_in, n_out);
         const int32_t *idx_c = lora ? idx + t0 * K : nullptr;
         const float *scale_c = (lora && scale) ? scale + t0 * K : nullptr;
+        if (g_fused_decode_enabled && decode_fused_fits(Tc, K, wd, cfg) &&
+            decode_tiles_fit_sync(n_out) &&
+            decode_sync_words(n_out) * sizeof(uint32_t) <= SYNC_BYTES) {
+            hipError_t e = launch_decode_fused(xb + t0 * n_in, (const uint16_t *)W, Tc, n_in,
+                                               n_out, part, cfg, lora ? &g : nullptr, idx_c, K,
+                                               scale_c, lora ? upart : nullptr, sync,
+                                               yb + t0 * n_out, stream);
+            if (e == hipSuccess)
+                continue;
+            if (e != hipErrorCooperativeLaunchTooLarge && e != hipErrorNotSupported)
+                return hip_status(e, "fused decode launch");
+            (void)hipGetLastError();   // not resident on this device: two-kernel path
+        }
         hipError_t e = launch_decode_gemm(xb + t0 * n_in, (const uint16_t *)W, Tc, n_in, n_out,
-                                          part, cfg, lora ? &g : nullptr, idx_c, K, scale_c,
-                                          lora ? v : nullptr, stream);
+                                          part, cfg, lora ? &g : nullptr, idx_c, K,
+                                          lora ? upart : nullptr, stream);
         if (e != hipSuccess)
             return hip_status(e, "decode gemm launch");
-        e = launch_expand_tokens(v, Tc, n_out, g, idx_c, lora ? K : 0, part, cfg.sk,
-                                 yb + t0 * n_out, stream);
+        e = launch_expand_tokens(upart, cfg.sk, 1, scale_c, Tc, n_out, g, idx_c, lora ? K : 0,
+                                 part, cfg.sk, yb + t0 * n_out, stream);
         if (e != hipSuccess)
             return hip_status(e, "expand launch");
     }

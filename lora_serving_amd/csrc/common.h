@@ -83,4 +83,12 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int *total)
     return incl - v;
 }
 
+// s_barrier that waits only for this wave's LDS operations, not for its outstanding global
+// loads (a __syncthreads fence waits for every outstanding memory operation); the "memory"
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace mlora

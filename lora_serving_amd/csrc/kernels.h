@@ -7,6 +7,9 @@
 namespace mlora {
 
 constexpr int SORT_UNIT = 1024;   // entries per wave in the counting sort
+constexpr int MLORA_MAX_SLICES_DEV = 4;
+constexpr int MLORA_MAX_RANK_DEV = 512;
+constexpr int MLORA_MAX_K_DEV = 8;
 
 // ---- plan.hip ----------------------------------------------------------------------------
 size_t sort_workspace_bytes(int64_t n, int32_t nkeys);
@@ -28,13 +31,17 @@ struct SlotGeom {
 hipError_t launch_shrink_pairs(const uint16_t *x, int64_t T, int64_t n_in, const SlotGeom &g,
                                const int32_t *idx, int32_t K, const float *scale, float *v,
                                hipStream_t stream);
-// y[t][n] = bf16(base + delta): base = y (accumulate) or the sum of n_part fp32 partials
-// part[n_part][T][n_out]; rows whose slots are all -1 get exactly base.
-hipError_t launch_expand_tokens(const float *v, int64_t T, int64_t n_out, const SlotGeom &g,
+// One workgroup per (token, 1024 output rows):
+//   v_j = coef_j * sum_{s < n_vsplit} vsrc[s][j][t][:], coef_j = scale[t][j]*factor[a] if
+//   apply_coef else 1;  y[t][n] = bf16(base + sum_j B[a_j][n][:] . v_j[slice(n)]), where
+//   base = y[t][n] (accumulate mode, part == nullptr; rows with no adapter untouched) or the sum
+//   of n_part fp32 partials part[s][t][n].
+hipError_t launch_expand_tokens(const float *vsrc, int n_vsplit, int apply_coef,
+                                const float *scale, int64_t T, int64_t n_out, const SlotGeom &g,
                                 const int32_t *idx, int32_t K, const float *part, int32_t n_part,
                                 uint16_t *y, hipStream_t stream);
 
-// ---- gemm_decode.hip: skinny base GEMM for T <= 128 -------------------------------------------
+// ---- gemm_decode.hip: skinny base GEMM for T <= 64 -------------------------------------------
 struct DecodeCfg {
     int tt;        // token tiles of 16
     int sk;        // split of n_in across workgroups
@@ -43,11 +50,22 @@ struct DecodeCfg {
 };
 DecodeCfg decode_config(int64_t T, int64_t n_in, int64_t n_out);
 size_t decode_partial_bytes(int64_t T, int64_t n_in, int64_t n_out);
-// part[sk][T][n_out] = x[:, krange] W[:, krange]^T ; if v != nullptr the same launch also runs
-// the per-pair shrink (horizontal fusion: no dependency between the two halves).
+// part[s][t][n] = x[t, split s] . W[n, split s]; with upart != nullptr the same launch writes
+// the unscaled shrink partials upart[s][j][t][0:n_slices*R] of every pair (-1 pairs skipped).
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, int64_t T, int64_t n_in,
                               int64_t n_out, float *part, const DecodeCfg &cfg,
-                              const SlotGeom *g, const int32_t *idx, int32_t K,
-                              const float *scale, float *v, hipStream_t stream);
+                              const SlotGeom *g, const int32_t *idx, int32_t K, float *upart,
+                              hipStream_t stream);
+// Whole decode layer in one cooperative launch: y = bf16(W x + LoRA delta).  sync: counter
+// words (decode_sync_words), zero on entry and left zero on exit.  g == nullptr: base only.
+size_t decode_sync_words(int64_t n_out);
+bool decode_tiles_fit_sync(int64_t n_out);
+bool decode_fused_fits(int64_t T, int32_t K, int32_t wd, const DecodeCfg &cfg);
+hipError_t launch_decode_fused(const uint16_t *x, const uint16_t *W, int64_t T, int64_t n_in,
+                               int64_t n_out, float *part, const DecodeCfg &cfg, const SlotGeom *g,
+                               const int32_t *idx, int32_t K, const float *scale, float *upart,
+                               uint32_t *sync, uint16_t *y, hipStream_t stream);
+// zero fill of n 32-bit words (a kernel, not a memset node)
+hipError_t launch_zero_words(uint32_t *p, size_t n, hipStream_t stream);
 
 }  // namespace mlora
