@@ -105,12 +105,15 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()     # the stream the library launches on
+
+    # timed region: K steps back to back, one event pair around all of them
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    ev0.record()
+    ev0.record(stream)
     for i in range(args.steps):
         step(i)
-    ev1.record()
+    ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
     tokens_per_s = L.T / (ms * 1e-3)
@@ -127,7 +130,8 @@ def main():
                    "distinct_adapters": alg["distinct_adapters"], "rotating_sets": nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "scope": "whole step"},
+                     "scope": "whole step (all kernels of the layer)",
+                     "algorithmic_bytes": alg["bytes"]},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)

@@ -99,9 +99,10 @@ Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S,
     return L;
 }
 
-// The fused decode kernel needs every workgroup resident at once (cooperative launch); when
-// the grid does not fit, the two-kernel path runs instead.  Off switch for comparisons.
-bool g_fused_decode_enabled = std::getenv("MLORA_DECODE_TWO_KERNELS") == nullptr;
+// The one-launch decode kernel needs every workgroup resident at once (checked against the
+// device's occupancy); it is opt-in (MLORA_DECODE_FUSED=1) while it is slower than the
+// two-kernel path on MI355X.
+bool g_fused_decode_enabled = std::getenv("MLORA_DECODE_FUSED") != nullptr;
 
 thread_local char g_last_error[256] = "";
 
