@@ -66,6 +66,8 @@ typedef enum {
 
 /* flags of mlora_linear */
 #define MLORA_NO_ADAPTERS 1u      /* host hint: no token uses an adapter; run the base only    */
+#define MLORA_PATH_DECODE 2u      /* force the decode kernels (token chunks of 64)             */
+#define MLORA_PATH_TILED 4u       /* force the tiled prefill kernels (256-token tiles)         */
 
 /*
  * The adapter slot set of ONE layer: S slots, each R wide (R = max_lora_rank), an adapter of
@@ -177,7 +179,10 @@ mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_
  *   x  bf16 [T][n_in];  W  bf16 [n_out][n_in] (row n is output n);  y  bf16 [T][n_out] (out)
  *   idx, scale as in mlora_shrink.  slots may be NULL only with MLORA_NO_ADAPTERS.
  * With flags & MLORA_NO_ADAPTERS no LoRA kernel is launched (y = bf16(W x)); without it, an
- * all-sentinel map gives the same values.  T = 0 is a no-op.
+ * all-sentinel map gives the same values.  T = 0 is a no-op.  By default the library picks
+ * the decode kernels for small batches and the tiled kernels when the batch fills the GPU
+ * with 256 x 256 output tiles; MLORA_PATH_DECODE / MLORA_PATH_TILED force one (both set:
+ * MLORA_ERR_ARG).  mlora_workspace_size() covers either path.
  */
 mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in, int64_t n_out,
                           const mlora_slots *slots, const int32_t *idx, int32_t K,

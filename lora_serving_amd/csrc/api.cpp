@@ -76,17 +76,23 @@ struct Layout {
     size_t sort_cnt = 0;   // counting-sort scratch (plan)
     size_t v = 0;          // fp32 [sk][K][Tc][n_slices*R] shrink partials (decode path)
     size_t part = 0;       // fp32 partial sums of the decode GEMM
+    size_t pre = 0;        // prefill path: tile lists and V blocks
     size_t total = 0;
-    size_t off_sync = 0, off_sort = 0, off_v = 0, off_part = 0;
+    size_t off_sync = 0, off_sort = 0, off_v = 0, off_part = 0, off_pre = 0;
 };
 
 constexpr size_t SYNC_BYTES = 64 * 1024;   // fixed, so mlora_workspace_init knows its size
 
-Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t wd)
+// Regions for both paths, so one workspace size serves any flags.
+Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t R,
+                   int32_t n_slices)
 {
     Layout L;
+    const int32_t wd = n_slices * R;
     L.sync = SYNC_BYTES;
     L.sort_cnt = align_up(sort_workspace_bytes(T * K, S));
+    if (T > 0)
+        L.pre = align_up(prefill_workspace_bytes(prefill_config(T, K, n_in, n_out, S, R, n_slices)));
     const int64_t Tc = std::min<int64_t>(T, DECODE_MAX_T);
     const int64_t sk = Tc > 0 ? decode_config(Tc, n_in, n_out).sk : 0;
     L.v = align_up((size_t)sk * K * Tc * wd * sizeof(float));
@@ -95,7 +101,8 @@ Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S,
     L.off_sort = L.off_sync + L.sync;
     L.off_v = L.off_sort + L.sort_cnt;
     L.off_part = L.off_v + L.v;
-    L.total = L.off_part + L.part;
+    L.off_pre = L.off_part + L.part;
+    L.total = L.off_pre + L.pre;
     return L;
 }
 
@@ -167,7 +174,7 @@ size_t mlora_workspace_size(int64_t T, int32_t K, int64_t n_in, int64_t n_out,
     SlotGeom g;
     if (check_slots(slots, n_out, false, &g) != MLORA_OK)
         return 0;
-    return make_layout(T, K, n_in, n_out, g.S, g.n_slices * g.R).total + 256;
+    return make_layout(T, K, n_in, n_out, g.S, g.R, g.n_slices).total + 256;
 }
 
 mlora_status mlora_validate(const int32_t *idx, int64_t T, int32_t K, const mlora_slots *slots,
@@ -271,6 +278,8 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
 {
     if (T < 0 || n_in <= 0 || n_out <= 0 || K < 1 || K > MLORA_MAX_K)
         return MLORA_ERR_ARG;
+    if ((flags & MLORA_PATH_DECODE) && (flags & MLORA_PATH_TILED))
+        return MLORA_ERR_ARG;
     if (n_in % 8 != 0)
         return MLORA_ERR_SHAPE;
     if (n_in > INT32_MAX / 2 || n_out > INT32_MAX / 2)
@@ -278,13 +287,15 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
     const bool lora = (flags & MLORA_NO_ADAPTERS) == 0;
     SlotGeom g;
     std::memset(&g, 0, sizeof g);
-    int32_t S = 1, wd = 8;
+    int32_t S = 1, wd = 8, R = 8, n_slices = 1;
     if (lora || slots != nullptr) {
         mlora_status st = check_slots(slots, n_out, lora, &g);
         if (st != MLORA_OK)
             return st;
         S = g.S;
-        wd = g.n_slices * g.R;
+        R = g.R;
+        n_slices = g.n_slices;
+        wd = n_slices * R;
     }
     if (T == 0)
         return MLORA_OK;
@@ -293,7 +304,7 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
         return MLORA_ERR_ARG;
     if (lora && idx == nullptr)
         return MLORA_ERR_ARG;
-    const Layout L = make_layout(T, K, n_in, n_out, S, wd);
+    const Layout L = make_layout(T, K, n_in, n_out, S, R, n_slices);
     if (ws == nullptr || ws_bytes < L.total)
         return MLORA_ERR_WORKSPACE;
     uint8_t *wsb = (uint8_t *)ws;
@@ -304,6 +315,15 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
     uint32_t *sync = (uint32_t *)(wsb + L.off_sync);
     const uint16_t *xb = (const uint16_t *)x;
     uint16_t *yb = (uint16_t *)y;
+    const bool force_decode = (flags & MLORA_PATH_DECODE) != 0;
+    const bool force_tiled = (flags & MLORA_PATH_TILED) != 0;
+    if (force_tiled || (!force_decode && prefill_worth_it(T, n_out))) {
+        const PrefillCfg pc = prefill_config(T, K, n_in, n_out, S, R, n_slices);
+        return hip_status(launch_prefill(xb, (const uint16_t *)W, T, n_in, n_out,
+                                         lora ? &g : nullptr, idx, K, scale, yb, pc,
+                                         wsb + L.off_pre, stream),
+                          "prefill launch");
+    }
     // Token chunks of at most DECODE_MAX_T go through the decode kernels.
     for (int64_t t0 = 0; t0 < T; t0 += DECODE_MAX_T) {
         const int64_t Tc = std::min<int64_t>(DECODE_MAX_T, T - t0);

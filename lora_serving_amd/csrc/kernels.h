@@ -68,4 +68,20 @@ hipError_t launch_decode_fused(const uint16_t *x, const uint16_t *W, int64_t T, 
 // zero fill of n 32-bit words (a kernel, not a memset node)
 hipError_t launch_zero_words(uint32_t *p, size_t n, hipStream_t stream);
 
+// ---- gemm_prefill.hip: tiled MFMA GEMM with the LoRA delta as extra K-steps ---------------
+struct PrefillCfg {
+    int n_mtiles, n_ntiles;   // 256-token x 256-row output tiles
+    int list_stride;          // max distinct adapters per token tile
+    int64_t vcat_tile_elems;  // bf16 elements of one tile's V block
+};
+PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t R,
+                          int32_t n_slices);
+size_t prefill_workspace_bytes(const PrefillCfg &c);
+bool prefill_worth_it(int64_t T, int64_t n_out);
+// y = bf16(x W^T + LoRA delta); g == nullptr: base only.  ws: prefill_workspace_bytes(c).
+hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64_t n_in,
+                          int64_t n_out, const SlotGeom *g, const int32_t *idx, int32_t K,
+                          const float *scale, uint16_t *y, const PrefillCfg &c, void *ws,
+                          hipStream_t stream);
+
 }  // namespace mlora

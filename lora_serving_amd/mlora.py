@@ -28,6 +28,8 @@ MLORA_MAX_RANK = 512
 MLORA_MAX_SLOTS = 16384
 MLORA_MAX_K = 8
 MLORA_NO_ADAPTERS = 1
+MLORA_PATH_DECODE = 2
+MLORA_PATH_TILED = 4
 
 EXPORTS = ("mlora_status_string", "mlora_last_error", "mlora_factor", "mlora_slot_bytes",
            "mlora_workspace_size", "mlora_workspace_init",

@@ -78,6 +78,55 @@ def test_linear_and_delta_small(oracle_mod, case):
     check_delta(oracle_mod, L, D, label=f"small{seed}")
 
 
+TILED = [
+    # seed, T, n_in, n_out, S, R, K, slices   (tiled prefill kernels forced)
+    (41, 300, 392, 520, 7, 16, 3, [260, 130, 130]),
+    (42, 257, 256, 256, 5, 64, 1, None),
+    (43, 700, 1032, 600, 9, 8, 2, [300, 300]),
+    (44, 64, 128, 136, 3, 32, 1, None),
+    (45, 520, 512, 1024, 40, 16, 3, [512, 256, 256]),
+]
+
+
+@pytest.mark.parametrize("case", TILED, ids=[f"t{c[0]}" for c in TILED])
+def test_tiled_path_small(oracle_mod, case):
+    from lora_serving_amd import mlora
+    seed, T, n_in, n_out, S, R, K, slices = case
+    for contiguous in (True, False):
+        L = synth.random_layer(seed, T=T, n_in=n_in, n_out=n_out, S=S, R=R, K=K,
+                               slice_sizes=slices, p_sentinel=0.25, contiguous=contiguous)
+        say(f"[tiled] seed={seed} T={T} n_in={n_in} n_out={n_out} K={K} R={R} "
+            f"contiguous={contiguous}")
+        D = DevLayer(L)
+        y = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_TILED))
+        y_ref = oracle_mod.linear(L)
+        ok = tol_ok(y, y_ref)
+        assert ok.all(), f"tiled {seed}: worst {worst(y, y_ref):.3e}, {np.sum(~ok)} out"
+        # the tiled and the decode kernels agree within the same bound
+        y2 = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_DECODE))
+        assert tol_ok(y2, y_ref).all()
+
+
+def test_tiled_sentinel_rows_and_k3_invariance():
+    from lora_serving_amd import mlora
+    L1 = synth.random_layer(46, T=300, n_in=256, n_out=512, S=6, R=16, K=1, p_sentinel=0.3)
+    L1.idx[::4] = -1
+    D1 = DevLayer(L1)
+    y1 = from_dev_bf16(D1.linear(flags=mlora.MLORA_PATH_TILED))
+    y0 = from_dev_bf16(D1.linear(flags=mlora.MLORA_PATH_TILED | mlora.MLORA_NO_ADAPTERS))
+    rows = np.where(L1.idx[:, 0] == -1)[0]
+    assert np.array_equal(y1[rows], y0[rows])
+    L3 = synth.random_layer(46, T=300, n_in=256, n_out=512, S=6, R=16, K=1, p_sentinel=0.3)
+    L3.idx[::4] = -1
+    idx = np.full((L1.T, 3), -1, np.int32)
+    idx[:, 2] = L3.idx[:, 0]
+    sc = np.ones((L1.T, 3), np.float32)
+    sc[:, 2] = L3.scale[:, 0]
+    L3.idx, L3.scale, L3.K = idx, sc, 3
+    y3 = from_dev_bf16(DevLayer(L3).linear(flags=mlora.MLORA_PATH_TILED))
+    assert np.array_equal(y3, y1)
+
+
 def test_shrink_matches_oracle(oracle_mod):
     L = synth.random_layer(21, T=33, n_in=1024, n_out=96, S=6, R=16, K=3,
                            slice_sizes=[32, 32, 32], p_sentinel=0.3)
