@@ -1,11 +1,16 @@
 """Benchmark of the multi-LoRA adapted linear layer on one MI355X.
 
-One step = one mlora_linear call (base product, per-token LoRA shrink and expand, accumulate
-and round) over the decode workload: T = 64 one-token requests through a 4096 -> 4096 bf16
-layer with 100 resident rank-16 adapters (alpha 32), 6 tokens on the base model only.
-Inputs are resident in HBM before the timed region; the step cycles through enough distinct
-copies of {x, W, A, B, y} (over twice the 256 MB Infinity Cache) that every step's bytes come
-from HBM.  Prints one JSON line.
+One step = one mlora_linear call per layer of the workload (base product, LoRA shrink and
+expand, accumulate and round y once).  The default workload is the decode batch: T = 64
+one-token requests through a 4096 -> 4096 bf16 layer with 100 resident rank-16 adapters
+(alpha 32), 6 tokens on the base model only.  Inputs are resident in HBM before the timed
+region; when one copy of the inputs fits the 256 MB Infinity Cache, the step cycles through
+enough distinct copies of {x, W, A, B, y} (over 600 MB) that every step's bytes come from HBM.
+Prints one JSON line.
+
+Other workloads (--workload): tiny, prefill (16384 tokens, 4096 -> 11008, 100 x rank 64),
+mixed_qkv (256 decode + 2048 prefill tokens, merged QKV 4096 -> 6144, ranks 8/16/64 padded to
+64), compose (8192 tokens, K = 3 slots, 4096 -> 4096 and 11008 -> 4096 layers).
 """
 from __future__ import annotations
 
@@ -23,55 +28,89 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 METRIC = "multi-LoRA layer tokens/s + % HBM GB/s (decode) / % MFMA peak (prefill)"
 
+DESCRIPTIONS = {
+    "tiny": "tiny: T=16, 256->256, 4 adapters rank 8 alpha 16, P(-1)=0.25, K=1",
+    "decode": "bgmv_decode: T=64 one-token requests, 4096->4096 bf16, 100 adapters rank 16 "
+              "alpha 32, 6 tokens base-only, K=1",
+    "prefill": "sgmv_prefill: T=16384 = 32 requests x 512 contiguous tokens, 4096->11008 bf16, "
+               "100 adapters rank 64 alpha 128, request adapter ~ Zipf(1.1), K=1",
+    "mixed_qkv": "mixed_qkv: T=2304 = 256 decode + 2048 prefill tokens, merged QKV "
+                 "4096->(4096,1024,1024), 64 adapters ranks {8,16,64} padded to 64, alpha 2r",
+    "compose": "k3_compose: T=8192 = 64 requests x 128 tokens, K=3 slots, 32 adapters rank 16 "
+               "alpha 32 (half rsLoRA), s~U(0.2,1); layers 4096->4096 and 11008->4096",
+}
+
 
 def algorithmic(L):
-    """Bytes and flops the method itself must move / compute for one call: W, x, y once, each
-    distinct used adapter's A and B rows once at its true rank, the index map and scales."""
+    """Bytes and flops the method itself must move / compute for one call of the layer: W, x, y
+    once, each distinct used adapter's A and B rows once at its true rank, the index map and
+    scales; flops 2 T n_in n_out plus 2 r (n_slices n_in + n_out) per used (token, slot)."""
     import numpy as np
     used = np.unique(L.idx[L.idx >= 0])
-    adapter = sum(int(L.rank[a]) * (L.n_slices * L.n_in + L.n_out) * 2 for a in used)
-    a_only = sum(int(L.rank[a]) * L.n_slices * L.n_in * 2 for a in used)
-    base = L.n_out * L.n_in * 2 + L.T * L.n_in * 2 + L.T * L.n_out * 2
+    a_bytes = sum(int(L.rank[a]) * L.n_slices * L.n_in * 2 for a in used)
+    b_bytes = sum(int(L.rank[a]) * L.n_out * 2 for a in used)
+    w_bytes = L.n_out * L.n_in * 2
+    x_bytes = L.T * L.n_in * 2
+    y_bytes = L.T * L.n_out * 2
     meta = L.idx.size * 4 + L.scale.size * 4 + L.S * 4
-    flops = 2.0 * L.T * L.n_in * L.n_out
-    for t in range(L.T):
-        for j in range(L.K):
-            a = L.idx[t, j]
-            if a >= 0:
-                flops += 2.0 * int(L.rank[a]) * (L.n_slices * L.n_in + L.n_out)
-    return {"bytes": base + adapter + meta, "adapter_bytes": adapter, "a_bytes": a_only,
-            "W_bytes": L.n_out * L.n_in * 2, "x_bytes": L.T * L.n_in * 2,
-            "distinct_adapters": int(len(used)), "flops": flops}
+    ranks = np.where(L.idx >= 0, L.rank[np.maximum(L.idx, 0)], 0).astype(np.float64)
+    base_flops = 2.0 * L.T * L.n_in * L.n_out
+    shrink_flops = float(np.sum(2.0 * ranks * L.n_slices * L.n_in))
+    expand_flops = float(np.sum(2.0 * ranks * L.n_out))
+    return {"bytes": w_bytes + x_bytes + y_bytes + a_bytes + b_bytes + meta,
+            "flops": base_flops + shrink_flops + expand_flops,
+            "distinct_adapters": int(len(used)),
+            # the part of the call done by the main product kernel, per path
+            "decode_kernel_bytes": w_bytes + x_bytes + a_bytes + meta,
+            "decode_kernel_flops": base_flops + shrink_flops,
+            "tiled_kernel_bytes": w_bytes + x_bytes + y_bytes + b_bytes + meta,
+            "tiled_kernel_flops": base_flops + expand_flops}
 
 
-def cpu_baseline(L, budget_s: float):
-    """The oracle, as it stands, on the host cores: whole batches until budget_s has passed."""
+def cpu_baseline(layers, budget_s: float):
+    """The oracle, as it stands, on the host cores, on a bounded sample of the workload's
+    tokens (whole batches while they take under the budget), scaled to tokens/s."""
+    import numpy as np
     import oracle
     oracle.build(force=False)
+    total_tokens = sum(L.T for L in layers) / len(layers)
     t0 = time.perf_counter()
-    n = 0
+    n_tok = 0
+    rounds = 0
+    rng = np.random.default_rng(0)
     while True:
-        oracle.linear(L)
-        n += 1
+        for L in layers:
+            if L.T <= 128:
+                oracle.linear(L)
+                n_tok += L.T / len(layers)
+            else:
+                toks = np.sort(rng.choice(L.T, size=32, replace=False))
+                oracle.linear(L, tokens=toks)
+                n_tok += 32 / len(layers)
+        rounds += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
     cores = len(os.sched_getaffinity(0))
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    return {"value": n * L.T / el, "unit": "tokens/s", "cores": min(cores, threads),
+    what = ("full batches" if all(L.T <= 128 for L in layers)
+            else "random 32-token samples per layer")
+    return {"value": n_tok / el, "unit": "tokens/s", "cores": min(cores, threads),
             "kind": "oracle",
-            "sample": f"{n} full batches of the same {L.T}-token workload ({n * L.T} tokens, "
-                      f"{el:.1f} s, fp64 oracle, OpenMP over tokens)"}
+            "sample": f"{rounds} rounds of {what} of the same workload ({n_tok:.0f} tokens of "
+                      f"{total_tokens:.0f} per step, {el:.1f} s, fp64 oracle, OpenMP over tokens)"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (0 = per workload)")
+    ap.add_argument("--warmup", type=int, default=-1)
+    ap.add_argument("--workload", default="decode", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--sets", type=int, default=0, help="rotating input copies (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--flags", type=int, default=0, help="extra mlora_linear flags")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -82,59 +121,105 @@ def main():
     from lora_serving_amd import mlora, synth
     from tests.gpu_util import DevLayer
 
-    L = synth.workload_decode()
-    alg = algorithmic(L)
-    D = DevLayer(L)
-    per_set = (D.x.numel() + D.W.numel() + D.A.numel() + D.B.numel()) * 2 + L.T * L.n_out * 2
-    nsets = args.sets or max(2, -(-600 * 2 ** 20 // per_set))
+    layers = synth.WORKLOADS[args.workload]()
+    if not isinstance(layers, list):
+        layers = [layers]
+    decode_like = all(L.T <= 128 for L in layers)
+    steps = args.steps or (2000 if decode_like else 20)
+    warmup = args.warmup if args.warmup >= 0 else (100 if decode_like else 3)
+    algs = [algorithmic(L) for L in layers]
+    devs = [DevLayer(L) for L in layers]
+
+    # rotating copies so that decode-sized steps read HBM, not the Infinity Cache
+    per_set = sum((D.x.numel() + D.W.numel() + D.A.numel() + D.B.numel()) * 2 +
+                  D.L.T * D.L.n_out * 2 for D in devs)
+    nsets = args.sets or (max(2, -(-600 * 2 ** 20 // per_set)) if per_set < 256 * 2 ** 20 else 1)
     sets = []
     for i in range(nsets):
-        if i == 0:
-            x, W, A, B = D.x, D.W, D.A, D.B
-        else:
-            x, W, A, B = D.x.clone(), D.W.clone(), D.A.clone(), D.B.clone()
-        slots = mlora.Slots(A, B, D.factor, slice_start=[int(v) for v in L.slice_start])
-        y = torch.empty((L.T, L.n_out), dtype=torch.bfloat16, device="cuda")
-        sets.append((x, W, slots, y))
-    idx, scale, ws = D.idx, D.scale, D.ws
+        one = []
+        for D in devs:
+            if i == 0:
+                x, W, A, B = D.x, D.W, D.A, D.B
+            else:
+                x, W, A, B = D.x.clone(), D.W.clone(), D.A.clone(), D.B.clone()
+            slots = mlora.Slots(A, B, D.factor, slice_start=[int(v) for v in D.L.slice_start])
+            y = torch.empty((D.L.T, D.L.n_out), dtype=torch.bfloat16, device="cuda")
+            one.append((x, W, slots, y, D))
+        sets.append(one)
 
     def step(i):
-        x, W, slots, y = sets[i % nsets]
-        mlora.mlora_linear(x, W, slots, idx, scale, y, ws=ws)
+        for (x, W, slots, y, D) in sets[i % nsets]:
+            mlora.mlora_linear(x, W, slots, D.idx, D.scale, y, flags=args.flags, ws=D.ws)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()     # the stream the library launches on
-
-    # timed region: K steps back to back, one event pair around all of them
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    tokens_per_s = L.T / (ms * 1e-3)
-    achieved = alg["bytes"] / (ms * 1e-3) / 1e9
-
+    ms = ev0.elapsed_time(ev1) / steps
+    # Main product kernel: HIP events that the library records on the launch stream around
+    # each of its launches, over a second timed region of the same length (the event pairs
+    # add a few microseconds per launch, so the step time above is taken without them).
+    launches_per_step = sum((L.T + 63) // 64 if decode_like else 1 for L in layers)
+    cap = steps * launches_per_step
+    torch.cuda.synchronize()
+    mlora.mlora_trace_start(cap)
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    kernel_ms = mlora.mlora_trace_stop(cap)
+    if len(kernel_ms) != cap:
+        raise RuntimeError(f"expected {cap} traced launches, got {len(kernel_ms)}")
+    k_avg_ms = sum(kernel_ms) / len(kernel_ms)
+    T = layers[0].T
+    tokens_per_s = T / (ms * 1e-3)
+    tot_bytes = sum(a["bytes"] for a in algs)
+    tot_flops = sum(a["flops"] for a in algs)
+    fused = os.environ.get("MLORA_DECODE_FUSED") is not None
+    if decode_like:
+        if fused:
+            kname = "mlora::decode_gemm_kernel<.., true> (whole layer in one launch)"
+            k_bytes = tot_bytes
+        else:
+            kname = "mlora::decode_gemm_kernel<.., false> (base product + shrink)"
+            k_bytes = sum(a["decode_kernel_bytes"] for a in algs)
+        k_bytes /= launches_per_step
+        achieved = k_bytes / (k_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                "kernel": kname, "kernel_avg_us": k_avg_ms * 1e3,
+                "algorithmic_bytes_per_launch": k_bytes,
+                "step_achieved_GBps": tot_bytes / (ms * 1e-3) / 1e9}
+    else:
+        kname = "mlora::prefill_gemm_kernel (base product + LoRA expand as extra K-steps)"
+        k_flops = sum(a["tiled_kernel_flops"] for a in algs) / launches_per_step
+        achieved = k_flops / (k_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                "kernel": kname, "kernel_avg_us": k_avg_ms * 1e3,
+                "algorithmic_flops_per_launch": k_flops,
+                "step_achieved_TFLOPs": tot_flops / (ms * 1e-3) / 1e12}
     out = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "steps": steps, "warmup": warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; random bf16 weights and adapters)",
-        "config": {"workload": "bgmv_decode: T=64 one-token requests, 4096->4096 bf16, "
-                               "100 adapters rank 16 alpha 32, 6 tokens base-only, K=1",
-                   "T": L.T, "n_in": L.n_in, "n_out": L.n_out, "S": L.S, "R": L.R, "K": L.K,
-                   "distinct_adapters": alg["distinct_adapters"], "rotating_sets": nsets},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "scope": "whole step (all kernels of the layer)",
-                     "algorithmic_bytes": alg["bytes"]},
+        "config": {"workload": DESCRIPTIONS[args.workload], "T": T,
+                   "layers": [[L.n_in, L.n_out] for L in layers], "S": layers[0].S,
+                   "R": layers[0].R, "K": layers[0].K,
+                   "distinct_adapters": [a["distinct_adapters"] for a in algs],
+                   "rotating_sets": nsets},
+        "roofline": roof,
+        "step_algorithmic": {"bytes": tot_bytes, "flops": tot_flops},
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -189,6 +189,20 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
                           const float *scale, void *y, uint32_t flags, void *ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/*
+ * Profiling hook (not part of the computation).  mlora_trace_start creates 2*capacity HIP
+ * events (no device memory); from then on every mlora_linear call records one event on its
+ * stream right before and one right after each launch of its main product kernel (the decode
+ * GEMM, the one-launch decode kernel or the tiled GEMM), for the first `capacity` launches.
+ * mlora_trace_stop waits for the recorded events, writes the duration of launch i in
+ * milliseconds to ms[i] (host array of `capacity` floats; NULL discards them), releases the
+ * events and returns the number of durations written (-1 on a HIP error).
+ * Process-wide state, guarded by a lock; start returns MLORA_ERR_ARG unless
+ * 1 <= capacity <= 2^20 and MLORA_ERR_HIP if an event cannot be created.
+ */
+mlora_status mlora_trace_start(int32_t capacity);
+int32_t mlora_trace_stop(float *ms, int32_t capacity);
+
 #ifdef __cplusplus
 }
 #endif

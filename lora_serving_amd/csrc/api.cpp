@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -122,9 +123,91 @@ mlora_status hip_status(hipError_t e, const char *where = "launch")
     return MLORA_ERR_HIP;
 }
 
+// Profiling hook: event pairs around the main product kernel of each mlora_linear call.
+struct Trace {
+    std::mutex mu;
+    std::vector<hipEvent_t> begin, end;
+    int32_t count = 0;
+    bool active = false;
+} g_trace;
+
+void trace_release()
+{
+    for (hipEvent_t e : g_trace.begin)
+        (void)hipEventDestroy(e);
+    for (hipEvent_t e : g_trace.end)
+        (void)hipEventDestroy(e);
+    g_trace.begin.clear();
+    g_trace.end.clear();
+    g_trace.count = 0;
+    g_trace.active = false;
+}
+
 }  // namespace
 
+namespace mlora {
+
+void trace_mark(hipStream_t stream, bool begin)
+{
+    if (!g_trace.active)
+        return;
+    std::lock_guard<std::mutex> lock(g_trace.mu);
+    if (!g_trace.active || g_trace.count >= (int32_t)g_trace.begin.size())
+        return;
+    if (begin) {
+        (void)hipEventRecord(g_trace.begin[g_trace.count], stream);
+    } else {
+        (void)hipEventRecord(g_trace.end[g_trace.count], stream);
+        ++g_trace.count;
+    }
+}
+
+}  // namespace mlora
+
 extern "C" {
+
+mlora_status mlora_trace_start(int32_t capacity)
+{
+    if (capacity < 1 || capacity > (1 << 20))
+        return MLORA_ERR_ARG;
+    std::lock_guard<std::mutex> lock(g_trace.mu);
+    trace_release();
+    g_trace.begin.resize(capacity);
+    g_trace.end.resize(capacity);
+    for (int32_t i = 0; i < capacity; ++i) {
+        hipError_t e = hipEventCreate(&g_trace.begin[i]);
+        if (e == hipSuccess)
+            e = hipEventCreate(&g_trace.end[i]);
+        if (e != hipSuccess) {
+            g_trace.begin.resize(i + 1);
+            g_trace.end.resize(i + 1);
+            trace_release();
+            return hip_status(e, "trace event");
+        }
+    }
+    g_trace.active = true;
+    return MLORA_OK;
+}
+
+int32_t mlora_trace_stop(float *ms, int32_t capacity)
+{
+    std::lock_guard<std::mutex> lock(g_trace.mu);
+    const int32_t n = std::min(g_trace.count, std::max<int32_t>(capacity, 0));
+    int32_t out = n;
+    for (int32_t i = 0; i < n && ms != nullptr; ++i) {
+        hipError_t e = hipEventSynchronize(g_trace.end[i]);
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms[i], g_trace.begin[i], g_trace.end[i]);
+        if (e != hipSuccess) {
+            (void)hip_status(e, "trace read");
+            out = -1;
+            break;
+        }
+    }
+    trace_release();
+    return out;
+}
+
 
 const char *mlora_last_error(void) { return g_last_error; }
 
@@ -333,19 +416,23 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
         if (g_fused_decode_enabled && decode_fused_fits(Tc, K, wd, cfg) &&
             decode_tiles_fit_sync(n_out) &&
             decode_sync_words(n_out) * sizeof(uint32_t) <= SYNC_BYTES) {
+            trace_mark(stream, true);
             hipError_t e = launch_decode_fused(xb + t0 * n_in, (const uint16_t *)W, Tc, n_in,
                                                n_out, part, cfg, lora ? &g : nullptr, idx_c, K,
                                                scale_c, lora ? upart : nullptr, sync,
                                                yb + t0 * n_out, stream);
+            trace_mark(stream, false);
             if (e == hipSuccess)
                 continue;
             if (e != hipErrorCooperativeLaunchTooLarge && e != hipErrorNotSupported)
                 return hip_status(e, "fused decode launch");
             (void)hipGetLastError();   // not resident on this device: two-kernel path
         }
+        trace_mark(stream, true);
         hipError_t e = launch_decode_gemm(xb + t0 * n_in, (const uint16_t *)W, Tc, n_in, n_out,
                                           part, cfg, lora ? &g : nullptr, idx_c, K,
                                           lora ? upart : nullptr, stream);
+        trace_mark(stream, false);
         if (e != hipSuccess)
             return hip_status(e, "decode gemm launch");
         e = launch_expand_tokens(upart, cfg.sk, 1, scale_c, Tc, n_out, g, idx_c, lora ? K : 0,

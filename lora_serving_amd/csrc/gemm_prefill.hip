@@ -570,9 +570,12 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
             return e;
         attr = true;
     }
+    trace_mark(stream, true);
     hipLaunchKernelGGL(prefill_gemm_kernel, dim3((unsigned)(c.n_mtiles * c.n_ntiles)),
                        dim3(PF_THREADS), lds, stream, a);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    trace_mark(stream, false);
+    return e;
 }
 
 }  // namespace mlora

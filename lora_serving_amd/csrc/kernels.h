@@ -79,6 +79,9 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
 size_t prefill_workspace_bytes(const PrefillCfg &c);
 bool prefill_worth_it(int64_t T, int64_t n_out);
 // y = bf16(x W^T + LoRA delta); g == nullptr: base only.  ws: prefill_workspace_bytes(c).
+// Profiling hook (mlora_trace_start): records the begin/end event of the main product kernel.
+void trace_mark(hipStream_t stream, bool begin);
+
 hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64_t n_in,
                           int64_t n_out, const SlotGeom *g, const int32_t *idx, int32_t K,
                           const float *scale, uint16_t *y, const PrefillCfg &c, void *ws,

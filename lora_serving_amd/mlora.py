@@ -33,7 +33,8 @@ MLORA_PATH_TILED = 4
 
 EXPORTS = ("mlora_status_string", "mlora_last_error", "mlora_factor", "mlora_slot_bytes",
            "mlora_workspace_size", "mlora_workspace_init",
-           "mlora_validate", "mlora_plan", "mlora_shrink", "mlora_expand", "mlora_linear")
+           "mlora_validate", "mlora_plan", "mlora_shrink", "mlora_expand", "mlora_linear",
+           "mlora_trace_start", "mlora_trace_stop")
 
 _P = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -71,6 +72,10 @@ _lib.mlora_expand.argtypes = [_P, _i64, _i64, _SLOTS_P, _P, _i32, _P, _P]
 _lib.mlora_linear.restype = ctypes.c_int
 _lib.mlora_linear.argtypes = [_P, _P, _i64, _i64, _i64, _SLOTS_P, _P, _i32, _P, _P, ctypes.c_uint32,
                               _P, ctypes.c_size_t, _P]
+_lib.mlora_trace_start.restype = ctypes.c_int
+_lib.mlora_trace_start.argtypes = [_i32]
+_lib.mlora_trace_stop.restype = _i32
+_lib.mlora_trace_stop.argtypes = [ctypes.POINTER(ctypes.c_float), _i32]
 
 
 class MloraError(RuntimeError):
@@ -248,3 +253,16 @@ def mlora_linear(x, W, slots: Slots | None, idx, scale, y, flags: int = 0, ws=No
                              _ptr(y), flags, _ptr(ws),
                              0 if ws is None else ws.numel() * ws.element_size(),
                              _stream(stream)), "mlora_linear")
+
+
+def mlora_trace_start(capacity: int):
+    _check(_lib.mlora_trace_start(capacity), "mlora_trace_start")
+
+
+def mlora_trace_stop(capacity: int) -> list:
+    """Durations (ms) of the main product kernel launches recorded since mlora_trace_start."""
+    buf = (ctypes.c_float * max(capacity, 1))()
+    n = _lib.mlora_trace_stop(buf, capacity)
+    if n < 0:
+        raise MloraError(MLORA_ERR_HIP, "mlora_trace_stop")
+    return [float(buf[i]) for i in range(n)]

@@ -136,6 +136,12 @@ def test_other_entry_points_argument_checks(m):
     assert L.mlora_validate(0x1000, 0, 1, ctypes.byref(s), ok, None, None) == m.MLORA_OK
 
 
+def test_trace_hook_argument_checks(m):
+    assert m._lib.mlora_trace_start(0) == m.MLORA_ERR_ARG
+    assert m._lib.mlora_trace_start((1 << 20) + 1) == m.MLORA_ERR_ARG
+    assert m._lib.mlora_trace_stop(None, 0) == 0    # nothing recorded, nothing to release
+
+
 def test_status_strings(m):
     for code in range(8):
         assert m.mlora_status_string(code)
