@@ -73,7 +73,7 @@ mlora_status check_slots(const mlora_slots *s, int64_t n_out, bool need_data, Sl
 // Workspace layout of one call; every region 256-byte aligned.  The counter words at the
 // start must be zero before the first call (mlora_workspace_init); every call leaves them zero.
 struct Layout {
-    size_t sync = 0;       // uint32 counters of the fused decode kernel
+    size_t sync = 0;       // reserved words, zeroed by mlora_workspace_init
     size_t sort_cnt = 0;   // counting-sort scratch (plan)
     size_t v = 0;          // fp32 [sk][K][Tc][n_slices*R] shrink partials (decode path)
     size_t part = 0;       // fp32 partial sums of the decode GEMM
@@ -82,7 +82,7 @@ struct Layout {
     size_t off_sync = 0, off_sort = 0, off_v = 0, off_part = 0, off_pre = 0;
 };
 
-constexpr size_t SYNC_BYTES = 64 * 1024;   // fixed, so mlora_workspace_init knows its size
+constexpr size_t SYNC_BYTES = DECODE_SYNC_BYTES;   // fixed, so mlora_workspace_init knows it
 
 // Regions for both paths, so one workspace size serves any flags.
 Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t R,
@@ -95,9 +95,13 @@ Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S,
     if (T > 0)
         L.pre = align_up(prefill_workspace_bytes(prefill_config(T, K, n_in, n_out, S, R, n_slices)));
     const int64_t Tc = std::min<int64_t>(T, DECODE_MAX_T);
-    const int64_t sk = Tc > 0 ? decode_config(Tc, n_in, n_out).sk : 0;
-    L.v = align_up((size_t)sk * K * Tc * wd * sizeof(float));
-    L.part = Tc > 0 ? align_up(decode_partial_bytes(Tc, n_in, n_out)) : 0;
+    L.v = 0;
+    L.part = 0;
+    if (Tc > 0) {
+        const int64_t sk = decode_config(Tc, n_in, n_out).sk;
+        L.v = align_up((size_t)sk * K * Tc * wd * sizeof(float));
+        L.part = align_up(decode_partial_bytes(Tc, n_in, n_out));
+    }
     L.off_sync = 0;
     L.off_sort = L.off_sync + L.sync;
     L.off_v = L.off_sort + L.sort_cnt;
@@ -106,11 +110,6 @@ Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S,
     L.total = L.off_pre + L.pre;
     return L;
 }
-
-// The one-launch decode kernel needs every workgroup resident at once (checked against the
-// device's occupancy); it is opt-in (MLORA_DECODE_FUSED=1) while it is slower than the
-// two-kernel path on MI355X.
-bool g_fused_decode_enabled = std::getenv("MLORA_DECODE_FUSED") != nullptr;
 
 thread_local char g_last_error[256] = "";
 
@@ -370,7 +369,7 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
     const bool lora = (flags & MLORA_NO_ADAPTERS) == 0;
     SlotGeom g;
     std::memset(&g, 0, sizeof g);
-    int32_t S = 1, wd = 8, R = 8, n_slices = 1;
+    int32_t S = 1, R = 8, n_slices = 1;
     if (lora || slots != nullptr) {
         mlora_status st = check_slots(slots, n_out, lora, &g);
         if (st != MLORA_OK)
@@ -378,7 +377,6 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
         S = g.S;
         R = g.R;
         n_slices = g.n_slices;
-        wd = n_slices * R;
     }
     if (T == 0)
         return MLORA_OK;
@@ -395,7 +393,6 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
         return MLORA_ERR_ARG;
     float *upart = (float *)(wsb + L.off_v);
     float *part = (float *)(wsb + L.off_part);
-    uint32_t *sync = (uint32_t *)(wsb + L.off_sync);
     const uint16_t *xb = (const uint16_t *)x;
     uint16_t *yb = (uint16_t *)y;
     const bool force_decode = (flags & MLORA_PATH_DECODE) != 0;
@@ -407,27 +404,12 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
                                          wsb + L.off_pre, stream),
                           "prefill launch");
     }
-    // Token chunks of at most DECODE_MAX_T go through the decode kernels.
+    // Token chunks of at most DECODE_MAX_T: base GEMM + shrink pieces, then the finish kernel.
     for (int64_t t0 = 0; t0 < T; t0 += DECODE_MAX_T) {
         const int64_t Tc = std::min<int64_t>(DECODE_MAX_T, T - t0);
         const DecodeCfg cfg = decode_config(Tc, n_in, n_out);
         const int32_t *idx_c = lora ? idx + t0 * K : nullptr;
         const float *scale_c = (lora && scale) ? scale + t0 * K : nullptr;
-        if (g_fused_decode_enabled && decode_fused_fits(Tc, K, wd, cfg) &&
-            decode_tiles_fit_sync(n_out) &&
-            decode_sync_words(n_out) * sizeof(uint32_t) <= SYNC_BYTES) {
-            trace_mark(stream, true);
-            hipError_t e = launch_decode_fused(xb + t0 * n_in, (const uint16_t *)W, Tc, n_in,
-                                               n_out, part, cfg, lora ? &g : nullptr, idx_c, K,
-                                               scale_c, lora ? upart : nullptr, sync,
-                                               yb + t0 * n_out, stream);
-            trace_mark(stream, false);
-            if (e == hipSuccess)
-                continue;
-            if (e != hipErrorCooperativeLaunchTooLarge && e != hipErrorNotSupported)
-                return hip_status(e, "fused decode launch");
-            (void)hipGetLastError();   // not resident on this device: two-kernel path
-        }
         trace_mark(stream, true);
         hipError_t e = launch_decode_gemm(xb + t0 * n_in, (const uint16_t *)W, Tc, n_in, n_out,
                                           part, cfg, lora ? &g : nullptr, idx_c, K,
@@ -435,10 +417,10 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
         trace_mark(stream, false);
         if (e != hipSuccess)
             return hip_status(e, "decode gemm launch");
-        e = launch_expand_tokens(upart, cfg.sk, 1, scale_c, Tc, n_out, g, idx_c, lora ? K : 0,
-                                 part, cfg.sk, yb + t0 * n_out, stream);
+        e = launch_decode_finish(part, cfg.sk, cfg.n_tiles, lora ? upart : nullptr, scale_c, Tc,
+                                 n_out, lora ? &g : nullptr, idx_c, K, yb + t0 * n_out, stream);
         if (e != hipSuccess)
-            return hip_status(e, "expand launch");
+            return hip_status(e, "decode finish launch");
     }
     return MLORA_OK;
 }

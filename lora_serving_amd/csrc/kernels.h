@@ -50,21 +50,20 @@ struct DecodeCfg {
 };
 DecodeCfg decode_config(int64_t T, int64_t n_in, int64_t n_out);
 size_t decode_partial_bytes(int64_t T, int64_t n_in, int64_t n_out);
-// part[s][t][n] = x[t, split s] . W[n, split s]; with upart != nullptr the same launch writes
-// the unscaled shrink partials upart[s][j][t][0:n_slices*R] of every pair (-1 pairs skipped).
+// part[s][tile][t][0:64] = x[t, split s] . W[tile*64 + (0:64), split s]; with upart != nullptr
+// the same launch writes the unscaled shrink partials upart[s][j][t][0:n_slices*R] of every
+// pair (-1 pairs skipped).
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, int64_t T, int64_t n_in,
                               int64_t n_out, float *part, const DecodeCfg &cfg,
                               const SlotGeom *g, const int32_t *idx, int32_t K, float *upart,
                               hipStream_t stream);
-// Whole decode layer in one cooperative launch: y = bf16(W x + LoRA delta).  sync: counter
-// words (decode_sync_words), zero on entry and left zero on exit.  g == nullptr: base only.
-size_t decode_sync_words(int64_t n_out);
-bool decode_tiles_fit_sync(int64_t n_out);
-bool decode_fused_fits(int64_t T, int32_t K, int32_t wd, const DecodeCfg &cfg);
-hipError_t launch_decode_fused(const uint16_t *x, const uint16_t *W, int64_t T, int64_t n_in,
-                               int64_t n_out, float *part, const DecodeCfg &cfg, const SlotGeom *g,
-                               const int32_t *idx, int32_t K, const float *scale, float *upart,
-                               uint32_t *sync, uint16_t *y, hipStream_t stream);
+// ---- decode_finish.hip: y = bf16(sum of the split partials + LoRA delta), T <= 64 ----------
+// part: fp32 [sk][n_tiles][T][64] (launch_decode_gemm); upart: fp32 [sk][K][T][wd] unscaled
+// shrink pieces (nullptr: base only, g unused)
+hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, const float *upart,
+                                const float *scale, int64_t T, int64_t n_out, const SlotGeom *g,
+                                const int32_t *idx, int32_t K, uint16_t *y, hipStream_t stream);
+constexpr size_t DECODE_SYNC_BYTES = 64 * 1024;   // reserved words at the start of the workspace
 // zero fill of n 32-bit words (a kernel, not a memset node)
 hipError_t launch_zero_words(uint32_t *p, size_t n, hipStream_t stream);
 
