@@ -18,7 +18,8 @@ using namespace mlora;
 
 namespace {
 
-constexpr int64_t DECODE_MAX_T = 64;    // token chunk of the decode kernels
+constexpr int64_t DECODE_MAX_T = 64;          // token chunk of the decode kernels
+constexpr int64_t PREFILL_MAX_T = 4096 * 256; // token chunk of the tiled kernels
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -93,7 +94,8 @@ Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S,
     L.sync = SYNC_BYTES;
     L.sort_cnt = align_up(sort_workspace_bytes(T * K, S));
     if (T > 0)
-        L.pre = align_up(prefill_workspace_bytes(prefill_config(T, K, n_in, n_out, S, R, n_slices)));
+        L.pre = align_up(prefill_workspace_bytes(
+            prefill_config(std::min<int64_t>(T, PREFILL_MAX_T), K, n_in, n_out, S, R, n_slices)));
     const int64_t Tc = std::min<int64_t>(T, DECODE_MAX_T);
     L.v = 0;
     L.part = 0;
@@ -398,11 +400,20 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
     const bool force_decode = (flags & MLORA_PATH_DECODE) != 0;
     const bool force_tiled = (flags & MLORA_PATH_TILED) != 0;
     if (force_tiled || (!force_decode && prefill_worth_it(T, n_out))) {
-        const PrefillCfg pc = prefill_config(T, K, n_in, n_out, S, R, n_slices);
-        return hip_status(launch_prefill(xb, (const uint16_t *)W, T, n_in, n_out,
-                                         lora ? &g : nullptr, idx, K, scale, yb, pc,
-                                         wsb + L.off_pre, stream),
-                          "prefill launch");
+        // chunks of at most PREFILL_MAX_T tokens (the shrink's tile table lives in LDS)
+        for (int64_t t0 = 0; t0 < T; t0 += PREFILL_MAX_T) {
+            const int64_t Tc = std::min<int64_t>(PREFILL_MAX_T, T - t0);
+            const PrefillCfg pc = prefill_config(Tc, K, n_in, n_out, S, R, n_slices);
+            mlora_status st = hip_status(
+                launch_prefill(xb + t0 * n_in, (const uint16_t *)W, Tc, n_in, n_out,
+                               lora ? &g : nullptr, lora ? idx + t0 * K : nullptr, K,
+                               (lora && scale) ? scale + t0 * K : nullptr, yb + t0 * n_out, pc,
+                               wsb + L.off_pre, stream),
+                "prefill launch");
+            if (st != MLORA_OK)
+                return st;
+        }
+        return MLORA_OK;
     }
     // Token chunks of at most DECODE_MAX_T: base GEMM + shrink pieces, then the finish kernel.
     for (int64_t t0 = 0; t0 < T; t0 += DECODE_MAX_T) {

@@ -132,169 +132,191 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
 // ------------------------------------------------------------------------------------------
 // 2. SGMV shrink into V
 // ------------------------------------------------------------------------------------------
+// The tile's D adapters are stacked into one "cat" matrix A_cat (D * n_slices * R rows), so the
+// shrink of a tile is one dense product V_tile = X_tile A_cat^T; a token that does not use
+// adapter d gets coefficient 0 for d's columns (the zeros the GEMM's extra K-steps expect).
+// Item = (tile m, 64-token chunk c, 64-row block rb of A_cat); the items of all tiles are
+// numbered through a prefix over the tiles' row-block counts and shared out to a persistent
+// grid.  Inside an item the 4 waves split n_in, each holding the full 64 x 64 result in
+// MFMA accumulators, with operands loaded straight into the MFMA layout two k-steps ahead;
+// the 4 partial tiles are added in LDS in wave order and written as bf16 hi/lo pairs.
+constexpr int SH_THREADS = 256;
+constexpr int SH_MAX_TILES = 4096;   // tiles whose item prefix fits LDS
+
 struct ShrinkArgs {
     const uint16_t *x;
     int T, n_in, K;
     SlotGeom g;
     const int32_t *idx;
     const float *scale;
-    int n_mtiles, list_stride, n_wb;
-    const int32_t *tile_D, *tile_list, *tile_cnt;
+    int n_mtiles, list_stride;
+    const int32_t *tile_D, *tile_list;
     uint16_t *vcat;
     int64_t vcat_tile_elems;
 };
 
-// item = (m, d, c, wb): tile m, its d-th adapter, tokens [64c, 64c+64) of that adapter's
-// gathered tokens, A rows [64 wb, 64 wb + 64) of the adapter's n_slices*R rows
-__global__ __launch_bounds__(256) void sgmv_shrink_kernel(ShrinkArgs P)
+__device__ __forceinline__ void sh_load(const uint16_t *const (&ap)[4], const uint16_t *const (&xp)[4],
+                                        int col, int kend, u32x4 (&af)[4], u32x4 (&xf)[4])
 {
-    __shared__ int s_tok[PF_BM];
-    __shared__ float s_coef[PF_BM];
-    __shared__ int s_n;
+    // the pointers already include this lane's chunk offset 8 * (lane / 16)
+    const int off = ((threadIdx.x & 63) >> 4) * 8;
+    const bool ok = col + off < kend;
+    const int c = ok ? col : -off;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const u32x4 av = *(const u32x4 *)(ap[b] + c);
+        const u32x4 xv = *(const u32x4 *)(xp[b] + c);
+        af[b] = ok ? av : u32x4{0u, 0u, 0u, 0u};
+        xf[b] = ok ? xv : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+__device__ __forceinline__ void sh_mfma(const u32x4 (&af)[4], const u32x4 (&xf)[4],
+                                        f32x4 (&acc)[4][4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, xf[j]), acc[i][j], 0,
+                0, 0);
+}
+
+__global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
+{
+    extern __shared__ __attribute__((aligned(16))) float sh_lds[];
+    float4 *red = (float4 *)sh_lds;                           // [4 waves][16][64] float4
+    int *pre = (int *)(sh_lds + 4 * 16 * 64 * 4);             // [n_mtiles + 1] item prefix
     __shared__ int wsum[4];
-    __shared__ __attribute__((aligned(16))) uint16_t sa[64 * 64];   // A rows x 64 columns
-    __shared__ __attribute__((aligned(16))) uint16_t sx[64 * 64];   // gathered x rows
     const SlotGeom &g = P.g;
-    const int R = g.R;
-    const int wd = g.n_slices * R;
+    const int R = g.R, wd = g.n_slices * R;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t n_items = (int64_t)P.n_mtiles * P.list_stride * (PF_BM / 64) * P.n_wb;
+    const int r = lane & 15, gq = lane >> 4;
 
-    for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-        int64_t rest = item;
-        const int wb = (int)(rest % P.n_wb);
-        rest /= P.n_wb;
-        const int c = (int)(rest % (PF_BM / 64));
-        rest /= (PF_BM / 64);
-        const int d = (int)(rest % P.list_stride);
-        const int m = (int)(rest / P.list_stride);
-        const int D = P.tile_D[m];
-        if (d >= D)
-            continue;
-        const int ntok_a = P.tile_cnt[(int64_t)m * P.list_stride + d];
-        if (c * 64 >= ntok_a && c > 0)
-            continue;
-        const int a = P.tile_list[(int64_t)m * P.list_stride + d];
-        const int t0 = m * PF_BM;
-        const int nt = min(PF_BM, P.T - t0);
-        const float fa = g.factor[a];
-
-        // gather the tile's tokens that use a (in token order) and their coefficients
-        int use = 0;
-        float coef = 0.f;
-        const int tl = threadIdx.x;      // PF_BM == blockDim.x
-        if (tl < nt) {
-            const int32_t *it = P.idx + (int64_t)(t0 + tl) * P.K;
-            for (int j = 0; j < P.K; ++j)
-                if (it[j] == a) {
-                    use = 1;
-                    coef += (P.scale ? P.scale[(int64_t)(t0 + tl) * P.K + j] : 1.f) * fa;
-                }
-        }
+    // items of tile m: 4 chunks x ceil(D_m * wd / 64) row blocks
+    int base = 0;
+    for (int m0 = 0; m0 < P.n_mtiles; m0 += SH_THREADS) {
+        const int m = m0 + threadIdx.x;
+        const int cnt = m < P.n_mtiles ? 4 * ((P.tile_D[m] * wd + 63) / 64) : 0;
         int tot;
-        const int ex = wave_exclusive_scan(use, &tot);
+        const int ex = wave_exclusive_scan(cnt, &tot);
         if (lane == 0)
             wsum[wave] = tot;
         __syncthreads();
-        int before = 0;
-        for (int i = 0; i < wave; ++i)
-            before += wsum[i];
-        if (threadIdx.x == 0)
-            s_n = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-        if (use) {
-            s_tok[before + ex] = tl;
-            s_coef[before + ex] = coef;
+        int before = 0, all = 0;
+        for (int w = 0; w < 4; ++w) {
+            before += w < wave ? wsum[w] : 0;
+            all += wsum[w];
+        }
+        if (m < P.n_mtiles)
+            pre[m] = base + before + ex;
+        base += all;
+        __syncthreads();
+    }
+    const int total = base;
+
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        // tile: last m with pre[m] <= item
+        int lo = 0, hi = P.n_mtiles - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= item)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const int m = lo;
+        const int local = item - pre[m];
+        const int c = local & 3, rb = local >> 2;
+        const int D = P.tile_D[m];
+        const int32_t *list = P.tile_list + (int64_t)m * P.list_stride;
+        const int t0 = m * PF_BM + c * 64;
+        const int rows_cat = D * wd;
+
+        const uint16_t *ap[4], *xp[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int ar = min(rb * 64 + b * 16 + r, rows_cat - 1);
+            const int d = ar / wd;
+            ap[b] = g.A + ((int64_t)list[d] * wd + (ar - d * wd)) * P.n_in + gq * 8;
+            xp[b] = P.x + (int64_t)min(t0 + b * 16 + r, P.T - 1) * P.n_in + gq * 8;
+        }
+        // this wave's columns: [kb, kend), a multiple of 32 wide (the last may be short)
+        const int kq = ((P.n_in + 4 * 32 - 1) / (4 * 32)) * 32;
+        const int kb = wave * kq;
+        const int kend = min(P.n_in, kb + kq);
+        const int nsteps = kend > kb ? (kend - kb + 31) / 32 : 0;
+
+        f32x4 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 a0[4], x0[4], a1[4], x1[4];
+        sh_load(ap, xp, kb, kend, a0, x0);
+        sh_load(ap, xp, kb + 32, kend, a1, x1);
+        for (int st = 0; st < nsteps; st += 2) {
+            sh_mfma(a0, x0, acc);
+            sh_load(ap, xp, kb + (st + 2) * 32, kend, a0, x0);
+            sh_mfma(a1, x1, acc);
+            sh_load(ap, xp, kb + (st + 3) * 32, kend, a1, x1);
+        }
+
+        // lane holds A_cat rows rb*64 + 16i + 4gq + e of token t0 + 16j + r
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                red[(wave * 16 + i * 4 + j) * 64 + lane] =
+                    float4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        __syncthreads();
+        // thread: token tl = tid / 4, 16 consecutive rows q*16 .. q*16+15 (q = tid % 4)
+        const int tl = threadIdx.x >> 2, q = threadIdx.x & 3;
+        const int t = t0 + tl;
+        if (t < P.T && t < m * PF_BM + PF_BM) {
+            const int32_t *it = P.idx + (int64_t)t * P.K;
+            const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
+            uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems +
+                             (int64_t)(t - m * PF_BM) * (g.n_slices * kxs);
+            int dprev = -1;
+            float cf = 0.f;
+            for (int e = 0; e < 16; ++e) {
+                const int ar = rb * 64 + q * 16 + e;
+                if (ar >= rows_cat)
+                    break;
+                const int d = ar / wd;
+                if (d != dprev) {
+                    const int a = list[d];
+                    cf = 0.f;
+                    for (int j = 0; j < P.K; ++j)
+                        if (it[j] == a)
+                            cf += (P.scale ? P.scale[(int64_t)t * P.K + j] : 1.f) * g.factor[a];
+                    dprev = d;
+                }
+                // element (row ar, token tl) sits in block (i = ar/16, j = tl/16), lane
+                // (tl % 16) + 16 * ((ar % 16) / 4), component ar % 4
+                const int arl = q * 16 + e;
+                const int i = arl >> 4, jb = tl >> 4;
+                const int ln = (tl & 15) + 16 * ((arl & 15) >> 2), comp = arl & 3;
+                float sum = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float4 v4 = red[(w * 16 + i * 4 + jb) * 64 + ln];
+                    sum += comp == 0 ? v4.x : comp == 1 ? v4.y : comp == 2 ? v4.z : v4.w;
+                }
+                const float v = cf * sum;
+                const uint16_t vh = f32_to_bf16(v);
+                const uint16_t vl = f32_to_bf16(v - bf16_to_f32(vh));
+                const int rr = ar - d * wd;          // row within the adapter: slice sg, rank rho
+                const int sg = rr / R, rho = rr - sg * R;
+                uint16_t *vp = vrow + sg * kxs + d * 2 * R + rho;
+                vp[0] = vh;
+                vp[R] = vl;
+            }
         }
         __syncthreads();
-        const int n_use = s_n;
-        const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
-        const int pitch = g.n_slices * kxs;
-        uint16_t *vt = P.vcat + (int64_t)m * P.vcat_tile_elems;
-        const int ar0 = wb * 64;                    // first A row of this item
-        const int nar = min(64, wd - ar0);
-
-        // chunk 0 also writes the zeros of the tokens (and tile rows) that do not use a
-        if (c == 0) {
-            const int row = threadIdx.x;   // tile row
-            if (!use) {
-                for (int q = 0; q < nar; ++q) {
-                    const int ar = ar0 + q;
-                    const int sg = ar / R;
-                    uint16_t *vp = vt + (int64_t)row * pitch + sg * kxs + d * 2 * R + (ar - sg * R);
-                    vp[0] = 0;
-                    vp[R] = 0;
-                }
-            }
-        }
-        const int r0 = c * 64;
-        const int nrow = min(64, n_use - r0);
-        if (nrow <= 0)
-            continue;
-
-        // D[ar][row] = sum_k A[a][ar][k] x[tok_row][k]: wave w owns A rows 16w..16w+15,
-        // 4 token tiles of 16
-        f32x4 acc[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint16_t *Aa = g.A + ((int64_t)a * wd + ar0) * P.n_in;
-        for (int k0 = 0; k0 < P.n_in; k0 += 64) {
-            // stage A rows (64 x 64) and gathered x rows (64 x 64): 512 + 512 chunks
-            for (int e = threadIdx.x; e < 1024; e += 256) {
-                const int isx = e >= 512;
-                const int ee = e & 511;
-                const int row = ee >> 3, cc = ee & 7;
-                const int k = k0 + cc * 8;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (!isx) {
-                    if (row < nar && k < P.n_in)
-                        v = *(const u32x4 *)(Aa + (int64_t)row * P.n_in + k);
-                    *(u32x4 *)(sa + (row * 8 + pf_swz(row, cc)) * 8) = v;
-                } else {
-                    if (row < nrow && k < P.n_in)
-                        v = *(const u32x4 *)(P.x + (int64_t)(t0 + s_tok[r0 + row]) * P.n_in + k);
-                    *(u32x4 *)(sx + (row * 8 + pf_swz(row, cc)) * 8) = v;
-                }
-            }
-            __syncthreads();
-            const int r = lane & 15, gq = lane >> 4;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int cch = ks * 4 + gq;
-                const int arow = wave * 16 + r;
-                const bf16x8 av = *(const bf16x8 *)(sa + (arow * 8 + pf_swz(arow, cch)) * 8);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int xrow = q * 16 + r;
-                    const bf16x8 bv = *(const bf16x8 *)(sx + (xrow * 8 + pf_swz(xrow, cch)) * 8);
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[q], 0, 0, 0);
-                }
-            }
-            __syncthreads();
-        }
-        // lane holds A rows 16*wave + 4*(lane/16) + e of token column 16q + lane%16
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = q * 16 + (lane & 15);
-            if (row >= nrow)
-                continue;
-            const int tok = s_tok[r0 + row];
-            const float cf = s_coef[r0 + row];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int arl = wave * 16 + (lane >> 4) * 4 + e;
-                if (arl >= nar)
-                    continue;
-                const int ar = ar0 + arl;
-                const int sg = ar / R;
-                const float v = cf * acc[q][e];
-                const uint16_t hi = f32_to_bf16(v);
-                const uint16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
-                uint16_t *vp = vt + (int64_t)tok * pitch + sg * kxs + d * 2 * R + (ar - sg * R);
-                vp[0] = hi;
-                vp[R] = lo;
-            }
-        }
     }
 }
 
@@ -314,47 +336,54 @@ struct GemmArgs {
     int list_stride;
 };
 
-// Loads this thread's 4 + 4 chunks of k-tile kt (main or extra) into registers.
+// This thread's 4 + 4 chunks of one k-tile: chunk cc of rows (tid >> 3) + 64 i, i < 4.
 struct PfLoad {
     u32x4 w[4], x[4];
 };
 
-__device__ __forceinline__ void pf_load(const GemmArgs &P, int m0, int n0, int kt, int nk_main,
-                                        int m, int D, int kxs, int sg_lo, int kb_per_slice,
-                                        PfLoad &L)
+// Base k-tile at column k: branch-free (rows are clamped to valid ones; a chunk past n_in is
+// loaded from the start of its row and replaced by zeros), so the loads of a tile stay in
+// flight together.  wrow / xrow already point at this thread's chunk, column (tid & 7) * 8.
+__device__ __forceinline__ void pf_load_main(const uint16_t *const (&wrow)[4],
+                                             const uint16_t *const (&xrow)[4], int k, int n_in,
+                                             PfLoad &L)
 {
-    const int R = P.g.R;
+    const int c8 = (threadIdx.x & 7) * 8;
+    const bool ok = k + c8 < n_in;
+    const int kc = ok ? k : -c8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int e = threadIdx.x + i * PF_THREADS;   // 0..2047
-        const int row = e >> 3, cc = e & 7;
-        u32x4 wv = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+        const u32x4 wv = *(const u32x4 *)(wrow[i] + kc);
+        const u32x4 xv = *(const u32x4 *)(xrow[i] + kc);
+        L.w[i] = ok ? wv : u32x4{0u, 0u, 0u, 0u};
+        L.x[i] = ok ? xv : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// LoRA k-tile ke of the tile's extra K range (slices sg_lo.., kb_per_slice tiles each): the
+// V side comes from the tile's V block, the B side is B[a_d][n][rho..rho+8) for the tile's
+// d-th adapter when row n lies in the slice, else zero.  Branch-free as above.
+__device__ __forceinline__ void pf_load_extra(const GemmArgs &P, const uint16_t *vtile, int n0,
+                                              int ke, int D, int kxs, int sg_lo,
+                                              int kb_per_slice, const int *slist, PfLoad &L)
+{
+    const int R = P.g.R;
+    const int cc = threadIdx.x & 7;
+    const int sg = sg_lo + ke / kb_per_slice;
+    const int kk = (ke % kb_per_slice) * PF_BK + cc * 8;     // column within the slice block
+    const int dd = kk / (2 * R);
+    const int rho = (kk - dd * 2 * R) & (R - 1);
+    const int a = slist[min(dd, D - 1)];
+    const int s_lo = P.g.slice_start[sg], s_hi = P.g.slice_start[sg + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = (threadIdx.x >> 3) + 64 * i;
         const int n = n0 + row;
-        const int t = m0 + row;
-        if (kt < nk_main) {
-            const int k = kt * PF_BK + cc * 8;
-            if (n < P.n_out && k < P.n_in)
-                wv = *(const u32x4 *)(P.W + (int64_t)n * P.n_in + k);
-            if (t < P.T && k < P.n_in)
-                xv = *(const u32x4 *)(P.x + (int64_t)t * P.n_in + k);
-        } else {
-            const int ke = kt - nk_main;
-            const int sg = sg_lo + ke / kb_per_slice;
-            const int kk = (ke % kb_per_slice) * PF_BK + cc * 8;   // column within the slice block
-            // V side: tile row `row`, column sg*kxs + kk
-            if (t < P.T)
-                xv = *(const u32x4 *)(P.vcat + (int64_t)m * P.vcat_tile_elems +
-                                      (int64_t)row * (P.g.n_slices * kxs) + sg * kxs + kk);
-            // B side: B[a_d][n][rho..rho+8) (for the hi and the lo half) when row n is in slice sg
-            const int dd = kk / (2 * R);
-            if (n < P.n_out && dd < D && n >= P.g.slice_start[sg] && n < P.g.slice_start[sg + 1]) {
-                const int a = P.tile_list[(int64_t)m * P.list_stride + dd];
-                const int rho = (kk - dd * 2 * R) % R;
-                wv = *(const u32x4 *)(P.g.B + ((int64_t)a * P.n_out + n) * R + rho);
-            }
-        }
-        L.w[i] = wv;
-        L.x[i] = xv;
+        const bool ok = dd < D && n >= s_lo && n < s_hi;      // s_hi <= n_out
+        const int nc = min(n, P.n_out - 1);
+        const u32x4 bv = *(const u32x4 *)(P.g.B + ((int64_t)a * P.n_out + nc) * R + rho);
+        L.w[i] = ok ? bv : u32x4{0u, 0u, 0u, 0u};
+        L.x[i] = *(const u32x4 *)(vtile + (int64_t)row * (P.g.n_slices * kxs) + sg * kxs + kk);
     }
 }
 
@@ -369,12 +398,38 @@ __device__ __forceinline__ void pf_store(uint16_t *sw, uint16_t *sx, const PfLoa
     }
 }
 
+// MFMAs of one k-tile held in LDS: wave (wn, wm) owns W rows wn*64 .. +64 and tokens
+// wm*128 .. +128.
+__device__ __forceinline__ void pf_compute(const uint16_t *sw, const uint16_t *sx, int wn, int wm,
+                                           int r, int gq, f32x4 (&acc)[4][8])
+{
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int cch = ks * 4 + gq;
+        bf16x8 af[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = wn * 64 + i * 16 + r;
+            af[i] = *(const bf16x8 *)(sw + (row * 8 + pf_swz(row, cch)) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = wm * 128 + j * 16 + r;
+            const bf16x8 bv = *(const bf16x8 *)(sx + (row * 8 + pf_swz(row, cch)) * 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv, acc[i][j], 0, 0, 0);
+        }
+    }
+}
+
 __global__ __launch_bounds__(PF_THREADS) void prefill_gemm_kernel(GemmArgs P)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t pf_lds[];
-    // [buf][W tile 256 x 64 | x tile 256 x 64]
+    // [buf][W tile 256 x 64 | x tile 256 x 64], then the tile's adapter list
     uint16_t *sw0 = pf_lds, *sx0 = pf_lds + PF_BN * PF_BK;
     uint16_t *sw1 = pf_lds + 2 * PF_BN * PF_BK, *sx1 = sw1 + PF_BN * PF_BK;
+    int *slist = (int *)(pf_lds + 4 * PF_BN * PF_BK);
 
     // tile order: groups of 8 n-tiles per m-tile, m fastest inside a group
     const int GN = 8;
@@ -403,9 +458,22 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_gemm_kernel(GemmArgs P)
             sg_hi = sg_lo;
             while (sg_hi + 1 < P.g.n_slices && nlast >= P.g.slice_start[sg_hi + 1])
                 ++sg_hi;
+            for (int d = threadIdx.x; d < D; d += PF_THREADS)
+                slist[d] = P.tile_list[(int64_t)mt * P.list_stride + d];
         }
     }
-    const int nk = nk_main + (D > 0 ? (sg_hi - sg_lo + 1) * kb_per_slice : 0);
+    const int nk_extra = D > 0 ? (sg_hi - sg_lo + 1) * kb_per_slice : 0;
+    const uint16_t *vtile = P.vcat + (int64_t)mt * P.vcat_tile_elems;
+
+    // this thread's rows (clamped to valid ones: their results are never stored)
+    const int cc = threadIdx.x & 7;
+    const uint16_t *wrow[4], *xrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = (threadIdx.x >> 3) + 64 * i;
+        wrow[i] = P.W + (int64_t)min(n0 + row, P.n_out - 1) * P.n_in + cc * 8;
+        xrow[i] = P.x + (int64_t)min(m0 + row, P.T - 1) * P.n_in + cc * 8;
+    }
 
     f32x4 acc[4][8];
 #pragma unroll
@@ -415,37 +483,34 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_gemm_kernel(GemmArgs P)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     PfLoad L;
-    pf_load(P, m0, n0, 0, nk_main, mt, D, kxs, sg_lo, kb_per_slice, L);
+    pf_load_main(wrow, xrow, 0, P.n_in, L);
     pf_store(sw0, sx0, L);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
-        if (more)
-            pf_load(P, m0, n0, kt + 1, nk_main, mt, D, kxs, sg_lo, kb_per_slice, L);
-        const uint16_t *sw = (kt & 1) ? sw1 : sw0;
-        const uint16_t *sx = (kt & 1) ? sx1 : sx0;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int cch = ks * 4 + gq;
-            bf16x8 af[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wn * 64 + i * 16 + r;
-                af[i] = *(const bf16x8 *)(sw + (row * 8 + pf_swz(row, cch)) * 8);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int row = wm * 128 + j * 16 + r;
-                const bf16x8 bv = *(const bf16x8 *)(sx + (row * 8 + pf_swz(row, cch)) * 8);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv, acc[i][j], 0,
-                                                                        0, 0);
-            }
-        }
-        if (more)
-            pf_store((kt & 1) ? sw0 : sw1, (kt & 1) ? sx0 : sx1, L);
+    // base K: tile kt+1 is loaded while tile kt is multiplied (the load past the last tile is
+    // masked to zeros and not used)
+    int buf = 0;
+    for (int kt = 0; kt < nk_main; ++kt) {
+        pf_load_main(wrow, xrow, (kt + 1) * PF_BK, P.n_in, L);
+        pf_compute(buf ? sw1 : sw0, buf ? sx1 : sx0, wn, wm, r, gq, acc);
+        if (kt + 1 < nk_main)
+            pf_store(buf ? sw0 : sw1, buf ? sx0 : sx1, L);
         __syncthreads();
+        buf ^= 1;
+    }
+    // LoRA K: the tile's V block against the gathered B rows
+    if (nk_extra > 0) {
+        pf_load_extra(P, vtile, n0, 0, D, kxs, sg_lo, kb_per_slice, slist, L);
+        pf_store(buf ? sw1 : sw0, buf ? sx1 : sx0, L);
+        __syncthreads();
+        for (int ke = 0; ke < nk_extra; ++ke) {
+            pf_load_extra(P, vtile, n0, min(ke + 1, nk_extra - 1), D, kxs, sg_lo, kb_per_slice,
+                          slist, L);
+            pf_compute(buf ? sw1 : sw0, buf ? sx1 : sx0, wn, wm, r, gq, acc);
+            if (ke + 1 < nk_extra)
+                pf_store(buf ? sw0 : sw1, buf ? sx0 : sx1, L);
+            __syncthreads();
+            buf ^= 1;
+        }
     }
 
     // lane holds rows n0 + wn*64 + i*16 + 4*gq + (0..3) of token m0 + wm*128 + j*16 + r
@@ -513,6 +578,8 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
     p += lists;
     uint16_t *vcat = (uint16_t *)p;
 
+    if (g != nullptr && c.n_mtiles > SH_MAX_TILES)
+        return hipErrorInvalidValue;   // callers split larger batches
     if (g != nullptr) {
         const size_t lds = (size_t)((g->S + 31) / 32) * 4 + (size_t)g->S * 4;
         static size_t lds_allowed = 64 * 1024;
@@ -536,13 +603,20 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
         s.scale = scale;
         s.n_mtiles = c.n_mtiles;
         s.list_stride = c.list_stride;
-        s.n_wb = (g->n_slices * g->R + 63) / 64;
         s.tile_D = tile_D;
         s.tile_list = tile_list;
-        s.tile_cnt = tile_cnt;
         s.vcat = vcat;
         s.vcat_tile_elems = c.vcat_tile_elems;
-        hipLaunchKernelGGL(sgmv_shrink_kernel, dim3(1024), dim3(256), 0, stream, s);
+        const size_t sh_lds = (size_t)4 * 16 * 64 * sizeof(float4) + ((size_t)c.n_mtiles + 1) * sizeof(int);
+        static size_t sh_allowed = 64 * 1024;
+        if (sh_lds > sh_allowed) {
+            hipError_t e = hipFuncSetAttribute((const void *)sgmv_shrink_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh_lds);
+            if (e != hipSuccess)
+                return e;
+            sh_allowed = sh_lds;
+        }
+        hipLaunchKernelGGL(sgmv_shrink_kernel, dim3(1024), dim3(SH_THREADS), sh_lds, stream, s);
     }
     GemmArgs a{};
     a.x = x;
@@ -561,14 +635,15 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
     a.tile_D = tile_D;
     a.tile_list = tile_list;
     a.list_stride = c.list_stride;
-    const size_t lds = (size_t)4 * PF_BN * PF_BK * sizeof(uint16_t);   // 128 KB
-    static bool attr = false;
-    if (!attr) {
+    const size_t lds = (size_t)4 * PF_BN * PF_BK * sizeof(uint16_t) +    // 128 KB of tiles
+                       (size_t)c.list_stride * sizeof(int32_t);           // adapter list
+    static size_t lds_allowed = 0;
+    if (lds > lds_allowed) {
         hipError_t e = hipFuncSetAttribute((const void *)prefill_gemm_kernel,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
             return e;
-        attr = true;
+        lds_allowed = lds;
     }
     trace_mark(stream, true);
     hipLaunchKernelGGL(prefill_gemm_kernel, dim3((unsigned)(c.n_mtiles * c.n_ntiles)),
