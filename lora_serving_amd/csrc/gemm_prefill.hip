@@ -36,7 +36,6 @@ namespace mlora {
 constexpr int PF_BM = 256;   // tokens per tile
 constexpr int PF_BN = 256;   // rows of W per tile
 constexpr int PF_BK = 64;    // columns per K-step
-constexpr int PF_THREADS = 512;
 
 __device__ __forceinline__ int pf_swz(int row, int c) { return c ^ (row & 7); }
 
@@ -336,100 +335,92 @@ struct GemmArgs {
     int list_stride;
 };
 
-// This thread's 4 + 4 chunks of one k-tile: chunk cc of rows (tid >> 3) + 64 i, i < 4.
-struct PfLoad {
-    u32x4 w[4], x[4];
-};
+// GEMM: 256 W rows x 256 tokens per workgroup, 8 waves (4 along W rows x 2 along tokens,
+// 64 x 128 each), k-steps of 32 columns.  Operand tiles go from global memory straight into
+// LDS (global_load_lds_dwordx4, no register staging) through a ring of 4 stages of 32 KB, three
+// stages ahead of the MFMAs; each wave waits for its own copies of the next stage and a
+// barrier (LDS only) publishes them.  A stage holds W[256][32] and X[256][32], 64 bytes a row;
+// the 16-byte chunk c of row r sits at position c ^ ((r >> 2) & 3), so the 16 rows x 64 bytes
+// that one MFMA operand read covers hit distinct bank groups.  Chunks past n_in, masked B rows
+// and padding come from a static block of zeros.
+constexpr int PF_KS = 32;                  // columns per stage
+constexpr int PF_STAGES = 4;
+constexpr int PF_STAGE_BYTES = 2 * 256 * PF_KS * 2;
 
-// Base k-tile at column k: branch-free (rows are clamped to valid ones; a chunk past n_in is
-// loaded from the start of its row and replaced by zeros), so the loads of a tile stay in
-// flight together.  wrow / xrow already point at this thread's chunk, column (tid & 7) * 8.
-__device__ __forceinline__ void pf_load_main(const uint16_t *const (&wrow)[4],
-                                             const uint16_t *const (&xrow)[4], int k, int n_in,
-                                             PfLoad &L)
+__device__ __attribute__((aligned(64))) uint32_t pf_zero16[16];   // never written: zeros
+
+__device__ __forceinline__ void pf_dma(const void *g, uint16_t *lds)
 {
-    const int c8 = (threadIdx.x & 7) * 8;
-    const bool ok = k + c8 < n_in;
-    const int kc = ok ? k : -c8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u32x4 wv = *(const u32x4 *)(wrow[i] + kc);
-        const u32x4 xv = *(const u32x4 *)(xrow[i] + kc);
-        L.w[i] = ok ? wv : u32x4{0u, 0u, 0u, 0u};
-        L.x[i] = ok ? xv : u32x4{0u, 0u, 0u, 0u};
-    }
+    __builtin_amdgcn_global_load_lds(g, (void __attribute__((address_space(3))) *)lds, 16, 0, 0);
 }
 
-// LoRA k-tile ke of the tile's extra K range (slices sg_lo.., kb_per_slice tiles each): the
-// V side comes from the tile's V block, the B side is B[a_d][n][rho..rho+8) for the tile's
-// d-th adapter when row n lies in the slice, else zero.  Branch-free as above.
-__device__ __forceinline__ void pf_load_extra(const GemmArgs &P, const uint16_t *vtile, int n0,
-                                              int ke, int D, int kxs, int sg_lo,
-                                              int kb_per_slice, const int *slist, PfLoad &L)
+// Issues this wave's copies of stage q (k-step q: base columns q*32 while q < nk_main, then
+// the LoRA extra steps) into buffer `st`: 2 blocks of 16 W rows and 2 of 16 tokens per wave.
+__device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q, int nk_main,
+                                         int nk_extra, int m0, int n0, const uint16_t *vtile,
+                                         int D, int kxs, int sg_lo, int kb_per_slice,
+                                         const int *slist, int wave, int lane)
 {
-    const int R = P.g.R;
-    const int cc = threadIdx.x & 7;
-    const int sg = sg_lo + ke / kb_per_slice;
-    const int kk = (ke % kb_per_slice) * PF_BK + cc * 8;     // column within the slice block
-    const int dd = kk / (2 * R);
-    const int rho = (kk - dd * 2 * R) & (R - 1);
-    const int a = slist[min(dd, D - 1)];
-    const int s_lo = P.g.slice_start[sg], s_hi = P.g.slice_start[sg + 1];
+    const int rr = lane >> 2;                       // row within the 16-row block
+    const int c = (lane & 3) ^ ((rr >> 2) & 3);     // chunk this lane's position holds
+    uint16_t *sw = st, *sx = st + 256 * PF_KS;
+    if (q < nk_main) {
+        const int k = q * PF_KS + c * 8;
+        const bool ok = k < P.n_in;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (threadIdx.x >> 3) + 64 * i;
-        const int n = n0 + row;
-        const bool ok = dd < D && n >= s_lo && n < s_hi;      // s_hi <= n_out
-        const int nc = min(n, P.n_out - 1);
-        const u32x4 bv = *(const u32x4 *)(P.g.B + ((int64_t)a * P.n_out + nc) * R + rho);
-        L.w[i] = ok ? bv : u32x4{0u, 0u, 0u, 0u};
-        L.x[i] = *(const u32x4 *)(vtile + (int64_t)row * (P.g.n_slices * kxs) + sg * kxs + kk);
-    }
-}
-
-__device__ __forceinline__ void pf_store(uint16_t *sw, uint16_t *sx, const PfLoad &L)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = threadIdx.x + i * PF_THREADS;
-        const int row = e >> 3, cc = e & 7;
-        *(u32x4 *)(sw + (row * 8 + pf_swz(row, cc)) * 8) = L.w[i];
-        *(u32x4 *)(sx + (row * 8 + pf_swz(row, cc)) * 8) = L.x[i];
-    }
-}
-
-// MFMAs of one k-tile held in LDS: wave (wn, wm) owns W rows wn*64 .. +64 and tokens
-// wm*128 .. +128.
-__device__ __forceinline__ void pf_compute(const uint16_t *sw, const uint16_t *sx, int wn, int wm,
-                                           int r, int gq, f32x4 (&acc)[4][8])
-{
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const int cch = ks * 4 + gq;
-        bf16x8 af[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = wn * 64 + i * 16 + r;
-            af[i] = *(const bf16x8 *)(sw + (row * 8 + pf_swz(row, cch)) * 8);
+        for (int b = 0; b < 2; ++b) {
+            const int row = (wave * 2 + b) * 16 + rr;
+            const uint16_t *gw = P.W + (int64_t)min(n0 + row, P.n_out - 1) * P.n_in + k;
+            const uint16_t *gx = P.x + (int64_t)min(m0 + row, P.T - 1) * P.n_in + k;
+            pf_dma(ok ? (const void *)gw : (const void *)pf_zero16, sw + (wave * 2 + b) * 16 * PF_KS);
+            pf_dma(ok ? (const void *)gx : (const void *)pf_zero16, sx + (wave * 2 + b) * 16 * PF_KS);
         }
+    } else {
+        const int R = P.g.R;
+        const int ke = min(q - nk_main, nk_extra - 1);
+        const int sg = sg_lo + ke / kb_per_slice;
+        const int kk = (ke % kb_per_slice) * PF_KS + c * 8;   // column within the slice block
+        const int dd = kk / (2 * R);
+        const int rho = (kk - dd * 2 * R) & (R - 1);
+        const int a = slist[min(dd, D - 1)];
+        const int s_lo = P.g.slice_start[sg], s_hi = P.g.slice_start[sg + 1];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = wm * 128 + j * 16 + r;
-            const bf16x8 bv = *(const bf16x8 *)(sx + (row * 8 + pf_swz(row, cch)) * 8);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv, acc[i][j], 0, 0, 0);
+        for (int b = 0; b < 2; ++b) {
+            const int row = (wave * 2 + b) * 16 + rr;
+            const int n = n0 + row;
+            const bool ok = dd < D && n >= s_lo && n < s_hi;   // s_hi <= n_out
+            const uint16_t *gb = P.g.B + ((int64_t)a * P.n_out + min(n, P.n_out - 1)) * R + rho;
+            const uint16_t *gv = vtile + (int64_t)row * (P.g.n_slices * kxs) + sg * kxs + kk;
+            pf_dma(ok ? (const void *)gb : (const void *)pf_zero16, sw + (wave * 2 + b) * 16 * PF_KS);
+            pf_dma((const void *)gv, sx + (wave * 2 + b) * 16 * PF_KS);
         }
     }
 }
 
-__global__ __launch_bounds__(PF_THREADS) void prefill_gemm_kernel(GemmArgs P)
+// MFMAs of one stage: wave (wn, wm) owns W rows wn*64 .. +64 and tokens wm*128 .. +128.
+__device__ __forceinline__ void pf_compute(const uint16_t *st, int wn, int wm, int r, int gq,
+                                           f32x4 (&acc)[4][8])
+{
+    const uint16_t *sw = st, *sx = st + 256 * PF_KS;
+    const int pos = gq ^ ((r >> 2) & 3);
+    bf16x8 af[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        af[i] = *(const bf16x8 *)(sw + ((wn * 64 + i * 16 + r) * 4 + pos) * 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const bf16x8 bv = *(const bf16x8 *)(sx + ((wm * 128 + j * 16 + r) * 4 + pos) * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv, acc[i][j], 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t pf_lds[];
-    // [buf][W tile 256 x 64 | x tile 256 x 64], then the tile's adapter list
-    uint16_t *sw0 = pf_lds, *sx0 = pf_lds + PF_BN * PF_BK;
-    uint16_t *sw1 = pf_lds + 2 * PF_BN * PF_BK, *sx1 = sw1 + PF_BN * PF_BK;
-    int *slist = (int *)(pf_lds + 4 * PF_BN * PF_BK);
+    // [stage][W 256 x 32 | X 256 x 32], then the tile's adapter list
+    int *slist = (int *)(pf_lds + PF_STAGES * PF_STAGE_BYTES / 2);
 
     // tile order: groups of 8 n-tiles per m-tile, m fastest inside a group
     const int GN = 8;
@@ -445,35 +436,27 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_gemm_kernel(GemmArgs P)
     const int wn = wave & 3, wm = wave >> 2;
     const int r = lane & 15, gq = lane >> 4;
 
-    const int nk_main = (P.n_in + PF_BK - 1) / PF_BK;
+    const int nk_main = (P.n_in + PF_KS - 1) / PF_KS;
     int D = 0, kxs = 0, sg_lo = 0, sg_hi = -1, kb_per_slice = 1;
     if (P.lora) {
         D = P.tile_D[mt];
         kxs = ((D * 2 * P.g.R + PF_BK - 1) / PF_BK) * PF_BK;
         if (D > 0) {
-            kb_per_slice = kxs / PF_BK;
+            kb_per_slice = kxs / PF_KS;
             const int nlast = min(n0 + PF_BN, P.n_out) - 1;
             while (sg_lo + 1 < P.g.n_slices && n0 >= P.g.slice_start[sg_lo + 1])
                 ++sg_lo;
             sg_hi = sg_lo;
             while (sg_hi + 1 < P.g.n_slices && nlast >= P.g.slice_start[sg_hi + 1])
                 ++sg_hi;
-            for (int d = threadIdx.x; d < D; d += PF_THREADS)
+            for (int d = threadIdx.x; d < D; d += 512)
                 slist[d] = P.tile_list[(int64_t)mt * P.list_stride + d];
         }
     }
     const int nk_extra = D > 0 ? (sg_hi - sg_lo + 1) * kb_per_slice : 0;
+    const int nk = nk_main + nk_extra;
     const uint16_t *vtile = P.vcat + (int64_t)mt * P.vcat_tile_elems;
-
-    // this thread's rows (clamped to valid ones: their results are never stored)
-    const int cc = threadIdx.x & 7;
-    const uint16_t *wrow[4], *xrow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (threadIdx.x >> 3) + 64 * i;
-        wrow[i] = P.W + (int64_t)min(n0 + row, P.n_out - 1) * P.n_in + cc * 8;
-        xrow[i] = P.x + (int64_t)min(m0 + row, P.T - 1) * P.n_in + cc * 8;
-    }
+    __syncthreads();   // slist
 
     f32x4 acc[4][8];
 #pragma unroll
@@ -482,36 +465,23 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_gemm_kernel(GemmArgs P)
         for (int j = 0; j < 8; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    PfLoad L;
-    pf_load_main(wrow, xrow, 0, P.n_in, L);
-    pf_store(sw0, sx0, L);
-    __syncthreads();
-    // base K: tile kt+1 is loaded while tile kt is multiplied (the load past the last tile is
-    // masked to zeros and not used)
-    int buf = 0;
-    for (int kt = 0; kt < nk_main; ++kt) {
-        pf_load_main(wrow, xrow, (kt + 1) * PF_BK, P.n_in, L);
-        pf_compute(buf ? sw1 : sw0, buf ? sx1 : sx0, wn, wm, r, gq, acc);
-        if (kt + 1 < nk_main)
-            pf_store(buf ? sw0 : sw1, buf ? sx0 : sx1, L);
-        __syncthreads();
-        buf ^= 1;
+    // stages past the last k-step repeat it (never read), so every iteration issues the same
+    // number of copies and the wait counts below stay exact
+#pragma unroll
+    for (int q = 0; q < PF_STAGES; ++q)
+        pf_issue(P, pf_lds + q * (PF_STAGE_BYTES / 2), min(q, nk - 1), nk_main, nk_extra, m0, n0,
+                 vtile, D, kxs, sg_lo, kb_per_slice, slist, wave, lane);
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");   // stage 0 (4 copies per stage)
+    lds_barrier();
+    for (int q = 0; q < nk; ++q) {
+        uint16_t *st = pf_lds + (q & (PF_STAGES - 1)) * (PF_STAGE_BYTES / 2);
+        pf_compute(st, wn, wm, r, gq, acc);
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // stage q+1
+        lds_barrier();                                      // also: stage q fully read
+        pf_issue(P, st, min(q + PF_STAGES, nk - 1), nk_main, nk_extra, m0, n0, vtile, D, kxs,
+                 sg_lo, kb_per_slice, slist, wave, lane);
     }
-    // LoRA K: the tile's V block against the gathered B rows
-    if (nk_extra > 0) {
-        pf_load_extra(P, vtile, n0, 0, D, kxs, sg_lo, kb_per_slice, slist, L);
-        pf_store(buf ? sw1 : sw0, buf ? sx1 : sx0, L);
-        __syncthreads();
-        for (int ke = 0; ke < nk_extra; ++ke) {
-            pf_load_extra(P, vtile, n0, min(ke + 1, nk_extra - 1), D, kxs, sg_lo, kb_per_slice,
-                          slist, L);
-            pf_compute(buf ? sw1 : sw0, buf ? sx1 : sx0, wn, wm, r, gq, acc);
-            if (ke + 1 < nk_extra)
-                pf_store(buf ? sw0 : sw1, buf ? sx0 : sx1, L);
-            __syncthreads();
-            buf ^= 1;
-        }
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no copy outlives the workgroup
 
     // lane holds rows n0 + wn*64 + i*16 + 4*gq + (0..3) of token m0 + wm*128 + j*16 + r
 #pragma unroll
@@ -635,7 +605,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
     a.tile_D = tile_D;
     a.tile_list = tile_list;
     a.list_stride = c.list_stride;
-    const size_t lds = (size_t)4 * PF_BN * PF_BK * sizeof(uint16_t) +    // 128 KB of tiles
+    const size_t lds = (size_t)PF_STAGES * PF_STAGE_BYTES +               // 128 KB of stages
                        (size_t)c.list_stride * sizeof(int32_t);           // adapter list
     static size_t lds_allowed = 0;
     if (lds > lds_allowed) {
@@ -646,8 +616,8 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
         lds_allowed = lds;
     }
     trace_mark(stream, true);
-    hipLaunchKernelGGL(prefill_gemm_kernel, dim3((unsigned)(c.n_mtiles * c.n_ntiles)),
-                       dim3(PF_THREADS), lds, stream, a);
+    hipLaunchKernelGGL(prefill_gemm_kernel, dim3((unsigned)(c.n_mtiles * c.n_ntiles)), dim3(512),
+                       lds, stream, a);
     const hipError_t e = hipGetLastError();
     trace_mark(stream, false);
     return e;
