@@ -422,11 +422,17 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
     // [stage][W 256 x 32 | X 256 x 32], then the tile's adapter list
     int *slist = (int *)(pf_lds + PF_STAGES * PF_STAGE_BYTES / 2);
 
-    // tile order: groups of 8 n-tiles per m-tile, m fastest inside a group
+    // Workgroups are dealt to the 8 XCDs round robin (their own L2 each): give every XCD a
+    // contiguous run of logical tiles, ordered in groups of 8 n-tiles per m-tile, so the
+    // tiles an XCD runs together share their x and W panels in its L2.  Any bijection is
+    // correct; this one only decides which tiles meet in which cache.
+    const int nwg = gridDim.x;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int lt = xcd * (nwg >> 3) + min(xcd, nwg & 7) + slot;
     const int GN = 8;
     const int per_group = GN * P.n_mtiles;
-    const int grp = blockIdx.x / per_group;
-    const int rem = blockIdx.x - grp * per_group;
+    const int grp = lt / per_group;
+    const int rem = lt - grp * per_group;
     const int gn = min(GN, P.n_ntiles - grp * GN);
     const int mt = rem / gn;
     const int nt = grp * GN + (rem - mt * gn);
