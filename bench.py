@@ -67,6 +67,31 @@ def algorithmic(L):
             "tiled_kernel_flops": base_flops + expand_flops}
 
 
+def committed_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the counter summary committed under profiles/
+    (FETCH_SIZE and WRITE_SIZE runs, calibrated with a plain copy kernel), or None when there is
+    none or the kernel's sources changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        fields = {}
+        for line in open(path):
+            line = line.strip()
+            if line.startswith("traffic_") and ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        if fields.get("traffic_kernel") != kernel:
+            continue
+        h = hashlib.sha256()
+        for f in fields.get("traffic_sources", "").split():
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != fields.get("traffic_sources_sha256"):
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    return None
+
+
 def cpu_baseline(layers, budget_s: float):
     """The oracle, as it stands, on the host cores, on a bounded sample of the workload's
     tokens (whole batches while they take under the budget), scaled to tokens/s."""
@@ -111,6 +136,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--flags", type=int, default=0, help="extra mlora_linear flags")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain copy kernel over MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -151,6 +178,15 @@ def main():
         for (x, W, slots, y, D) in sets[i % nsets]:
             mlora.mlora_linear(x, W, slots, D.idx, D.scale, y, flags=args.flags, ws=D.ws)
 
+    if args.calibrate_copy:
+        # a plain elementwise copy of known size, for scaling the HBM byte counters
+        src = torch.ones(args.calibrate_copy * 2 ** 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -181,18 +217,13 @@ def main():
     tokens_per_s = T / (ms * 1e-3)
     tot_bytes = sum(a["bytes"] for a in algs)
     tot_flops = sum(a["flops"] for a in algs)
-    fused = os.environ.get("MLORA_DECODE_FUSED") is not None
     if decode_like:
-        if fused:
-            kname = "mlora::decode_gemm_kernel<.., true> (whole layer in one launch)"
-            k_bytes = tot_bytes
-        else:
-            kname = "mlora::decode_gemm_kernel<.., false> (base product + shrink)"
-            k_bytes = sum(a["decode_kernel_bytes"] for a in algs)
-        k_bytes /= launches_per_step
+        kname = "mlora::decode_gemm_kernel (base product + LoRA shrink)"
+        k_bytes = sum(a["decode_kernel_bytes"] for a in algs) / launches_per_step
         achieved = k_bytes / (k_avg_ms * 1e-3) / 1e9
+        traffic = committed_traffic("decode_gemm_kernel") if args.workload == "decode" else None
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                 "kernel": kname, "kernel_avg_us": k_avg_ms * 1e3,
                 "algorithmic_bytes_per_launch": k_bytes,
                 "step_achieved_GBps": tot_bytes / (ms * 1e-3) / 1e9}

@@ -176,9 +176,10 @@ mlora_status mlora_trace_start(int32_t capacity)
     g_trace.begin.resize(capacity);
     g_trace.end.resize(capacity);
     for (int32_t i = 0; i < capacity; ++i) {
-        hipError_t e = hipEventCreate(&g_trace.begin[i]);
+        // no system-scope fence at the record: the pair then costs far less than a fenced one
+        hipError_t e = hipEventCreateWithFlags(&g_trace.begin[i], hipEventDisableSystemFence);
         if (e == hipSuccess)
-            e = hipEventCreate(&g_trace.end[i]);
+            e = hipEventCreateWithFlags(&g_trace.end[i], hipEventDisableSystemFence);
         if (e != hipSuccess) {
             g_trace.begin.resize(i + 1);
             g_trace.end.resize(i + 1);
