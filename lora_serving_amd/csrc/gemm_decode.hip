@@ -35,6 +35,16 @@ constexpr int DEC_ROWS = 64;    // rows of W per workgroup
 constexpr int DEC_WK = 128;     // columns of n_in per wave
 constexpr int DEC_WAVES = 8;
 
+// 16 bytes at row + c when ok, else 16 zero bytes read from a static block: the choice is
+// made on the address, so the load's result is used as is (no select that would wait for the
+// load right after issuing it) and no branch splits the load stream.
+__device__ __attribute__((aligned(64))) uint32_t dec_zero16[16];   // never written: zeros
+
+__device__ __forceinline__ u32x4 dec_ld16(const uint16_t *row, int c, bool ok)
+{
+    return *(const u32x4 *)(ok ? row + c : (const uint16_t *)dec_zero16);
+}
+
 // Shrink piece of pair p, A rows r0..r0+15: D[16 rows][16 tokens] = A rows x (the token tile
 // holding t), one MFMA per 32 columns on fragments already in registers; the pair's token
 // column is summed over the 8 waves (fixed order) and written to upart[s][j][t][r0..].
@@ -124,9 +134,8 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
         for (int ks = 0; ks < 4; ++ks) {
             const int row = tt * 16 + ks * 4 + gq;
             const int c = kw + r * 8;
-            xf[tt][ks] = (wave_on && row < T && c < n_in)
-                             ? *(const u32x4 *)(x + (int64_t)row * n_in + c)
-                             : u32x4{0u, 0u, 0u, 0u};
+            xf[tt][ks] = dec_ld16(x + (int64_t)min(row, T - 1) * n_in, c,
+                                  wave_on && row < T && c < n_in);
         }
     // ---- first shrink piece of this workgroup: pair p = tile, rows 0..15 of A[a]
     const int wd = g.n_slices * g.R;
@@ -134,14 +143,15 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
     if (upart != nullptr && tile < P.n_pairs)
         a0 = P.idx[tile];
     u32x4 af[4];
-    if (a0 >= 0) {
-        const int arow = min(r, wd - 1);
-        const uint16_t *ap = g.A + ((int64_t)a0 * wd + arow) * n_in;
+    {
+        // issued whether or not the pair has an adapter (slot 0's rows then, or x's first row
+        // without LoRA; unused either way)
+        const int arow = min(r, max(wd, 1) - 1);
+        const uint16_t *ap = upart != nullptr ? g.A + ((int64_t)max(a0, 0) * wd + arow) * n_in : x;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int c = col(ks);
-            af[ks] = (wave_on && c < n_in && r < wd) ? *(const u32x4 *)(ap + c)
-                                                     : u32x4{0u, 0u, 0u, 0u};
+            af[ks] = dec_ld16(ap, c, a0 >= 0 && wave_on && c < n_in && r < wd);
         }
     }
 
@@ -155,10 +165,12 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
             const int row = tile * DEC_ROWS + rt * 16 + r;
             const uint16_t *wrow = W + (int64_t)min(row, n_out - 1) * n_in;
             const int c = col(ks);
-            wf[rt][ks] = (wave_on && c < n_in && row < n_out) ? *(const u32x4 *)(wrow + c)
-                                                              : u32x4{0u, 0u, 0u, 0u};
+            wf[rt][ks] = dec_ld16(wrow, c, wave_on && c < n_in && row < n_out);
         }
     }
+    // every load of the workgroup's slice is in flight before the first wait below (keeps the
+    // scheduler from hoisting the x transpose, and its waits, between the W loads)
+    asm volatile("" ::: "memory");
 
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
@@ -212,8 +224,7 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int c = col(ks);
-                    afr[ks] = (wave_on && c < n_in && arow < wd) ? *(const u32x4 *)(ap + c)
-                                                                 : u32x4{0u, 0u, 0u, 0u};
+                    afr[ks] = dec_ld16(ap, c, wave_on && c < n_in && arow < wd);
                 }
                 decode_shrink_piece<TT>(xf, afr, p, r0, K, T, wd, s, wave, r, gq, sred, upart);
             }
