@@ -22,6 +22,10 @@ constexpr int DF_TOK = 16;        // tokens per workgroup
 constexpr int DF_THREADS = 256;   // 16 tokens x 16 groups of 4 rows
 constexpr int DF_BPRE_R = 16;     // ranks up to which slot 0's B rows are prefetched
 
+// Masked loads read this static block instead (the choice is made on the address, so no
+// select waits for a load right after it is issued).
+__device__ __attribute__((aligned(64))) float df_zero[16];   // never written: zeros
+
 // 8 bf16 (packed) times 8 fp32, summed in order
 __device__ __forceinline__ float dot8(const u32x4 b, const float *v)
 {
@@ -35,6 +39,27 @@ __device__ __forceinline__ float dot8(const u32x4 b, const float *v)
     d += bf16_lo(b.w) * v[6];
     d += bf16_hi(b.w) * v[7];
     return d;
+}
+
+// Loads the split partials of this thread's 4 rows (up to DF_PQ in flight; more splits are
+// added in further groups) without waiting for them.
+constexpr int DF_PQ = 8;
+
+// v of one (slot j, slice sg) for the block's tokens: element e0..e0+3 of the [DF_TOK][R]
+// block, the pieces of the sk splits (zeros for a -1 slot) loaded into pv.
+__device__ __forceinline__ void df_vload(const float *upart, int sk, int64_t pstride, int K, int T,
+                                         int wd, int R, int t0, int j, int sg, int e0,
+                                         const int *sidx, const float *scale, const float *factor,
+                                         float4 (&pv)[DF_PQ], float &sc, float &fa)
+{
+    const int tt = e0 / R, c = e0 - tt * R;
+    const int a = sidx[tt * K + j];
+    const float *src = upart + ((int64_t)j * T + t0 + tt) * wd + sg * R + c;
+#pragma unroll
+    for (int sp = 0; sp < DF_PQ; ++sp)
+        pv[sp] = *(const float4 *)(a >= 0 && sp < sk ? src + sp * pstride : df_zero);
+    sc = *(scale ? scale + (t0 + tt) * K + j : df_zero + 1);    // df_zero[1] stands for "no scale"
+    fa = *(a >= 0 ? factor + a : df_zero);
 }
 
 __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
@@ -54,31 +79,27 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
     const int n = row0 + g4 * 4;                  // first of this thread's 4 rows
     const bool lora = upart != nullptr;
     const int R = g.R, wd = g.n_slices * R;
+    const int64_t pstride = (int64_t)K * T * wd;
 
-    if (lora && threadIdx.x < nt * K)
-        sidx[threadIdx.x] = idx[t0 * K + threadIdx.x];
+    // ---- phase 1: the slot map and the first DF_PQ split partials, all in flight
+    const bool has_idx = lora && (int)threadIdx.x < nt * K;
+    const int32_t my_idx = *(has_idx ? idx + t0 * K + threadIdx.x : (const int32_t *)df_zero);
+    const float *psrc = part + ((int64_t)tile * T + min(t, T - 1)) * DF_ROWS + g4 * 4;
+    const int64_t sstride = (int64_t)n_tiles * T * DF_ROWS;
+    float4 pq[DF_PQ];
+#pragma unroll
+    for (int sp = 0; sp < DF_PQ; ++sp)
+        pq[sp] = *(const float4 *)(sp < sk ? psrc + sp * sstride : df_zero);
+    asm volatile("" ::: "memory");
 
-    // base: split partials of this thread's 4 rows, in split order
-    float4 base = {0.f, 0.f, 0.f, 0.f};
-    if (tl < nt) {
-        const float *src = part + ((int64_t)tile * T + t) * DF_ROWS + g4 * 4;
-        const int64_t sstride = (int64_t)n_tiles * T * DF_ROWS;
-#pragma unroll 4
-        for (int sp = 0; sp < sk; ++sp) {
-            const float4 o = *(const float4 *)(src + sp * sstride);
-            base.x += o.x;
-            base.y += o.y;
-            base.z += o.z;
-            base.w += o.w;
-        }
-    }
-
-    // LoRA delta, one (slot j, slice sg) at a time: v[j][t0 + tt][sg*R .. sg*R + R) =
-    // coef * (pieces summed in split order), zero for -1 slots, staged in LDS.  For small
-    // ranks the B rows of slot 0 are loaded before the staging, so the two loads overlap.
     float d4[4] = {0.f, 0.f, 0.f, 0.f};
     if (lora) {
-        lds_barrier();   // sidx visible
+        // ---- phase 2: the slot map in LDS
+        if (has_idx)
+            sidx[threadIdx.x] = my_idx;
+        lds_barrier();
+        // ---- phase 3: slot 0's B rows for this thread (small ranks) and the first round's
+        //      pieces, all in flight before anything waits
         int rsg[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -89,45 +110,57 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
             rsg[i] = sg;
         }
         const bool pre = R <= DF_BPRE_R;
+        const int a0 = tl < nt ? sidx[tl * K] : -1;
         u32x4 bp[4][DF_BPRE_R / 8];
-        if (pre) {
-            const int a = tl < nt ? sidx[tl * K] : -1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint16_t *brow = g.B + ((int64_t)max(a, 0) * n_out + min(n + i, n_out - 1)) * R;
+        for (int i = 0; i < 4; ++i) {
+            const uint16_t *brow = g.B + ((int64_t)max(a0, 0) * n_out + min(n + i, n_out - 1)) * R;
 #pragma unroll
-                for (int u = 0; u < DF_BPRE_R / 8; ++u)
-                    bp[i][u] = (a >= 0 && u * 8 < R) ? *(const u32x4 *)(brow + u * 8)
-                                                     : u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int u = 0; u < DF_BPRE_R / 8; ++u)
+                bp[i][u] = *(const u32x4 *)((pre && a0 >= 0 && u * 8 < R)
+                                                ? (const void *)(brow + u * 8)
+                                                : (const void *)df_zero);
         }
-        const int64_t pstride = (int64_t)K * T * wd;
-        const int nv = nt * R;                    // a multiple of 8
+        const int nv = nt * R;                     // a multiple of 8
+        const int e0 = threadIdx.x * 4;
+        float4 pv[DF_PQ];
+        float sc = 0.f, fa = 0.f;
+        if (e0 < nv)
+            df_vload(upart, sk, pstride, K, T, wd, R, t0, 0, 0, e0, sidx, scale, g.factor, pv, sc,
+                     fa);
+        asm volatile("" ::: "memory");
+
+        // ---- phase 4: v in LDS one (slot, slice) round at a time, then the expand
         for (int j = 0; j < K; ++j) {
             for (int sg = 0; sg < g.n_slices; ++sg) {
                 if (j + sg > 0)
-                    lds_barrier();                // the previous round's reads are done
-                for (int e0 = threadIdx.x * 4; e0 < nv; e0 += DF_THREADS * 4) {
-                    const int tt = e0 / R, c = e0 - tt * R;
+                    lds_barrier();                 // the previous round's reads are done
+                for (int e = e0; e < nv; e += DF_THREADS * 4) {
+                    if (j + sg > 0 || e != e0)
+                        df_vload(upart, sk, pstride, K, T, wd, R, t0, j, sg, e, sidx, scale,
+                                 g.factor, pv, sc, fa);
+                    const int tt = e / R;
                     const int a = sidx[tt * K + j];
                     float4 sum = {0.f, 0.f, 0.f, 0.f};
-                    if (a >= 0) {
-                        const float *src = upart + ((int64_t)j * T + t0 + tt) * wd + sg * R + c;
-#pragma unroll 4
-                        for (int sp = 0; sp < sk; ++sp) {
-                            const float4 o = *(const float4 *)(src + sp * pstride);
-                            sum.x += o.x;
-                            sum.y += o.y;
-                            sum.z += o.z;
-                            sum.w += o.w;
-                        }
-                        const float cf = (scale ? scale[(t0 + tt) * K + j] : 1.f) * g.factor[a];
-                        sum.x *= cf;
-                        sum.y *= cf;
-                        sum.z *= cf;
-                        sum.w *= cf;
+#pragma unroll
+                    for (int sp = 0; sp < DF_PQ; ++sp) {
+                        sum.x += pv[sp].x;
+                        sum.y += pv[sp].y;
+                        sum.z += pv[sp].z;
+                        sum.w += pv[sp].w;
                     }
-                    *(float4 *)(vl + e0) = sum;
+                    // splits past DF_PQ (rare): added in split order after the first ones
+                    for (int sp = DF_PQ; sp < sk; ++sp) {
+                        const float4 o = *(const float4 *)(a >= 0 ? upart + ((int64_t)j * T + t0 + tt) * wd +
+                                                                        sg * R + (e - tt * R) + sp * pstride
+                                                                  : df_zero);
+                        sum.x += o.x;
+                        sum.y += o.y;
+                        sum.z += o.z;
+                        sum.w += o.w;
+                    }
+                    const float cf = a >= 0 ? (scale ? sc : 1.f) * fa : 0.f;
+                    *(float4 *)(vl + e) = float4{sum.x * cf, sum.y * cf, sum.z * cf, sum.w * cf};
                 }
                 lds_barrier();
                 const int a = tl < nt ? sidx[tl * K + j] : -1;
@@ -154,10 +187,26 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
             }
         }
     }
-    const float4 delta = {d4[0], d4[1], d4[2], d4[3]};
+
+    // ---- base: the split partials in split order
+    float4 base = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < DF_PQ; ++sp) {
+        base.x += pq[sp].x;
+        base.y += pq[sp].y;
+        base.z += pq[sp].z;
+        base.w += pq[sp].w;
+    }
+    for (int sp = DF_PQ; sp < sk; ++sp) {
+        const float4 o = *(const float4 *)(psrc + sp * sstride);
+        base.x += o.x;
+        base.y += o.y;
+        base.z += o.z;
+        base.w += o.w;
+    }
     if (tl >= nt)
         return;
-    const float o4[4] = {base.x + delta.x, base.y + delta.y, base.z + delta.z, base.w + delta.w};
+    const float o4[4] = {base.x + d4[0], base.y + d4[1], base.z + d4[2], base.w + d4[3]};
     uint16_t *yo = y + (int64_t)t * n_out + n;
     if (n + 3 < n_out && (n_out & 3) == 0) {
         *(u32x2 *)yo = u32x2{pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3])};
