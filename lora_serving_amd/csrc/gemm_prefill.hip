@@ -35,9 +35,11 @@ namespace mlora {
 
 constexpr int PF_BM = 256;   // tokens per tile
 constexpr int PF_BN = 256;   // rows of W per tile
-constexpr int PF_BK = 64;    // columns per K-step
+constexpr int PF_BK = 64;    // column granule of a tile's V block (its width is a multiple)
 
-__device__ __forceinline__ int pf_swz(int row, int c) { return c ^ (row & 7); }
+// Masked loads read this static block instead of choosing zero after the load: the choice is
+// made on the address, so nothing waits for a load right after it is issued.
+__device__ __attribute__((aligned(64))) uint32_t pf_zero16[16];   // never written: zeros
 
 // ------------------------------------------------------------------------------------------
 // 1. tile plan
@@ -160,13 +162,10 @@ __device__ __forceinline__ void sh_load(const uint16_t *const (&ap)[4], const ui
     // the pointers already include this lane's chunk offset 8 * (lane / 16)
     const int off = ((threadIdx.x & 63) >> 4) * 8;
     const bool ok = col + off < kend;
-    const int c = ok ? col : -off;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        const u32x4 av = *(const u32x4 *)(ap[b] + c);
-        const u32x4 xv = *(const u32x4 *)(xp[b] + c);
-        af[b] = ok ? av : u32x4{0u, 0u, 0u, 0u};
-        xf[b] = ok ? xv : u32x4{0u, 0u, 0u, 0u};
+        af[b] = *(const u32x4 *)(ok ? (const void *)(ap[b] + col) : (const void *)pf_zero16);
+        xf[b] = *(const u32x4 *)(ok ? (const void *)(xp[b] + col) : (const void *)pf_zero16);
     }
 }
 
@@ -346,8 +345,6 @@ struct GemmArgs {
 constexpr int PF_KS = 32;                  // columns per stage
 constexpr int PF_STAGES = 4;
 constexpr int PF_STAGE_BYTES = 2 * 256 * PF_KS * 2;
-
-__device__ __attribute__((aligned(64))) uint32_t pf_zero16[16];   // never written: zeros
 
 __device__ __forceinline__ void pf_dma(const void *g, uint16_t *lds)
 {
