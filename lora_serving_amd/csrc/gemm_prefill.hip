@@ -339,9 +339,12 @@ struct GemmArgs {
 // LDS (global_load_lds_dwordx4, no register staging) through a ring of 4 stages of 32 KB, three
 // stages ahead of the MFMAs; each wave waits for its own copies of the next stage and a
 // barrier (LDS only) publishes them.  A stage holds W[256][32] and X[256][32], 64 bytes a row;
-// the 16-byte chunk c of row r sits at position c ^ ((r >> 2) & 3), so the 16 rows x 64 bytes
-// that one MFMA operand read covers hit distinct bank groups.  Chunks past n_in, masked B rows
-// and padding come from a static block of zeros.
+// one copy instruction fills a contiguous 1 KB block (lane L writes bytes 16 L..16 L+15: 16
+// rows, 4 lanes per row so each row is read as 64 contiguous bytes), and the 16-byte chunk c
+// of row r sits at position c ^ ((r >> 1) & 3) of its row.  With that swizzle the operand read
+// of a 16 x 32 fragment (lane (r, g) reads row r, chunk g) has no LDS bank conflicts on
+// gfx950 (the plain layout and the (r >> 2) swizzle both measured two-way conflicts).
+// Chunks past n_in, masked B rows and padding are copied from a static block of zeros.
 constexpr int PF_KS = 32;                  // columns per stage
 constexpr int PF_STAGES = 4;
 constexpr int PF_STAGE_BYTES = 2 * 256 * PF_KS * 2;
@@ -359,7 +362,7 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
                                          const int *slist, int wave, int lane)
 {
     const int rr = lane >> 2;                       // row within the 16-row block
-    const int c = (lane & 3) ^ ((rr >> 2) & 3);     // chunk this lane's position holds
+    const int c = (lane & 3) ^ ((rr >> 1) & 3);     // chunk this lane's position holds
     uint16_t *sw = st, *sx = st + 256 * PF_KS;
     if (q < nk_main) {
         const int k = q * PF_KS + c * 8;
@@ -399,7 +402,7 @@ __device__ __forceinline__ void pf_compute(const uint16_t *st, int wn, int wm, i
                                            f32x4 (&acc)[4][8])
 {
     const uint16_t *sw = st, *sx = st + 256 * PF_KS;
-    const int pos = gq ^ ((r >> 2) & 3);
+    const int pos = gq ^ ((r >> 1) & 3);
     bf16x8 af[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
