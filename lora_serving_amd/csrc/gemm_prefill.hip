@@ -346,7 +346,7 @@ struct GemmArgs {
 // gfx950 (the plain layout and the (r >> 2) swizzle both measured two-way conflicts).
 // Chunks past n_in, masked B rows and padding are copied from a static block of zeros.
 constexpr int PF_KS = 32;                  // columns per stage
-constexpr int PF_STAGES = 4;
+constexpr int PF_STAGES = 5;
 constexpr int PF_STAGE_BYTES = 2 * 256 * PF_KS * 2;
 
 __device__ __forceinline__ void pf_dma(const void *g, uint16_t *lds)
@@ -382,7 +382,7 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
         const int kk = (ke % kb_per_slice) * PF_KS + c * 8;   // column within the slice block
         const int dd = kk / (2 * R);
         const int rho = (kk - dd * 2 * R) & (R - 1);
-        const int a = slist[min(dd, D - 1)];
+        const int a = slist[min(dd, D - 1)];   // the tile's adapter list (global, L2-resident)
         const int s_lo = P.g.slice_start[sg], s_hi = P.g.slice_start[sg + 1];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -420,7 +420,6 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t pf_lds[];
     // [stage][W 256 x 32 | X 256 x 32], then the tile's adapter list
-    int *slist = (int *)(pf_lds + PF_STAGES * PF_STAGE_BYTES / 2);
 
     // Workgroups are dealt to the 8 XCDs round robin (their own L2 each): give every XCD a
     // contiguous run of logical tiles, ordered in groups of 8 n-tiles per m-tile, so the
@@ -455,14 +454,12 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
             sg_hi = sg_lo;
             while (sg_hi + 1 < P.g.n_slices && nlast >= P.g.slice_start[sg_hi + 1])
                 ++sg_hi;
-            for (int d = threadIdx.x; d < D; d += 512)
-                slist[d] = P.tile_list[(int64_t)mt * P.list_stride + d];
         }
     }
     const int nk_extra = D > 0 ? (sg_hi - sg_lo + 1) * kb_per_slice : 0;
     const int nk = nk_main + nk_extra;
     const uint16_t *vtile = P.vcat + (int64_t)mt * P.vcat_tile_elems;
-    __syncthreads();   // slist
+    const int *slist = P.tile_list + (int64_t)mt * P.list_stride;
 
     f32x4 acc[4][8];
 #pragma unroll
@@ -477,15 +474,17 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
     for (int q = 0; q < PF_STAGES; ++q)
         pf_issue(P, pf_lds + q * (PF_STAGE_BYTES / 2), min(q, nk - 1), nk_main, nk_extra, m0, n0,
                  vtile, D, kxs, sg_lo, kb_per_slice, slist, wave, lane);
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");   // stage 0 (4 copies per stage)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // stage 0 (4 copies per stage)
     lds_barrier();
+    int buf = 0;
     for (int q = 0; q < nk; ++q) {
-        uint16_t *st = pf_lds + (q & (PF_STAGES - 1)) * (PF_STAGE_BYTES / 2);
+        uint16_t *st = pf_lds + buf * (PF_STAGE_BYTES / 2);
         pf_compute(st, wn, wm, r, gq, acc);
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // stage q+1
+        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // stage q+1
         lds_barrier();                                      // also: stage q fully read
         pf_issue(P, st, min(q + PF_STAGES, nk - 1), nk_main, nk_extra, m0, n0, vtile, D, kxs,
                  sg_lo, kb_per_slice, slist, wave, lane);
+        buf = buf == PF_STAGES - 1 ? 0 : buf + 1;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no copy outlives the workgroup
 
@@ -611,8 +610,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
     a.tile_D = tile_D;
     a.tile_list = tile_list;
     a.list_stride = c.list_stride;
-    const size_t lds = (size_t)PF_STAGES * PF_STAGE_BYTES +               // 128 KB of stages
-                       (size_t)c.list_stride * sizeof(int32_t);           // adapter list
+    const size_t lds = (size_t)PF_STAGES * PF_STAGE_BYTES;                // 160 KB of stages
     static size_t lds_allowed = 0;
     if (lds > lds_allowed) {
         hipError_t e = hipFuncSetAttribute((const void *)prefill_gemm_kernel,
