@@ -154,7 +154,18 @@ struct ShrinkArgs {
     const int32_t *tile_D, *tile_list;
     uint16_t *vcat;
     int64_t vcat_tile_elems;
+    int32_t *tile_ord;    // out: ordinal of a scattered tile (< sc_cap), else -1
+    int32_t *sc_tiles;    // out: [sc_cap] tile of each ordinal, then their count
+    int sc_cap;
 };
+
+// A tile is "scattered" when its stacked adapters would add more than n_in / 2 k-columns per
+// slice to the GEMM (e.g. 256 decode tokens over 64 adapters): its expand then runs per token
+// (sc_expand_kernel) and the GEMM leaves fp32 sums for it instead of extra k-steps.
+__device__ __forceinline__ bool tile_scattered(int D, int R, int n_in)
+{
+    return D > 0 && (int64_t)D * 2 * R > n_in / 2;
+}
 
 __device__ __forceinline__ void sh_load(const uint16_t *const (&ap)[4], const uint16_t *const (&xp)[4],
                                         int col, int kend, u32x4 (&af)[4], u32x4 (&xf)[4])
@@ -186,32 +197,50 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
     extern __shared__ __attribute__((aligned(16))) float sh_lds[];
     float4 *red = (float4 *)sh_lds;                           // [4 waves][16][64] float4
     int *pre = (int *)(sh_lds + 4 * 16 * 64 * 4);             // [n_mtiles + 1] item prefix
-    __shared__ int wsum[4];
+    __shared__ int wsum[8];
     const SlotGeom &g = P.g;
     const int R = g.R, wd = g.n_slices * R;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, gq = lane >> 4;
 
-    // items of tile m: 4 chunks x ceil(D_m * wd / 64) row blocks
-    int base = 0;
+    // items of tile m: 4 chunks x ceil(D_m * wd / 64) row blocks; workgroup 0 also numbers
+    // the scattered tiles
+    int base = 0, sc_base = 0;
     for (int m0 = 0; m0 < P.n_mtiles; m0 += SH_THREADS) {
         const int m = m0 + threadIdx.x;
-        const int cnt = m < P.n_mtiles ? 4 * ((P.tile_D[m] * wd + 63) / 64) : 0;
-        int tot;
+        const int Dm = m < P.n_mtiles ? P.tile_D[m] : 0;
+        const int cnt = 4 * ((Dm * wd + 63) / 64);
+        const int scm = m < P.n_mtiles && tile_scattered(Dm, R, P.n_in) ? 1 : 0;
+        int tot, sc_tot;
         const int ex = wave_exclusive_scan(cnt, &tot);
-        if (lane == 0)
+        const int sc_ex = wave_exclusive_scan(scm, &sc_tot);
+        if (lane == 0) {
             wsum[wave] = tot;
+            wsum[4 + wave] = sc_tot;
+        }
         __syncthreads();
-        int before = 0, all = 0;
+        int before = 0, all = 0, sc_before = 0, sc_all = 0;
         for (int w = 0; w < 4; ++w) {
             before += w < wave ? wsum[w] : 0;
             all += wsum[w];
+            sc_before += w < wave ? wsum[4 + w] : 0;
+            sc_all += wsum[4 + w];
         }
         if (m < P.n_mtiles)
             pre[m] = base + before + ex;
+        if (blockIdx.x == 0 && m < P.n_mtiles) {
+            const int ord = sc_base + sc_before + sc_ex;
+            const bool kept = scm && ord < P.sc_cap;
+            P.tile_ord[m] = kept ? ord : -1;
+            if (kept)
+                P.sc_tiles[ord] = m;
+        }
         base += all;
+        sc_base += sc_all;
         __syncthreads();
     }
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        P.sc_tiles[P.sc_cap] = min(sc_base, P.sc_cap);
     const int total = base;
 
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
@@ -332,6 +361,8 @@ struct GemmArgs {
     int64_t vcat_tile_elems;
     const int32_t *tile_D, *tile_list;
     int list_stride;
+    const int32_t *tile_ord;   // scattered tile ordinal (sgmv_shrink_kernel), or -1
+    float *part_sc;            // fp32 [sc_cap][256][n_out] sums of scattered tiles
 };
 
 // GEMM: 256 W rows x 256 tokens per workgroup, 8 waves (4 along W rows x 2 along tokens,
@@ -443,7 +474,9 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
 
     const int nk_main = (P.n_in + PF_KS - 1) / PF_KS;
     int D = 0, kxs = 0, sg_lo = 0, sg_hi = -1, kb_per_slice = 1;
-    if (P.lora) {
+    // a scattered tile gets no extra k-steps: its fp32 sums go to part_sc for the expand kernel
+    const int ord = P.lora ? P.tile_ord[mt] : -1;
+    if (P.lora && ord < 0) {
         D = P.tile_D[mt];
         kxs = ((D * 2 * P.g.R + PF_BK - 1) / PF_BK) * PF_BK;
         if (D > 0) {
@@ -489,6 +522,27 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no copy outlives the workgroup
 
     // lane holds rows n0 + wn*64 + i*16 + 4*gq + (0..3) of token m0 + wm*128 + j*16 + r
+    if (ord >= 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int tl = wm * 128 + j * 16 + r;
+            if (m0 + tl >= P.T)
+                continue;
+            float *po = P.part_sc + ((int64_t)ord * PF_BM + tl) * P.n_out;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = n0 + wn * 64 + i * 16 + gq * 4;
+                if (n + 3 < P.n_out && (P.n_out & 3) == 0) {
+                    *(float4 *)(po + n) = float4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                } else {
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < P.n_out)
+                            po[n + e] = acc[i][j][e];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int t = m0 + wm * 128 + j * 16 + r;
@@ -512,6 +566,119 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
 }
 
 // ------------------------------------------------------------------------------------------
+// 4. expand of the scattered tiles, per token
+// ------------------------------------------------------------------------------------------
+// One workgroup per (scattered tile, 16 tokens, 64 rows); thread (token, 4 rows).  For each of
+// the token's distinct slots, v = hi + lo of the tile's V block (the coefficients are already
+// in it) against B[a][n][:], added to the GEMM's fp32 sum and rounded once.  A slot that repeats
+// an earlier one of the same token is skipped: its coefficient was summed into that column.
+struct ScArgs {
+    int T, n_out, K;
+    SlotGeom g;
+    const int32_t *idx;
+    const int32_t *tile_D, *tile_list;
+    int list_stride;
+    const uint16_t *vcat;
+    int64_t vcat_tile_elems;
+    const int32_t *sc_tiles;
+    int sc_cap, n_chunks;
+    const float *part_sc;
+    uint16_t *y;
+};
+
+__device__ __forceinline__ void sc_expand_item(const ScArgs &P, int item, int *sc_list)
+{
+    const int nc = item % P.n_chunks;
+    const int rest = item / P.n_chunks;
+    const int tg = rest % (PF_BM / 16), ord = rest / (PF_BM / 16);
+    const int m = P.sc_tiles[ord];
+    const int t0 = m * PF_BM + tg * 16;
+    const SlotGeom &g = P.g;
+    const int R = g.R;
+    const int D = P.tile_D[m];
+    for (int d = threadIdx.x; d < D; d += 256)
+        sc_list[d] = P.tile_list[(int64_t)m * P.list_stride + d];
+    __syncthreads();
+    const int tl = threadIdx.x >> 4, g4 = threadIdx.x & 15;
+    const int t = t0 + tl;
+    const int n = nc * 64 + g4 * 4;
+    if (t >= P.T || n >= P.n_out)
+        return;
+    const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
+    const uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems +
+                           (int64_t)(t - m * PF_BM) * (g.n_slices * kxs);
+    const float *po = P.part_sc + ((int64_t)ord * PF_BM + (t - m * PF_BM)) * P.n_out + n;
+    float o4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o4[i] = n + i < P.n_out ? po[i] : 0.f;
+    const int32_t *it = P.idx + (int64_t)t * P.K;
+    for (int j = 0; j < P.K; ++j) {
+        const int a = it[j];
+        if (a < 0)
+            continue;
+        bool dup = false;
+        for (int jj = 0; jj < j; ++jj)
+            dup |= it[jj] == a;
+        if (dup)
+            continue;
+        int lo = 0, hi = D - 1;                 // position of a in the ascending list
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (sc_list[mid] < a)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        const int d = lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ni = n + i;
+            if (ni >= P.n_out)
+                break;
+            int sg = 0;
+            while (sg + 1 < g.n_slices && ni >= g.slice_start[sg + 1])
+                ++sg;
+            const uint16_t *vh = vrow + sg * kxs + d * 2 * R;
+            const uint16_t *brow = g.B + ((int64_t)a * P.n_out + ni) * R;
+            float acc = 0.f;
+            for (int rho = 0; rho < R; rho += 8) {
+                const u32x4 hv = *(const u32x4 *)(vh + rho);
+                const u32x4 lv = *(const u32x4 *)(vh + R + rho);
+                const u32x4 bv = *(const u32x4 *)(brow + rho);
+                acc += (bf16_lo(hv.x) + bf16_lo(lv.x)) * bf16_lo(bv.x);
+                acc += (bf16_hi(hv.x) + bf16_hi(lv.x)) * bf16_hi(bv.x);
+                acc += (bf16_lo(hv.y) + bf16_lo(lv.y)) * bf16_lo(bv.y);
+                acc += (bf16_hi(hv.y) + bf16_hi(lv.y)) * bf16_hi(bv.y);
+                acc += (bf16_lo(hv.z) + bf16_lo(lv.z)) * bf16_lo(bv.z);
+                acc += (bf16_hi(hv.z) + bf16_hi(lv.z)) * bf16_hi(bv.z);
+                acc += (bf16_lo(hv.w) + bf16_lo(lv.w)) * bf16_lo(bv.w);
+                acc += (bf16_hi(hv.w) + bf16_hi(lv.w)) * bf16_hi(bv.w);
+            }
+            o4[i] += acc;
+        }
+    }
+    uint16_t *yo = P.y + (int64_t)t * P.n_out + n;
+    if (n + 3 < P.n_out && (P.n_out & 3) == 0) {
+        *(u32x2 *)yo = u32x2{pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3])};
+    } else {
+        for (int i = 0; i < 4; ++i)
+            if (n + i < P.n_out)
+                yo[i] = f32_to_bf16(o4[i]);
+    }
+}
+
+__global__ __launch_bounds__(256) void sc_expand_kernel(ScArgs P)
+{
+    extern __shared__ int sc_list[];          // the tile's adapters, ascending
+    const int n_items = P.sc_tiles[P.sc_cap] * (PF_BM / 16) * P.n_chunks;
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        sc_expand_item(P, item, sc_list);
+        __syncthreads();                      // sc_list is reloaded by the next item
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t R,
                           int32_t n_slices)
 {
@@ -521,16 +688,37 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
     c.list_stride = (int)std::min<int64_t>((int64_t)PF_BM * K, S);
     const int64_t kxs_max = ((int64_t)c.list_stride * 2 * R + PF_BK - 1) / PF_BK * PF_BK;
     c.vcat_tile_elems = (int64_t)PF_BM * n_slices * kxs_max;
+    // fp32 sums of up to sc_cap scattered tiles, within 64 MiB (at least one tile)
+    c.n_out = n_out;
+    c.sc_cap = (int)std::min<int64_t>(
+        c.n_mtiles, std::max<int64_t>(1, (64ll << 20) / ((int64_t)PF_BM * n_out * 4)));
     (void)n_in;
     return c;
 }
 
-size_t prefill_workspace_bytes(const PrefillCfg &c)
+// Workspace regions of the tiled path, each 256-byte aligned, in this order.
+struct PrefillLayout {
+    size_t tile_D, tile_list, tile_cnt, tile_ord, sc_tiles, part_sc, vcat, total;
+};
+
+static size_t al256(size_t v) { return (v + 255) / 256 * 256; }
+
+static PrefillLayout prefill_layout(const PrefillCfg &c)
 {
-    const size_t lists = (size_t)c.n_mtiles * c.list_stride * sizeof(int32_t);
-    return ((size_t)c.n_mtiles * sizeof(int32_t) + 255) / 256 * 256 + 2 * ((lists + 255) / 256 * 256) +
-           (size_t)c.n_mtiles * c.vcat_tile_elems * sizeof(uint16_t);
+    PrefillLayout L;
+    const size_t lists = al256((size_t)c.n_mtiles * c.list_stride * sizeof(int32_t));
+    L.tile_D = 0;
+    L.tile_list = L.tile_D + al256((size_t)c.n_mtiles * sizeof(int32_t));
+    L.tile_cnt = L.tile_list + lists;
+    L.tile_ord = L.tile_cnt + lists;
+    L.sc_tiles = L.tile_ord + al256((size_t)c.n_mtiles * sizeof(int32_t));
+    L.part_sc = L.sc_tiles + al256(((size_t)c.sc_cap + 1) * sizeof(int32_t));
+    L.vcat = L.part_sc + al256((size_t)c.sc_cap * PF_BM * (size_t)c.n_out * sizeof(float));
+    L.total = L.vcat + (size_t)c.n_mtiles * c.vcat_tile_elems * sizeof(uint16_t);
+    return L;
 }
+
+size_t prefill_workspace_bytes(const PrefillCfg &c) { return prefill_layout(c).total; }
 
 bool prefill_worth_it(int64_t T, int64_t n_out)
 {
@@ -544,14 +732,14 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
                           hipStream_t stream)
 {
     uint8_t *p = (uint8_t *)ws;
-    int32_t *tile_D = (int32_t *)p;
-    p += ((size_t)c.n_mtiles * sizeof(int32_t) + 255) / 256 * 256;
-    const size_t lists = ((size_t)c.n_mtiles * c.list_stride * sizeof(int32_t) + 255) / 256 * 256;
-    int32_t *tile_list = (int32_t *)p;
-    p += lists;
-    int32_t *tile_cnt = (int32_t *)p;
-    p += lists;
-    uint16_t *vcat = (uint16_t *)p;
+    const PrefillLayout WL = prefill_layout(c);
+    int32_t *tile_D = (int32_t *)(p + WL.tile_D);
+    int32_t *tile_list = (int32_t *)(p + WL.tile_list);
+    int32_t *tile_cnt = (int32_t *)(p + WL.tile_cnt);
+    int32_t *tile_ord = (int32_t *)(p + WL.tile_ord);
+    int32_t *sc_tiles = (int32_t *)(p + WL.sc_tiles);
+    float *part_sc = (float *)(p + WL.part_sc);
+    uint16_t *vcat = (uint16_t *)(p + WL.vcat);
 
     if (g != nullptr && c.n_mtiles > SH_MAX_TILES)
         return hipErrorInvalidValue;   // callers split larger batches
@@ -582,6 +770,9 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
         s.tile_list = tile_list;
         s.vcat = vcat;
         s.vcat_tile_elems = c.vcat_tile_elems;
+        s.tile_ord = tile_ord;
+        s.sc_tiles = sc_tiles;
+        s.sc_cap = c.sc_cap;
         const size_t sh_lds = (size_t)4 * 16 * 64 * sizeof(float4) + ((size_t)c.n_mtiles + 1) * sizeof(int);
         static size_t sh_allowed = 64 * 1024;
         if (sh_lds > sh_allowed) {
@@ -610,6 +801,8 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
     a.tile_D = tile_D;
     a.tile_list = tile_list;
     a.list_stride = c.list_stride;
+    a.tile_ord = tile_ord;
+    a.part_sc = part_sc;
     const size_t lds = (size_t)PF_STAGES * PF_STAGE_BYTES;                // 160 KB of stages
     static size_t lds_allowed = 0;
     if (lds > lds_allowed) {
@@ -622,8 +815,30 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
     trace_mark(stream, true);
     hipLaunchKernelGGL(prefill_gemm_kernel, dim3((unsigned)(c.n_mtiles * c.n_ntiles)), dim3(512),
                        lds, stream, a);
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     trace_mark(stream, false);
+    if (e == hipSuccess && g != nullptr) {
+        ScArgs x2{};
+        x2.T = (int)T;
+        x2.n_out = (int)n_out;
+        x2.K = K;
+        x2.g = *g;
+        x2.idx = idx;
+        x2.tile_D = tile_D;
+        x2.tile_list = tile_list;
+        x2.list_stride = c.list_stride;
+        x2.vcat = vcat;
+        x2.vcat_tile_elems = c.vcat_tile_elems;
+        x2.sc_tiles = sc_tiles;
+        x2.sc_cap = c.sc_cap;
+        x2.n_chunks = (int)((n_out + 63) / 64);
+        x2.part_sc = part_sc;
+        x2.y = y;
+        const size_t xl = (size_t)c.list_stride * sizeof(int32_t);
+        const unsigned grid = (unsigned)std::min<int64_t>((int64_t)c.sc_cap * (PF_BM / 16) * x2.n_chunks, 2048);
+        hipLaunchKernelGGL(sc_expand_kernel, dim3(grid), dim3(256), xl, stream, x2);
+        e = hipGetLastError();
+    }
     return e;
 }
 

@@ -72,6 +72,8 @@ struct PrefillCfg {
     int n_mtiles, n_ntiles;   // 256-token x 256-row output tiles
     int list_stride;          // max distinct adapters per token tile
     int64_t vcat_tile_elems;  // bf16 elements of one tile's V block
+    int sc_cap;               // scattered tiles whose expand runs outside the GEMM
+    int64_t n_out;
 };
 PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t R,
                           int32_t n_slices);
