@@ -44,16 +44,60 @@ __device__ __attribute__((aligned(64))) uint32_t pf_zero16[16];   // never writt
 // ------------------------------------------------------------------------------------------
 // 1. tile plan
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restrict__ idx, int T,
-                                                        int K, int S, int R, int n_slices,
-                                                        int list_stride, int32_t *tile_D,
-                                                        int32_t *tile_list, int32_t *tile_cnt,
-                                                        uint16_t *vcat, int64_t vcat_tile_elems)
+// A tile is "scattered" when its stacked adapters would add more than n_in / 2 k-columns per
+// slice to the GEMM (e.g. 256 decode tokens over 64 adapters): its shrink and expand then run per
+// adapter over that adapter's tokens only (sgmv_shrink_kernel's group items, sc_expand_kernel),
+// and the GEMM leaves fp32 sums for it instead of extra k-steps.
+__device__ __forceinline__ bool tile_scattered(int D, int R, int n_in)
 {
-    extern __shared__ uint32_t plan_lds[];         // bits[(S+31)/32] then cnt[S]
+    return D > 0 && (int64_t)D * 2 * R > n_in / 2;
+}
+
+// Exclusive scan of two values over the 256 threads of a workgroup; ws holds 8 ints.
+__device__ __forceinline__ void block_scan2(int v1, int v2, int *ws, int &ex1, int &ex2, int &all1,
+                                            int &all2)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int t1, t2;
+    const int e1 = wave_exclusive_scan(v1, &t1);
+    const int e2 = wave_exclusive_scan(v2, &t2);
+    if (lane == 0) {
+        ws[wv] = t1;
+        ws[4 + wv] = t2;
+    }
+    __syncthreads();
+    int b1 = 0, b2 = 0;
+    all1 = 0;
+    all2 = 0;
+    for (int w = 0; w < 4; ++w) {
+        b1 += w < wv ? ws[w] : 0;
+        b2 += w < wv ? ws[4 + w] : 0;
+        all1 += ws[w];
+        all2 += ws[4 + w];
+    }
+    __syncthreads();
+    ex1 = b1 + e1;
+    ex2 = b2 + e2;
+}
+
+// One workgroup of 256 threads per tile.  For a scattered tile it also lists, per adapter of
+// the tile (list order), the tile-local tokens that use it: tile_tok[toff[d] ..toff[d+1]), in
+// groups of 16 numbered by gpre[d] = sum over d' < d of ceil(count / 16).  The order of the
+// tokens inside a list is whatever the atomics give; each token's results do not depend on it.
+__global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restrict__ idx, int T,
+                                                        int K, int S, int R, int n_slices, int n_in,
+                                                        int list_stride, int32_t *tile_D,
+                                                        int32_t *tile_list, int32_t *tile_toff,
+                                                        int32_t *tile_gpre, uint8_t *tile_tok,
+                                                        int tok_stride, uint16_t *vcat,
+                                                        int64_t vcat_tile_elems)
+{
+    extern __shared__ uint32_t plan_lds[];         // bits[(S+31)/32], cnt[S], lst[list_stride]
     const int nw = (S + 31) / 32;
     uint32_t *bits = plan_lds;
     int *cnt = (int *)(plan_lds + nw);
+    int *lst = cnt + S;
+    __shared__ int wsum[8];
     const int m = blockIdx.x;
     const int t0 = m * PF_BM;
     const int nt = min(PF_BM, T - t0);
@@ -79,41 +123,66 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
     }
     __syncthreads();
     // ascending list of the set bits: exclusive scan of per-word popcounts
-    __shared__ int wsum[4];
     int base = 0;
     for (int w0 = 0; w0 < nw; w0 += blockDim.x) {
         const int w = w0 + threadIdx.x;
         const uint32_t b = w < nw ? bits[w] : 0u;
-        const int pc = __popc(b);
-        int tot;
-        const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-        int ex = wave_exclusive_scan(pc, &tot);
-        if (lane == 0)
-            wsum[wv] = tot;
-        __syncthreads();
-        int before = 0, all = 0;
-        for (int i = 0; i < 4; ++i) {
-            if (i < wv)
-                before += wsum[i];
-            all += wsum[i];
-        }
-        __syncthreads();
-        int pos = base + before + ex;
+        int ex, unused, all, unused2;
+        block_scan2(__popc(b), 0, wsum, ex, unused, all, unused2);
+        int pos = base + ex;
         uint32_t bb = b;
         while (bb) {
             const int bit = __ffs(bb) - 1;
             bb &= bb - 1;
             const int a = w * 32 + bit;
             tile_list[(int64_t)m * list_stride + pos] = a;
-            tile_cnt[(int64_t)m * list_stride + pos] = cnt[a];
+            lst[pos] = a;
             ++pos;
         }
         base += all;
     }
     if (threadIdx.x == 0)
         tile_D[m] = base;
-    // zero the padding columns [2*D*R, KXs) of every slice block of this tile's V
     const int D = base;
+    if (tile_scattered(D, R, n_in)) {
+        __syncthreads();                          // lst complete
+        int32_t *toff = tile_toff + (int64_t)m * (list_stride + 1);
+        int32_t *gpre = tile_gpre + (int64_t)m * (list_stride + 1);
+        int obase = 0, gbase = 0;
+        for (int d0 = 0; d0 < D; d0 += blockDim.x) {
+            const int d = d0 + threadIdx.x;
+            const int c = d < D ? cnt[lst[d]] : 0;
+            int oex, gex, oall, gall;
+            block_scan2(c, (c + 15) >> 4, wsum, oex, gex, oall, gall);
+            if (d < D) {
+                toff[d] = obase + oex;
+                gpre[d] = gbase + gex;
+                cnt[lst[d]] = obase + oex;        // now the next free place of adapter lst[d]
+            }
+            obase += oall;
+            gbase += gall;
+        }
+        if (threadIdx.x == 0) {
+            toff[D] = obase;
+            gpre[D] = gbase;
+        }
+        __syncthreads();
+        uint8_t *tok = tile_tok + (int64_t)m * tok_stride;
+        for (int tl = threadIdx.x; tl < nt; tl += blockDim.x) {
+            const int32_t *it = idx + (int64_t)(t0 + tl) * K;
+            for (int j = 0; j < K; ++j) {
+                const int a = it[j];
+                if (a < 0)
+                    continue;
+                bool dup = false;
+                for (int jj = 0; jj < j; ++jj)
+                    dup |= it[jj] == a;
+                if (!dup)
+                    tok[atomicAdd(&cnt[a], 1)] = (uint8_t)tl;
+            }
+        }
+    }
+    // zero the padding columns [2*D*R, KXs) of every slice block of this tile's V
     const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
     const int pad = kxs - D * 2 * R;
     if (pad > 0) {
@@ -157,15 +226,10 @@ struct ShrinkArgs {
     int32_t *tile_ord;    // out: ordinal of a scattered tile (< sc_cap), else -1
     int32_t *sc_tiles;    // out: [sc_cap] tile of each ordinal, then their count
     int sc_cap;
+    const int32_t *tile_toff, *tile_gpre;   // scattered tiles: token lists (tile plan)
+    const uint8_t *tile_tok;
+    int tok_stride;
 };
-
-// A tile is "scattered" when its stacked adapters would add more than n_in / 2 k-columns per
-// slice to the GEMM (e.g. 256 decode tokens over 64 adapters): its expand then runs per token
-// (sc_expand_kernel) and the GEMM leaves fp32 sums for it instead of extra k-steps.
-__device__ __forceinline__ bool tile_scattered(int D, int R, int n_in)
-{
-    return D > 0 && (int64_t)D * 2 * R > n_in / 2;
-}
 
 __device__ __forceinline__ void sh_load(const uint16_t *const (&ap)[4], const uint16_t *const (&xp)[4],
                                         int col, int kend, u32x4 (&af)[4], u32x4 (&xf)[4])
@@ -192,56 +256,263 @@ __device__ __forceinline__ void sh_mfma(const u32x4 (&af)[4], const u32x4 (&xf)[
                 0, 0);
 }
 
-__global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
+// Coefficient of adapter a for token t: the sum of s[t][j] * f[a] over the slots j holding a.
+__device__ __forceinline__ float sh_coef(const ShrinkArgs &P, int t, int a)
 {
-    extern __shared__ __attribute__((aligned(16))) float sh_lds[];
-    float4 *red = (float4 *)sh_lds;                           // [4 waves][16][64] float4
-    int *pre = (int *)(sh_lds + 4 * 16 * 64 * 4);             // [n_mtiles + 1] item prefix
-    __shared__ int wsum[8];
+    const int32_t *it = P.idx + (int64_t)t * P.K;
+    float cf = 0.f;
+    for (int j = 0; j < P.K; ++j)
+        if (it[j] == a)
+            cf += (P.scale ? P.scale[(int64_t)t * P.K + j] : 1.f) * P.g.factor[a];
+    return cf;
+}
+
+// v as the pair hi = bf16(v), lo = bf16(v - hi), R columns apart
+__device__ __forceinline__ void sh_store_v(uint16_t *vp, int R, float v)
+{
+    const uint16_t vh = f32_to_bf16(v);
+    vp[0] = vh;
+    vp[R] = f32_to_bf16(v - bf16_to_f32(vh));
+}
+
+// The k-columns [kb, kend) of this wave: n_in split in 4, each part a multiple of 32 wide (the
+// last may be short).
+__device__ __forceinline__ void sh_wave_cols(int n_in, int wave, int &kb, int &kend, int &nsteps)
+{
+    const int kq = ((n_in + 4 * 32 - 1) / (4 * 32)) * 32;
+    kb = wave * kq;
+    kend = min(n_in, kb + kq);
+    nsteps = kend > kb ? (kend - kb + 31) / 32 : 0;
+}
+
+// Cat item (tile m, 64-token chunk, 64-row block of A_cat): every token of the chunk against
+// every stacked adapter row.
+__device__ __forceinline__ void sh_cat_item(const ShrinkArgs &P, int m, int local, float4 *red)
+{
     const SlotGeom &g = P.g;
     const int R = g.R, wd = g.n_slices * R;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, gq = lane >> 4;
+    const int c = local & 3, rb = local >> 2;
+    const int D = P.tile_D[m];
+    const int32_t *list = P.tile_list + (int64_t)m * P.list_stride;
+    const int t0 = m * PF_BM + c * 64;
+    const int rows_cat = D * wd;
 
-    // items of tile m: 4 chunks x ceil(D_m * wd / 64) row blocks; workgroup 0 also numbers
-    // the scattered tiles
+    const uint16_t *ap[4], *xp[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int ar = min(rb * 64 + b * 16 + r, rows_cat - 1);
+        const int d = ar / wd;
+        ap[b] = g.A + ((int64_t)list[d] * wd + (ar - d * wd)) * P.n_in + gq * 8;
+        xp[b] = P.x + (int64_t)min(t0 + b * 16 + r, P.T - 1) * P.n_in + gq * 8;
+    }
+    int kb, kend, nsteps;
+    sh_wave_cols(P.n_in, wave, kb, kend, nsteps);
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 a0[4], x0[4], a1[4], x1[4];
+    sh_load(ap, xp, kb, kend, a0, x0);
+    sh_load(ap, xp, kb + 32, kend, a1, x1);
+    for (int st = 0; st < nsteps; st += 2) {
+        sh_mfma(a0, x0, acc);
+        sh_load(ap, xp, kb + (st + 2) * 32, kend, a0, x0);
+        sh_mfma(a1, x1, acc);
+        sh_load(ap, xp, kb + (st + 3) * 32, kend, a1, x1);
+    }
+
+    // lane holds A_cat rows rb*64 + 16i + 4gq + e of token t0 + 16j + r
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            red[(wave * 16 + i * 4 + j) * 64 + lane] =
+                float4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+    __syncthreads();
+    // thread: token tl = tid / 4, 16 consecutive rows q*16 .. q*16+15 (q = tid % 4)
+    const int tl = threadIdx.x >> 2, q = threadIdx.x & 3;
+    const int t = t0 + tl;
+    if (t < P.T && t < m * PF_BM + PF_BM) {
+        const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
+        uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems +
+                         (int64_t)(t - m * PF_BM) * (g.n_slices * kxs);
+        int dprev = -1;
+        float cf = 0.f;
+        for (int e = 0; e < 16; ++e) {
+            const int ar = rb * 64 + q * 16 + e;
+            if (ar >= rows_cat)
+                break;
+            const int d = ar / wd;
+            if (d != dprev) {
+                cf = sh_coef(P, t, list[d]);
+                dprev = d;
+            }
+            // element (row ar, token tl) sits in block (i = ar/16, j = tl/16), lane
+            // (tl % 16) + 16 * ((ar % 16) / 4), component ar % 4
+            const int arl = q * 16 + e;
+            const int i = arl >> 4, jb = tl >> 4;
+            const int ln = (tl & 15) + 16 * ((arl & 15) >> 2), comp = arl & 3;
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float4 v4 = red[(w * 16 + i * 4 + jb) * 64 + ln];
+                sum += comp == 0 ? v4.x : comp == 1 ? v4.y : comp == 2 ? v4.z : v4.w;
+            }
+            const int rr = ar - d * wd;          // row within the adapter: slice sg, rank rho
+            const int sg = rr / R, rho = rr - sg * R;
+            sh_store_v(vrow + sg * kxs + d * 2 * R + rho, R, cf * sum);
+        }
+    }
+    __syncthreads();
+}
+
+// Group item of a scattered tile (token group gidx of one adapter, 32-row block rb of that
+// adapter's n_slices * R rows of A): only the up to 16 tokens that use the adapter, gathered
+// as the MFMA's token columns, against 32 rows; SG_ST k-steps of loads in flight.
+constexpr int SG_ROWS = 32;
+constexpr int SG_ST = 4;
+
+__device__ __forceinline__ void sg_load(const uint16_t *const (&ap)[2], const uint16_t *xp, bool xok,
+                                        int col, int kend, u32x4 (&af)[2], u32x4 &xf)
+{
+    const int off = ((threadIdx.x & 63) >> 4) * 8;
+    const bool ok = col + off < kend;
+    af[0] = *(const u32x4 *)(ok ? (const void *)(ap[0] + col) : (const void *)pf_zero16);
+    af[1] = *(const u32x4 *)(ok ? (const void *)(ap[1] + col) : (const void *)pf_zero16);
+    xf = *(const u32x4 *)(ok && xok ? (const void *)(xp + col) : (const void *)pf_zero16);
+}
+
+__device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int local, float4 *red)
+{
+    const SlotGeom &g = P.g;
+    const int R = g.R, wd = g.n_slices * R;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, gq = lane >> 4;
+    const int RB = (wd + SG_ROWS - 1) / SG_ROWS;
+    const int gidx = local / RB, rb = local - gidx * RB;
+    const int D = P.tile_D[m];
+    const int32_t *gp = P.tile_gpre + (int64_t)m * (P.list_stride + 1);
+    const int32_t *to = P.tile_toff + (int64_t)m * (P.list_stride + 1);
+    int lo = 0, hi = D - 1;                   // the adapter: last d with gp[d] <= gidx
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (gp[mid] <= gidx)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const int d = lo;
+    const int a = P.tile_list[(int64_t)m * P.list_stride + d];
+    const int s0 = to[d] + 16 * (gidx - gp[d]);
+    const int ng = min(16, to[d + 1] - s0);
+    const uint8_t *tk = P.tile_tok + (int64_t)m * P.tok_stride + s0;
+    const bool xok = r < ng;
+    const uint16_t *xp = P.x + ((int64_t)m * PF_BM + (xok ? tk[r] : 0)) * P.n_in + gq * 8;
+    const uint16_t *ap[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const int row = min(rb * SG_ROWS + f * 16 + r, wd - 1);
+        ap[f] = g.A + ((int64_t)a * wd + row) * P.n_in + gq * 8;
+    }
+    int kb, kend, nsteps;
+    sh_wave_cols(P.n_in, wave, kb, kend, nsteps);
+
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    u32x4 af[SG_ST][2], xf[SG_ST];
+#pragma unroll
+    for (int s = 0; s < SG_ST; ++s)
+        sg_load(ap, xp, xok, kb + s * 32, kend, af[s], xf[s]);
+    for (int st = 0; st < nsteps; st += SG_ST) {
+#pragma unroll
+        for (int s = 0; s < SG_ST; ++s) {
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, af[s][f]), __builtin_bit_cast(bf16x8, xf[s]), acc[f],
+                    0, 0, 0);
+            sg_load(ap, xp, xok, kb + (st + s + SG_ST) * 32, kend, af[s], xf[s]);
+        }
+    }
+
+    // lane holds rows rb*32 + 16f + 4gq + e of gathered token r
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+        red[(wave * 2 + f) * 64 + lane] = float4{acc[f][0], acc[f][1], acc[f][2], acc[f][3]};
+    __syncthreads();
+    // thread: gathered token j = tid % 16, rows 2 * (tid / 16) and the next
+    const int j = threadIdx.x & 15, rp = (threadIdx.x >> 4) * 2;
+    if (j < ng) {
+        const int tl = tk[j];
+        const float cf = sh_coef(P, m * PF_BM + tl, a);
+        const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
+        uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems + (int64_t)tl * (g.n_slices * kxs) +
+                         d * 2 * R;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int rl = rp + e, row = rb * SG_ROWS + rl;
+            if (row >= wd)
+                break;
+            const int f = rl >> 4, rr = rl & 15;
+            const int ln = j + 16 * (rr >> 2), comp = rr & 3;
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float4 v4 = red[(w * 2 + f) * 64 + ln];
+                sum += comp == 0 ? v4.x : comp == 1 ? v4.y : comp == 2 ? v4.z : v4.w;
+            }
+            const int sg = row / R, rho = row - sg * R;
+            sh_store_v(vrow + sg * kxs + rho, R, cf * sum);
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
+{
+    extern __shared__ __attribute__((aligned(16))) float sh_lds[];
+    float4 *red = (float4 *)sh_lds;                           // [4 waves][16][64] float4
+    int *pre = (int *)(sh_lds + 4 * 16 * 64 * 4);             // [n_mtiles] item prefix
+    uint8_t *grouped = (uint8_t *)(pre + P.n_mtiles);         // [n_mtiles] 1: group items
+    __shared__ int wsum[8];
+    const int wd = P.g.n_slices * P.g.R;
+    const int RBg = (wd + SG_ROWS - 1) / SG_ROWS;
+
+    // Items of tile m: group items (a scattered tile whose ordinal is below sc_cap) or cat
+    // items, 4 chunks x ceil(D_m * wd / 64) row blocks; workgroup 0 also numbers the
+    // scattered tiles.
     int base = 0, sc_base = 0;
     for (int m0 = 0; m0 < P.n_mtiles; m0 += SH_THREADS) {
         const int m = m0 + threadIdx.x;
         const int Dm = m < P.n_mtiles ? P.tile_D[m] : 0;
-        const int cnt = 4 * ((Dm * wd + 63) / 64);
-        const int scm = m < P.n_mtiles && tile_scattered(Dm, R, P.n_in) ? 1 : 0;
-        int tot, sc_tot;
-        const int ex = wave_exclusive_scan(cnt, &tot);
-        const int sc_ex = wave_exclusive_scan(scm, &sc_tot);
-        if (lane == 0) {
-            wsum[wave] = tot;
-            wsum[4 + wave] = sc_tot;
+        const int scm = m < P.n_mtiles && tile_scattered(Dm, P.g.R, P.n_in) ? 1 : 0;
+        int sc_ex, sc_all, ex, all, u0, u1;
+        block_scan2(scm, 0, wsum, sc_ex, u0, sc_all, u1);
+        const int ord = sc_base + sc_ex;
+        const bool kept = scm && ord < P.sc_cap;
+        const int cnt = kept ? P.tile_gpre[(int64_t)m * (P.list_stride + 1) + Dm] * RBg
+                             : 4 * ((Dm * wd + 63) / 64);
+        block_scan2(cnt, 0, wsum, ex, u0, all, u1);
+        if (m < P.n_mtiles) {
+            pre[m] = base + ex;
+            grouped[m] = kept ? 1 : 0;
         }
-        __syncthreads();
-        int before = 0, all = 0, sc_before = 0, sc_all = 0;
-        for (int w = 0; w < 4; ++w) {
-            before += w < wave ? wsum[w] : 0;
-            all += wsum[w];
-            sc_before += w < wave ? wsum[4 + w] : 0;
-            sc_all += wsum[4 + w];
-        }
-        if (m < P.n_mtiles)
-            pre[m] = base + before + ex;
         if (blockIdx.x == 0 && m < P.n_mtiles) {
-            const int ord = sc_base + sc_before + sc_ex;
-            const bool kept = scm && ord < P.sc_cap;
             P.tile_ord[m] = kept ? ord : -1;
             if (kept)
                 P.sc_tiles[ord] = m;
         }
         base += all;
         sc_base += sc_all;
-        __syncthreads();
     }
     if (blockIdx.x == 0 && threadIdx.x == 0)
         P.sc_tiles[P.sc_cap] = min(sc_base, P.sc_cap);
     const int total = base;
+    __syncthreads();
 
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
         // tile: last m with pre[m] <= item
@@ -253,97 +524,10 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
             else
                 hi = mid - 1;
         }
-        const int m = lo;
-        const int local = item - pre[m];
-        const int c = local & 3, rb = local >> 2;
-        const int D = P.tile_D[m];
-        const int32_t *list = P.tile_list + (int64_t)m * P.list_stride;
-        const int t0 = m * PF_BM + c * 64;
-        const int rows_cat = D * wd;
-
-        const uint16_t *ap[4], *xp[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int ar = min(rb * 64 + b * 16 + r, rows_cat - 1);
-            const int d = ar / wd;
-            ap[b] = g.A + ((int64_t)list[d] * wd + (ar - d * wd)) * P.n_in + gq * 8;
-            xp[b] = P.x + (int64_t)min(t0 + b * 16 + r, P.T - 1) * P.n_in + gq * 8;
-        }
-        // this wave's columns: [kb, kend), a multiple of 32 wide (the last may be short)
-        const int kq = ((P.n_in + 4 * 32 - 1) / (4 * 32)) * 32;
-        const int kb = wave * kq;
-        const int kend = min(P.n_in, kb + kq);
-        const int nsteps = kend > kb ? (kend - kb + 31) / 32 : 0;
-
-        f32x4 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        u32x4 a0[4], x0[4], a1[4], x1[4];
-        sh_load(ap, xp, kb, kend, a0, x0);
-        sh_load(ap, xp, kb + 32, kend, a1, x1);
-        for (int st = 0; st < nsteps; st += 2) {
-            sh_mfma(a0, x0, acc);
-            sh_load(ap, xp, kb + (st + 2) * 32, kend, a0, x0);
-            sh_mfma(a1, x1, acc);
-            sh_load(ap, xp, kb + (st + 3) * 32, kend, a1, x1);
-        }
-
-        // lane holds A_cat rows rb*64 + 16i + 4gq + e of token t0 + 16j + r
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                red[(wave * 16 + i * 4 + j) * 64 + lane] =
-                    float4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-        __syncthreads();
-        // thread: token tl = tid / 4, 16 consecutive rows q*16 .. q*16+15 (q = tid % 4)
-        const int tl = threadIdx.x >> 2, q = threadIdx.x & 3;
-        const int t = t0 + tl;
-        if (t < P.T && t < m * PF_BM + PF_BM) {
-            const int32_t *it = P.idx + (int64_t)t * P.K;
-            const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
-            uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems +
-                             (int64_t)(t - m * PF_BM) * (g.n_slices * kxs);
-            int dprev = -1;
-            float cf = 0.f;
-            for (int e = 0; e < 16; ++e) {
-                const int ar = rb * 64 + q * 16 + e;
-                if (ar >= rows_cat)
-                    break;
-                const int d = ar / wd;
-                if (d != dprev) {
-                    const int a = list[d];
-                    cf = 0.f;
-                    for (int j = 0; j < P.K; ++j)
-                        if (it[j] == a)
-                            cf += (P.scale ? P.scale[(int64_t)t * P.K + j] : 1.f) * g.factor[a];
-                    dprev = d;
-                }
-                // element (row ar, token tl) sits in block (i = ar/16, j = tl/16), lane
-                // (tl % 16) + 16 * ((ar % 16) / 4), component ar % 4
-                const int arl = q * 16 + e;
-                const int i = arl >> 4, jb = tl >> 4;
-                const int ln = (tl & 15) + 16 * ((arl & 15) >> 2), comp = arl & 3;
-                float sum = 0.f;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const float4 v4 = red[(w * 16 + i * 4 + jb) * 64 + ln];
-                    sum += comp == 0 ? v4.x : comp == 1 ? v4.y : comp == 2 ? v4.z : v4.w;
-                }
-                const float v = cf * sum;
-                const uint16_t vh = f32_to_bf16(v);
-                const uint16_t vl = f32_to_bf16(v - bf16_to_f32(vh));
-                const int rr = ar - d * wd;          // row within the adapter: slice sg, rank rho
-                const int sg = rr / R, rho = rr - sg * R;
-                uint16_t *vp = vrow + sg * kxs + d * 2 * R + rho;
-                vp[0] = vh;
-                vp[R] = vl;
-            }
-        }
-        __syncthreads();
+        if (grouped[lo])
+            sh_group_item(P, lo, item - pre[lo], red);
+        else
+            sh_cat_item(P, lo, item - pre[lo], red);
     }
 }
 
@@ -541,7 +725,7 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
                 }
             }
         }
-        return;
+        // and the bf16 base product below, which stays the output of tokens with no adapter
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -566,115 +750,197 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
 }
 
 // ------------------------------------------------------------------------------------------
-// 4. expand of the scattered tiles, per token
+// 4. expand of the scattered tiles, per adapter
 // ------------------------------------------------------------------------------------------
-// One workgroup per (scattered tile, 16 tokens, 64 rows); thread (token, 4 rows).  For each of
-// the token's distinct slots, v = hi + lo of the tile's V block (the coefficients are already
-// in it) against B[a][n][:], added to the GEMM's fp32 sum and rounded once.  A slot that repeats
-// an earlier one of the same token is skipped: its coefficient was summed into that column.
+// Item = (scattered tile, token group of one adapter, 256-row chunk of the output): B[a]'s rows
+// are the MFMA's A operand, the gathered tokens' V columns (hi and lo halves, one MFMA each) the
+// B operand; 4 waves of 64 rows, 16 tokens.  Pass p (one launch each, p < K) adds, for every
+// token, the adapter that is its p-th distinct one in ascending id order: the token's last
+// adapter writes y = bf16(sum), an earlier one writes the fp32 sum back for the next pass, so
+// every output is summed in one fixed order.  Tokens with no adapter keep the bf16 base product
+// the GEMM wrote for them.
 struct ScArgs {
-    int T, n_out, K;
+    int T, n_out, K, pass;
     SlotGeom g;
     const int32_t *idx;
     const int32_t *tile_D, *tile_list;
     int list_stride;
+    const int32_t *tile_toff, *tile_gpre;
+    const uint8_t *tile_tok;
+    int tok_stride;
     const uint16_t *vcat;
     int64_t vcat_tile_elems;
     const int32_t *sc_tiles;
     int sc_cap, n_chunks;
-    const float *part_sc;
+    float *part_sc;
     uint16_t *y;
 };
 
-__device__ __forceinline__ void sc_expand_item(const ScArgs &P, int item, int *sc_list)
+constexpr int SC_ROWS = 256;   // output rows of an expand item
+
+__device__ __forceinline__ int sc_slice(const SlotGeom &g, int n)
 {
-    const int nc = item % P.n_chunks;
-    const int rest = item / P.n_chunks;
-    const int tg = rest % (PF_BM / 16), ord = rest / (PF_BM / 16);
-    const int m = P.sc_tiles[ord];
-    const int t0 = m * PF_BM + tg * 16;
+    int sg = 0;
+    while (sg + 1 < g.n_slices && n >= g.slice_start[sg + 1])
+        ++sg;
+    return sg;
+}
+
+__device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int local)
+{
     const SlotGeom &g = P.g;
     const int R = g.R;
-    const int D = P.tile_D[m];
-    for (int d = threadIdx.x; d < D; d += 256)
-        sc_list[d] = P.tile_list[(int64_t)m * P.list_stride + d];
-    __syncthreads();
-    const int tl = threadIdx.x >> 4, g4 = threadIdx.x & 15;
-    const int t = t0 + tl;
-    const int n = nc * 64 + g4 * 4;
-    if (t >= P.T || n >= P.n_out)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, gq = lane >> 4;
+    const int m = P.sc_tiles[ord];
+    const int gidx = local / P.n_chunks, nc = local - gidx * P.n_chunks;
+    const int n0 = nc * SC_ROWS + wave * 64;
+    if (n0 >= P.n_out)
         return;
-    const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
-    const uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems +
-                           (int64_t)(t - m * PF_BM) * (g.n_slices * kxs);
-    const float *po = P.part_sc + ((int64_t)ord * PF_BM + (t - m * PF_BM)) * P.n_out + n;
-    float o4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        o4[i] = n + i < P.n_out ? po[i] : 0.f;
-    const int32_t *it = P.idx + (int64_t)t * P.K;
-    for (int j = 0; j < P.K; ++j) {
-        const int a = it[j];
-        if (a < 0)
-            continue;
-        bool dup = false;
-        for (int jj = 0; jj < j; ++jj)
-            dup |= it[jj] == a;
-        if (dup)
-            continue;
-        int lo = 0, hi = D - 1;                 // position of a in the ascending list
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (sc_list[mid] < a)
-                lo = mid + 1;
-            else
-                hi = mid;
-        }
-        const int d = lo;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ni = n + i;
-            if (ni >= P.n_out)
-                break;
-            int sg = 0;
-            while (sg + 1 < g.n_slices && ni >= g.slice_start[sg + 1])
-                ++sg;
-            const uint16_t *vh = vrow + sg * kxs + d * 2 * R;
-            const uint16_t *brow = g.B + ((int64_t)a * P.n_out + ni) * R;
-            float acc = 0.f;
-            for (int rho = 0; rho < R; rho += 8) {
-                const u32x4 hv = *(const u32x4 *)(vh + rho);
-                const u32x4 lv = *(const u32x4 *)(vh + R + rho);
-                const u32x4 bv = *(const u32x4 *)(brow + rho);
-                acc += (bf16_lo(hv.x) + bf16_lo(lv.x)) * bf16_lo(bv.x);
-                acc += (bf16_hi(hv.x) + bf16_hi(lv.x)) * bf16_hi(bv.x);
-                acc += (bf16_lo(hv.y) + bf16_lo(lv.y)) * bf16_lo(bv.y);
-                acc += (bf16_hi(hv.y) + bf16_hi(lv.y)) * bf16_hi(bv.y);
-                acc += (bf16_lo(hv.z) + bf16_lo(lv.z)) * bf16_lo(bv.z);
-                acc += (bf16_hi(hv.z) + bf16_hi(lv.z)) * bf16_hi(bv.z);
-                acc += (bf16_lo(hv.w) + bf16_lo(lv.w)) * bf16_lo(bv.w);
-                acc += (bf16_hi(hv.w) + bf16_hi(lv.w)) * bf16_hi(bv.w);
+    const int D = P.tile_D[m];
+    const int32_t *gp = P.tile_gpre + (int64_t)m * (P.list_stride + 1);
+    const int32_t *to = P.tile_toff + (int64_t)m * (P.list_stride + 1);
+    int lo = 0, hi = D - 1;                   // the adapter: last d with gp[d] <= gidx
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (gp[mid] <= gidx)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const int d = lo;
+    const int a = P.tile_list[(int64_t)m * P.list_stride + d];
+    const int s0 = to[d] + 16 * (gidx - gp[d]);
+    const int ng = min(16, to[d + 1] - s0);
+    const bool tok_ok = r < ng;
+    const int tl = tok_ok ? P.tile_tok[(int64_t)m * P.tok_stride + s0 + r] : 0;
+    const int t = m * PF_BM + tl;
+
+    // this pass's adapter of the token: its rank among the token's distinct ids, and their count
+    int below = 0, n_dist = 0;
+    if (tok_ok) {
+        const int32_t *it = P.idx + (int64_t)t * P.K;
+        for (int j = 0; j < P.K; ++j) {
+            const int b = it[j];
+            bool dup = b < 0;
+            for (int jj = 0; jj < j; ++jj)
+                dup |= it[jj] == b;
+            if (!dup) {
+                ++n_dist;
+                below += b < a ? 1 : 0;
             }
-            o4[i] += acc;
         }
     }
-    uint16_t *yo = P.y + (int64_t)t * P.n_out + n;
-    if (n + 3 < P.n_out && (P.n_out & 3) == 0) {
-        *(u32x2 *)yo = u32x2{pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3])};
-    } else {
-        for (int i = 0; i < 4; ++i)
-            if (n + i < P.n_out)
-                yo[i] = f32_to_bf16(o4[i]);
+    const bool act = tok_ok && below == P.pass;
+    const bool last = below == n_dist - 1;
+
+    const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
+    const uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems + (int64_t)tl * (g.n_slices * kxs) +
+                           d * 2 * R + gq * 8;
+    const uint16_t *brow0 = g.B + (int64_t)a * P.n_out * R + gq * 8;
+    float *po = P.part_sc + ((int64_t)ord * PF_BM + tl) * P.n_out;
+
+    // the fp32 sums of this lane's outputs, loaded first
+    f32x4 acc[4], prt[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const int n = n0 + f * 16 + gq * 4;
+        acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (n + 3 < P.n_out && (P.n_out & 3) == 0) {
+            const float4 v = *(const float4 *)(act ? (const void *)(po + n) : (const void *)pf_zero16);
+            prt[f] = f32x4{v.x, v.y, v.z, v.w};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                prt[f][e] = act && n + e < P.n_out ? po[n + e] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const int nf = n0 + f * 16;
+        if (nf >= P.n_out)
+            break;
+        const int nb = nf + r;                // this lane's B row
+        const int sg_lo = sc_slice(g, nf), sg_hi = sc_slice(g, min(nf + 15, P.n_out - 1));
+        const int sg_b = sc_slice(g, min(nb, P.n_out - 1));
+        for (int sg = sg_lo; sg <= sg_hi; ++sg) {
+            const bool row_ok = nb < P.n_out && sg_b == sg;
+            for (int k = 0; k < R; k += 32) {
+                const bool kok = k + gq * 8 < R;
+                const u32x4 bv = *(const u32x4 *)(row_ok && kok ? (const void *)(brow0 + (int64_t)nb * R + k)
+                                                                : (const void *)pf_zero16);
+                const uint16_t *vp = vrow + sg * kxs + k;
+                const u32x4 vh = *(const u32x4 *)(tok_ok && kok ? (const void *)vp : (const void *)pf_zero16);
+                const u32x4 vl = *(const u32x4 *)(tok_ok && kok ? (const void *)(vp + R) : (const void *)pf_zero16);
+                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, bv), __builtin_bit_cast(bf16x8, vh), acc[f], 0, 0, 0);
+                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, bv), __builtin_bit_cast(bf16x8, vl), acc[f], 0, 0, 0);
+            }
+        }
+    }
+    if (!act)
+        return;
+    // lane holds rows n0 + 16f + 4gq + e of token t
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const int n = n0 + f * 16 + gq * 4;
+        if (n >= P.n_out)
+            break;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = prt[f][e] + acc[f][e];
+        if (n + 3 < P.n_out && (P.n_out & 3) == 0) {
+            if (last)
+                *(u32x2 *)(P.y + (int64_t)t * P.n_out + n) =
+                    u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            else
+                *(float4 *)(po + n) = float4{o[0], o[1], o[2], o[3]};
+        } else {
+            for (int e = 0; e < 4; ++e) {
+                if (n + e >= P.n_out)
+                    break;
+                if (last)
+                    P.y[(int64_t)t * P.n_out + n + e] = f32_to_bf16(o[e]);
+                else
+                    po[n + e] = o[e];
+            }
+        }
     }
 }
 
 __global__ __launch_bounds__(256) void sc_expand_kernel(ScArgs P)
 {
-    extern __shared__ int sc_list[];          // the tile's adapters, ascending
-    const int n_items = P.sc_tiles[P.sc_cap] * (PF_BM / 16) * P.n_chunks;
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        sc_expand_item(P, item, sc_list);
-        __syncthreads();                      // sc_list is reloaded by the next item
+    extern __shared__ int sc_pre[];           // [sc_cap + 1] item prefix over the scattered tiles
+    __shared__ int wsum[8];
+    const int n_sc = P.sc_tiles[P.sc_cap];
+    int base = 0;
+    for (int o0 = 0; o0 < n_sc; o0 += 256) {
+        const int o = o0 + threadIdx.x;
+        int cnt = 0;
+        if (o < n_sc) {
+            const int m = P.sc_tiles[o];
+            cnt = P.tile_gpre[(int64_t)m * (P.list_stride + 1) + P.tile_D[m]] * P.n_chunks;
+        }
+        int ex, all, u0, u1;
+        block_scan2(cnt, 0, wsum, ex, u0, all, u1);
+        if (o < n_sc)
+            sc_pre[o] = base + ex;
+        base += all;
+    }
+    __syncthreads();
+    const int total = base;
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        int lo = 0, hi = n_sc - 1;            // scattered tile: last o with sc_pre[o] <= item
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sc_pre[mid] <= item)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        sc_expand_item(P, lo, item - sc_pre[lo]);
     }
 }
 
@@ -690,6 +956,7 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
     c.vcat_tile_elems = (int64_t)PF_BM * n_slices * kxs_max;
     // fp32 sums of up to sc_cap scattered tiles, within 64 MiB (at least one tile)
     c.n_out = n_out;
+    c.tok_stride = PF_BM * K;
     c.sc_cap = (int)std::min<int64_t>(
         c.n_mtiles, std::max<int64_t>(1, (64ll << 20) / ((int64_t)PF_BM * n_out * 4)));
     (void)n_in;
@@ -698,7 +965,8 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
 
 // Workspace regions of the tiled path, each 256-byte aligned, in this order.
 struct PrefillLayout {
-    size_t tile_D, tile_list, tile_cnt, tile_ord, sc_tiles, part_sc, vcat, total;
+    size_t tile_D, tile_list, tile_toff, tile_gpre, tile_tok, tile_ord, sc_tiles, part_sc, vcat,
+        total;
 };
 
 static size_t al256(size_t v) { return (v + 255) / 256 * 256; }
@@ -707,10 +975,13 @@ static PrefillLayout prefill_layout(const PrefillCfg &c)
 {
     PrefillLayout L;
     const size_t lists = al256((size_t)c.n_mtiles * c.list_stride * sizeof(int32_t));
+    const size_t offs = al256((size_t)c.n_mtiles * (c.list_stride + 1) * sizeof(int32_t));
     L.tile_D = 0;
     L.tile_list = L.tile_D + al256((size_t)c.n_mtiles * sizeof(int32_t));
-    L.tile_cnt = L.tile_list + lists;
-    L.tile_ord = L.tile_cnt + lists;
+    L.tile_toff = L.tile_list + lists;
+    L.tile_gpre = L.tile_toff + offs;
+    L.tile_tok = L.tile_gpre + offs;
+    L.tile_ord = L.tile_tok + al256((size_t)c.n_mtiles * c.tok_stride);
     L.sc_tiles = L.tile_ord + al256((size_t)c.n_mtiles * sizeof(int32_t));
     L.part_sc = L.sc_tiles + al256(((size_t)c.sc_cap + 1) * sizeof(int32_t));
     L.vcat = L.part_sc + al256((size_t)c.sc_cap * PF_BM * (size_t)c.n_out * sizeof(float));
@@ -735,7 +1006,9 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
     const PrefillLayout WL = prefill_layout(c);
     int32_t *tile_D = (int32_t *)(p + WL.tile_D);
     int32_t *tile_list = (int32_t *)(p + WL.tile_list);
-    int32_t *tile_cnt = (int32_t *)(p + WL.tile_cnt);
+    int32_t *tile_toff = (int32_t *)(p + WL.tile_toff);
+    int32_t *tile_gpre = (int32_t *)(p + WL.tile_gpre);
+    uint8_t *tile_tok = p + WL.tile_tok;
     int32_t *tile_ord = (int32_t *)(p + WL.tile_ord);
     int32_t *sc_tiles = (int32_t *)(p + WL.sc_tiles);
     float *part_sc = (float *)(p + WL.part_sc);
@@ -744,7 +1017,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
     if (g != nullptr && c.n_mtiles > SH_MAX_TILES)
         return hipErrorInvalidValue;   // callers split larger batches
     if (g != nullptr) {
-        const size_t lds = (size_t)((g->S + 31) / 32) * 4 + (size_t)g->S * 4;
+        const size_t lds = (size_t)((g->S + 31) / 32) * 4 + (size_t)g->S * 4 + (size_t)c.list_stride * 4;
         static size_t lds_allowed = 64 * 1024;
         if (lds > lds_allowed) {
             hipError_t e = hipFuncSetAttribute((const void *)tile_plan_kernel,
@@ -754,8 +1027,9 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
             lds_allowed = lds;
         }
         hipLaunchKernelGGL(tile_plan_kernel, dim3(c.n_mtiles), dim3(256), lds, stream, idx,
-                           (int)T, K, g->S, g->R, g->n_slices, c.list_stride, tile_D, tile_list,
-                           tile_cnt, vcat, c.vcat_tile_elems);
+                           (int)T, K, g->S, g->R, g->n_slices, (int)n_in, c.list_stride, tile_D,
+                           tile_list, tile_toff, tile_gpre, tile_tok, c.tok_stride, vcat,
+                           c.vcat_tile_elems);
         ShrinkArgs s{};
         s.x = x;
         s.T = (int)T;
@@ -773,7 +1047,11 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
         s.tile_ord = tile_ord;
         s.sc_tiles = sc_tiles;
         s.sc_cap = c.sc_cap;
-        const size_t sh_lds = (size_t)4 * 16 * 64 * sizeof(float4) + ((size_t)c.n_mtiles + 1) * sizeof(int);
+        s.tile_toff = tile_toff;
+        s.tile_gpre = tile_gpre;
+        s.tile_tok = tile_tok;
+        s.tok_stride = c.tok_stride;
+        const size_t sh_lds = (size_t)4 * 16 * 64 * sizeof(float4) + (size_t)c.n_mtiles * (sizeof(int) + 1);
         static size_t sh_allowed = 64 * 1024;
         if (sh_lds > sh_allowed) {
             hipError_t e = hipFuncSetAttribute((const void *)sgmv_shrink_kernel,
@@ -827,17 +1105,26 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
         x2.tile_D = tile_D;
         x2.tile_list = tile_list;
         x2.list_stride = c.list_stride;
+        x2.tile_toff = tile_toff;
+        x2.tile_gpre = tile_gpre;
+        x2.tile_tok = tile_tok;
+        x2.tok_stride = c.tok_stride;
         x2.vcat = vcat;
         x2.vcat_tile_elems = c.vcat_tile_elems;
         x2.sc_tiles = sc_tiles;
         x2.sc_cap = c.sc_cap;
-        x2.n_chunks = (int)((n_out + 63) / 64);
+        x2.n_chunks = (int)((n_out + SC_ROWS - 1) / SC_ROWS);
         x2.part_sc = part_sc;
         x2.y = y;
-        const size_t xl = (size_t)c.list_stride * sizeof(int32_t);
-        const unsigned grid = (unsigned)std::min<int64_t>((int64_t)c.sc_cap * (PF_BM / 16) * x2.n_chunks, 2048);
-        hipLaunchKernelGGL(sc_expand_kernel, dim3(grid), dim3(256), xl, stream, x2);
-        e = hipGetLastError();
+        const size_t xl = ((size_t)c.sc_cap + 1) * sizeof(int32_t);
+        // items per scattered tile: at most (256 K / 16 + list_stride) groups x n_chunks
+        const int64_t items = (int64_t)c.sc_cap * (PF_BM * K / 16 + c.list_stride) * x2.n_chunks;
+        const unsigned grid = (unsigned)std::min<int64_t>(items, 1024);
+        for (int pass = 0; pass < K && e == hipSuccess; ++pass) {
+            x2.pass = pass;
+            hipLaunchKernelGGL(sc_expand_kernel, dim3(grid), dim3(256), xl, stream, x2);
+            e = hipGetLastError();
+        }
     }
     return e;
 }

@@ -74,6 +74,7 @@ struct PrefillCfg {
     int64_t vcat_tile_elems;  // bf16 elements of one tile's V block
     int sc_cap;               // scattered tiles whose expand runs outside the GEMM
     int64_t n_out;
+    int tok_stride;           // bytes of a tile's per-adapter token lists (256 K)
 };
 PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t R,
                           int32_t n_slices);
