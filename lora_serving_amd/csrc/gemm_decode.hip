@@ -118,6 +118,12 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
     const bool wave_on = kw < n_in && wave * DEC_WK < P.ks_cols;
     float *upart = P.upart;
 
+    // slot id of this workgroup's first shrink pair, read first (the A addresses wait for it)
+    const int wd = g.n_slices * g.R;
+    int a0 = -1;
+    if (upart != nullptr && tile < P.n_pairs)
+        a0 = P.idx[tile];
+
     // column of the chunk this lane supplies at k-step ks: the 4 lanes of a row read 64
     // contiguous bytes per instruction (16 cache lines per wave instruction)
     auto col = [&](int ks) { return kw + (ks * 4 + gq) * 8; };
@@ -137,11 +143,8 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
             xf[tt][ks] = dec_ld16(x + (int64_t)min(row, T - 1) * n_in, c,
                                   wave_on && row < T && c < n_in);
         }
-    // ---- first shrink piece of this workgroup: pair p = tile, rows 0..15 of A[a]
-    const int wd = g.n_slices * g.R;
-    int a0 = -1;
-    if (upart != nullptr && tile < P.n_pairs)
-        a0 = P.idx[tile];
+    // ---- the A rows of the first shrink piece of this workgroup: pair p = tile, rows 0..15 of
+    //      A[a] (used after the base products; summed over the waves with the base tiles)
     u32x4 af[4];
     {
         // issued whether or not the pair has an adapter (slot 0's rows then, or x's first row
@@ -191,9 +194,6 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
             xf[tt][ks] = *(const u32x4 *)(xl + (row * 16 + (c ^ (row & 15))) * 8);
         }
 
-    if (a0 >= 0)
-        decode_shrink_piece<TT>(xf, af, tile, 0, K, T, wd, s, wave, r, gq, sred, upart);
-
     // ---- base products
     f32x4 acc[4][TT];
 #pragma unroll
@@ -211,23 +211,25 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
                     __builtin_bit_cast(bf16x8, wf[rt][ks]), __builtin_bit_cast(bf16x8, xf[tt][ks]),
                     acc[rt][tt], 0, 0, 0);
 
-    // ---- remaining shrink pieces (other row groups, other pairs of this tile)
-    if (upart != nullptr) {
-        for (int p = tile; p < P.n_pairs; p += n_tiles) {
-            const int a = P.idx[p];
-            if (a < 0)
-                continue;
-            for (int r0 = (p == tile ? 16 : 0); r0 < wd; r0 += 16) {
-                u32x4 afr[4];
-                const int arow = r0 + r;
-                const uint16_t *ap = g.A + ((int64_t)a * wd + min(arow, wd - 1)) * n_in;
+    // ---- first shrink piece: its token's column goes to sred and is summed over the waves
+    //      together with the base tiles below (no barrier of its own)
+    const int t0p = tile / K;
+    if (a0 >= 0) {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int c = col(ks);
-                    afr[ks] = dec_ld16(ap, c, wave_on && c < n_in && arow < wd);
-                }
-                decode_shrink_piece<TT>(xf, afr, p, r0, K, T, wd, s, wave, r, gq, sred, upart);
+        for (int q = 0; q < TT; ++q) {
+            if (q == (t0p >> 4)) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, af[ks]), __builtin_bit_cast(bf16x8, xf[q][ks]), d,
+                        0, 0, 0);
             }
+        }
+        if (r == (t0p & 15)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sred[wave][gq * 4 + i] = d[i];
         }
     }
 
@@ -241,6 +243,13 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
             red4[wave * SLOTS + (rt * TT + tt) * 64 + lane] =
                 float4{acc[rt][tt][0], acc[rt][tt][1], acc[rt][tt][2], acc[rt][tt][3]};
     lds_barrier();
+    if (a0 >= 0 && threadIdx.x < 16 && (int)threadIdx.x < wd) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < DEC_WAVES; ++w)
+            sum += sred[w][threadIdx.x];
+        upart[(((int64_t)s * K + (tile - t0p * K)) * T + t0p) * wd + threadIdx.x] = sum;
+    }
     for (int sl = threadIdx.x; sl < SLOTS; sl += 512) {
         float4 sum = red4[sl];
 #pragma unroll
@@ -258,6 +267,32 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
         const int rloc = rt * 16 + (ln >> 4) * 4;   // row within the tile
         if (tok < T)
             *(float4 *)(P.part + (((int64_t)s * n_tiles + tile) * T + tok) * DEC_ROWS + rloc) = sum;
+    }
+
+    // ---- remaining shrink pieces (other row groups, other pairs of this tile); sred is
+    //      reused once every wave is past the reads above
+    if (upart != nullptr) {
+        bool synced = false;
+        for (int p = tile; p < P.n_pairs; p += n_tiles) {
+            const int a = P.idx[p];
+            if (a < 0)
+                continue;
+            for (int r0 = (p == tile ? 16 : 0); r0 < wd; r0 += 16) {
+                if (!synced) {
+                    lds_barrier();
+                    synced = true;
+                }
+                u32x4 afr[4];
+                const int arow = r0 + r;
+                const uint16_t *ap = g.A + ((int64_t)a * wd + min(arow, wd - 1)) * n_in;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int c = col(ks);
+                    afr[ks] = dec_ld16(ap, c, wave_on && c < n_in && arow < wd);
+                }
+                decode_shrink_piece<TT>(xf, afr, p, r0, K, T, wd, s, wave, r, gq, sred, upart);
+            }
+        }
     }
 }
 DecodeCfg decode_config(int64_t T, int64_t n_in, int64_t n_out)
