@@ -25,9 +25,8 @@
  *  - Device pointers unless marked "host".  bf16 buffers are passed as void* holding bfloat16
  *    bits.  Everything is row-major and contiguous; base pointers must be 16-byte aligned.
  *  - The caller owns every buffer.  The library allocates no device memory on these calls:
- *    scratch space comes in through (ws, ws_bytes), sized by mlora_workspace_size().  A new
- *    workspace is prepared once with mlora_workspace_init(); every call leaves it ready for
- *    the next one.
+ *    scratch space comes in through (ws, ws_bytes), sized by mlora_workspace_size(); its
+ *    contents need no preparation and carry nothing from one call to the next.
  *  - Calls enqueue work on `stream` and return; the status reports only the synchronous
  *    argument checks and launch errors (MLORA_ERR_HIP).  No exception crosses the ABI.
  *  - Calls on one stream are ordered; two calls that share a workspace must not overlap.
@@ -114,14 +113,6 @@ int64_t mlora_slot_bytes(int32_t S, int32_t R, int64_t n_in, int64_t n_out, int3
  */
 size_t mlora_workspace_size(int64_t T, int32_t K, int64_t n_in, int64_t n_out,
                             const mlora_slots *slots);
-
-/*
- * Prepares a newly allocated workspace (>= 64 KiB, 16-byte aligned) for its first use: zeroes
- * the completion counters that the one-launch decode kernel keeps at its start (a kernel on
- * `stream`, no memset).  Every later call returns the counters to zero, so this is needed only
- * once per allocation (and again if a call on it was ever aborted).
- */
-mlora_status mlora_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Synchronous check of an index map and of the adapter ranks (blocks on `stream`).

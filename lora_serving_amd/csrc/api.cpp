@@ -71,19 +71,16 @@ mlora_status check_slots(const mlora_slots *s, int64_t n_out, bool need_data, Sl
     return MLORA_OK;
 }
 
-// Workspace layout of one call; every region 256-byte aligned.  The counter words at the
-// start must be zero before the first call (mlora_workspace_init); every call leaves them zero.
+// Workspace layout of one call; every region 256-byte aligned.  No region carries state from
+// one call to the next.
 struct Layout {
-    size_t sync = 0;       // reserved words, zeroed by mlora_workspace_init
     size_t sort_cnt = 0;   // counting-sort scratch (plan)
     size_t v = 0;          // fp32 [sk][K][Tc][n_slices*R] shrink partials (decode path)
     size_t part = 0;       // fp32 partial sums of the decode GEMM
     size_t pre = 0;        // prefill path: tile lists and V blocks
     size_t total = 0;
-    size_t off_sync = 0, off_sort = 0, off_v = 0, off_part = 0, off_pre = 0;
+    size_t off_sort = 0, off_v = 0, off_part = 0, off_pre = 0;
 };
-
-constexpr size_t SYNC_BYTES = DECODE_SYNC_BYTES;   // fixed, so mlora_workspace_init knows it
 
 // Regions for both paths, so one workspace size serves any flags.
 Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t R,
@@ -91,7 +88,6 @@ Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S,
 {
     Layout L;
     const int32_t wd = n_slices * R;
-    L.sync = SYNC_BYTES;
     L.sort_cnt = align_up(sort_workspace_bytes(T * K, S));
     if (T > 0)
         L.pre = align_up(prefill_workspace_bytes(
@@ -104,8 +100,7 @@ Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S,
         L.v = align_up((size_t)sk * K * Tc * wd * sizeof(float));
         L.part = align_up(decode_partial_bytes(Tc, n_in, n_out));
     }
-    L.off_sync = 0;
-    L.off_sort = L.off_sync + L.sync;
+    L.off_sort = 0;
     L.off_v = L.off_sort + L.sort_cnt;
     L.off_part = L.off_v + L.v;
     L.off_pre = L.off_part + L.part;
@@ -226,14 +221,6 @@ const char *mlora_status_string(mlora_status status)
     case MLORA_ERR_UNSUPPORTED: return "outside the supported limits";
     }
     return "unknown status";
-}
-
-mlora_status mlora_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream)
-{
-    if (ws == nullptr || ws_bytes < SYNC_BYTES || !aligned16(ws))
-        return MLORA_ERR_ARG;
-    return hip_status(launch_zero_words((uint32_t *)ws, SYNC_BYTES / sizeof(uint32_t), stream),
-                      "workspace init");
 }
 
 float mlora_factor(float alpha, int32_t r, int32_t use_rslora)

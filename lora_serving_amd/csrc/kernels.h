@@ -63,9 +63,6 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, int64_t T, i
 hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, const float *upart,
                                 const float *scale, int64_t T, int64_t n_out, const SlotGeom *g,
                                 const int32_t *idx, int32_t K, uint16_t *y, hipStream_t stream);
-constexpr size_t DECODE_SYNC_BYTES = 64 * 1024;   // reserved words at the start of the workspace
-// zero fill of n 32-bit words (a kernel, not a memset node)
-hipError_t launch_zero_words(uint32_t *p, size_t n, hipStream_t stream);
 
 // ---- gemm_prefill.hip: tiled MFMA GEMM with the LoRA delta as extra K-steps ---------------
 struct PrefillCfg {

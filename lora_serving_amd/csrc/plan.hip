@@ -137,22 +137,6 @@ __global__ __launch_bounds__(64) void sort_scatter(const int32_t *__restrict__ k
     }
 }
 
-__global__ void zero_words_kernel(uint32_t *p, size_t n)
-{
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-         i += (size_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
-}
-
-hipError_t launch_zero_words(uint32_t *p, size_t n, hipStream_t stream)
-{
-    if (n == 0)
-        return hipSuccess;
-    const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 1024);
-    hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, stream, p, n);
-    return hipGetLastError();
-}
-
 static int key_bits(int32_t nkeys)
 {
     int b = 0;

@@ -32,7 +32,7 @@ MLORA_PATH_DECODE = 2
 MLORA_PATH_TILED = 4
 
 EXPORTS = ("mlora_status_string", "mlora_last_error", "mlora_factor", "mlora_slot_bytes",
-           "mlora_workspace_size", "mlora_workspace_init",
+           "mlora_workspace_size",
            "mlora_validate", "mlora_plan", "mlora_shrink", "mlora_expand", "mlora_linear",
            "mlora_trace_start", "mlora_trace_stop")
 
@@ -58,8 +58,6 @@ _lib.mlora_slot_bytes.restype = _i64
 _lib.mlora_slot_bytes.argtypes = [_i32, _i32, _i64, _i64, _i32]
 _lib.mlora_workspace_size.restype = ctypes.c_size_t
 _lib.mlora_workspace_size.argtypes = [_i64, _i32, _i64, _i64, _SLOTS_P]
-_lib.mlora_workspace_init.restype = ctypes.c_int
-_lib.mlora_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
 _lib.mlora_validate.restype = ctypes.c_int
 _lib.mlora_validate.argtypes = [_P, _i64, _i32, _SLOTS_P, _P, ctypes.POINTER(_i64), _P]
 _lib.mlora_plan.restype = ctypes.c_int
@@ -164,21 +162,13 @@ def mlora_workspace_size(T: int, K: int, n_in: int, n_out: int, slots: Slots) ->
     return int(_lib.mlora_workspace_size(T, K, n_in, n_out, slots.ref))
 
 
-def mlora_workspace_init(ws, stream=None):
-    _need(ws, (__import__("torch").uint8,), "ws")
-    _check(_lib.mlora_workspace_init(_ptr(ws), ws.numel(), _stream(stream)),
-           "mlora_workspace_init")
-
-
 def workspace(T: int, K: int, n_in: int, n_out: int, slots: Slots, device="cuda"):
-    """A workspace of mlora_workspace_size() bytes, prepared with mlora_workspace_init()."""
+    """A workspace of mlora_workspace_size() bytes."""
     import torch
     n = mlora_workspace_size(T, K, n_in, n_out, slots)
     if n == 0:
         raise MloraError(MLORA_ERR_ARG, "mlora_workspace_size")
-    ws = torch.empty(n, dtype=torch.uint8, device=device)
-    mlora_workspace_init(ws)
-    return ws
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def mlora_validate(idx, slots: Slots, rank=None, stream=None):
