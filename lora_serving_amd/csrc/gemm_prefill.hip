@@ -594,10 +594,19 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
         const int R = P.g.R;
         const int ke = min(q - nk_main, nk_extra - 1);
         const int sg = sg_lo + ke / kb_per_slice;
-        const int kk = (ke % kb_per_slice) * PF_KS + c * 8;   // column within the slice block
+        const int kk0 = (ke % kb_per_slice) * PF_KS;          // first column of the step
+        const int kk = kk0 + c * 8;                           // column within the slice block
         const int dd = kk / (2 * R);
         const int rho = (kk - dd * 2 * R) & (R - 1);
-        const int a = slist[min(dd, D - 1)];   // the tile's adapter list (global, L2-resident)
+        // the step's 32 columns meet at most two adapters (2R >= 16): dd0 and dd0 + 1.  Their
+        // ids are read with scalar loads (constant address space), which wait on the scalar
+        // counter only: a vector load here would also wait for every copy in flight.
+        const int dd0 = __builtin_amdgcn_readfirstlane(kk0 / (2 * R));
+        const __attribute__((address_space(4))) int *cl =
+            (const __attribute__((address_space(4))) int *)slist;
+        const int a_lo = cl[min(dd0, D - 1)];
+        const int a_hi = cl[min(dd0 + 1, D - 1)];
+        const int a = dd == dd0 ? a_lo : a_hi;
         const int s_lo = P.g.slice_start[sg], s_hi = P.g.slice_start[sg + 1];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
