@@ -550,18 +550,18 @@ struct GemmArgs {
 };
 
 // GEMM: 256 W rows x 256 tokens per workgroup, 8 waves (4 along W rows x 2 along tokens,
-// 64 x 128 each), k-steps of 32 columns.  Operand tiles go from global memory straight into
-// LDS (global_load_lds_dwordx4, no register staging) through a ring of 4 stages of 32 KB, three
-// stages ahead of the MFMAs; each wave waits for its own copies of the next stage and a
-// barrier (LDS only) publishes them.  A stage holds W[256][32] and X[256][32], 64 bytes a row;
-// one copy instruction fills a contiguous 1 KB block (lane L writes bytes 16 L..16 L+15: 16
-// rows, 4 lanes per row so each row is read as 64 contiguous bytes), and the 16-byte chunk c
-// of row r sits at position c ^ ((r >> 1) & 3) of its row.  With that swizzle the operand read
-// of a 16 x 32 fragment (lane (r, g) reads row r, chunk g) has no LDS bank conflicts on
-// gfx950 (the plain layout and the (r >> 2) swizzle both measured two-way conflicts).
+// 64 x 128 each), k-steps of 64 columns.  Operand tiles go from global memory straight into
+// LDS (global_load_lds_dwordx4, no register staging), double buffered (2 stages of 64 KB), one
+// stage ahead of the MFMAs; each wave waits for its own copies of the next stage and a barrier
+// (LDS only) publishes them.  A stage holds W[256][64] and X[256][64], 128 bytes a row: one
+// copy instruction fills a contiguous 1 KB block (lane L writes bytes 16 L..16 L+15: 8 rows,
+// 8 lanes per row), so every request to L2 is a whole 128-byte line.  (With 64-byte rows the
+// copies were bound by the CU's outstanding L2 requests, each carrying half a line.)  The
+// 16-byte chunk c of row r sits at position c ^ (r & 7) of its row; with that swizzle the
+// operand reads (16 rows x 16 bytes per lane group) measured free of LDS bank conflicts.
 // Chunks past n_in, masked B rows and padding are copied from a static block of zeros.
-constexpr int PF_KS = 32;                  // columns per stage
-constexpr int PF_STAGES = 5;
+constexpr int PF_KS = 64;                  // columns per stage
+constexpr int PF_STAGES = 2;
 constexpr int PF_STAGE_BYTES = 2 * 256 * PF_KS * 2;
 
 __device__ __forceinline__ void pf_dma(const void *g, uint16_t *lds)
@@ -569,26 +569,26 @@ __device__ __forceinline__ void pf_dma(const void *g, uint16_t *lds)
     __builtin_amdgcn_global_load_lds(g, (void __attribute__((address_space(3))) *)lds, 16, 0, 0);
 }
 
-// Issues this wave's copies of stage q (k-step q: base columns q*32 while q < nk_main, then
-// the LoRA extra steps) into buffer `st`: 2 blocks of 16 W rows and 2 of 16 tokens per wave.
+// Issues this wave's copies of stage q (k-step q: base columns q*64 while q < nk_main, then
+// the LoRA extra steps) into buffer `st`: 4 blocks of 8 W rows and 4 of 8 tokens per wave.
 __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q, int nk_main,
                                          int nk_extra, int m0, int n0, const uint16_t *vtile,
                                          int D, int kxs, int sg_lo, int kb_per_slice,
                                          const int *slist, int wave, int lane)
 {
-    const int rr = lane >> 2;                       // row within the 16-row block
-    const int c = (lane & 3) ^ ((rr >> 1) & 3);     // chunk this lane's position holds
+    const int rr = lane >> 3;                       // row within the 8-row block
+    const int c = (lane & 7) ^ rr;                  // chunk this lane's position holds
     uint16_t *sw = st, *sx = st + 256 * PF_KS;
     if (q < nk_main) {
         const int k = q * PF_KS + c * 8;
         const bool ok = k < P.n_in;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int row = (wave * 2 + b) * 16 + rr;
+        for (int b = 0; b < 4; ++b) {
+            const int row = (wave * 4 + b) * 8 + rr;
             const uint16_t *gw = P.W + (int64_t)min(n0 + row, P.n_out - 1) * P.n_in + k;
             const uint16_t *gx = P.x + (int64_t)min(m0 + row, P.T - 1) * P.n_in + k;
-            pf_dma(ok ? (const void *)gw : (const void *)pf_zero16, sw + (wave * 2 + b) * 16 * PF_KS);
-            pf_dma(ok ? (const void *)gx : (const void *)pf_zero16, sx + (wave * 2 + b) * 16 * PF_KS);
+            pf_dma(ok ? (const void *)gw : (const void *)pf_zero16, sw + (wave * 4 + b) * 8 * PF_KS);
+            pf_dma(ok ? (const void *)gx : (const void *)pf_zero16, sx + (wave * 4 + b) * 8 * PF_KS);
         }
     } else {
         const int R = P.g.R;
@@ -598,45 +598,52 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
         const int kk = kk0 + c * 8;                           // column within the slice block
         const int dd = kk / (2 * R);
         const int rho = (kk - dd * 2 * R) & (R - 1);
-        // the step's 32 columns meet at most two adapters (2R >= 16): dd0 and dd0 + 1.  Their
+        // the step's 64 columns meet at most four adapters (2R >= 16): dd0 .. dd0 + 3.  Their
         // ids are read with scalar loads (constant address space), which wait on the scalar
         // counter only: a vector load here would also wait for every copy in flight.
         const int dd0 = __builtin_amdgcn_readfirstlane(kk0 / (2 * R));
         const __attribute__((address_space(4))) int *cl =
             (const __attribute__((address_space(4))) int *)slist;
-        const int a_lo = cl[min(dd0, D - 1)];
-        const int a_hi = cl[min(dd0 + 1, D - 1)];
-        const int a = dd == dd0 ? a_lo : a_hi;
+        const int a0 = cl[min(dd0, D - 1)];
+        const int a1 = cl[min(dd0 + 1, D - 1)];
+        const int a2 = cl[min(dd0 + 2, D - 1)];
+        const int a3 = cl[min(dd0 + 3, D - 1)];
+        const int e = dd - dd0;
+        const int a = e == 0 ? a0 : e == 1 ? a1 : e == 2 ? a2 : a3;
         const int s_lo = P.g.slice_start[sg], s_hi = P.g.slice_start[sg + 1];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int row = (wave * 2 + b) * 16 + rr;
+        for (int b = 0; b < 4; ++b) {
+            const int row = (wave * 4 + b) * 8 + rr;
             const int n = n0 + row;
             const bool ok = dd < D && n >= s_lo && n < s_hi;   // s_hi <= n_out
             const uint16_t *gb = P.g.B + ((int64_t)a * P.n_out + min(n, P.n_out - 1)) * R + rho;
             const uint16_t *gv = vtile + (int64_t)row * (P.g.n_slices * kxs) + sg * kxs + kk;
-            pf_dma(ok ? (const void *)gb : (const void *)pf_zero16, sw + (wave * 2 + b) * 16 * PF_KS);
-            pf_dma((const void *)gv, sx + (wave * 2 + b) * 16 * PF_KS);
+            pf_dma(ok ? (const void *)gb : (const void *)pf_zero16, sw + (wave * 4 + b) * 8 * PF_KS);
+            pf_dma((const void *)gv, sx + (wave * 4 + b) * 8 * PF_KS);
         }
     }
 }
 
-// MFMAs of one stage: wave (wn, wm) owns W rows wn*64 .. +64 and tokens wm*128 .. +128.
+// MFMAs of one stage (two k-steps of 32): wave (wn, wm) owns W rows wn*64 .. +64 and tokens
+// wm*128 .. +128.
 __device__ __forceinline__ void pf_compute(const uint16_t *st, int wn, int wm, int r, int gq,
                                            f32x4 (&acc)[4][8])
 {
     const uint16_t *sw = st, *sx = st + 256 * PF_KS;
-    const int pos = gq ^ ((r >> 1) & 3);
-    bf16x8 af[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        af[i] = *(const bf16x8 *)(sw + ((wn * 64 + i * 16 + r) * 4 + pos) * 8);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const bf16x8 bv = *(const bf16x8 *)(sx + ((wm * 128 + j * 16 + r) * 4 + pos) * 8);
+    for (int ks = 0; ks < 2; ++ks) {
+        const int pos = (ks * 4 + gq) ^ (r & 7);
+        bf16x8 af[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv, acc[i][j], 0, 0, 0);
+            af[i] = *(const bf16x8 *)(sw + ((wn * 64 + i * 16 + r) * 8 + pos) * 8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bf16x8 bv = *(const bf16x8 *)(sx + ((wm * 128 + j * 16 + r) * 8 + pos) * 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv, acc[i][j], 0, 0, 0);
+        }
     }
 }
 
@@ -700,17 +707,15 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
     for (int q = 0; q < PF_STAGES; ++q)
         pf_issue(P, pf_lds + q * (PF_STAGE_BYTES / 2), min(q, nk - 1), nk_main, nk_extra, m0, n0,
                  vtile, D, kxs, sg_lo, kb_per_slice, slist, wave, lane);
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // stage 0 (4 copies per stage)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");    // stage 0 (8 copies per stage)
     lds_barrier();
-    int buf = 0;
     for (int q = 0; q < nk; ++q) {
-        uint16_t *st = pf_lds + buf * (PF_STAGE_BYTES / 2);
+        uint16_t *st = pf_lds + (q & 1) * (PF_STAGE_BYTES / 2);
         pf_compute(st, wn, wm, r, gq, acc);
-        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // stage q+1
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stage q+1
         lds_barrier();                                      // also: stage q fully read
         pf_issue(P, st, min(q + PF_STAGES, nk - 1), nk_main, nk_extra, m0, n0, vtile, D, kxs,
                  sg_lo, kb_per_slice, slist, wave, lane);
-        buf = buf == PF_STAGES - 1 ? 0 : buf + 1;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no copy outlives the workgroup
 
@@ -1090,7 +1095,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
     a.list_stride = c.list_stride;
     a.tile_ord = tile_ord;
     a.part_sc = part_sc;
-    const size_t lds = (size_t)PF_STAGES * PF_STAGE_BYTES;                // 160 KB of stages
+    const size_t lds = (size_t)PF_STAGES * PF_STAGE_BYTES;                // 128 KB of stages
     static size_t lds_allowed = 0;
     if (lds > lds_allowed) {
         hipError_t e = hipFuncSetAttribute((const void *)prefill_gemm_kernel,
