@@ -92,6 +92,43 @@ def committed_traffic(kernel: str):
     return None
 
 
+def measured_ceilings(roof):
+    """Ceilings measured in the same process, next to the datasheet peaks: a plain device copy
+    (bytes read + written per second) and a large bf16 GEMM through torch.matmul (hipBLASLt);
+    plus the main kernel's achieved figure as a fraction of the matching one."""
+    import torch
+    n = 2 ** 28                                  # 1 GiB of fp32, 4x the Infinity Cache
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * n * 4 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(m, m, dtype=torch.bfloat16, device="cuda").t().contiguous()
+    for _ in range(2):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 2.0 * m ** 3 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    probe = copy_gbps if roof["unit"] == "GB/s" else gemm_tf
+    return {"copy_GBps": copy_gbps, "gemm_bf16_TFLOPs": gemm_tf,
+            "gemm_shape": [m, m, m], "achieved_over_probe": roof["achieved"] / probe}
+
+
 def cpu_baseline(layers, budget_s: float):
     """The oracle, as it stands, on the host cores, on a bounded sample of the workload's
     tokens (whole batches while they take under the budget), scaled to tokens/s."""
@@ -138,6 +175,8 @@ def main():
     ap.add_argument("--flags", type=int, default=0, help="extra mlora_linear flags")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain copy kernel over MIB MiB (counter calibration)")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the measured copy-bandwidth and bf16 GEMM ceilings")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -213,6 +252,14 @@ def main():
     if len(kernel_ms) != cap:
         raise RuntimeError(f"expected {cap} traced launches, got {len(kernel_ms)}")
     k_avg_ms = sum(kernel_ms) / len(kernel_ms)
+    # single-call latency: one input set, each call waited for (no rotation, launch included)
+    lat = []
+    for i in range(50 if decode_like else 5):
+        t0 = time.perf_counter()
+        step(0)
+        torch.cuda.synchronize()
+        lat.append(time.perf_counter() - t0)
+    single_call_us = sorted(lat)[len(lat) // 2] * 1e6
     T = layers[0].T
     tokens_per_s = T / (ms * 1e-3)
     tot_bytes = sum(a["bytes"] for a in algs)
@@ -249,6 +296,9 @@ def main():
         "roofline": roof,
         "step_algorithmic": {"bytes": tot_bytes, "flops": tot_flops},
     }
+    out["single_call_us"] = single_call_us
+    if not args.no_probes:
+        out["probes"] = measured_ceilings(roof)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -107,6 +107,21 @@ def test_tiled_path_small(oracle_mod, case):
         assert tol_ok(y2, y_ref).all()
 
 
+def test_tiled_scattered_tiles_beyond_capacity(oracle_mod):
+    """Wide n_out keeps the fp32 sums of only one scattered tile: the first takes the per-adapter
+    shrink/expand route, the other two the extra-k-step route; both against the oracle."""
+    from lora_serving_amd import mlora
+    L = synth.random_layer(48, T=768, n_in=64, n_out=70000, S=8, R=16, K=2, p_sentinel=0.2,
+                           contiguous=False)
+    say(f"[tiled-cap] T={L.T} n_in={L.n_in} n_out={L.n_out} K={L.K}")
+    D = DevLayer(L)
+    y = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_TILED))
+    toks = np.arange(0, L.T, 11, dtype=np.int64)
+    y_ref = oracle_mod.linear(L, tokens=toks)
+    ok = tol_ok(y[toks], y_ref)
+    assert ok.all(), f"worst {worst(y[toks], y_ref):.3e}, {np.sum(~ok)} out"
+
+
 def test_tiled_sentinel_rows_and_k3_invariance():
     from lora_serving_amd import mlora
     L1 = synth.random_layer(46, T=300, n_in=256, n_out=512, S=6, R=16, K=1, p_sentinel=0.3)
