@@ -10,7 +10,8 @@ Prints one JSON line.
 
 Other workloads (--workload): tiny, prefill (16384 tokens, 4096 -> 11008, 100 x rank 64),
 mixed_qkv (256 decode + 2048 prefill tokens, merged QKV 4096 -> 6144, ranks 8/16/64 padded to
-64), compose (8192 tokens, K = 3 slots, 4096 -> 4096 and 11008 -> 4096 layers).
+64), compose (8192 tokens, K = 3 slots, 4096 -> 4096 and 11008 -> 4096 layers), lm_head
+(the decode batch on a 4096 -> 100,000 vocabulary projection).
 """
 from __future__ import annotations
 
@@ -38,6 +39,8 @@ DESCRIPTIONS = {
                  "4096->(4096,1024,1024), 64 adapters ranks {8,16,64} padded to 64, alpha 2r",
     "compose": "k3_compose: T=8192 = 64 requests x 128 tokens, K=3 slots, 32 adapters rank 16 "
                "alpha 32 (half rsLoRA), s~U(0.2,1); layers 4096->4096 and 11008->4096",
+    "lm_head": "lm_head: T=64 one-token requests, 4096->100000 (vocabulary) bf16, 100 adapters "
+               "rank 16 alpha 32, 6 tokens base-only, K=1",
 }
 
 

@@ -129,7 +129,7 @@ def make_layer(name: str, seed: int, rng: np.random.Generator, idx: np.ndarray, 
 
 
 # ----------------------------------------------------------------------------------------
-# The five workloads
+# The workloads
 # ----------------------------------------------------------------------------------------
 def finite_zipf_cdf(n: int, s: float) -> np.ndarray:
     """Cumulative distribution of P(a) proportional to (a+1)^-s over a = 0..n-1."""
@@ -227,8 +227,18 @@ def workload_compose(seed: int = 1004, n_req: int = 64, req_len: int = 128, S: i
     return layers
 
 
+def workload_lm_head(seed: int = 1005) -> Layer:
+    """LM-head LoRA at decode: the decode mapping (64 one-token requests, 100 adapters of rank
+    16, 6 tokens base-only) on a vocabulary-wide output, 4096 -> 100,000 (not a multiple of the
+    64-row tile, so the last tile is ragged)."""
+    L = workload_decode(seed=seed, n_out=100_000)
+    L.name = "lm_head"
+    return L
+
+
 WORKLOADS = {
     "tiny": workload_tiny,
+    "lm_head": workload_lm_head,
     "decode": workload_decode,
     "prefill": workload_prefill,
     "mixed_qkv": workload_mixed_qkv,

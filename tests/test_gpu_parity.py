@@ -182,7 +182,7 @@ def _sample_tokens(L, n=48, seed=0):
     return np.array(toks, np.int64)
 
 
-@pytest.mark.parametrize("which", ["prefill", "mixed_qkv", "compose"])
+@pytest.mark.parametrize("which", ["prefill", "mixed_qkv", "compose", "lm_head"])
 def test_large_workloads_sampled(oracle_mod, which):
     layers = synth.WORKLOADS[which]()
     if not isinstance(layers, list):
