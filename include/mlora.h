@@ -115,6 +115,28 @@ size_t mlora_workspace_size(int64_t T, int32_t K, int64_t n_in, int64_t n_out,
                             const mlora_slots *slots);
 
 /*
+ * Slot activation ("Multi-LoRA Serving Explained": slots sized for max_lora_rank R, an adapter
+ * of rank r < R zero-padded in its slot; an adapter whose rank exceeds R is rejected).  Loads
+ * one adapter into slot `slot` of a slot set whose device buffers are A, B and factor (the
+ * same buffers and layout as mlora_slots: A bf16 [S][n_slices][R][n_in], B bf16 [S][n_out][R],
+ * factor fp32 [S]):
+ *   A_src  bf16 [n_slices][r][n_in]   the adapter's down matrices (host or device memory)
+ *   B_src  bf16 [n_out][r]            its up matrix (host or device memory)
+ *   r      its true rank, 1 <= r <= R, else MLORA_ERR_RANK
+ *   f      its scale factor (mlora_factor), written to factor[slot]
+ * Rows r..R-1 of the slot's A and columns r..R-1 of its B are set to zero.  Everything is
+ * enqueued on `stream` (asynchronous copies, then one kernel; no memset): host sources must
+ * stay valid until the stream reaches the call, and are copied asynchronously only when
+ * pinned.  The slot must not be in use by work in flight on other streams.  MLORA_ERR_ARG on
+ * a NULL pointer, slot outside [0, S) or sizes below 1; MLORA_ERR_UNSUPPORTED outside the
+ * limits above (S, R, n_slices).
+ */
+mlora_status mlora_slot_load(void *A, void *B, float *factor, int32_t S, int32_t R,
+                             int32_t n_slices, int64_t n_in, int64_t n_out, int32_t slot,
+                             const void *A_src, const void *B_src, int32_t r, float f,
+                             hipStream_t stream);
+
+/*
  * Synchronous check of an index map and of the adapter ranks (blocks on `stream`).
  *   idx   int32 [T][K] device
  *   rank  int32 [S] host, true adapter ranks (may be NULL to skip the rank check)
@@ -184,7 +206,7 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
  * Profiling hook (not part of the computation).  mlora_trace_start creates 2*capacity HIP
  * events (no device memory); from then on every mlora_linear call records one event on its
  * stream right before and one right after each launch of its main product kernel (the decode
- * GEMM, the one-launch decode kernel or the tiled GEMM), for the first `capacity` launches.
+ * GEMM or the tiled GEMM), for the first `capacity` launches.
  * mlora_trace_stop waits for the recorded events, writes the duration of launch i in
  * milliseconds to ms[i] (host array of `capacity` floats; NULL discards them), releases the
  * events and returns the number of durations written (-1 on a HIP error).

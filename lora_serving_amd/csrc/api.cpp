@@ -249,6 +249,37 @@ size_t mlora_workspace_size(int64_t T, int32_t K, int64_t n_in, int64_t n_out,
     return make_layout(T, K, n_in, n_out, g.S, g.R, g.n_slices).total + 256;
 }
 
+mlora_status mlora_slot_load(void *A, void *B, float *factor, int32_t S, int32_t R,
+                             int32_t n_slices, int64_t n_in, int64_t n_out, int32_t slot,
+                             const void *A_src, const void *B_src, int32_t r, float f,
+                             hipStream_t stream)
+{
+    if (A == nullptr || B == nullptr || factor == nullptr || A_src == nullptr ||
+        B_src == nullptr || n_in < 1 || n_out < 1 || S < 1 || slot < 0 || slot >= S)
+        return MLORA_ERR_ARG;
+    if (S > MLORA_MAX_SLOTS || R < 8 || R > MLORA_MAX_RANK || !is_pow2(R) || n_slices < 1 ||
+        n_slices > MLORA_MAX_SLICES)
+        return MLORA_ERR_UNSUPPORTED;
+    if (r < 1 || r > R)
+        return MLORA_ERR_RANK;
+    uint16_t *a_slot = (uint16_t *)A + (int64_t)slot * n_slices * R * n_in;
+    uint16_t *b_slot = (uint16_t *)B + (int64_t)slot * n_out * R;
+    const uint16_t *a_src = (const uint16_t *)A_src;
+    for (int32_t s = 0; s < n_slices; ++s)
+        if (hipError_t e = hipMemcpyAsync(a_slot + (int64_t)s * R * n_in,
+                                          a_src + (int64_t)s * r * n_in, (size_t)r * n_in * 2,
+                                          hipMemcpyDefault, stream);
+            e != hipSuccess)
+            return hip_status(e, "copy of A rows");
+    if (hipError_t e = hipMemcpy2DAsync(b_slot, (size_t)R * 2, B_src, (size_t)r * 2, (size_t)r * 2,
+                                        (size_t)n_out, hipMemcpyDefault, stream);
+        e != hipSuccess)
+        return hip_status(e, "copy of B columns");
+    return hip_status(launch_slot_pad(a_slot, b_slot, factor + slot, R, r, n_slices, n_in, n_out,
+                                      f, stream),
+                      "slot padding");
+}
+
 mlora_status mlora_validate(const int32_t *idx, int64_t T, int32_t K, const mlora_slots *slots,
                             const int32_t *rank, int64_t *bad_value, hipStream_t stream)
 {

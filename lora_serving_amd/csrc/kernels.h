@@ -64,6 +64,12 @@ hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, 
                                 const float *scale, int64_t T, int64_t n_out, const SlotGeom *g,
                                 const int32_t *idx, int32_t K, uint16_t *y, hipStream_t stream);
 
+// ---- slot_load.hip: zero padding of a loaded slot and its scale factor ----------------------
+// A_slot: bf16 [n_slices][R][n_in] of the slot; B_slot: bf16 [n_out][R]; rows/columns >= r.
+hipError_t launch_slot_pad(uint16_t *A_slot, uint16_t *B_slot, float *factor, int32_t R,
+                           int32_t r, int32_t n_slices, int64_t n_in, int64_t n_out, float f,
+                           hipStream_t stream);
+
 // ---- gemm_prefill.hip: tiled MFMA GEMM with the LoRA delta as extra K-steps ---------------
 struct PrefillCfg {
     int n_mtiles, n_ntiles;   // 256-token x 256-row output tiles

@@ -32,7 +32,7 @@ MLORA_PATH_DECODE = 2
 MLORA_PATH_TILED = 4
 
 EXPORTS = ("mlora_status_string", "mlora_last_error", "mlora_factor", "mlora_slot_bytes",
-           "mlora_workspace_size",
+           "mlora_workspace_size", "mlora_slot_load",
            "mlora_validate", "mlora_plan", "mlora_shrink", "mlora_expand", "mlora_linear",
            "mlora_trace_start", "mlora_trace_stop")
 
@@ -58,6 +58,9 @@ _lib.mlora_slot_bytes.restype = _i64
 _lib.mlora_slot_bytes.argtypes = [_i32, _i32, _i64, _i64, _i32]
 _lib.mlora_workspace_size.restype = ctypes.c_size_t
 _lib.mlora_workspace_size.argtypes = [_i64, _i32, _i64, _i64, _SLOTS_P]
+_lib.mlora_slot_load.restype = ctypes.c_int
+_lib.mlora_slot_load.argtypes = [_P, _P, _P, _i32, _i32, _i32, _i64, _i64, _i32, _P, _P, _i32,
+                                 ctypes.c_float, _P]
 _lib.mlora_validate.restype = ctypes.c_int
 _lib.mlora_validate.argtypes = [_P, _i64, _i32, _SLOTS_P, _P, ctypes.POINTER(_i64), _P]
 _lib.mlora_plan.restype = ctypes.c_int
@@ -169,6 +172,21 @@ def workspace(T: int, K: int, n_in: int, n_out: int, slots: Slots, device="cuda"
     if n == 0:
         raise MloraError(MLORA_ERR_ARG, "mlora_workspace_size")
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mlora_slot_load(slots: Slots, n_in: int, slot: int, A_src, B_src, r: int, f: float,
+                    stream=None):
+    """Loads one adapter (A_src bf16 [n_slices][r][n_in], B_src bf16 [n_out][r]; host tensors
+    pinned for an asynchronous copy, or device tensors) into slot `slot` of `slots`, zero
+    padded to the slot width; writes f to the slot's factor."""
+    import torch
+    for t, name in ((A_src, "A_src"), (B_src, "B_src")):
+        if not t.is_contiguous() or t.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+            raise ValueError(f"{name} must be a contiguous bf16 tensor")
+    _check(_lib.mlora_slot_load(_ptr(slots.A), _ptr(slots.B), _ptr(slots.factor), slots.S,
+                                slots.R, slots.n_slices, int(n_in), slots.n_out, int(slot),
+                                _ptr(A_src), _ptr(B_src), int(r), float(f), _stream(stream)),
+           "mlora_slot_load")
 
 
 def mlora_validate(idx, slots: Slots, rank=None, stream=None):

@@ -136,6 +136,28 @@ def test_other_entry_points_argument_checks(m):
     assert L.mlora_validate(0x1000, 0, 1, ctypes.byref(s), ok, None, None) == m.MLORA_OK
 
 
+def test_slot_load_argument_checks(m):
+    """Rank above the slot width (the pages' rejection of ranks over max_lora_rank), rank 0,
+    slot outside [0, S), NULL buffers, unsupported slot widths: all refused before any copy."""
+    L = m._lib
+    args = dict(A=0x1000, B=0x2000, f=0x3000, S=4, R=16, ns=1, n_in=64, n_out=32, slot=1,
+                As=0x4000, Bs=0x5000, r=8)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.mlora_slot_load(a["A"], a["B"], a["f"], a["S"], a["R"], a["ns"], a["n_in"],
+                                 a["n_out"], a["slot"], a["As"], a["Bs"], a["r"], 2.0, None)
+    assert call(r=17) == m.MLORA_ERR_RANK
+    assert call(r=0) == m.MLORA_ERR_RANK
+    assert call(slot=4) == m.MLORA_ERR_ARG
+    assert call(slot=-1) == m.MLORA_ERR_ARG
+    assert call(A=None) == m.MLORA_ERR_ARG
+    assert call(Bs=None) == m.MLORA_ERR_ARG
+    assert call(n_in=0) == m.MLORA_ERR_ARG
+    assert call(R=12) == m.MLORA_ERR_UNSUPPORTED
+    assert call(ns=5) == m.MLORA_ERR_UNSUPPORTED
+
+
 def test_trace_hook_argument_checks(m):
     assert m._lib.mlora_trace_start(0) == m.MLORA_ERR_ARG
     assert m._lib.mlora_trace_start((1 << 20) + 1) == m.MLORA_ERR_ARG

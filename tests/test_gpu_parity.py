@@ -122,6 +122,43 @@ def test_tiled_scattered_tiles_beyond_capacity(oracle_mod):
     assert ok.all(), f"worst {worst(y[toks], y_ref):.3e}, {np.sum(~ok)} out"
 
 
+def test_slot_load_rebuilds_padded_slots():
+    """Slot activation: every adapter loaded at its true rank (host pinned sources and device
+    sources) over slots filled with NaN bits gives back the zero-padded slots bit for bit, and
+    the layer's output is unchanged; one adapter has the full slot width (no padding)."""
+    import torch
+    from lora_serving_amd import mlora
+    ranks = [8, 32, 16, 24, 5]
+    L = synth.random_layer(49, T=40, n_in=384, n_out=200, S=5, R=32, K=2,
+                           slice_sizes=[120, 80], ranks=ranks, p_sentinel=0.2)
+    say(f"[slot-load] S={L.S} R={L.R} ranks={ranks}")
+    D = DevLayer(L)
+    y0 = D.linear().clone()
+    A0, B0, f0 = D.A.clone(), D.B.clone(), D.factor.clone()
+    D.A.view(torch.int16).fill_(0x7FC0)        # bf16 NaN everywhere
+    D.B.view(torch.int16).fill_(0x7FC0)
+    D.factor.fill_(float("nan"))
+    keep = []                                   # sources stay alive until the copies are done
+    for a, r in enumerate(ranks):
+        A_src = np.ascontiguousarray(L.A[a, :, :r, :]).view(np.int16)
+        B_src = np.ascontiguousarray(L.B[a, :, :r]).view(np.int16)
+        if a % 2 == 0:                          # pinned host sources
+            As = torch.from_numpy(A_src).pin_memory()
+            Bs = torch.from_numpy(B_src).pin_memory()
+        else:                                   # device sources
+            As = torch.from_numpy(A_src).cuda()
+            Bs = torch.from_numpy(B_src).cuda()
+        keep.append((As, Bs))
+        mlora.mlora_slot_load(D.slots, L.n_in, a, As, Bs, r, float(f0[a].item()))
+    torch.cuda.synchronize()
+    del keep
+    assert torch.equal(D.A.view(torch.int16), A0.view(torch.int16))
+    assert torch.equal(D.B.view(torch.int16), B0.view(torch.int16))
+    assert torch.equal(D.factor, f0)
+    y1 = D.linear()
+    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
+
+
 def test_tiled_sentinel_rows_and_k3_invariance():
     from lora_serving_amd import mlora
     L1 = synth.random_layer(46, T=300, n_in=256, n_out=512, S=6, R=16, K=1, p_sentinel=0.3)
