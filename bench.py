@@ -211,7 +211,8 @@ def main():
                 x, W, A, B = D.x, D.W, D.A, D.B
             else:
                 x, W, A, B = D.x.clone(), D.W.clone(), D.A.clone(), D.B.clone()
-            slots = mlora.Slots(A, B, D.factor, slice_start=[int(v) for v in D.L.slice_start])
+            slots = mlora.Slots(A, B, D.factor, slice_start=[int(v) for v in D.L.slice_start],
+                                rank=D.rank)
             y = torch.empty((D.L.T, D.L.n_out), dtype=torch.bfloat16, device="cuda")
             one.append((x, W, slots, y, D))
         sets.append(one)

@@ -84,6 +84,10 @@ typedef struct {
     int32_t slice_start[MLORA_MAX_SLICES + 1]; /* host values: 0 = s_0 < s_1 < .. = n_out.
                                                   With n_slices == 1 it may be all zero,
                                                   meaning {0, n_out}.                        */
+    const int32_t *rank;    /* int32 [S] device: each slot's true rank r <= R, or NULL (= R).
+                               With it the kernels skip the zero padding beyond r (same
+                               results: the skipped products are exact zeros).  Values must be
+                               in [1, R] (mlora_validate); larger ones are read as R.        */
 } mlora_slots;
 
 /* Text for a status code (static storage). */

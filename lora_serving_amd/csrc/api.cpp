@@ -68,6 +68,7 @@ mlora_status check_slots(const mlora_slots *s, int64_t n_out, bool need_data, Sl
     g->A = (const uint16_t *)s->A;
     g->B = (const uint16_t *)s->B;
     g->factor = s->factor;
+    g->rank = s->rank;
     return MLORA_OK;
 }
 

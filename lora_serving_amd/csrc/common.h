@@ -83,6 +83,14 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int *total)
     return incl - v;
 }
 
+// True rank of slot a, rounded up to a multiple of 8 (the 16-byte chunk of the kernels' loads;
+// the slot's padding beyond the rank is zero, so the rounding adds exact zeros): R when the
+// slot set has no rank table, never more than R.
+__device__ __forceinline__ int slot_rank8(const int32_t *rank, int a, int R)
+{
+    return rank == nullptr ? R : min(R, (max(rank[a], 1) + 7) & ~7);
+}
+
 // s_barrier that waits only for this wave's LDS operations, not for its outstanding global
 // loads (a __syncthreads fence waits for every outstanding memory operation); the "memory"
 // clobber keeps the compiler from moving memory accesses across it.

@@ -148,7 +148,9 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
     u32x4 af[4];
     {
         // issued whether or not the pair has an adapter (slot 0's rows then, or x's first row
-        // without LoRA; unused either way)
+        // without LoRA; unused either way).  The slot's rank is not consulted here: it would
+        // put a second dependent scalar load in front of the W stream (rows past the rank are
+        // zero in memory, so reading them is exact).
         const int arow = min(r, max(wd, 1) - 1);
         const uint16_t *ap = upart != nullptr ? g.A + ((int64_t)max(a0, 0) * wd + arow) * n_in : x;
 #pragma unroll
@@ -285,10 +287,12 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
                 u32x4 afr[4];
                 const int arow = r0 + r;
                 const uint16_t *ap = g.A + ((int64_t)a * wd + min(arow, wd - 1)) * n_in;
+                // rows past the adapter's rank (zero padding) come from the zero block
+                const bool rok = arow < wd && arow % g.R < slot_rank8(g.rank, a, g.R);
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int c = col(ks);
-                    afr[ks] = dec_ld16(ap, c, wave_on && c < n_in && arow < wd);
+                    afr[ks] = dec_ld16(ap, c, rok && wave_on && c < n_in);
                 }
                 decode_shrink_piece<TT>(xf, afr, p, r0, K, T, wd, s, wave, r, gq, sred, upart);
             }

@@ -231,15 +231,16 @@ struct ShrinkArgs {
     int tok_stride;
 };
 
-__device__ __forceinline__ void sh_load(const uint16_t *const (&ap)[4], const uint16_t *const (&xp)[4],
-                                        int col, int kend, u32x4 (&af)[4], u32x4 (&xf)[4])
+__device__ __forceinline__ void sh_load(const uint16_t *const (&ap)[4], const bool (&aok)[4],
+                                        const uint16_t *const (&xp)[4], int col, int kend,
+                                        u32x4 (&af)[4], u32x4 (&xf)[4])
 {
     // the pointers already include this lane's chunk offset 8 * (lane / 16)
     const int off = ((threadIdx.x & 63) >> 4) * 8;
     const bool ok = col + off < kend;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        af[b] = *(const u32x4 *)(ok ? (const void *)(ap[b] + col) : (const void *)pf_zero16);
+        af[b] = *(const u32x4 *)(ok && aok[b] ? (const void *)(ap[b] + col) : (const void *)pf_zero16);
         xf[b] = *(const u32x4 *)(ok ? (const void *)(xp[b] + col) : (const void *)pf_zero16);
     }
 }
@@ -299,12 +300,18 @@ __device__ __forceinline__ void sh_cat_item(const ShrinkArgs &P, int m, int loca
     const int t0 = m * PF_BM + c * 64;
     const int rows_cat = D * wd;
 
+    // rows past their adapter's rank (zero padding) are not read: their fragments come from the
+    // zero block
     const uint16_t *ap[4], *xp[4];
+    bool aok[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        const int ar = min(rb * 64 + b * 16 + r, rows_cat - 1);
+        const int ar_raw = rb * 64 + b * 16 + r;
+        const int ar = min(ar_raw, rows_cat - 1);
         const int d = ar / wd;
-        ap[b] = g.A + ((int64_t)list[d] * wd + (ar - d * wd)) * P.n_in + gq * 8;
+        const int rr = ar - d * wd;
+        aok[b] = ar_raw < rows_cat && rr % R < slot_rank8(g.rank, list[d], R);
+        ap[b] = g.A + ((int64_t)list[d] * wd + rr) * P.n_in + gq * 8;
         xp[b] = P.x + (int64_t)min(t0 + b * 16 + r, P.T - 1) * P.n_in + gq * 8;
     }
     int kb, kend, nsteps;
@@ -317,13 +324,13 @@ __device__ __forceinline__ void sh_cat_item(const ShrinkArgs &P, int m, int loca
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 a0[4], x0[4], a1[4], x1[4];
-    sh_load(ap, xp, kb, kend, a0, x0);
-    sh_load(ap, xp, kb + 32, kend, a1, x1);
+    sh_load(ap, aok, xp, kb, kend, a0, x0);
+    sh_load(ap, aok, xp, kb + 32, kend, a1, x1);
     for (int st = 0; st < nsteps; st += 2) {
         sh_mfma(a0, x0, acc);
-        sh_load(ap, xp, kb + (st + 2) * 32, kend, a0, x0);
+        sh_load(ap, aok, xp, kb + (st + 2) * 32, kend, a0, x0);
         sh_mfma(a1, x1, acc);
-        sh_load(ap, xp, kb + (st + 3) * 32, kend, a1, x1);
+        sh_load(ap, aok, xp, kb + (st + 3) * 32, kend, a1, x1);
     }
 
     // lane holds A_cat rows rb*64 + 16i + 4gq + e of token t0 + 16j + r
@@ -377,13 +384,14 @@ __device__ __forceinline__ void sh_cat_item(const ShrinkArgs &P, int m, int loca
 constexpr int SG_ROWS = 32;
 constexpr int SG_ST = 4;
 
-__device__ __forceinline__ void sg_load(const uint16_t *const (&ap)[2], const uint16_t *xp, bool xok,
-                                        int col, int kend, u32x4 (&af)[2], u32x4 &xf)
+__device__ __forceinline__ void sg_load(const uint16_t *const (&ap)[2], const bool (&aok)[2],
+                                        const uint16_t *xp, bool xok, int col, int kend,
+                                        u32x4 (&af)[2], u32x4 &xf)
 {
     const int off = ((threadIdx.x & 63) >> 4) * 8;
     const bool ok = col + off < kend;
-    af[0] = *(const u32x4 *)(ok ? (const void *)(ap[0] + col) : (const void *)pf_zero16);
-    af[1] = *(const u32x4 *)(ok ? (const void *)(ap[1] + col) : (const void *)pf_zero16);
+    af[0] = *(const u32x4 *)(ok && aok[0] ? (const void *)(ap[0] + col) : (const void *)pf_zero16);
+    af[1] = *(const u32x4 *)(ok && aok[1] ? (const void *)(ap[1] + col) : (const void *)pf_zero16);
     xf = *(const u32x4 *)(ok && xok ? (const void *)(xp + col) : (const void *)pf_zero16);
 }
 
@@ -411,22 +419,30 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
     const int s0 = to[d] + 16 * (gidx - gp[d]);
     const int ng = min(16, to[d + 1] - s0);
     const uint8_t *tk = P.tile_tok + (int64_t)m * P.tok_stride + s0;
-    const bool xok = r < ng;
-    const uint16_t *xp = P.x + ((int64_t)m * PF_BM + (xok ? tk[r] : 0)) * P.n_in + gq * 8;
+    // rows past the adapter's rank (zero padding) are neither read nor multiplied: their
+    // fragments come from the zero block, and a block with no row below the rank skips the loop
+    const int rk = slot_rank8(g.rank, a, R);
     const uint16_t *ap[2];
+    bool aok[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-        const int row = min(rb * SG_ROWS + f * 16 + r, wd - 1);
-        ap[f] = g.A + ((int64_t)a * wd + row) * P.n_in + gq * 8;
+        const int row = rb * SG_ROWS + f * 16 + r;
+        aok[f] = row < wd && row % R < rk;
+        ap[f] = g.A + ((int64_t)a * wd + min(row, wd - 1)) * P.n_in + gq * 8;
     }
+    const bool any_row = __ballot(aok[0] || aok[1]) != 0ull;
+    const bool xok = r < ng && any_row;
+    const uint16_t *xp = P.x + ((int64_t)m * PF_BM + (r < ng ? tk[r] : 0)) * P.n_in + gq * 8;
     int kb, kend, nsteps;
     sh_wave_cols(P.n_in, wave, kb, kend, nsteps);
+    if (!any_row)
+        nsteps = 0;
 
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     u32x4 af[SG_ST][2], xf[SG_ST];
 #pragma unroll
     for (int s = 0; s < SG_ST; ++s)
-        sg_load(ap, xp, xok, kb + s * 32, kend, af[s], xf[s]);
+        sg_load(ap, aok, xp, xok, kb + s * 32, kend, af[s], xf[s]);
     for (int st = 0; st < nsteps; st += SG_ST) {
 #pragma unroll
         for (int s = 0; s < SG_ST; ++s) {
@@ -435,7 +451,7 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
                 acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8, af[s][f]), __builtin_bit_cast(bf16x8, xf[s]), acc[f],
                     0, 0, 0);
-            sg_load(ap, xp, xok, kb + (st + s + SG_ST) * 32, kend, af[s], xf[s]);
+            sg_load(ap, aok, xp, xok, kb + (st + s + SG_ST) * 32, kend, af[s], xf[s]);
         }
     }
 
@@ -847,6 +863,7 @@ __device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int loc
     }
     const bool act = tok_ok && below == P.pass;
     const bool last = below == n_dist - 1;
+    const int rk = slot_rank8(g.rank, a, R);
 
     const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
     const uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems + (int64_t)tl * (g.n_slices * kxs) +
@@ -879,8 +896,8 @@ __device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int loc
         const int sg_b = sc_slice(g, min(nb, P.n_out - 1));
         for (int sg = sg_lo; sg <= sg_hi; ++sg) {
             const bool row_ok = nb < P.n_out && sg_b == sg;
-            for (int k = 0; k < R; k += 32) {
-                const bool kok = k + gq * 8 < R;
+            for (int k = 0; k < rk; k += 32) {          // B columns past the rank are zero
+                const bool kok = k + gq * 8 < rk;
                 const u32x4 bv = *(const u32x4 *)(row_ok && kok ? (const void *)(brow0 + (int64_t)nb * R + k)
                                                                 : (const void *)pf_zero16);
                 const uint16_t *vp = vrow + sg * kxs + k;

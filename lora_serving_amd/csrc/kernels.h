@@ -22,6 +22,7 @@ struct SlotGeom {
     const uint16_t *A;      // [S][n_slices][R][n_in]
     const uint16_t *B;      // [S][n_out][R]
     const float *factor;    // [S]
+    const int32_t *rank;    // [S] true ranks (device), or nullptr: every slot R wide
     int32_t S, R, n_slices;
     int32_t slice_start[5];
 };

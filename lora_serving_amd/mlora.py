@@ -43,7 +43,8 @@ _i32 = ctypes.c_int32
 
 class mlora_slots(ctypes.Structure):
     _fields_ = [("A", _P), ("B", _P), ("factor", _P), ("S", _i32), ("R", _i32),
-                ("n_slices", _i32), ("slice_start", _i32 * (MLORA_MAX_SLICES + 1))]
+                ("n_slices", _i32), ("slice_start", _i32 * (MLORA_MAX_SLICES + 1)),
+                ("rank", _P)]
 
 
 _SLOTS_P = ctypes.POINTER(mlora_slots)
@@ -139,13 +140,15 @@ def _bf16(t, name):
 
 class Slots:
     """One layer's adapter slots: A [S][n_slices][R][n_in] bf16, B [S][n_out][R] bf16,
-    factor [S] fp32 (device tensors), plus the host slice table."""
+    factor [S] fp32 (device tensors), plus the host slice table and optionally the slots' true
+    ranks (int32 [S] device tensor; None = every slot R wide)."""
 
-    def __init__(self, A, B, factor, slice_start=None):
+    def __init__(self, A, B, factor, slice_start=None, rank=None):
         import torch
         self.A = _bf16(A, "A")
         self.B = _bf16(B, "B")
         self.factor = _need(factor, (torch.float32,), "factor")
+        self.rank = None if rank is None else _need(rank, (torch.int32,), "rank")
         S, n_slices, R, _ = A.shape
         self.S, self.n_slices, self.R = int(S), int(n_slices), int(R)
         self.n_out = int(B.shape[1])
@@ -154,7 +157,8 @@ class Slots:
             for i, v in enumerate(slice_start):
                 st[i] = int(v)
         self.struct = mlora_slots(_ptr(self.A), _ptr(self.B), _ptr(self.factor), self.S, self.R,
-                                  self.n_slices, (_i32 * (MLORA_MAX_SLICES + 1))(*st))
+                                  self.n_slices, (_i32 * (MLORA_MAX_SLICES + 1))(*st),
+                                  _ptr(self.rank))
 
     @property
     def ref(self):

@@ -43,6 +43,8 @@ class DevLayer:
         f = np.array([mlora.mlora_factor(L.alpha[a], int(L.rank[a]), bool(L.rslora[a]))
                       for a in range(L.S)], np.float32)
         self.factor = torch.from_numpy(f).to(device)
+        # the slots' true ranks (passed to the library only when a caller asks for them)
+        self.rank = torch.from_numpy(np.ascontiguousarray(L.rank, np.int32)).to(device)
         self.slots = mlora.Slots(self.A, self.B, self.factor,
                                  slice_start=[int(v) for v in L.slice_start])
         self.ws = mlora.workspace(L.T, L.K, L.n_in, L.n_out, self.slots, device)

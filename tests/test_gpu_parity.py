@@ -159,6 +159,40 @@ def test_slot_load_rebuilds_padded_slots():
     assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
 
 
+RANKED = [
+    # seed, T, contiguous, path
+    (50, 300, False, "decode"),
+    (51, 300, False, "tiled"),     # 9 adapters in every tile: the scattered route
+    (52, 600, True, "tiled"),      # runs of tokens: stacked (dense) tiles
+]
+
+
+@pytest.mark.parametrize("case", RANKED, ids=[f"r{c[0]}-{c[3]}" for c in RANKED])
+def test_rank_table_skips_padding_exactly(oracle_mod, case):
+    """With the slots' true ranks the kernels skip the zero padding; the products they skip are
+    exact zeros, so the layer's output is bit-identical to the rank-blind run (and within the
+    tolerance of the oracle)."""
+    import torch
+    from lora_serving_amd import mlora
+    seed, T, contiguous, path = case
+    ranks = [8, 16, 64, 24, 8, 40, 16, 5, 64]
+    L = synth.random_layer(seed, T=T, n_in=512, n_out=384, S=9, R=64, K=2,
+                           slice_sizes=[256, 64, 64], ranks=ranks, p_sentinel=0.2,
+                           contiguous=contiguous)
+    say(f"[ranked] seed={seed} T={T} contiguous={contiguous} path={path}")
+    flags = mlora.MLORA_PATH_DECODE if path == "decode" else mlora.MLORA_PATH_TILED
+    D = DevLayer(L)
+    y0 = D.linear(flags=flags).clone()
+    rank_dev = torch.tensor(ranks, dtype=torch.int32, device="cuda")
+    D.slots = mlora.Slots(D.A, D.B, D.factor, slice_start=[int(v) for v in L.slice_start],
+                          rank=rank_dev)
+    y1 = D.linear(flags=flags)
+    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
+    yy = from_dev_bf16(y1)
+    y_ref = oracle_mod.linear(L)
+    assert tol_ok(yy, y_ref).all(), f"worst {worst(yy, y_ref):.3e}"
+
+
 def test_tiled_sentinel_rows_and_k3_invariance():
     from lora_serving_amd import mlora
     L1 = synth.random_layer(46, T=300, n_in=256, n_out=512, S=6, R=16, K=1, p_sentinel=0.3)
