@@ -66,6 +66,8 @@ SMALL = [
     (5, 128, 1024, 1000, 9, 32, 2, None),
     (6, 129, 320, 264, 6, 16, 3, [200, 32, 32]),
     (7, 300, 2056, 136, 11, 8, 1, None),
+    (8, 20, 512, 4096, 5, 16, 3, [2048, 1024, 1024]),   # 60 pairs over 5 slots: grouped shrink
+    (9, 64, 256, 4096, 40, 32, 1, None),                # 64 pairs, wd > 16: grouped + per pair
 ]
 
 
