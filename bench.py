@@ -178,6 +178,10 @@ def main():
     ap.add_argument("--flags", type=int, default=0, help="extra mlora_linear flags")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain copy kernel over MIB MiB (counter calibration)")
+    ap.add_argument("--w-layout", default="auto", choices=["auto", "packed", "rowmajor"],
+                    help="base weight as given (row-major) or packed once before timing "
+                         "(mlora_pack_weight; same output bits); auto = packed for decode-sized "
+                         "batches, where it is faster, row-major for the tiled path")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured copy-bandwidth and bf16 GEMM ceilings")
     args = ap.parse_args()
@@ -194,6 +198,8 @@ def main():
     if not isinstance(layers, list):
         layers = [layers]
     decode_like = all(L.T <= 128 for L in layers)
+    if args.w_layout == "auto":
+        args.w_layout = "packed" if decode_like else "rowmajor"
     steps = args.steps or (2000 if decode_like else 20)
     warmup = args.warmup if args.warmup >= 0 else (100 if decode_like else 3)
     algs = [algorithmic(L) for L in layers]
@@ -214,12 +220,16 @@ def main():
             slots = mlora.Slots(A, B, D.factor, slice_start=[int(v) for v in D.L.slice_start],
                                 rank=D.rank)
             y = torch.empty((D.L.T, D.L.n_out), dtype=torch.bfloat16, device="cuda")
+            if args.w_layout == "packed":
+                W = mlora.mlora_pack_weight(W)
             one.append((x, W, slots, y, D))
         sets.append(one)
 
+    wflag = mlora.MLORA_W_PACKED if args.w_layout == "packed" else 0
+
     def step(i):
         for (x, W, slots, y, D) in sets[i % nsets]:
-            mlora.mlora_linear(x, W, slots, D.idx, D.scale, y, flags=args.flags, ws=D.ws)
+            mlora.mlora_linear(x, W, slots, D.idx, D.scale, y, flags=args.flags | wflag, ws=D.ws)
 
     if args.calibrate_copy:
         # a plain elementwise copy of known size, for scaling the HBM byte counters
@@ -296,7 +306,7 @@ def main():
                    "layers": [[L.n_in, L.n_out] for L in layers], "S": layers[0].S,
                    "R": layers[0].R, "K": layers[0].K,
                    "distinct_adapters": [a["distinct_adapters"] for a in algs],
-                   "rotating_sets": nsets},
+                   "rotating_sets": nsets, "w_layout": args.w_layout},
         "roofline": roof,
         "step_algorithmic": {"bytes": tot_bytes, "flops": tot_flops},
     }

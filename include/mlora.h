@@ -67,6 +67,7 @@ typedef enum {
 #define MLORA_NO_ADAPTERS 1u      /* host hint: no token uses an adapter; run the base only    */
 #define MLORA_PATH_DECODE 2u      /* force the decode kernels (token chunks of 64)             */
 #define MLORA_PATH_TILED 4u       /* force the tiled prefill kernels (256-token tiles)         */
+#define MLORA_W_PACKED 8u         /* W is in the packed layout of mlora_pack_weight            */
 
 /*
  * The adapter slot set of ONE layer: S slots, each R wide (R = max_lora_rank), an adapter of
@@ -141,6 +142,23 @@ mlora_status mlora_slot_load(void *A, void *B, float *factor, int32_t S, int32_t
                              hipStream_t stream);
 
 /*
+ * Packed base weight (a relayout for the matrix cores, done once when a weight is loaded; not
+ * from the pages): the layer's W bf16 [n_out][n_in] rearranged so that each 16-row x 32-column
+ * block is 1 KB contiguous in the order the v_mfma_f32_16x16x32_bf16 A operand takes it
+ * (lane l: row l % 16, columns 8 (l / 16) .. +8), blocks ordered by row group, then column
+ * block; zero padded to 16 rows and 32 columns:
+ *   Wp[rg][kb][l][e] = W[16 rg + l % 16][32 kb + 8 (l / 16) + e]
+ * mlora_packed_weight_bytes returns its size (0 on invalid sizes); mlora_pack_weight writes it
+ * (one kernel on `stream`; W and Wp device, 16-byte aligned, not overlapping).  mlora_linear
+ * with MLORA_W_PACKED then takes Wp in place of W and gives the same output bits: the
+ * kernels read whole cache lines of W per load instruction.  MLORA_ERR_ARG on NULL or
+ * misaligned pointers or sizes below 1, MLORA_ERR_SHAPE if n_in is not a multiple of 8.
+ */
+int64_t mlora_packed_weight_bytes(int64_t n_out, int64_t n_in);
+mlora_status mlora_pack_weight(const void *W, int64_t n_out, int64_t n_in, void *Wp,
+                               hipStream_t stream);
+
+/*
  * Synchronous check of an index map and of the adapter ranks (blocks on `stream`).
  *   idx   int32 [T][K] device
  *   rank  int32 [S] host, true adapter ranks (may be NULL to skip the rank check)
@@ -199,7 +217,8 @@ mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_
  * all-sentinel map gives the same values.  T = 0 is a no-op.  By default the library picks
  * the decode kernels for small batches and the tiled kernels when the batch fills the GPU
  * with 256 x 256 output tiles; MLORA_PATH_DECODE / MLORA_PATH_TILED force one (both set:
- * MLORA_ERR_ARG).  mlora_workspace_size() covers either path.
+ * MLORA_ERR_ARG).  mlora_workspace_size() covers either path.  With MLORA_W_PACKED, W points
+ * to the packed layout written by mlora_pack_weight (same output bits).
  */
 mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in, int64_t n_out,
                           const mlora_slots *slots, const int32_t *idx, int32_t K,

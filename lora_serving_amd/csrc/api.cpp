@@ -250,6 +250,25 @@ size_t mlora_workspace_size(int64_t T, int32_t K, int64_t n_in, int64_t n_out,
     return make_layout(T, K, n_in, n_out, g.S, g.R, g.n_slices).total + 256;
 }
 
+int64_t mlora_packed_weight_bytes(int64_t n_out, int64_t n_in)
+{
+    if (n_out < 1 || n_in < 1)
+        return 0;
+    return packed_weight_elems(n_out, n_in) * 2;
+}
+
+mlora_status mlora_pack_weight(const void *W, int64_t n_out, int64_t n_in, void *Wp,
+                               hipStream_t stream)
+{
+    if (W == nullptr || Wp == nullptr || n_out < 1 || n_in < 1 || !aligned16(W) ||
+        !aligned16(Wp))
+        return MLORA_ERR_ARG;
+    if (n_in % 8 != 0)
+        return MLORA_ERR_SHAPE;
+    return hip_status(launch_pack_weight((const uint16_t *)W, n_out, n_in, (uint16_t *)Wp, stream),
+                      "pack weight");
+}
+
 mlora_status mlora_slot_load(void *A, void *B, float *factor, int32_t S, int32_t R,
                              int32_t n_slices, int64_t n_in, int64_t n_out, int32_t slot,
                              const void *A_src, const void *B_src, int32_t r, float f,
@@ -419,13 +438,14 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
     uint16_t *yb = (uint16_t *)y;
     const bool force_decode = (flags & MLORA_PATH_DECODE) != 0;
     const bool force_tiled = (flags & MLORA_PATH_TILED) != 0;
+    const bool packed = (flags & MLORA_W_PACKED) != 0;
     if (force_tiled || (!force_decode && prefill_worth_it(T, n_out))) {
         // chunks of at most PREFILL_MAX_T tokens (the shrink's tile table lives in LDS)
         for (int64_t t0 = 0; t0 < T; t0 += PREFILL_MAX_T) {
             const int64_t Tc = std::min<int64_t>(PREFILL_MAX_T, T - t0);
             const PrefillCfg pc = prefill_config(Tc, K, n_in, n_out, S, R, n_slices);
             mlora_status st = hip_status(
-                launch_prefill(xb + t0 * n_in, (const uint16_t *)W, Tc, n_in, n_out,
+                launch_prefill(xb + t0 * n_in, (const uint16_t *)W, packed, Tc, n_in, n_out,
                                lora ? &g : nullptr, lora ? idx + t0 * K : nullptr, K,
                                (lora && scale) ? scale + t0 * K : nullptr, yb + t0 * n_out, pc,
                                wsb + L.off_pre, stream),
@@ -442,8 +462,8 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
         const int32_t *idx_c = lora ? idx + t0 * K : nullptr;
         const float *scale_c = (lora && scale) ? scale + t0 * K : nullptr;
         trace_mark(stream, true);
-        hipError_t e = launch_decode_gemm(xb + t0 * n_in, (const uint16_t *)W, Tc, n_in, n_out,
-                                          part, cfg, lora ? &g : nullptr, idx_c, K,
+        hipError_t e = launch_decode_gemm(xb + t0 * n_in, (const uint16_t *)W, packed, Tc, n_in,
+                                          n_out, part, cfg, lora ? &g : nullptr, idx_c, K,
                                           lora ? upart : nullptr, stream);
         trace_mark(stream, false);
         if (e != hipSuccess)

@@ -97,9 +97,10 @@ struct DecodeArgs {
     float *part;       // [sk][n_tiles][T][64]
     float *upart;      // [sk][K][T][wd] or nullptr (no LoRA)
     int n_pairs;
+    int n_rg, n_kb;    // packed W: row groups of 16, column blocks of 32
 };
 
-template <int TT>
+template <int TT, bool PW>
 __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
 {
     extern __shared__ __attribute__((aligned(16))) float red[];   // [8][4][TT][64] float4
@@ -167,10 +168,18 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            const int row = tile * DEC_ROWS + rt * 16 + r;
-            const uint16_t *wrow = W + (int64_t)min(row, n_out - 1) * n_in;
-            const int c = col(ks);
-            wf[rt][ks] = dec_ld16(wrow, c, wave_on && c < n_in && row < n_out);
+            if constexpr (PW) {
+                // packed W: the fragment (row group, column block) is 1 KB in lane order
+                const int rg = tile * 4 + rt, kb = (kw >> 5) + ks;
+                const bool ok = wave_on && rg < P.n_rg && kb < P.n_kb;
+                const uint16_t *wp = W + (((int64_t)min(rg, P.n_rg - 1) * P.n_kb + min(kb, P.n_kb - 1)) * 64 + lane) * 8;
+                wf[rt][ks] = *(const u32x4 *)(ok ? (const void *)wp : (const void *)dec_zero16);
+            } else {
+                const int row = tile * DEC_ROWS + rt * 16 + r;
+                const uint16_t *wrow = W + (int64_t)min(row, n_out - 1) * n_in;
+                const int c = col(ks);
+                wf[rt][ks] = dec_ld16(wrow, c, wave_on && c < n_in && row < n_out);
+            }
         }
     }
     // every load of the workgroup's slice is in flight before the first wait below (keeps the
@@ -321,25 +330,25 @@ size_t decode_partial_bytes(int64_t T, int64_t n_in, int64_t n_out)
     return (size_t)c.sk * c.n_tiles * (size_t)T * DEC_ROWS * sizeof(float);
 }
 
-template <int TT>
+template <int TT, bool PW>
 static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, hipStream_t stream)
 {
     const size_t lds = (size_t)DEC_WAVES * 4 * TT * 64 * sizeof(float4);
     static size_t lds_allowed = 64 * 1024;
     if (lds > lds_allowed) {
-        hipError_t e = hipFuncSetAttribute((const void *)decode_gemm_kernel<TT>,
+        hipError_t e = hipFuncSetAttribute((const void *)decode_gemm_kernel<TT, PW>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
             return e;
         lds_allowed = lds;
     }
     const dim3 grid((unsigned)(c.n_tiles * c.sk)), block(512);
-    hipLaunchKernelGGL((decode_gemm_kernel<TT>), grid, block, lds, stream, a);
+    hipLaunchKernelGGL((decode_gemm_kernel<TT, PW>), grid, block, lds, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, int64_t T, int64_t n_in,
-                              int64_t n_out, float *part, const DecodeCfg &c,
+hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed, int64_t T,
+                              int64_t n_in, int64_t n_out, float *part, const DecodeCfg &c,
                               const SlotGeom *g, const int32_t *idx, int32_t K, float *upart,
                               hipStream_t stream)
 {
@@ -360,10 +369,15 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, int64_t T, i
         a.upart = upart;
         a.n_pairs = (int)(T * K);
     }
-    switch (c.tt) {
-    case 1: return launch_tf<1>(a, c, stream);
-    case 2: return launch_tf<2>(a, c, stream);
-    case 4: return launch_tf<4>(a, c, stream);
+    a.n_rg = (int)((n_out + 15) / 16);
+    a.n_kb = (int)((n_in + 31) / 32);
+    switch (c.tt * 2 + (packed ? 1 : 0)) {
+    case 2: return launch_tf<1, false>(a, c, stream);
+    case 3: return launch_tf<1, true>(a, c, stream);
+    case 4: return launch_tf<2, false>(a, c, stream);
+    case 5: return launch_tf<2, true>(a, c, stream);
+    case 8: return launch_tf<4, false>(a, c, stream);
+    case 9: return launch_tf<4, true>(a, c, stream);
     default: return hipErrorInvalidValue;
     }
 }

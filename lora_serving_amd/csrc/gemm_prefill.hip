@@ -563,6 +563,7 @@ struct GemmArgs {
     int list_stride;
     const int32_t *tile_ord;   // scattered tile ordinal (sgmv_shrink_kernel), or -1
     float *part_sc;            // fp32 [sc_cap][256][n_out] sums of scattered tiles
+    int n_rg, n_kb;            // packed W: row groups of 16, column blocks of 32
 };
 
 // GEMM: 256 W rows x 256 tokens per workgroup, 8 waves (4 along W rows x 2 along tokens,
@@ -587,6 +588,9 @@ __device__ __forceinline__ void pf_dma(const void *g, uint16_t *lds)
 
 // Issues this wave's copies of stage q (k-step q: base columns q*64 while q < nk_main, then
 // the LoRA extra steps) into buffer `st`: 4 blocks of 8 W rows and 4 of 8 tokens per wave.
+// With a packed W (PW) the W side of a stage is 32 fragments of 16 rows x 32 columns in lane
+// order instead (4 per wave), for the base steps and the LoRA steps alike.
+template <bool PW>
 __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q, int nk_main,
                                          int nk_extra, int m0, int n0, const uint16_t *vtile,
                                          int D, int kxs, int sg_lo, int kb_per_slice,
@@ -601,9 +605,17 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int row = (wave * 4 + b) * 8 + rr;
-            const uint16_t *gw = P.W + (int64_t)min(n0 + row, P.n_out - 1) * P.n_in + k;
+            if constexpr (PW) {
+                const int f = wave * 4 + b, rg = (n0 >> 4) + (f >> 1), kb = 2 * q + (f & 1);
+                const uint16_t *gw = P.W + (((int64_t)min(rg, P.n_rg - 1) * P.n_kb +
+                                             min(kb, P.n_kb - 1)) * 64 + lane) * 8;
+                pf_dma(rg < P.n_rg && kb < P.n_kb ? (const void *)gw : (const void *)pf_zero16,
+                       sw + f * 512);
+            } else {
+                const uint16_t *gw = P.W + (int64_t)min(n0 + row, P.n_out - 1) * P.n_in + k;
+                pf_dma(ok ? (const void *)gw : (const void *)pf_zero16, sw + (wave * 4 + b) * 8 * PF_KS);
+            }
             const uint16_t *gx = P.x + (int64_t)min(m0 + row, P.T - 1) * P.n_in + k;
-            pf_dma(ok ? (const void *)gw : (const void *)pf_zero16, sw + (wave * 4 + b) * 8 * PF_KS);
             pf_dma(ok ? (const void *)gx : (const void *)pf_zero16, sx + (wave * 4 + b) * 8 * PF_KS);
         }
     } else {
@@ -630,11 +642,25 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int row = (wave * 4 + b) * 8 + rr;
-            const int n = n0 + row;
-            const bool ok = dd < D && n >= s_lo && n < s_hi;   // s_hi <= n_out
-            const uint16_t *gb = P.g.B + ((int64_t)a * P.n_out + min(n, P.n_out - 1)) * R + rho;
+            if constexpr (PW) {
+                // fragment layout: this lane holds row f/2*16 + lane%16, chunk (f%2)*4 + lane/16
+                const int f = wave * 4 + b;
+                const int bn = n0 + (f >> 1) * 16 + (lane & 15);
+                const int bkk = kk0 + ((f & 1) * 4 + (lane >> 4)) * 8;
+                const int bdd = bkk / (2 * R);
+                const int brho = (bkk - bdd * 2 * R) & (R - 1);
+                const int be = bdd - dd0;
+                const int ba = be == 0 ? a0 : be == 1 ? a1 : be == 2 ? a2 : a3;
+                const bool bok = bdd < D && bn >= s_lo && bn < s_hi;
+                const uint16_t *gb = P.g.B + ((int64_t)ba * P.n_out + min(bn, P.n_out - 1)) * R + brho;
+                pf_dma(bok ? (const void *)gb : (const void *)pf_zero16, sw + f * 512);
+            } else {
+                const int n = n0 + row;
+                const bool ok = dd < D && n >= s_lo && n < s_hi;   // s_hi <= n_out
+                const uint16_t *gb = P.g.B + ((int64_t)a * P.n_out + min(n, P.n_out - 1)) * R + rho;
+                pf_dma(ok ? (const void *)gb : (const void *)pf_zero16, sw + (wave * 4 + b) * 8 * PF_KS);
+            }
             const uint16_t *gv = vtile + (int64_t)row * (P.g.n_slices * kxs) + sg * kxs + kk;
-            pf_dma(ok ? (const void *)gb : (const void *)pf_zero16, sw + (wave * 4 + b) * 8 * PF_KS);
             pf_dma((const void *)gv, sx + (wave * 4 + b) * 8 * PF_KS);
         }
     }
@@ -642,6 +668,7 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
 
 // MFMAs of one stage (two k-steps of 32): wave (wn, wm) owns W rows wn*64 .. +64 and tokens
 // wm*128 .. +128.
+template <bool PW>
 __device__ __forceinline__ void pf_compute(const uint16_t *st, int wn, int wm, int r, int gq,
                                            f32x4 (&acc)[4][8])
 {
@@ -651,8 +678,12 @@ __device__ __forceinline__ void pf_compute(const uint16_t *st, int wn, int wm, i
         const int pos = (ks * 4 + gq) ^ (r & 7);
         bf16x8 af[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            af[i] = *(const bf16x8 *)(sw + ((wn * 64 + i * 16 + r) * 8 + pos) * 8);
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (PW)
+                af[i] = *(const bf16x8 *)(sw + (((wn * 4 + i) * 2 + ks) * 64 + gq * 16 + r) * 8);
+            else
+                af[i] = *(const bf16x8 *)(sw + ((wn * 64 + i * 16 + r) * 8 + pos) * 8);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const bf16x8 bv = *(const bf16x8 *)(sx + ((wm * 128 + j * 16 + r) * 8 + pos) * 8);
@@ -663,6 +694,7 @@ __device__ __forceinline__ void pf_compute(const uint16_t *st, int wn, int wm, i
     }
 }
 
+template <bool PW>
 __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t pf_lds[];
@@ -721,16 +753,16 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
     // number of copies and the wait counts below stay exact
 #pragma unroll
     for (int q = 0; q < PF_STAGES; ++q)
-        pf_issue(P, pf_lds + q * (PF_STAGE_BYTES / 2), min(q, nk - 1), nk_main, nk_extra, m0, n0,
+        pf_issue<PW>(P, pf_lds + q * (PF_STAGE_BYTES / 2), min(q, nk - 1), nk_main, nk_extra, m0, n0,
                  vtile, D, kxs, sg_lo, kb_per_slice, slist, wave, lane);
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");    // stage 0 (8 copies per stage)
     lds_barrier();
     for (int q = 0; q < nk; ++q) {
         uint16_t *st = pf_lds + (q & 1) * (PF_STAGE_BYTES / 2);
-        pf_compute(st, wn, wm, r, gq, acc);
+        pf_compute<PW>(st, wn, wm, r, gq, acc);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stage q+1
         lds_barrier();                                      // also: stage q fully read
-        pf_issue(P, st, min(q + PF_STAGES, nk - 1), nk_main, nk_extra, m0, n0, vtile, D, kxs,
+        pf_issue<PW>(P, st, min(q + PF_STAGES, nk - 1), nk_main, nk_extra, m0, n0, vtile, D, kxs,
                  sg_lo, kb_per_slice, slist, wave, lane);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no copy outlives the workgroup
@@ -1028,10 +1060,10 @@ bool prefill_worth_it(int64_t T, int64_t n_out)
     return T >= 512 && tiles >= 128;
 }
 
-hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64_t n_in,
-                          int64_t n_out, const SlotGeom *g, const int32_t *idx, int32_t K,
-                          const float *scale, uint16_t *y, const PrefillCfg &c, void *ws,
-                          hipStream_t stream)
+hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int64_t T,
+                          int64_t n_in, int64_t n_out, const SlotGeom *g, const int32_t *idx,
+                          int32_t K, const float *scale, uint16_t *y, const PrefillCfg &c,
+                          void *ws, hipStream_t stream)
 {
     uint8_t *p = (uint8_t *)ws;
     const PrefillLayout WL = prefill_layout(c);
@@ -1112,18 +1144,25 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64
     a.list_stride = c.list_stride;
     a.tile_ord = tile_ord;
     a.part_sc = part_sc;
+    a.n_rg = (int)((n_out + 15) / 16);
+    a.n_kb = (int)((n_in + 31) / 32);
     const size_t lds = (size_t)PF_STAGES * PF_STAGE_BYTES;                // 128 KB of stages
-    static size_t lds_allowed = 0;
-    if (lds > lds_allowed) {
-        hipError_t e = hipFuncSetAttribute((const void *)prefill_gemm_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const void *kfn = packed ? (const void *)prefill_gemm_kernel<true>
+                             : (const void *)prefill_gemm_kernel<false>;
+    static size_t lds_allowed[2] = {0, 0};
+    if (lds > lds_allowed[packed ? 1 : 0]) {
+        hipError_t e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
             return e;
-        lds_allowed = lds;
+        lds_allowed[packed ? 1 : 0] = lds;
     }
     trace_mark(stream, true);
-    hipLaunchKernelGGL(prefill_gemm_kernel, dim3((unsigned)(c.n_mtiles * c.n_ntiles)), dim3(512),
-                       lds, stream, a);
+    if (packed)
+        hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3((unsigned)(c.n_mtiles * c.n_ntiles)),
+                           dim3(512), lds, stream, a);
+    else
+        hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3((unsigned)(c.n_mtiles * c.n_ntiles)),
+                           dim3(512), lds, stream, a);
     hipError_t e = hipGetLastError();
     trace_mark(stream, false);
     if (e == hipSuccess && g != nullptr) {

@@ -54,8 +54,9 @@ size_t decode_partial_bytes(int64_t T, int64_t n_in, int64_t n_out);
 // part[s][tile][t][0:64] = x[t, split s] . W[tile*64 + (0:64), split s]; with upart != nullptr
 // the same launch writes the unscaled shrink partials upart[s][j][t][0:n_slices*R] of every
 // pair (-1 pairs skipped).
-hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, int64_t T, int64_t n_in,
-                              int64_t n_out, float *part, const DecodeCfg &cfg,
+// W: row-major [n_out][n_in], or the packed layout of pack.hip when `packed`.
+hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed, int64_t T,
+                              int64_t n_in, int64_t n_out, float *part, const DecodeCfg &cfg,
                               const SlotGeom *g, const int32_t *idx, int32_t K, float *upart,
                               hipStream_t stream);
 // ---- decode_finish.hip: y = bf16(sum of the split partials + LoRA delta), T <= 64 ----------
@@ -64,6 +65,12 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, int64_t T, i
 hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, const float *upart,
                                 const float *scale, int64_t T, int64_t n_out, const SlotGeom *g,
                                 const int32_t *idx, int32_t K, uint16_t *y, hipStream_t stream);
+
+// ---- pack.hip: W in the matrix cores' fragment order ------------------------------------------
+// Wp[rg][kb][lane][8] = W[16 rg + lane % 16][32 kb + 8 (lane / 16) + e], zero padded.
+int64_t packed_weight_elems(int64_t n_out, int64_t n_in);
+hipError_t launch_pack_weight(const uint16_t *W, int64_t n_out, int64_t n_in, uint16_t *Wp,
+                              hipStream_t stream);
 
 // ---- slot_load.hip: zero padding of a loaded slot and its scale factor ----------------------
 // A_slot: bf16 [n_slices][R][n_in] of the slot; B_slot: bf16 [n_out][R]; rows/columns >= r.
@@ -88,9 +95,9 @@ bool prefill_worth_it(int64_t T, int64_t n_out);
 // Profiling hook (mlora_trace_start): records the begin/end event of the main product kernel.
 void trace_mark(hipStream_t stream, bool begin);
 
-hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, int64_t T, int64_t n_in,
-                          int64_t n_out, const SlotGeom *g, const int32_t *idx, int32_t K,
-                          const float *scale, uint16_t *y, const PrefillCfg &c, void *ws,
-                          hipStream_t stream);
+hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int64_t T,
+                          int64_t n_in, int64_t n_out, const SlotGeom *g, const int32_t *idx,
+                          int32_t K, const float *scale, uint16_t *y, const PrefillCfg &c,
+                          void *ws, hipStream_t stream);
 
 }  // namespace mlora

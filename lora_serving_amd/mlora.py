@@ -30,9 +30,11 @@ MLORA_MAX_K = 8
 MLORA_NO_ADAPTERS = 1
 MLORA_PATH_DECODE = 2
 MLORA_PATH_TILED = 4
+MLORA_W_PACKED = 8
 
 EXPORTS = ("mlora_status_string", "mlora_last_error", "mlora_factor", "mlora_slot_bytes",
-           "mlora_workspace_size", "mlora_slot_load",
+           "mlora_workspace_size", "mlora_slot_load", "mlora_packed_weight_bytes",
+           "mlora_pack_weight",
            "mlora_validate", "mlora_plan", "mlora_shrink", "mlora_expand", "mlora_linear",
            "mlora_trace_start", "mlora_trace_stop")
 
@@ -59,6 +61,10 @@ _lib.mlora_slot_bytes.restype = _i64
 _lib.mlora_slot_bytes.argtypes = [_i32, _i32, _i64, _i64, _i32]
 _lib.mlora_workspace_size.restype = ctypes.c_size_t
 _lib.mlora_workspace_size.argtypes = [_i64, _i32, _i64, _i64, _SLOTS_P]
+_lib.mlora_packed_weight_bytes.restype = _i64
+_lib.mlora_packed_weight_bytes.argtypes = [_i64, _i64]
+_lib.mlora_pack_weight.restype = ctypes.c_int
+_lib.mlora_pack_weight.argtypes = [_P, _i64, _i64, _P, _P]
 _lib.mlora_slot_load.restype = ctypes.c_int
 _lib.mlora_slot_load.argtypes = [_P, _P, _P, _i32, _i32, _i32, _i64, _i64, _i32, _P, _P, _i32,
                                  ctypes.c_float, _P]
@@ -178,6 +184,25 @@ def workspace(T: int, K: int, n_in: int, n_out: int, slots: Slots, device="cuda"
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def mlora_packed_weight_bytes(n_out: int, n_in: int) -> int:
+    return int(_lib.mlora_packed_weight_bytes(int(n_out), int(n_in)))
+
+
+def mlora_pack_weight(W, stream=None):
+    """The packed copy of a bf16 [n_out][n_in] device weight (a new device tensor), for
+    mlora_linear(..., flags=MLORA_W_PACKED)."""
+    import torch
+    _bf16(W, "W")
+    n_out, n_in = int(W.shape[0]), int(W.shape[1])
+    nbytes = mlora_packed_weight_bytes(n_out, n_in)
+    if nbytes <= 0:
+        raise MloraError(MLORA_ERR_ARG, "mlora_packed_weight_bytes")
+    Wp = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=W.device)
+    _check(_lib.mlora_pack_weight(_ptr(W), n_out, n_in, _ptr(Wp), _stream(stream)),
+           "mlora_pack_weight")
+    return Wp
+
+
 def mlora_slot_load(slots: Slots, n_in: int, slot: int, A_src, B_src, r: int, f: float,
                     stream=None):
     """Loads one adapter (A_src bf16 [n_slices][r][n_in], B_src bf16 [n_out][r]; host tensors
@@ -253,7 +278,7 @@ def mlora_linear(x, W, slots: Slots | None, idx, scale, y, flags: int = 0, ws=No
     _bf16(W, "W")
     _bf16(y, "y")
     T, n_in = x.shape
-    n_out = W.shape[0]
+    n_out = y.shape[1]          # W may be the packed (1-D) layout under MLORA_W_PACKED
     K = 1
     if idx is not None:
         _need(idx, (torch.int32,), "idx")

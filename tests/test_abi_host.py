@@ -158,6 +158,19 @@ def test_slot_load_argument_checks(m):
     assert call(ns=5) == m.MLORA_ERR_UNSUPPORTED
 
 
+def test_packed_weight_size_and_argument_checks(m):
+    L = m._lib
+    # padded to 16 rows and 32 columns, 2 bytes each
+    assert m.mlora_packed_weight_bytes(4096, 4096) == 4096 * 4096 * 2
+    assert m.mlora_packed_weight_bytes(100000, 4096) == 100000 * 4096 * 2
+    assert m.mlora_packed_weight_bytes(520, 392) == 528 * 416 * 2
+    assert m.mlora_packed_weight_bytes(0, 64) == 0
+    assert L.mlora_pack_weight(None, 16, 64, 0x2000, None) == m.MLORA_ERR_ARG
+    assert L.mlora_pack_weight(0x1000, 16, 64, None, None) == m.MLORA_ERR_ARG
+    assert L.mlora_pack_weight(0x1008, 16, 64, 0x2000, None) == m.MLORA_ERR_ARG   # misaligned
+    assert L.mlora_pack_weight(0x1000, 16, 60, 0x2000, None) == m.MLORA_ERR_SHAPE
+
+
 def test_trace_hook_argument_checks(m):
     assert m._lib.mlora_trace_start(0) == m.MLORA_ERR_ARG
     assert m._lib.mlora_trace_start((1 << 20) + 1) == m.MLORA_ERR_ARG

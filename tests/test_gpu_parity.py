@@ -195,6 +195,51 @@ def test_rank_table_skips_padding_exactly(oracle_mod, case):
     assert tol_ok(yy, y_ref).all(), f"worst {worst(yy, y_ref):.3e}"
 
 
+def pack_reference(Wbits, n_out, n_in):
+    """The packed layout written out directly: Wp[rg][kb][l][e] = W[16 rg + l % 16]
+    [32 kb + 8 (l // 16) + e], zero padded."""
+    n_rg, n_kb = -(-n_out // 16), -(-n_in // 32)
+    Wpad = np.zeros((n_rg * 16, n_kb * 32), np.uint16)
+    Wpad[:n_out, :n_in] = Wbits
+    out = np.zeros((n_rg, n_kb, 64, 8), np.uint16)
+    for l in range(64):
+        out[:, :, l, :] = Wpad.reshape(n_rg, 16, n_kb, 32)[:, l % 16, :, 8 * (l // 16):
+                                                             8 * (l // 16) + 8]
+    return out.reshape(-1)
+
+
+PACKED = [
+    # seed, T, n_in, n_out, K, path
+    (60, 64, 4096, 4096, 1, "decode"),
+    (61, 37, 392, 520, 3, "decode"),
+    (62, 300, 392, 520, 3, "tiled"),
+    (63, 520, 1032, 1000, 1, "tiled"),
+]
+
+
+@pytest.mark.parametrize("case", PACKED, ids=[f"w{c[0]}-{c[5]}" for c in PACKED])
+def test_packed_weight_same_bits(oracle_mod, case):
+    """mlora_pack_weight writes the documented layout, and mlora_linear on the packed weight
+    gives the same output bits as on the row-major one (decode and tiled kernels)."""
+    import torch
+    from lora_serving_amd import mlora
+    seed, T, n_in, n_out, K, path = case
+    L = synth.random_layer(seed, T=T, n_in=n_in, n_out=n_out, S=6, R=16, K=K, p_sentinel=0.2,
+                           contiguous=(path == "tiled"))
+    say(f"[packed] seed={seed} T={T} n_in={n_in} n_out={n_out} path={path}")
+    D = DevLayer(L)
+    Wp = mlora.mlora_pack_weight(D.W)
+    torch.cuda.synchronize()
+    got = Wp.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, pack_reference(L.W, n_out, n_in))
+    flags = mlora.MLORA_PATH_DECODE if path == "decode" else mlora.MLORA_PATH_TILED
+    y0 = D.linear(flags=flags).clone()
+    y1 = torch.empty_like(y0)
+    mlora.mlora_linear(D.x, Wp, D.slots, D.idx, D.scale, y1, flags=flags | mlora.MLORA_W_PACKED,
+                       ws=D.ws)
+    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
+
+
 def test_tiled_sentinel_rows_and_k3_invariance():
     from lora_serving_amd import mlora
     L1 = synth.random_layer(46, T=300, n_in=256, n_out=512, S=6, R=16, K=1, p_sentinel=0.3)
