@@ -240,6 +240,39 @@ def test_packed_weight_same_bits(oracle_mod, case):
     assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
 
 
+@pytest.mark.parametrize("path", ["decode", "tiled"])
+def test_limits_rank_slots_slices(oracle_mod, path):
+    """The widest slots (R = 512), the most slots per token (K = 8) and the most slices (4)."""
+    from lora_serving_amd import mlora
+    L = synth.random_layer(70, T=70 if path == "decode" else 300, n_in=512, n_out=640, S=5,
+                           R=512, K=8, slice_sizes=[160, 160, 160, 160], p_sentinel=0.3,
+                           contiguous=(path == "tiled"))
+    say(f"[limits] path={path} T={L.T} R={L.R} K={L.K} slices={L.n_slices}")
+    flags = mlora.MLORA_PATH_DECODE if path == "decode" else mlora.MLORA_PATH_TILED
+    D = DevLayer(L)
+    y = from_dev_bf16(D.linear(flags=flags))
+    y_ref = oracle_mod.linear(L)
+    assert tol_ok(y, y_ref).all(), f"worst {worst(y, y_ref):.3e}"
+
+
+def test_tiled_path_chunks_past_a_million_tokens(oracle_mod):
+    """More tokens than one tiled launch takes (4096 tiles of 256): the batch is cut in chunks;
+    tokens on both sides of the cut and the ragged end are checked against the oracle."""
+    from lora_serving_amd import mlora
+    T = 4096 * 256 + 300
+    L = synth.random_layer(71, T=T, n_in=64, n_out=64, S=4, R=8, K=1, p_sentinel=0.25,
+                           contiguous=True)
+    say(f"[million] T={T}")
+    D = DevLayer(L)
+    y = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_TILED))
+    cut = 4096 * 256
+    toks = np.array([0, 1, 255, 256, cut - 257, cut - 1, cut, cut + 1, cut + 255, cut + 256,
+                     T - 2, T - 1] + list(range(1000, T, 65537)), np.int64)
+    toks = np.unique(toks)
+    y_ref = oracle_mod.linear(L, tokens=toks)
+    assert tol_ok(y[toks], y_ref).all(), f"worst {worst(y[toks], y_ref):.3e}"
+
+
 def test_tiled_sentinel_rows_and_k3_invariance():
     from lora_serving_amd import mlora
     L1 = synth.random_layer(46, T=300, n_in=256, n_out=512, S=6, R=16, K=1, p_sentinel=0.3)
