@@ -39,6 +39,8 @@ DESCRIPTIONS = {
                  "4096->(4096,1024,1024), 64 adapters ranks {8,16,64} padded to 64, alpha 2r",
     "compose": "k3_compose: T=8192 = 64 requests x 128 tokens, K=3 slots, 32 adapters rank 16 "
                "alpha 32 (half rsLoRA), s~U(0.2,1); layers 4096->4096 and 11008->4096",
+    "decode256": "decode256: T=256 one-token requests, 4096->4096 bf16, 100 adapters rank 16 "
+                 "alpha 32, 26 tokens base-only, K=1",
     "lm_head": "lm_head: T=64 one-token requests, 4096->100000 (vocabulary) bf16, 100 adapters "
                "rank 16 alpha 32, 6 tokens base-only, K=1",
 }
@@ -197,7 +199,7 @@ def main():
     layers = synth.WORKLOADS[args.workload]()
     if not isinstance(layers, list):
         layers = [layers]
-    decode_like = all(L.T <= 128 for L in layers)
+    decode_like = all(L.T <= 512 for L in layers)
     if args.w_layout == "auto":
         args.w_layout = "packed" if decode_like else "rowmajor"
     steps = args.steps or (2000 if decode_like else 20)
@@ -255,7 +257,7 @@ def main():
     # Main product kernel: HIP events that the library records on the launch stream around
     # each of its launches, over a second timed region of the same length (the event pairs
     # add a few microseconds per launch, so the step time above is taken without them).
-    launches_per_step = sum((L.T + 63) // 64 if decode_like else 1 for L in layers)
+    launches_per_step = sum((L.T + 511) // 512 if decode_like else 1 for L in layers)
     cap = steps * launches_per_step
     torch.cuda.synchronize()
     mlora.mlora_trace_start(cap)

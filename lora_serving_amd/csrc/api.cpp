@@ -18,7 +18,7 @@ using namespace mlora;
 
 namespace {
 
-constexpr int64_t DECODE_MAX_T = 64;          // token chunk of the decode kernels
+constexpr int64_t DECODE_MAX_T = 512;         // tokens per decode launch (8 chunks of 64)
 constexpr int64_t PREFILL_MAX_T = 4096 * 256; // token chunk of the tiled kernels
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -76,7 +76,7 @@ mlora_status check_slots(const mlora_slots *s, int64_t n_out, bool need_data, Sl
 // one call to the next.
 struct Layout {
     size_t sort_cnt = 0;   // counting-sort scratch (plan)
-    size_t v = 0;          // fp32 [sk][K][Tc][n_slices*R] shrink partials (decode path)
+    size_t v = 0;          // fp32 per 64-token chunk [sk][K][64][n_slices*R] shrink partials
     size_t part = 0;       // fp32 partial sums of the decode GEMM
     size_t pre = 0;        // prefill path: tile lists and V blocks
     size_t total = 0;
@@ -98,7 +98,8 @@ Layout make_layout(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S,
     L.part = 0;
     if (Tc > 0) {
         const int64_t sk = decode_config(Tc, n_in, n_out).sk;
-        L.v = align_up((size_t)sk * K * Tc * wd * sizeof(float));
+        const int64_t chunks = (Tc + 63) / 64, per = chunks > 1 ? 64 : Tc;
+        L.v = align_up((size_t)chunks * sk * K * per * wd * sizeof(float));
         L.part = align_up(decode_partial_bytes(Tc, n_in, n_out));
     }
     L.off_sort = 0;
@@ -455,7 +456,8 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
         }
         return MLORA_OK;
     }
-    // Token chunks of at most DECODE_MAX_T: base GEMM + shrink pieces, then the finish kernel.
+    // Launches of at most DECODE_MAX_T tokens (chunks of 64 inside): base GEMM + shrink pieces,
+    // then the finish kernel.
     for (int64_t t0 = 0; t0 < T; t0 += DECODE_MAX_T) {
         const int64_t Tc = std::min<int64_t>(DECODE_MAX_T, T - t0);
         const DecodeCfg cfg = decode_config(Tc, n_in, n_out);

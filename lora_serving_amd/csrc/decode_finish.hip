@@ -21,6 +21,7 @@ constexpr int DF_ROWS = 64;       // rows of a tile (the GEMM's tile)
 constexpr int DF_TOK = 16;        // tokens per workgroup
 constexpr int DF_THREADS = 256;   // 16 tokens x 16 groups of 4 rows
 constexpr int DF_BPRE_R = 16;     // ranks up to which slot 0's B rows are prefetched
+constexpr int DF_CHUNK = 64;      // tokens of one chunk of the GEMM (one launch may hold several)
 
 // Masked loads read this static block instead (the choice is made on the address, so no
 // select waits for a load right after it is issued).
@@ -64,14 +65,29 @@ __device__ __forceinline__ void df_vload(const float *upart, int sk, int64_t pst
 
 __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
     const float *__restrict__ part, int sk, int n_tiles, const float *__restrict__ upart,
-    const float *__restrict__ scale, int T, int n_out, SlotGeom g, const int32_t *__restrict__ idx,
-    int K, uint16_t *__restrict__ y)
+    const float *__restrict__ scale, int T_all, int n_out, SlotGeom g,
+    const int32_t *__restrict__ idx, int K, uint16_t *__restrict__ y)
 {
     extern __shared__ __attribute__((aligned(16))) float vl[];   // [DF_TOK][R] of one (slot, slice)
     __shared__ int sidx[DF_TOK * MLORA_MAX_K_DEV];
-    const int n_tg = (T + DF_TOK - 1) / DF_TOK;
-    const int tile = blockIdx.x / n_tg;
-    const int t0 = (blockIdx.x - tile * n_tg) * DF_TOK;
+    // chunks of DF_CHUNK tokens (the GEMM's chunks): this workgroup's chunk and its inputs
+    const int n_tg = (min(T_all, DF_CHUNK) + DF_TOK - 1) / DF_TOK;
+    const int chunk = blockIdx.x / (n_tiles * n_tg);
+    const int bl = blockIdx.x - chunk * (n_tiles * n_tg);
+    const int T = min(DF_CHUNK, T_all - chunk * DF_CHUNK);
+    {
+        const int wd0 = g.n_slices * g.R;
+        part += (int64_t)chunk * sk * n_tiles * DF_CHUNK * DF_ROWS;
+        if (upart != nullptr)
+            upart += (int64_t)chunk * sk * K * DF_CHUNK * wd0;
+        if (idx != nullptr)
+            idx += (int64_t)chunk * DF_CHUNK * K;
+        if (scale != nullptr)
+            scale += (int64_t)chunk * DF_CHUNK * K;
+        y += (int64_t)chunk * DF_CHUNK * n_out;
+    }
+    const int tile = bl / n_tg;
+    const int t0 = (bl - tile * n_tg) * DF_TOK;
     const int nt = min(DF_TOK, T - t0);
     const int tl = threadIdx.x >> 4, g4 = threadIdx.x & 15;
     const int t = t0 + tl;
@@ -230,7 +246,9 @@ hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, 
         upart = nullptr;
         K = 1;
     }
-    const unsigned grid = (unsigned)(n_tiles * ((T + DF_TOK - 1) / DF_TOK));
+    const int64_t n_chunks = (T + DF_CHUNK - 1) / DF_CHUNK;
+    const unsigned grid =
+        (unsigned)(n_chunks * n_tiles * ((std::min<int64_t>(T, DF_CHUNK) + DF_TOK - 1) / DF_TOK));
     hipLaunchKernelGGL(decode_finish_kernel, dim3(grid), dim3(DF_THREADS), lds, stream, part, sk,
                        n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y);
     return hipGetLastError();

@@ -32,6 +32,7 @@
 namespace mlora {
 
 constexpr int DEC_ROWS = 64;    // rows of W per workgroup
+constexpr int DEC_CHUNK = 64;   // tokens of one chunk (several chunks may share a launch)
 constexpr int DEC_WK = 128;     // columns of n_in per wave
 constexpr int DEC_WAVES = 8;
 
@@ -94,9 +95,9 @@ struct DecodeArgs {
     const int32_t *idx;
     int K;
     const float *scale;
-    float *part;       // [sk][n_tiles][T][64]
-    float *upart;      // [sk][K][T][wd] or nullptr (no LoRA)
-    int n_pairs;
+    float *part;       // per chunk of 64 tokens: [sk][n_tiles][Tc][64]
+    float *upart;      // per chunk: [sk][K][Tc][wd], or nullptr (no LoRA)
+    int n_chunks;      // chunks of DEC_CHUNK tokens in this launch (T is their total)
     int n_rg, n_kb;    // packed W: row groups of 16, column blocks of 32
 };
 
@@ -105,25 +106,44 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
 {
     extern __shared__ __attribute__((aligned(16))) float red[];   // [8][4][TT][64] float4
     __shared__ float sred[DEC_WAVES][16];
-    const uint16_t *__restrict__ x = P.x;
     const uint16_t *__restrict__ W = P.W;
-    const int T = P.T, n_in = P.n_in, n_out = P.n_out, n_tiles = P.n_tiles, K = P.K;
+    const int n_in = P.n_in, n_out = P.n_out, n_tiles = P.n_tiles, K = P.K;
     const SlotGeom &g = P.g;
-    const int tile = blockIdx.x % n_tiles;
-    const int s = blockIdx.x / n_tiles;
+    const int wd = g.n_slices * g.R;
+    // Workgroup -> (token chunk, row tile, split).  With several chunks in one launch every XCD
+    // (workgroups are dealt to the 8 XCDs round robin) runs a contiguous range of (tile, split)
+    // pairs with the chunks innermost, so the chunks of one W slice run back to back on one XCD
+    // and read it from that XCD's L2 after the first.
+    int chunk = 0, tile, s;
+    if (P.n_chunks == 1) {
+        tile = blockIdx.x % n_tiles;
+        s = blockIdx.x / n_tiles;
+    } else {
+        const int nwg = gridDim.x, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        const int lt = xcd * (nwg >> 3) + min(xcd, nwg & 7) + slot;
+        chunk = lt % P.n_chunks;
+        const int pg = lt / P.n_chunks;
+        tile = pg % n_tiles;
+        s = pg / n_tiles;
+    }
+    const int T = min(DEC_CHUNK, P.T - chunk * DEC_CHUNK);
+    const uint16_t *__restrict__ x = P.x + (int64_t)chunk * DEC_CHUNK * n_in;
+    const int32_t *idx = P.idx != nullptr ? P.idx + (int64_t)chunk * DEC_CHUNK * K : nullptr;
+    float *part = P.part + (int64_t)chunk * P.sk * n_tiles * DEC_CHUNK * DEC_ROWS;
+    float *upart = P.upart != nullptr ? P.upart + (int64_t)chunk * P.sk * K * DEC_CHUNK * wd
+                                      : nullptr;
+    const int n_pairs = T * K;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;     // row (A operand) / token (B operand) within a 16-tile
     const int gq = lane >> 4;    // which 16-byte chunk group of the k-step this lane supplies
     const int kw = s * P.ks_cols + wave * DEC_WK;      // first column of this wave
     const bool wave_on = kw < n_in && wave * DEC_WK < P.ks_cols;
-    float *upart = P.upart;
 
     // slot id of this workgroup's first shrink pair, read first (the A addresses wait for it)
-    const int wd = g.n_slices * g.R;
     int a0 = -1;
-    if (upart != nullptr && tile < P.n_pairs)
-        a0 = P.idx[tile];
+    if (upart != nullptr && tile < n_pairs)
+        a0 = idx[tile];
 
     // column of the chunk this lane supplies at k-step ks: the 4 lanes of a row read 64
     // contiguous bytes per instruction (16 cache lines per wave instruction)
@@ -277,15 +297,15 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
         const int tok = tt * 16 + (ln & 15);
         const int rloc = rt * 16 + (ln >> 4) * 4;   // row within the tile
         if (tok < T)
-            *(float4 *)(P.part + (((int64_t)s * n_tiles + tile) * T + tok) * DEC_ROWS + rloc) = sum;
+            *(float4 *)(part + (((int64_t)s * n_tiles + tile) * T + tok) * DEC_ROWS + rloc) = sum;
     }
 
     // ---- remaining shrink pieces (other row groups, other pairs of this tile); sred is
     //      reused once every wave is past the reads above
     if (upart != nullptr) {
         bool synced = false;
-        for (int p = tile; p < P.n_pairs; p += n_tiles) {
-            const int a = P.idx[p];
+        for (int p = tile; p < n_pairs; p += n_tiles) {
+            const int a = idx[p];
             if (a < 0)
                 continue;
             for (int r0 = (p == tile ? 16 : 0); r0 < wd; r0 += 16) {
@@ -311,7 +331,7 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
 DecodeCfg decode_config(int64_t T, int64_t n_in, int64_t n_out)
 {
     DecodeCfg c;
-    c.tt = T <= 16 ? 1 : T <= 32 ? 2 : 4;   // callers pass T <= 64
+    c.tt = T <= 16 ? 1 : T <= 32 ? 2 : 4;   // more than 64 tokens: chunks of 64
     c.n_tiles = (int)((n_out + DEC_ROWS - 1) / DEC_ROWS);
     const int64_t wblocks = (n_in + DEC_WK - 1) / DEC_WK;          // 128-column blocks
     // each workgroup takes up to 8 blocks (one per wave); split further while the grid is
@@ -327,7 +347,9 @@ DecodeCfg decode_config(int64_t T, int64_t n_in, int64_t n_out)
 size_t decode_partial_bytes(int64_t T, int64_t n_in, int64_t n_out)
 {
     const DecodeCfg c = decode_config(T, n_in, n_out);
-    return (size_t)c.sk * c.n_tiles * (size_t)T * DEC_ROWS * sizeof(float);
+    const int64_t n_chunks = (T + DEC_CHUNK - 1) / DEC_CHUNK;
+    const int64_t per = n_chunks > 1 ? DEC_CHUNK : T;           // token stride of a chunk
+    return (size_t)n_chunks * c.sk * c.n_tiles * (size_t)per * DEC_ROWS * sizeof(float);
 }
 
 template <int TT, bool PW>
@@ -342,7 +364,7 @@ static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, hipStream_t strea
             return e;
         lds_allowed = lds;
     }
-    const dim3 grid((unsigned)(c.n_tiles * c.sk)), block(512);
+    const dim3 grid((unsigned)(a.n_chunks * c.n_tiles * c.sk)), block(512);
     hipLaunchKernelGGL((decode_gemm_kernel<TT, PW>), grid, block, lds, stream, a);
     return hipGetLastError();
 }
@@ -364,10 +386,10 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed,
     a.idx = idx;
     a.K = K;
     a.part = part;
+    a.n_chunks = (int)((T + DEC_CHUNK - 1) / DEC_CHUNK);
     if (g != nullptr && upart != nullptr) {
         a.g = *g;
         a.upart = upart;
-        a.n_pairs = (int)(T * K);
     }
     a.n_rg = (int)((n_out + 15) / 16);
     a.n_kb = (int)((n_in + 31) / 32);

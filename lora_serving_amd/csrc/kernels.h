@@ -53,7 +53,8 @@ DecodeCfg decode_config(int64_t T, int64_t n_in, int64_t n_out);
 size_t decode_partial_bytes(int64_t T, int64_t n_in, int64_t n_out);
 // part[s][tile][t][0:64] = x[t, split s] . W[tile*64 + (0:64), split s]; with upart != nullptr
 // the same launch writes the unscaled shrink partials upart[s][j][t][0:n_slices*R] of every
-// pair (-1 pairs skipped).
+// pair (-1 pairs skipped).  T above 64: chunks of 64 tokens in one launch, each with its own
+// part and upart blocks (token stride 64; decode_partial_bytes covers them all).
 // W: row-major [n_out][n_in], or the packed layout of pack.hip when `packed`.
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed, int64_t T,
                               int64_t n_in, int64_t n_out, float *part, const DecodeCfg &cfg,

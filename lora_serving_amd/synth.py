@@ -236,8 +236,17 @@ def workload_lm_head(seed: int = 1005) -> Layer:
     return L
 
 
+def workload_decode256(seed: int = 1006) -> Layer:
+    """A larger decode step: 256 one-token requests on the decode layer (4096 -> 4096, 100
+    adapters of rank 16, 26 tokens base-only)."""
+    L = workload_decode(seed=seed, T=256)
+    L.name = "decode256"
+    return L
+
+
 WORKLOADS = {
     "tiny": workload_tiny,
+    "decode256": workload_decode256,
     "lm_head": workload_lm_head,
     "decode": workload_decode,
     "prefill": workload_prefill,
