@@ -63,6 +63,7 @@ __device__ __forceinline__ void df_vload(const float *upart, int sk, int64_t pst
     fa = *(a >= 0 ? factor + a : df_zero);
 }
 
+template <bool MC>
 __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
     const float *__restrict__ part, int sk, int n_tiles, const float *__restrict__ upart,
     const float *__restrict__ scale, int T_all, int n_out, SlotGeom g,
@@ -71,11 +72,12 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
     extern __shared__ __attribute__((aligned(16))) float vl[];   // [DF_TOK][R] of one (slot, slice)
     __shared__ int sidx[DF_TOK * MLORA_MAX_K_DEV];
     // chunks of DF_CHUNK tokens (the GEMM's chunks): this workgroup's chunk and its inputs
-    const int n_tg = (min(T_all, DF_CHUNK) + DF_TOK - 1) / DF_TOK;
-    const int chunk = blockIdx.x / (n_tiles * n_tg);
-    const int bl = blockIdx.x - chunk * (n_tiles * n_tg);
-    const int T = min(DF_CHUNK, T_all - chunk * DF_CHUNK);
-    {
+    // (MC: several chunks; one chunk keeps the plain mapping and base pointers)
+    const int n_tg = ((MC ? DF_CHUNK : T_all) + DF_TOK - 1) / DF_TOK;
+    const int chunk = MC ? blockIdx.x / (n_tiles * n_tg) : 0;
+    const unsigned bl = blockIdx.x - chunk * (n_tiles * n_tg);
+    const int T = MC ? min(DF_CHUNK, T_all - chunk * DF_CHUNK) : T_all;
+    if constexpr (MC) {
         const int wd0 = g.n_slices * g.R;
         part += (int64_t)chunk * sk * n_tiles * DF_CHUNK * DF_ROWS;
         if (upart != nullptr)
@@ -249,8 +251,12 @@ hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, 
     const int64_t n_chunks = (T + DF_CHUNK - 1) / DF_CHUNK;
     const unsigned grid =
         (unsigned)(n_chunks * n_tiles * ((std::min<int64_t>(T, DF_CHUNK) + DF_TOK - 1) / DF_TOK));
-    hipLaunchKernelGGL(decode_finish_kernel, dim3(grid), dim3(DF_THREADS), lds, stream, part, sk,
-                       n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y);
+    if (n_chunks > 1)
+        hipLaunchKernelGGL(decode_finish_kernel<true>, dim3(grid), dim3(DF_THREADS), lds, stream,
+                           part, sk, n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y);
+    else
+        hipLaunchKernelGGL(decode_finish_kernel<false>, dim3(grid), dim3(DF_THREADS), lds, stream,
+                           part, sk, n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y);
     return hipGetLastError();
 }
 

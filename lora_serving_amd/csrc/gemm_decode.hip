@@ -97,11 +97,12 @@ struct DecodeArgs {
     const float *scale;
     float *part;       // per chunk of 64 tokens: [sk][n_tiles][Tc][64]
     float *upart;      // per chunk: [sk][K][Tc][wd], or nullptr (no LoRA)
-    int n_chunks;      // chunks of DEC_CHUNK tokens in this launch (T is their total)
+    int n_pairs;       // (token, slot) pairs of one chunk: T * K when there is one chunk
     int n_rg, n_kb;    // packed W: row groups of 16, column blocks of 32
+    int n_chunks;      // chunks of DEC_CHUNK tokens in this launch (T is their total)
 };
 
-template <int TT, bool PW>
+template <int TT, bool PW, bool MC>
 __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
 {
     extern __shared__ __attribute__((aligned(16))) float red[];   // [8][4][TT][64] float4
@@ -114,8 +115,9 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
     // (workgroups are dealt to the 8 XCDs round robin) runs a contiguous range of (tile, split)
     // pairs with the chunks innermost, so the chunks of one W slice run back to back on one XCD
     // and read it from that XCD's L2 after the first.
+    // (MC: several chunks; the one-chunk kernel keeps the plain mapping and base pointers)
     int chunk = 0, tile, s;
-    if (P.n_chunks == 1) {
+    if constexpr (!MC) {
         tile = blockIdx.x % n_tiles;
         s = blockIdx.x / n_tiles;
     } else {
@@ -126,13 +128,20 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
         tile = pg % n_tiles;
         s = pg / n_tiles;
     }
-    const int T = min(DEC_CHUNK, P.T - chunk * DEC_CHUNK);
-    const uint16_t *__restrict__ x = P.x + (int64_t)chunk * DEC_CHUNK * n_in;
-    const int32_t *idx = P.idx != nullptr ? P.idx + (int64_t)chunk * DEC_CHUNK * K : nullptr;
-    float *part = P.part + (int64_t)chunk * P.sk * n_tiles * DEC_CHUNK * DEC_ROWS;
-    float *upart = P.upart != nullptr ? P.upart + (int64_t)chunk * P.sk * K * DEC_CHUNK * wd
-                                      : nullptr;
-    const int n_pairs = T * K;
+    int T = P.T, n_pairs = P.n_pairs;   // one chunk: straight from the arguments
+    const uint16_t *__restrict__ x = P.x;
+    const int32_t *idx = P.idx;
+    float *part = P.part, *upart = P.upart;
+    if constexpr (MC) {
+        T = min(DEC_CHUNK, P.T - chunk * DEC_CHUNK);
+        n_pairs = T * K;
+        x += (int64_t)chunk * DEC_CHUNK * n_in;
+        if (idx != nullptr)
+            idx += (int64_t)chunk * DEC_CHUNK * K;
+        part += (int64_t)chunk * P.sk * n_tiles * DEC_CHUNK * DEC_ROWS;
+        if (upart != nullptr)
+            upart += (int64_t)chunk * P.sk * K * DEC_CHUNK * wd;
+    }
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;     // row (A operand) / token (B operand) within a 16-tile
@@ -352,21 +361,30 @@ size_t decode_partial_bytes(int64_t T, int64_t n_in, int64_t n_out)
     return (size_t)n_chunks * c.sk * c.n_tiles * (size_t)per * DEC_ROWS * sizeof(float);
 }
 
-template <int TT, bool PW>
-static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, hipStream_t stream)
+template <int TT, bool PW, bool MC>
+static hipError_t launch_tfm(DecodeArgs &a, const DecodeCfg &c, hipStream_t stream)
 {
     const size_t lds = (size_t)DEC_WAVES * 4 * TT * 64 * sizeof(float4);
     static size_t lds_allowed = 64 * 1024;
     if (lds > lds_allowed) {
-        hipError_t e = hipFuncSetAttribute((const void *)decode_gemm_kernel<TT, PW>,
+        hipError_t e = hipFuncSetAttribute((const void *)decode_gemm_kernel<TT, PW, MC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
             return e;
         lds_allowed = lds;
     }
     const dim3 grid((unsigned)(a.n_chunks * c.n_tiles * c.sk)), block(512);
-    hipLaunchKernelGGL((decode_gemm_kernel<TT, PW>), grid, block, lds, stream, a);
+    hipLaunchKernelGGL((decode_gemm_kernel<TT, PW, MC>), grid, block, lds, stream, a);
     return hipGetLastError();
+}
+
+template <int TT, bool PW>
+static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, hipStream_t stream)
+{
+    if constexpr (TT == 4)   // only full 64-token chunks come before the last one
+        if (a.n_chunks > 1)
+            return launch_tfm<TT, PW, true>(a, c, stream);
+    return launch_tfm<TT, PW, false>(a, c, stream);
 }
 
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed, int64_t T,
@@ -390,6 +408,7 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed,
     if (g != nullptr && upart != nullptr) {
         a.g = *g;
         a.upart = upart;
+        a.n_pairs = (int)(std::min<int64_t>(T, DEC_CHUNK) * K);
     }
     a.n_rg = (int)((n_out + 15) / 16);
     a.n_kb = (int)((n_in + 31) / 32);
