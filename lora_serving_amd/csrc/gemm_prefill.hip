@@ -9,8 +9,10 @@
 //
 //  1. tile plan (one workgroup per tile of PF_BM tokens): the distinct adapters used by the
 //     tile's (token, slot) pairs, ascending, and each adapter's number of tokens;
-//  2. SGMV shrink: for each (tile, adapter) the tokens that use it are gathered, and
-//     V[token][col(s, d, rho)] = c_t * sum_i A[a][s][rho][i] x[t][i] runs on the matrix cores,
+//  2. SGMV shrink: V[token][col(s, d, rho)] = c_t * sum_i A[a][s][rho][i] x[t][i] on the
+//     matrix cores (a tile with few adapters: one product of its x with the stacked A rows,
+//     n_in split across workgroups and the parts added in order by a second small kernel; a
+//     tile with many: each adapter's tokens gathered),
 //     c_t = sum over the token's slots holding a of s[t][j] * f[a].  V is kept as two bf16
 //     halves, hi = bf16(v) and lo = bf16(v - hi) (about 16 significant bits: a single bf16
 //     rounding of v breaks the layer's tolerance when s*f is large, e.g. rsLoRA at rank 64),
@@ -40,6 +42,13 @@ constexpr int PF_BK = 64;    // column granule of a tile's V block (its width is
 // Masked loads read this static block instead of choosing zero after the load: the choice is
 // made on the address, so nothing waits for a load right after it is issued.
 __device__ __attribute__((aligned(64))) uint32_t pf_zero16[16];   // never written: zeros
+
+// One 16-byte copy per lane from global memory straight into LDS (64 lanes: 1 KB contiguous
+// at lds).
+__device__ __forceinline__ void pf_dma(const void *g, uint16_t *lds)
+{
+    __builtin_amdgcn_global_load_lds(g, (void __attribute__((address_space(3))) *)lds, 16, 0, 0);
+}
 
 // ------------------------------------------------------------------------------------------
 // 1. tile plan
@@ -205,13 +214,28 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
 // The tile's D adapters are stacked into one "cat" matrix A_cat (D * n_slices * R rows), so the
 // shrink of a tile is one dense product V_tile = X_tile A_cat^T; a token that does not use
 // adapter d gets coefficient 0 for d's columns (the zeros the GEMM's extra K-steps expect).
-// Item = (tile m, 64-token chunk c, 64-row block rb of A_cat); the items of all tiles are
-// numbered through a prefix over the tiles' row-block counts and shared out to a persistent
-// grid.  Inside an item the 4 waves split n_in, each holding the full 64 x 64 result in
-// MFMA accumulators, with operands loaded straight into the MFMA layout two k-steps ahead;
-// the 4 partial tiles are added in LDS in wave order and written as bf16 hi/lo pairs.
+//
+// Dense item = (tile m, 128-row block rb of A_cat, part kp of n_in split in ks parts): all 256
+// tokens of the tile against the block's rows over the part's columns.  Operands are copied
+// straight into LDS (global_load_lds_dwordx4) in stages of 64 columns whose rows are 128 bytes
+// (whole cache lines per request), three stages deep (two in flight while one is multiplied);
+// wave w multiplies tokens 64w .. 64w+63 against the 128 rows.  With ks = 1 the item applies
+// the coefficients and writes V; with ks > 1 it writes its fp32 partial block and
+// shrink_reduce_kernel adds the parts in order.  ks is chosen in the kernel (every workgroup
+// computes the same value) so that there are about SD_TARGET items and the partial blocks fit
+// their workspace region.
+// Scattered tiles have group items instead (below).  The items of all tiles are numbered
+// through a prefix over the tiles and shared out to a persistent grid.
 constexpr int SH_THREADS = 256;
 constexpr int SH_MAX_TILES = 4096;   // tiles whose item prefix fits LDS
+constexpr int SD_ROWS = 128;         // A_cat rows of a dense item
+constexpr int SD_KS = 64;            // columns per stage
+constexpr int SD_STAGE_ELEMS = (PF_BM + SD_ROWS) * SD_KS;   // bf16: 256 x rows, then A rows
+constexpr int SD_STAGE_BYTES = SD_STAGE_ELEMS * 2;          // 48 KB
+constexpr int SD_KS_MAX = 8;         // most parts of n_in
+constexpr int SD_TARGET = 256;       // dense items aimed for
+constexpr int SD_PART_ELEMS = PF_BM * SD_ROWS;              // fp32 partial block of an item
+constexpr int SD_TABLE_BYTES = 9;    // LDS per tile for the item tables (pre, pbase, grouped)
 
 struct ShrinkArgs {
     const uint16_t *x;
@@ -229,33 +253,12 @@ struct ShrinkArgs {
     const int32_t *tile_toff, *tile_gpre;   // scattered tiles: token lists (tile plan)
     const uint8_t *tile_tok;
     int tok_stride;
+    float *sd_part;       // [sd_cap_slots][256][128] fp32 partial blocks (ks > 1)
+    int sd_cap_slots;
+    int32_t *tile_pbase;  // out: first partial slot / SD block of a dense tile, -1 otherwise
+    int32_t *sd_ks;       // out: ks of this launch
+    int stages;           // dense item stages in LDS (2 or 3)
 };
-
-__device__ __forceinline__ void sh_load(const uint16_t *const (&ap)[4], const bool (&aok)[4],
-                                        const uint16_t *const (&xp)[4], int col, int kend,
-                                        u32x4 (&af)[4], u32x4 (&xf)[4])
-{
-    // the pointers already include this lane's chunk offset 8 * (lane / 16)
-    const int off = ((threadIdx.x & 63) >> 4) * 8;
-    const bool ok = col + off < kend;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        af[b] = *(const u32x4 *)(ok && aok[b] ? (const void *)(ap[b] + col) : (const void *)pf_zero16);
-        xf[b] = *(const u32x4 *)(ok ? (const void *)(xp[b] + col) : (const void *)pf_zero16);
-    }
-}
-
-__device__ __forceinline__ void sh_mfma(const u32x4 (&af)[4], const u32x4 (&xf)[4],
-                                        f32x4 (&acc)[4][4])
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, xf[j]), acc[i][j], 0,
-                0, 0);
-}
 
 // Coefficient of adapter a for token t: the sum of s[t][j] * f[a] over the slots j holding a.
 __device__ __forceinline__ float sh_coef(const ShrinkArgs &P, int t, int a)
@@ -286,96 +289,174 @@ __device__ __forceinline__ void sh_wave_cols(int n_in, int wave, int &kb, int &k
     nsteps = kend > kb ? (kend - kb + 31) / 32 : 0;
 }
 
-// Cat item (tile m, 64-token chunk, 64-row block of A_cat): every token of the chunk against
-// every stacked adapter row.
-__device__ __forceinline__ void sh_cat_item(const ShrinkArgs &P, int m, int local, float4 *red)
+// The n_in split of the dense items: ks parts of kc columns (a multiple of SD_KS), for
+// total_rb 128-row blocks over all dense tiles.  The same on every workgroup and in the reduce.
+__device__ __forceinline__ void sd_split(int total_rb, int n_in, int cap_slots, int &ks, int &kc)
+{
+    int k0 = 1;
+    if (total_rb > 0) {
+        k0 = min(SD_KS_MAX, (SD_TARGET + total_rb - 1) / total_rb);
+        k0 = min(k0, cap_slots / total_rb);
+        k0 = min(k0, n_in / 256);
+        k0 = max(k0, 1);
+    }
+    kc = ((n_in + k0 - 1) / k0 + SD_KS - 1) / SD_KS * SD_KS;
+    ks = (n_in + kc - 1) / kc;
+}
+
+// Copies of stage q (columns c0 .. c0+63) into the stage buffer sb: wave w copies its 64 token
+// rows (8 instructions of 8 rows x 128 bytes) and A rows 32w .. 32w+31 (4 instructions).
+// Chunk c of row r sits at position c ^ (r & 7) of its row.
+__device__ __forceinline__ void sd_issue(uint16_t *sb, const uint16_t *const (&xr)[8],
+                                         const uint16_t *const (&ar)[4], uint32_t rmask, int c0,
+                                         int kend, int wave, int lane)
+{
+    const int c = ((lane & 7) ^ (lane >> 3)) * 8;
+    const bool ok = c0 + c < kend;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        pf_dma(ok && (rmask >> i & 1u) ? (const void *)(xr[i] + c0 + c) : (const void *)pf_zero16,
+               sb + (wave * 64 + i * 8) * SD_KS);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        pf_dma(ok && (rmask >> (8 + i) & 1u) ? (const void *)(ar[i] + c0 + c)
+                                             : (const void *)pf_zero16,
+               sb + (PF_BM + wave * 32 + i * 8) * SD_KS);
+}
+
+// MFMAs of one stage (two k-steps of 32): the wave's 4 token groups x ni row groups of 16.
+__device__ __forceinline__ void sd_compute(const uint16_t *sb, int wave, int r, int gq, int ni,
+                                           f32x4 (&acc)[8][4])
+{
+    const uint16_t *sx = sb, *sa = sb + PF_BM * SD_KS;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+        const int pos = (k2 * 4 + gq) ^ (r & 7);
+        bf16x8 xf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            xf[j] = *(const bf16x8 *)(sx + ((wave * 64 + j * 16 + r) * 8 + pos) * 8);
+        bf16x8 af[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            af[i] = *(const bf16x8 *)(sa + ((i * 16 + r) * 8 + pos) * 8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i < ni) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], xf[j], acc[i][j],
+                                                                        0, 0, 0);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void sh_dense_item(const ShrinkArgs &P, int m, int rb, int kp, int ks,
+                                              int kc, int slot, uint16_t *lds)
 {
     const SlotGeom &g = P.g;
     const int R = g.R, wd = g.n_slices * R;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, gq = lane >> 4;
-    const int c = local & 3, rb = local >> 2;
     const int D = P.tile_D[m];
     const int32_t *list = P.tile_list + (int64_t)m * P.list_stride;
-    const int t0 = m * PF_BM + c * 64;
     const int rows_cat = D * wd;
+    const int row0 = rb * SD_ROWS;
+    const int ni = min(8, (rows_cat - row0 + 15) / 16);   // row groups with a row of A_cat
+    const int kbeg = kp * kc, kend = min(P.n_in, kbeg + kc);
+    const int nst = (kend - kbeg + SD_KS - 1) / SD_KS;
 
-    // rows past their adapter's rank (zero padding) are not read: their fragments come from the
-    // zero block
-    const uint16_t *ap[4], *xp[4];
-    bool aok[4];
+    // row pointers of this lane's copies, and which of them are real rows (bit i: x row i,
+    // bit 8 + i: A row i; the others are copied from the zero block).  Rows past their
+    // adapter's rank (zero padding) are not read.
+    const int rr = lane >> 3;
+    const uint16_t *xr[8], *ar[4];
+    uint32_t rmask = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int ar_raw = rb * 64 + b * 16 + r;
-        const int ar = min(ar_raw, rows_cat - 1);
-        const int d = ar / wd;
-        const int rr = ar - d * wd;
-        aok[b] = ar_raw < rows_cat && rr % R < slot_rank8(g.rank, list[d], R);
-        ap[b] = g.A + ((int64_t)list[d] * wd + rr) * P.n_in + gq * 8;
-        xp[b] = P.x + (int64_t)min(t0 + b * 16 + r, P.T - 1) * P.n_in + gq * 8;
+    for (int i = 0; i < 8; ++i) {
+        const int t = m * PF_BM + wave * 64 + i * 8 + rr;
+        xr[i] = P.x + (int64_t)min(t, P.T - 1) * P.n_in;
+        rmask |= (t < P.T ? 1u : 0u) << i;
     }
-    int kb, kend, nsteps;
-    sh_wave_cols(P.n_in, wave, kb, kend, nsteps);
-
-    f32x4 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+        const int a_row = row0 + wave * 32 + i * 8 + rr;
+        const int d = min(a_row, rows_cat - 1) / wd;
+        const int rin = min(a_row, rows_cat - 1) - d * wd;
+        const bool ok = a_row < rows_cat && rin % R < slot_rank8(g.rank, list[d], R);
+        ar[i] = g.A + ((int64_t)list[d] * wd + rin) * P.n_in;
+        rmask |= (ok ? 1u : 0u) << (8 + i);
+    }
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 a0[4], x0[4], a1[4], x1[4];
-    sh_load(ap, aok, xp, kb, kend, a0, x0);
-    sh_load(ap, aok, xp, kb + 32, kend, a1, x1);
-    for (int st = 0; st < nsteps; st += 2) {
-        sh_mfma(a0, x0, acc);
-        sh_load(ap, aok, xp, kb + (st + 2) * 32, kend, a0, x0);
-        sh_mfma(a1, x1, acc);
-        sh_load(ap, aok, xp, kb + (st + 3) * 32, kend, a1, x1);
-    }
 
-    // lane holds A_cat rows rb*64 + 16i + 4gq + e of token t0 + 16j + r
+    // stages: issue up to S - 1 ahead; before multiplying stage q, wait for this wave's copies
+    // of it (12 per stage, in order) and publish them with a barrier; stage q + S - 1 then goes
+    // into the buffer stage q - 1 used, which every wave has finished with
+    const int S = P.stages;
+    for (int q = 0; q < S - 1 && q < nst; ++q)
+        sd_issue(lds + q * SD_STAGE_ELEMS, xr, ar, rmask, kbeg + q * SD_KS, kend, wave, lane);
+    for (int q = 0; q < nst; ++q) {
+        const int ahead = min(S - 2, nst - 1 - q);    // stages issued after q
+        if (ahead >= 1)
+            asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (q + S - 1 < nst)
+            sd_issue(lds + ((q + S - 1) % S) * SD_STAGE_ELEMS, xr, ar, rmask,
+                     kbeg + (q + S - 1) * SD_KS, kend, wave, lane);
+        sd_compute(lds + (q % S) * SD_STAGE_ELEMS, wave, r, gq, ni, acc);
+    }
+    __syncthreads();   // the stage buffers are free for the next item
+
+    // lane holds rows row0 + 16i + 4gq + e (e = 0..3) of token wave*64 + 16j + r
+    if (ks > 1) {
+        float *pb = P.sd_part + (int64_t)slot * SD_PART_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i) {
+            if (i < ni) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            red[(wave * 16 + i * 4 + j) * 64 + lane] =
-                float4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-    __syncthreads();
-    // thread: token tl = tid / 4, 16 consecutive rows q*16 .. q*16+15 (q = tid % 4)
-    const int tl = threadIdx.x >> 2, q = threadIdx.x & 3;
-    const int t = t0 + tl;
-    if (t < P.T && t < m * PF_BM + PF_BM) {
-        const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
-        uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems +
-                         (int64_t)(t - m * PF_BM) * (g.n_slices * kxs);
+                for (int j = 0; j < 4; ++j)
+                    *(float4 *)(pb + (wave * 64 + j * 16 + r) * SD_ROWS + i * 16 + gq * 4) =
+                        float4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+            }
+        }
+        return;
+    }
+    const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tl = wave * 64 + j * 16 + r;
+        const int t = m * PF_BM + tl;
+        if (t >= P.T)
+            continue;
+        uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems + (int64_t)tl * (g.n_slices * kxs);
         int dprev = -1;
         float cf = 0.f;
-        for (int e = 0; e < 16; ++e) {
-            const int ar = rb * 64 + q * 16 + e;
-            if (ar >= rows_cat)
-                break;
-            const int d = ar / wd;
-            if (d != dprev) {
-                cf = sh_coef(P, t, list[d]);
-                dprev = d;
-            }
-            // element (row ar, token tl) sits in block (i = ar/16, j = tl/16), lane
-            // (tl % 16) + 16 * ((ar % 16) / 4), component ar % 4
-            const int arl = q * 16 + e;
-            const int i = arl >> 4, jb = tl >> 4;
-            const int ln = (tl & 15) + 16 * ((arl & 15) >> 2), comp = arl & 3;
-            float sum = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float4 v4 = red[(w * 16 + i * 4 + jb) * 64 + ln];
-                sum += comp == 0 ? v4.x : comp == 1 ? v4.y : comp == 2 ? v4.z : v4.w;
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int a_row = row0 + i * 16 + gq * 4 + e;
+                if (i >= ni || a_row >= rows_cat)
+                    continue;
+                const int d = a_row / wd;
+                if (d != dprev) {
+                    cf = sh_coef(P, t, list[d]);
+                    dprev = d;
+                }
+                const int rin = a_row - d * wd, sg = rin / R, rho = rin - sg * R;
+                sh_store_v(vrow + sg * kxs + d * 2 * R + rho, R, cf * acc[i][j][e]);
             }
-            const int rr = ar - d * wd;          // row within the adapter: slice sg, rank rho
-            const int sg = rr / R, rho = rr - sg * R;
-            sh_store_v(vrow + sg * kxs + d * 2 * R + rho, R, cf * sum);
         }
     }
-    __syncthreads();
 }
 
 // Group item of a scattered tile (token group gidx of one adapter, 32-row block rb of that
@@ -491,42 +572,71 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
 __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
 {
     extern __shared__ __attribute__((aligned(16))) float sh_lds[];
+    // stage buffers of the dense items (the group items' reduction space shares them), then
+    // the item tables
+    uint16_t *stages = (uint16_t *)sh_lds;
     float4 *red = (float4 *)sh_lds;                           // [4 waves][16][64] float4
-    int *pre = (int *)(sh_lds + 4 * 16 * 64 * 4);             // [n_mtiles] item prefix
-    uint8_t *grouped = (uint8_t *)(pre + P.n_mtiles);         // [n_mtiles] 1: group items
+    int *pre = (int *)((uint8_t *)sh_lds + (size_t)P.stages * SD_STAGE_BYTES);   // item prefix
+    int *pbase = pre + P.n_mtiles;                            // first 128-row block of a tile
+    uint8_t *grouped = (uint8_t *)(pbase + P.n_mtiles);       // 1: group items
     __shared__ int wsum[8];
     const int wd = P.g.n_slices * P.g.R;
     const int RBg = (wd + SG_ROWS - 1) / SG_ROWS;
 
-    // Items of tile m: group items (a scattered tile whose ordinal is below sc_cap) or cat
-    // items, 4 chunks x ceil(D_m * wd / 64) row blocks; workgroup 0 also numbers the
-    // scattered tiles.
-    int base = 0, sc_base = 0;
+    // Pass 1: which tiles take group items (a scattered tile whose ordinal is below sc_cap),
+    // and the 128-row blocks of the others; workgroup 0 also numbers the scattered tiles.
+    int rb_base = 0, sc_base = 0;
     for (int m0 = 0; m0 < P.n_mtiles; m0 += SH_THREADS) {
         const int m = m0 + threadIdx.x;
         const int Dm = m < P.n_mtiles ? P.tile_D[m] : 0;
         const int scm = m < P.n_mtiles && tile_scattered(Dm, P.g.R, P.n_in) ? 1 : 0;
-        int sc_ex, sc_all, ex, all, u0, u1;
+        int sc_ex, sc_all, u0, u1;
         block_scan2(scm, 0, wsum, sc_ex, u0, sc_all, u1);
         const int ord = sc_base + sc_ex;
         const bool kept = scm && ord < P.sc_cap;
-        const int cnt = kept ? P.tile_gpre[(int64_t)m * (P.list_stride + 1) + Dm] * RBg
-                             : 4 * ((Dm * wd + 63) / 64);
-        block_scan2(cnt, 0, wsum, ex, u0, all, u1);
+        const int rbs = kept ? 0 : (Dm * wd + SD_ROWS - 1) / SD_ROWS;
+        int rb_ex, rb_all;
+        block_scan2(rbs, 0, wsum, rb_ex, u0, rb_all, u1);
         if (m < P.n_mtiles) {
-            pre[m] = base + ex;
             grouped[m] = kept ? 1 : 0;
+            pbase[m] = rbs > 0 ? rb_base + rb_ex : -1;
         }
         if (blockIdx.x == 0 && m < P.n_mtiles) {
             P.tile_ord[m] = kept ? ord : -1;
             if (kept)
                 P.sc_tiles[ord] = m;
         }
-        base += all;
+        rb_base += rb_all;
         sc_base += sc_all;
     }
     if (blockIdx.x == 0 && threadIdx.x == 0)
         P.sc_tiles[P.sc_cap] = min(sc_base, P.sc_cap);
+    int ks, kc;
+    sd_split(rb_base, P.n_in, P.sd_cap_slots, ks, kc);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        for (int m = threadIdx.x; m < P.n_mtiles; m += SH_THREADS)
+            P.tile_pbase[m] = pbase[m] >= 0 ? pbase[m] * ks : -1;
+        if (threadIdx.x == 0)
+            *P.sd_ks = ks;
+    }
+
+    // Pass 2: items of tile m: group items, or ks parts of each 128-row block
+    int base = 0;
+    for (int m0 = 0; m0 < P.n_mtiles; m0 += SH_THREADS) {
+        const int m = m0 + threadIdx.x;
+        int cnt = 0;
+        if (m < P.n_mtiles) {
+            const int Dm = P.tile_D[m];
+            cnt = grouped[m] ? P.tile_gpre[(int64_t)m * (P.list_stride + 1) + Dm] * RBg
+                             : ((Dm * wd + SD_ROWS - 1) / SD_ROWS) * ks;
+        }
+        int ex, all, u0, u1;
+        block_scan2(cnt, 0, wsum, ex, u0, all, u1);
+        if (m < P.n_mtiles)
+            pre[m] = base + ex;
+        base += all;
+    }
     const int total = base;
     __syncthreads();
 
@@ -540,10 +650,97 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
             else
                 hi = mid - 1;
         }
-        if (grouped[lo])
-            sh_group_item(P, lo, item - pre[lo], red);
-        else
-            sh_cat_item(P, lo, item - pre[lo], red);
+        const int local = item - pre[lo];
+        if (grouped[lo]) {
+            sh_group_item(P, lo, local, red);
+        } else {
+            const int rb = local / ks, kp = local - rb * ks;
+            sh_dense_item(P, lo, rb, kp, ks, kc, (pbase[lo] + rb) * ks + kp, stages);
+        }
+    }
+}
+
+// Adds the ks partial blocks of the dense tiles in part order, applies each token's
+// coefficients and writes V (bf16 hi/lo halves).  One workgroup per (tile, 16 tokens); each
+// thread takes 4 consecutive rows of A_cat for one token (one adapter and slice: R is a
+// multiple of 4), so its partials are float4 loads and its V halves 8-byte stores.  The
+// tokens' slot ids and scales, and the tile's adapter ids and factors (the first SR_D of them;
+// more are read from global memory), are staged in LDS first.  Nothing to do when the launch
+// used ks = 1 (the items wrote V themselves) or for group-item tiles.
+constexpr int SR_TOK = 16;
+constexpr int SR_D = 1024;
+
+__global__ __launch_bounds__(256) void shrink_reduce_kernel(ShrinkArgs P)
+{
+    __shared__ int s_idx[SR_TOK * MLORA_MAX_K_DEV];
+    __shared__ float s_sc[SR_TOK * MLORA_MAX_K_DEV];
+    __shared__ int s_a[SR_D];
+    __shared__ float s_f[SR_D];
+    const int m = blockIdx.x / (PF_BM / SR_TOK);
+    const int t0l = (blockIdx.x % (PF_BM / SR_TOK)) * SR_TOK;
+    const int ks = *P.sd_ks;
+    const int pb = P.tile_pbase[m];
+    const int nt = min(SR_TOK, P.T - (m * PF_BM + t0l));
+    if (ks <= 1 || pb < 0 || nt <= 0)
+        return;
+    const SlotGeom &g = P.g;
+    const int R = g.R, wd = g.n_slices * R, K = P.K;
+    const int D = P.tile_D[m];
+    const int32_t *list = P.tile_list + (int64_t)m * P.list_stride;
+    const int64_t tb = (int64_t)m * PF_BM + t0l;   // first token of the block
+    for (int i = threadIdx.x; i < nt * K; i += 256) {
+        s_idx[i] = P.idx[tb * K + i];
+        s_sc[i] = P.scale ? P.scale[tb * K + i] : 1.f;
+    }
+    for (int d = threadIdx.x; d < min(D, SR_D); d += 256) {
+        const int a = list[d];
+        s_a[d] = a;
+        s_f[d] = g.factor[a];
+    }
+    __syncthreads();
+    const int rows4 = D * wd / 4;                  // groups of 4 rows
+    const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
+    for (int e = threadIdx.x; e < nt * rows4; e += 256) {
+        const int tt = e / rows4, a_row = (e - tt * rows4) * 4;
+        const int tl = t0l + tt;
+        const int rb = a_row / SD_ROWS, rl = a_row - rb * SD_ROWS;
+        const float *src = P.sd_part + ((int64_t)(pb + rb * ks) * PF_BM + tl) * SD_ROWS + rl;
+        float4 pv[SD_KS_MAX];
+#pragma unroll
+        for (int kp = 0; kp < SD_KS_MAX; ++kp)
+            if (kp < ks)
+                pv[kp] = *(const float4 *)(src + (int64_t)kp * SD_PART_ELEMS);
+        float4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kp = 0; kp < SD_KS_MAX; ++kp) {
+            if (kp < ks) {
+                sum.x += pv[kp].x;
+                sum.y += pv[kp].y;
+                sum.z += pv[kp].z;
+                sum.w += pv[kp].w;
+            }
+        }
+        const int d = a_row / wd;
+        const int a = d < SR_D ? s_a[d] : list[d];
+        const float f = d < SR_D ? s_f[d] : g.factor[a];
+        float cf = 0.f;
+        for (int j = 0; j < K; ++j)
+            if (s_idx[tt * K + j] == a)
+                cf += s_sc[tt * K + j] * f;
+        const int rin = a_row - d * wd, sg = rin / R, rho = rin - sg * R;
+        uint16_t *vp = P.vcat + (int64_t)m * P.vcat_tile_elems + (int64_t)tl * (g.n_slices * kxs) +
+                       sg * kxs + d * 2 * R + rho;
+        const float v[4] = {cf * sum.x, cf * sum.y, cf * sum.z, cf * sum.w};
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            hi[i] = f32_to_bf16(v[i]);
+            lo[i] = f32_to_bf16(v[i] - bf16_to_f32(hi[i]));
+        }
+        *(u32x2 *)vp = u32x2{(uint32_t)hi[0] | (uint32_t)hi[1] << 16,
+                             (uint32_t)hi[2] | (uint32_t)hi[3] << 16};
+        *(u32x2 *)(vp + R) = u32x2{(uint32_t)lo[0] | (uint32_t)lo[1] << 16,
+                                   (uint32_t)lo[2] | (uint32_t)lo[3] << 16};
     }
 }
 
@@ -580,11 +777,6 @@ struct GemmArgs {
 constexpr int PF_KS = 64;                  // columns per stage
 constexpr int PF_STAGES = 2;
 constexpr int PF_STAGE_BYTES = 2 * 256 * PF_KS * 2;
-
-__device__ __forceinline__ void pf_dma(const void *g, uint16_t *lds)
-{
-    __builtin_amdgcn_global_load_lds(g, (void __attribute__((address_space(3))) *)lds, 16, 0, 0);
-}
 
 // Issues this wave's copies of stage q (k-step q: base columns q*64 while q < nk_main, then
 // the LoRA extra steps) into buffer `st`: 4 blocks of 8 W rows and 4 of 8 tokens per wave.
@@ -1022,6 +1214,11 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
     c.tok_stride = PF_BM * K;
     c.sc_cap = (int)std::min<int64_t>(
         c.n_mtiles, std::max<int64_t>(1, (64ll << 20) / ((int64_t)PF_BM * n_out * 4)));
+    // fp32 partial blocks of the dense shrink items: within 64 MiB, and no more than the most
+    // the launch can use (every tile dense with list_stride adapters, SD_KS_MAX parts)
+    const int64_t rbs_max = ((int64_t)c.list_stride * n_slices * R + SD_ROWS - 1) / SD_ROWS;
+    c.sd_cap_slots = (int)std::min<int64_t>(
+        (64ll << 20) / ((int64_t)SD_PART_ELEMS * 4), (int64_t)c.n_mtiles * rbs_max * SD_KS_MAX);
     (void)n_in;
     return c;
 }
@@ -1029,7 +1226,7 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
 // Workspace regions of the tiled path, each 256-byte aligned, in this order.
 struct PrefillLayout {
     size_t tile_D, tile_list, tile_toff, tile_gpre, tile_tok, tile_ord, sc_tiles, part_sc, vcat,
-        total;
+        tile_pbase, sd_ks, sd_part, total;
 };
 
 static size_t al256(size_t v) { return (v + 255) / 256 * 256; }
@@ -1048,7 +1245,10 @@ static PrefillLayout prefill_layout(const PrefillCfg &c)
     L.sc_tiles = L.tile_ord + al256((size_t)c.n_mtiles * sizeof(int32_t));
     L.part_sc = L.sc_tiles + al256(((size_t)c.sc_cap + 1) * sizeof(int32_t));
     L.vcat = L.part_sc + al256((size_t)c.sc_cap * PF_BM * (size_t)c.n_out * sizeof(float));
-    L.total = L.vcat + (size_t)c.n_mtiles * c.vcat_tile_elems * sizeof(uint16_t);
+    L.tile_pbase = L.vcat + al256((size_t)c.n_mtiles * c.vcat_tile_elems * sizeof(uint16_t));
+    L.sd_ks = L.tile_pbase + al256((size_t)c.n_mtiles * sizeof(int32_t));
+    L.sd_part = L.sd_ks + 256;
+    L.total = L.sd_part + (size_t)c.sd_cap_slots * SD_PART_ELEMS * sizeof(float);
     return L;
 }
 
@@ -1076,6 +1276,9 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     int32_t *sc_tiles = (int32_t *)(p + WL.sc_tiles);
     float *part_sc = (float *)(p + WL.part_sc);
     uint16_t *vcat = (uint16_t *)(p + WL.vcat);
+    int32_t *tile_pbase = (int32_t *)(p + WL.tile_pbase);
+    int32_t *sd_ks = (int32_t *)(p + WL.sd_ks);
+    float *sd_part = (float *)(p + WL.sd_part);
 
     if (g != nullptr && c.n_mtiles > SH_MAX_TILES)
         return hipErrorInvalidValue;   // callers split larger batches
@@ -1114,7 +1317,14 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         s.tile_gpre = tile_gpre;
         s.tile_tok = tile_tok;
         s.tok_stride = c.tok_stride;
-        const size_t sh_lds = (size_t)4 * 16 * 64 * sizeof(float4) + (size_t)c.n_mtiles * (sizeof(int) + 1);
+        s.sd_part = sd_part;
+        s.sd_cap_slots = c.sd_cap_slots;
+        s.tile_pbase = tile_pbase;
+        s.sd_ks = sd_ks;
+        // three dense stages while the item tables leave room in the 160 KB of LDS, else two
+        const size_t tables = (size_t)c.n_mtiles * SD_TABLE_BYTES;
+        s.stages = 3 * (size_t)SD_STAGE_BYTES + tables <= 160 * 1024 ? 3 : 2;
+        const size_t sh_lds = (size_t)s.stages * SD_STAGE_BYTES + tables;
         static size_t sh_allowed = 64 * 1024;
         if (sh_lds > sh_allowed) {
             hipError_t e = hipFuncSetAttribute((const void *)sgmv_shrink_kernel,
@@ -1124,6 +1334,8 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
             sh_allowed = sh_lds;
         }
         hipLaunchKernelGGL(sgmv_shrink_kernel, dim3(1024), dim3(SH_THREADS), sh_lds, stream, s);
+        hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)c.n_mtiles * (PF_BM / SR_TOK)),
+                           dim3(256), 0, stream, s);
     }
     GemmArgs a{};
     a.x = x;
