@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
                                                         int list_stride, int32_t *tile_D,
                                                         int32_t *tile_list, int32_t *tile_toff,
                                                         int32_t *tile_gpre, uint8_t *tile_tok,
-                                                        int tok_stride, uint16_t *vcat,
+                                                        int tok_stride, int4 *tile_grp,
+                                                        int grp_stride, uint16_t *vcat,
                                                         int64_t vcat_tile_elems)
 {
     extern __shared__ uint32_t plan_lds[];         // bits[(S+31)/32], cnt[S], lst[list_stride]
@@ -176,6 +177,13 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
             gpre[D] = gbase;
         }
         __syncthreads();
+        // one record per 16-token group: {position d, adapter, first list entry, tokens}
+        int4 *grp = tile_grp + (int64_t)m * grp_stride;
+        for (int d = threadIdx.x; d < D; d += blockDim.x) {
+            const int o0 = toff[d], o1 = toff[d + 1], g0 = gpre[d];
+            for (int o = o0; o < o1; o += 16)
+                grp[g0 + (o - o0) / 16] = int4{d, lst[d], o, min(16, o1 - o)};
+        }
         uint8_t *tok = tile_tok + (int64_t)m * tok_stride;
         for (int tl = threadIdx.x; tl < nt; tl += blockDim.x) {
             const int32_t *it = idx + (int64_t)(t0 + tl) * K;
@@ -253,6 +261,8 @@ struct ShrinkArgs {
     const int32_t *tile_toff, *tile_gpre;   // scattered tiles: token lists (tile plan)
     const uint8_t *tile_tok;
     int tok_stride;
+    const int4 *tile_grp;                   // scattered tiles: group records (tile plan)
+    int grp_stride;
     float *sd_part;       // [sd_cap_slots][256][128] fp32 partial blocks (ks > 1)
     int sd_cap_slots;
     int32_t *tile_pbase;  // out: first partial slot / SD block of a dense tile, -1 otherwise
@@ -485,20 +495,8 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
     const int RB = (wd + SG_ROWS - 1) / SG_ROWS;
     const int gidx = local / RB, rb = local - gidx * RB;
     const int D = P.tile_D[m];
-    const int32_t *gp = P.tile_gpre + (int64_t)m * (P.list_stride + 1);
-    const int32_t *to = P.tile_toff + (int64_t)m * (P.list_stride + 1);
-    int lo = 0, hi = D - 1;                   // the adapter: last d with gp[d] <= gidx
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (gp[mid] <= gidx)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    const int d = lo;
-    const int a = P.tile_list[(int64_t)m * P.list_stride + d];
-    const int s0 = to[d] + 16 * (gidx - gp[d]);
-    const int ng = min(16, to[d + 1] - s0);
+    const int4 gr = P.tile_grp[(int64_t)m * P.grp_stride + gidx];   // {d, adapter, s0, tokens}
+    const int d = gr.x, a = gr.y, s0 = gr.z, ng = gr.w;
     const uint8_t *tk = P.tile_tok + (int64_t)m * P.tok_stride + s0;
     // rows past the adapter's rank (zero padding) are neither read nor multiplied: their
     // fragments come from the zero block, and a block with no row below the rank skips the loop
@@ -1022,6 +1020,8 @@ struct ScArgs {
     const int32_t *tile_toff, *tile_gpre;
     const uint8_t *tile_tok;
     int tok_stride;
+    const int4 *tile_grp;
+    int grp_stride;
     const uint16_t *vcat;
     int64_t vcat_tile_elems;
     const int32_t *sc_tiles;
@@ -1040,32 +1040,19 @@ __device__ __forceinline__ int sc_slice(const SlotGeom &g, int n)
     return sg;
 }
 
-__device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int local)
+__device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int m, int local)
 {
     const SlotGeom &g = P.g;
     const int R = g.R;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, gq = lane >> 4;
-    const int m = P.sc_tiles[ord];
     const int gidx = local / P.n_chunks, nc = local - gidx * P.n_chunks;
     const int n0 = nc * SC_ROWS + wave * 64;
     if (n0 >= P.n_out)
         return;
     const int D = P.tile_D[m];
-    const int32_t *gp = P.tile_gpre + (int64_t)m * (P.list_stride + 1);
-    const int32_t *to = P.tile_toff + (int64_t)m * (P.list_stride + 1);
-    int lo = 0, hi = D - 1;                   // the adapter: last d with gp[d] <= gidx
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (gp[mid] <= gidx)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    const int d = lo;
-    const int a = P.tile_list[(int64_t)m * P.list_stride + d];
-    const int s0 = to[d] + 16 * (gidx - gp[d]);
-    const int ng = min(16, to[d + 1] - s0);
+    const int4 gr = P.tile_grp[(int64_t)m * P.grp_stride + gidx];   // {d, adapter, s0, tokens}
+    const int d = gr.x, a = gr.y, s0 = gr.z, ng = gr.w;
     const bool tok_ok = r < ng;
     const int tl = tok_ok ? P.tile_tok[(int64_t)m * P.tok_stride + s0 + r] : 0;
     const int t = m * PF_BM + tl;
@@ -1110,28 +1097,48 @@ __device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int loc
                 prt[f][e] = act && n + e < P.n_out ? po[n + e] : 0.f;
         }
     }
+    // B rows of the 4 row groups (lane row nb[f]) and their slices; a batch of 64 columns
+    // issues the V halves and all 4 groups' B fragments together, then its MFMAs.  Per group
+    // the sums run over (slice, column) in ascending order; a group outside the slice, rows
+    // past n_out and columns past the rank multiply zeros (B columns past the rank are zero).
+    int nb[4], sgb[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-        const int nf = n0 + f * 16;
-        if (nf >= P.n_out)
-            break;
-        const int nb = nf + r;                // this lane's B row
-        const int sg_lo = sc_slice(g, nf), sg_hi = sc_slice(g, min(nf + 15, P.n_out - 1));
-        const int sg_b = sc_slice(g, min(nb, P.n_out - 1));
-        for (int sg = sg_lo; sg <= sg_hi; ++sg) {
-            const bool row_ok = nb < P.n_out && sg_b == sg;
-            for (int k = 0; k < rk; k += 32) {          // B columns past the rank are zero
+        nb[f] = n0 + f * 16 + r;
+        sgb[f] = nb[f] < P.n_out ? sc_slice(g, nb[f]) : -1;
+    }
+    const int sg_lo = sc_slice(g, n0), sg_hi = sc_slice(g, min(n0 + 63, P.n_out - 1));
+    for (int sg = sg_lo; sg <= sg_hi; ++sg) {
+        for (int k0 = 0; k0 < rk; k0 += 64) {
+            u32x4 vh[2], vl[2], bv[4][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = k0 + h * 32;
                 const bool kok = k + gq * 8 < rk;
-                const u32x4 bv = *(const u32x4 *)(row_ok && kok ? (const void *)(brow0 + (int64_t)nb * R + k)
-                                                                : (const void *)pf_zero16);
                 const uint16_t *vp = vrow + sg * kxs + k;
-                const u32x4 vh = *(const u32x4 *)(tok_ok && kok ? (const void *)vp : (const void *)pf_zero16);
-                const u32x4 vl = *(const u32x4 *)(tok_ok && kok ? (const void *)(vp + R) : (const void *)pf_zero16);
-                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, bv), __builtin_bit_cast(bf16x8, vh), acc[f], 0, 0, 0);
-                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, bv), __builtin_bit_cast(bf16x8, vl), acc[f], 0, 0, 0);
+                vh[h] = *(const u32x4 *)(tok_ok && kok ? (const void *)vp : (const void *)pf_zero16);
+                vl[h] = *(const u32x4 *)(tok_ok && kok ? (const void *)(vp + R) : (const void *)pf_zero16);
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+                    bv[f][h] = *(const u32x4 *)(sgb[f] == sg && kok
+                                                    ? (const void *)(brow0 + (int64_t)nb[f] * R + k)
+                                                    : (const void *)pf_zero16);
             }
+            // all 12 loads in flight before the first MFMA (left alone, the compiler moves
+            // each load down to its MFMA)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, bv[f][h]), __builtin_bit_cast(bf16x8, vh[h]),
+                        acc[f], 0, 0, 0);
+                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, bv[f][h]), __builtin_bit_cast(bf16x8, vl[h]),
+                        acc[f], 0, 0, 0);
+                }
         }
     }
     if (!act)
@@ -1167,7 +1174,8 @@ __device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int loc
 
 __global__ __launch_bounds__(256) void sc_expand_kernel(ScArgs P)
 {
-    extern __shared__ int sc_pre[];           // [sc_cap + 1] item prefix over the scattered tiles
+    extern __shared__ int sc_pre[];           // [sc_cap] item prefix, then [sc_cap] tiles
+    int *sc_m = sc_pre + P.sc_cap;
     __shared__ int wsum[8];
     const int n_sc = P.sc_tiles[P.sc_cap];
     int base = 0;
@@ -1176,6 +1184,7 @@ __global__ __launch_bounds__(256) void sc_expand_kernel(ScArgs P)
         int cnt = 0;
         if (o < n_sc) {
             const int m = P.sc_tiles[o];
+            sc_m[o] = m;
             cnt = P.tile_gpre[(int64_t)m * (P.list_stride + 1) + P.tile_D[m]] * P.n_chunks;
         }
         int ex, all, u0, u1;
@@ -1195,7 +1204,7 @@ __global__ __launch_bounds__(256) void sc_expand_kernel(ScArgs P)
             else
                 hi = mid - 1;
         }
-        sc_expand_item(P, lo, item - sc_pre[lo]);
+        sc_expand_item(P, lo, sc_m[lo], item - sc_pre[lo]);
     }
 }
 
@@ -1212,6 +1221,7 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
     // fp32 sums of up to sc_cap scattered tiles, within 64 MiB (at least one tile)
     c.n_out = n_out;
     c.tok_stride = PF_BM * K;
+    c.grp_stride = PF_BM * K / 16 + c.list_stride;   // 16-token groups of a scattered tile
     c.sc_cap = (int)std::min<int64_t>(
         c.n_mtiles, std::max<int64_t>(1, (64ll << 20) / ((int64_t)PF_BM * n_out * 4)));
     // fp32 partial blocks of the dense shrink items: within 64 MiB, and no more than the most
@@ -1226,7 +1236,7 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
 // Workspace regions of the tiled path, each 256-byte aligned, in this order.
 struct PrefillLayout {
     size_t tile_D, tile_list, tile_toff, tile_gpre, tile_tok, tile_ord, sc_tiles, part_sc, vcat,
-        tile_pbase, sd_ks, sd_part, total;
+        tile_pbase, sd_ks, sd_part, tile_grp, total;
 };
 
 static size_t al256(size_t v) { return (v + 255) / 256 * 256; }
@@ -1248,7 +1258,8 @@ static PrefillLayout prefill_layout(const PrefillCfg &c)
     L.tile_pbase = L.vcat + al256((size_t)c.n_mtiles * c.vcat_tile_elems * sizeof(uint16_t));
     L.sd_ks = L.tile_pbase + al256((size_t)c.n_mtiles * sizeof(int32_t));
     L.sd_part = L.sd_ks + 256;
-    L.total = L.sd_part + (size_t)c.sd_cap_slots * SD_PART_ELEMS * sizeof(float);
+    L.tile_grp = L.sd_part + al256((size_t)c.sd_cap_slots * SD_PART_ELEMS * sizeof(float));
+    L.total = L.tile_grp + (size_t)c.n_mtiles * c.grp_stride * sizeof(int4);
     return L;
 }
 
@@ -1279,6 +1290,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     int32_t *tile_pbase = (int32_t *)(p + WL.tile_pbase);
     int32_t *sd_ks = (int32_t *)(p + WL.sd_ks);
     float *sd_part = (float *)(p + WL.sd_part);
+    int4 *tile_grp = (int4 *)(p + WL.tile_grp);
 
     if (g != nullptr && c.n_mtiles > SH_MAX_TILES)
         return hipErrorInvalidValue;   // callers split larger batches
@@ -1294,8 +1306,8 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         }
         hipLaunchKernelGGL(tile_plan_kernel, dim3(c.n_mtiles), dim3(256), lds, stream, idx,
                            (int)T, K, g->S, g->R, g->n_slices, (int)n_in, c.list_stride, tile_D,
-                           tile_list, tile_toff, tile_gpre, tile_tok, c.tok_stride, vcat,
-                           c.vcat_tile_elems);
+                           tile_list, tile_toff, tile_gpre, tile_tok, c.tok_stride, tile_grp,
+                           c.grp_stride, vcat, c.vcat_tile_elems);
         ShrinkArgs s{};
         s.x = x;
         s.T = (int)T;
@@ -1317,6 +1329,8 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         s.tile_gpre = tile_gpre;
         s.tile_tok = tile_tok;
         s.tok_stride = c.tok_stride;
+        s.tile_grp = tile_grp;
+        s.grp_stride = c.grp_stride;
         s.sd_part = sd_part;
         s.sd_cap_slots = c.sd_cap_slots;
         s.tile_pbase = tile_pbase;
@@ -1391,6 +1405,8 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         x2.tile_gpre = tile_gpre;
         x2.tile_tok = tile_tok;
         x2.tok_stride = c.tok_stride;
+        x2.tile_grp = tile_grp;
+        x2.grp_stride = c.grp_stride;
         x2.vcat = vcat;
         x2.vcat_tile_elems = c.vcat_tile_elems;
         x2.sc_tiles = sc_tiles;
@@ -1398,7 +1414,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         x2.n_chunks = (int)((n_out + SC_ROWS - 1) / SC_ROWS);
         x2.part_sc = part_sc;
         x2.y = y;
-        const size_t xl = ((size_t)c.sc_cap + 1) * sizeof(int32_t);
+        const size_t xl = (size_t)2 * c.sc_cap * sizeof(int32_t);
         // items per scattered tile: at most (256 K / 16 + list_stride) groups x n_chunks
         const int64_t items = (int64_t)c.sc_cap * (PF_BM * K / 16 + c.list_stride) * x2.n_chunks;
         const unsigned grid = (unsigned)std::min<int64_t>(items, 1024);
