@@ -273,6 +273,23 @@ def test_tiled_path_chunks_past_a_million_tokens(oracle_mod):
     assert tol_ok(y[toks], y_ref).all(), f"worst {worst(y[toks], y_ref):.3e}"
 
 
+def test_tiled_many_tiles_two_stage_shrink(oracle_mod):
+    """1821 tiles: the dense shrink items' LDS then holds two 48 KB stages (the tiles' item
+    tables take the rest), over three 64-column stages of n_in; tokens of the first, middle and
+    last tiles and the ragged end are checked against the oracle."""
+    from lora_serving_amd import mlora
+    T = 1820 * 256 + 77
+    L = synth.random_layer(72, T=T, n_in=192, n_out=96, S=6, R=16, K=2, p_sentinel=0.25,
+                           contiguous=True)
+    say(f"[two-stage] T={T} n_in={L.n_in}")
+    D = DevLayer(L)
+    y = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_TILED))
+    toks = np.unique(np.array([0, 1, 255, 256, 511, T // 2, T // 2 + 1, T - 78, T - 77, T - 2,
+                               T - 1] + list(range(333, T, 9973)), np.int64))
+    y_ref = oracle_mod.linear(L, tokens=toks)
+    assert tol_ok(y[toks], y_ref).all(), f"worst {worst(y[toks], y_ref):.3e}"
+
+
 def test_tiled_sentinel_rows_and_k3_invariance():
     from lora_serving_amd import mlora
     L1 = synth.random_layer(46, T=300, n_in=256, n_out=512, S=6, R=16, K=1, p_sentinel=0.3)
