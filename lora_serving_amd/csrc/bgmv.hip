@@ -7,26 +7,136 @@
 // and expand (y += v B).  The vLLM RFC on per-request composition (Proposed Change, step 4) runs
 // the K slots of a token inside one kernel pass, as both kernels here do.
 //
-// shrink: one workgroup (4 waves) per pair.  Lanes walk n_in in 16-byte chunks (A rows are
-//   read fully coalesced), keep 16 rank rows' partial dot products in registers, fold them
-//   with a wave "transpose reduction" (5 shuffle rounds leave every lane with one row's sum)
-//   and then across the 4 waves through LDS in a fixed order (deterministic).
+// shrink: one workgroup (4 waves) per (pair, block of RB rows of the pair's n_slices * R rows),
+//   RB = 16, 8 or 4 so that small batches still give every CU a workgroup.  Lanes walk n_in in
+//   16-byte chunks (A rows read fully coalesced), two chunks of loads issued before any is
+//   used, keep the RB rows' partial dot products in registers, fold them with a wave
+//   "transpose reduction" (every lane ends with one row's sum) and then across the 4 waves
+//   through LDS in a fixed order (deterministic).
 // expand: one workgroup per (token, block of output rows).  Lanes walk the contiguous
 //   B[a][rows][0..R) block 16 bytes at a time, so each lane holds 8 rank entries of one row;
 //   the R/8 lanes of a row finish the dot product with xor shuffles over the rank dimension.
-#include "bgmv_dev.h"
+#include "common.h"
+#include "kernels.h"
 
 namespace mlora {
 
-__global__ __launch_bounds__(256) void shrink_pairs_kernel(const uint16_t *__restrict__ x,
-                                                           int64_t T, int64_t n_in, SlotGeom g,
-                                                           const int32_t *__restrict__ idx,
-                                                           int32_t K,
-                                                           const float *__restrict__ scale,
-                                                           float *__restrict__ v)
+__device__ __forceinline__ float dot8_bf16(const u32x4 a, const float xf[8])
 {
-    __shared__ float red[64];
-    shrink_one_pair(x, T, n_in, g, idx, K, scale, v, blockIdx.x, red);
+    float s = 0.f;
+    s += bf16_lo(a.x) * xf[0];
+    s += bf16_hi(a.x) * xf[1];
+    s += bf16_lo(a.y) * xf[2];
+    s += bf16_hi(a.y) * xf[3];
+    s += bf16_lo(a.z) * xf[4];
+    s += bf16_hi(a.z) * xf[5];
+    s += bf16_lo(a.w) * xf[6];
+    s += bf16_hi(a.w) * xf[7];
+    return s;
+}
+
+// RB per-lane values -> every lane ends with the wave-wide sum of value number row_of(lane):
+// log2(RB) halving rounds (xor 32, 16, ...: a lane keeps the half its lane bit selects and adds
+// its partner's), then plain xor sums over the remaining lane bits.  row_of(lane) is read off
+// the lane bits 5, 4, ... used by the halving rounds.
+template <int RB>
+__device__ __forceinline__ float transpose_reduce(float (&acc)[RB])
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int half = RB / 2, bit = 5; half >= 1; half >>= 1, --bit) {
+        const bool hi = (lane >> bit) & 1;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const float keep = hi ? acc[half + i] : acc[i];
+            const float send = hi ? acc[i] : acc[half + i];
+            acc[i] = keep + __shfl_xor(send, 1 << bit, 64);
+        }
+    }
+    float r1 = acc[0];
+#pragma unroll
+    for (int bit = 5 - __builtin_ctz(RB); bit >= 0; --bit)
+        r1 += __shfl_xor(r1, 1 << bit, 64);
+    return r1;
+}
+
+template <int RB>
+__device__ __forceinline__ int transpose_row(int lane)
+{
+    int row = 0;
+#pragma unroll
+    for (int l = 0; (1 << l) < RB; ++l)
+        row = row * 2 + ((lane >> (5 - l)) & 1);
+    return row;
+}
+
+// Workgroup = (pair p, rows r0 .. r0 + RB - 1 of the pair's n_slices * R rows of v).
+template <int RB>
+__global__ __launch_bounds__(256) void shrink_rows_kernel(const uint16_t *__restrict__ x,
+                                                          int64_t T, int64_t n_in, SlotGeom g,
+                                                          const int32_t *__restrict__ idx,
+                                                          int32_t K,
+                                                          const float *__restrict__ scale,
+                                                          float *__restrict__ v)
+{
+    __shared__ float red[4 * RB];
+    const int wd = g.n_slices * g.R;
+    const int nrb = (wd + RB - 1) / RB;
+    const int64_t p = blockIdx.x / nrb;
+    const int r0 = (int)(blockIdx.x - p * nrb) * RB;
+    const int nr = min(RB, wd - r0);
+    const int64_t t = p / K;
+    const int j = (int)(p - t * K);
+    float *out = v + ((int64_t)j * T + t) * wd + r0;
+    const int a = idx[p];
+    if (a < 0) {
+        if ((int)threadIdx.x < nr)
+            out[threadIdx.x] = 0.f;
+        return;
+    }
+    const uint16_t *xt = x + t * n_in;
+    const uint16_t *Aa = g.A + ((int64_t)a * wd + r0) * n_in;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+
+    float acc[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+        acc[r] = 0.f;
+    // two 16-byte chunks per lane in flight: x and the RB rows of both, then their products
+    const int64_t step = (int64_t)blockDim.x * 8;
+    for (int64_t k0 = (int64_t)threadIdx.x * 8; k0 < n_in; k0 += 2 * step) {
+        u32x4 xv[2], av[2][RB];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t k = k0 + h * step;
+            const bool ok = k < n_in;
+            xv[h] = ok ? *(const u32x4 *)(xt + k) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+                av[h][r] = ok && r < nr ? *(const u32x4 *)(Aa + (int64_t)r * n_in + k)
+                                        : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float xf[8] = {bf16_lo(xv[h].x), bf16_hi(xv[h].x), bf16_lo(xv[h].y),
+                                 bf16_hi(xv[h].y), bf16_lo(xv[h].z), bf16_hi(xv[h].z),
+                                 bf16_lo(xv[h].w), bf16_hi(xv[h].w)};
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+                acc[r] += dot8_bf16(av[h][r], xf);
+        }
+    }
+    const float s = transpose_reduce<RB>(acc);
+    if ((lane & (64 / RB - 1)) == 0)
+        red[wave * RB + transpose_row<RB>(lane)] = s;
+    __syncthreads();
+    if ((int)threadIdx.x < nr) {
+        const int rr = threadIdx.x;
+        const float coef = (scale ? scale[p] : 1.f) * g.factor[a];
+        const float tot = ((red[rr] + red[RB + rr]) + red[2 * RB + rr]) + red[3 * RB + rr];
+        out[rr] = coef * tot;
+    }
 }
 
 hipError_t launch_shrink_pairs(const uint16_t *x, int64_t T, int64_t n_in, const SlotGeom &g,
@@ -36,8 +146,19 @@ hipError_t launch_shrink_pairs(const uint16_t *x, int64_t T, int64_t n_in, const
     const int64_t P = T * K;
     if (P == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(shrink_pairs_kernel, dim3((unsigned)P), dim3(256), 0, stream, x, T, n_in,
-                       g, idx, K, scale, v);
+    const int wd = g.n_slices * g.R;
+    // rows per workgroup: 16 while that already gives 256 workgroups, else fewer
+    const int RB = P * ((wd + 15) / 16) >= 256 ? 16 : P * ((wd + 7) / 8) >= 256 ? 8 : 4;
+    const unsigned grid = (unsigned)(P * ((wd + RB - 1) / RB));
+    if (RB == 16)
+        hipLaunchKernelGGL(shrink_rows_kernel<16>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
+                           g, idx, K, scale, v);
+    else if (RB == 8)
+        hipLaunchKernelGGL(shrink_rows_kernel<8>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
+                           g, idx, K, scale, v);
+    else
+        hipLaunchKernelGGL(shrink_rows_kernel<4>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
+                           g, idx, K, scale, v);
     return hipGetLastError();
 }
 
@@ -75,14 +196,8 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(
     const int r4 = threadIdx.x * 4;       // first of this thread's 4 output rows
     const bool vec = ((n_out & 3) == 0) && r4 + 3 < nrows;
 
-    bool any = false;
-    for (int j = 0; j < K; ++j)
-        any |= idx[t * K + j] >= 0;
-    if (!any && part == nullptr)
-        return;   // accumulate mode: rows with no adapter are left untouched
-
-    // base of this thread's rows: the first EXPAND_PQ partial loads are issued now and only
-    // summed at the end, so their latency overlaps the B loads
+    // base of this thread's rows, loaded first and only used at the end, so its latency
+    // overlaps the slot map and the B loads: the first EXPAND_PQ partials, or y itself
     constexpr int EXPAND_PQ = 8;
     float4 pq[EXPAND_PQ];
     const bool use_pq = part != nullptr && vec;
@@ -92,6 +207,16 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(
             if (sp < n_part)
                 pq[sp] = *(const float4 *)(part + ((int64_t)sp * T + t) * n_out + n0 + r4);
     }
+    const bool use_y = part == nullptr && vec;
+    u32x2 yv = {0u, 0u};
+    if (use_y)
+        yv = *(const u32x2 *)(y + t * n_out + n0 + r4);
+
+    bool any = false;
+    for (int j = 0; j < K; ++j)
+        any |= idx[t * K + j] >= 0;
+    if (!any && part == nullptr)
+        return;   // accumulate mode: rows with no adapter are left untouched
 
     for (int r = threadIdx.x; r < EXPAND_ROWS; r += blockDim.x)
         delta[r] = 0.f;
@@ -174,6 +299,11 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(
                 for (int q = 0; q < 4 && r4 + q < nrows; ++q)
                     base[q] += pp[q];
             }
+        } else if (use_y) {
+            base[0] = bf16_lo(yv.x);
+            base[1] = bf16_hi(yv.x);
+            base[2] = bf16_lo(yv.y);
+            base[3] = bf16_hi(yv.y);
         } else {
             const uint16_t *yy = y + t * n_out + n0 + r4;
             for (int q = 0; q < 4 && r4 + q < nrows; ++q)
