@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 METRIC = "multi-LoRA layer tokens/s + % HBM GB/s (decode) / % MFMA peak (prefill)"
+METRIC_BGMV = "BGMV shrink + expand tokens/s + % HBM GB/s (the standalone mlora_shrink / mlora_expand pair)"
 
 DESCRIPTIONS = {
     "tiny": "tiny: T=16, 256->256, 4 adapters rank 8 alpha 16, P(-1)=0.25, K=1",
@@ -69,7 +70,12 @@ def algorithmic(L):
             "decode_kernel_bytes": w_bytes + x_bytes + a_bytes + meta,
             "decode_kernel_flops": base_flops + shrink_flops,
             "tiled_kernel_bytes": w_bytes + x_bytes + y_bytes + b_bytes + meta,
-            "tiled_kernel_flops": base_flops + expand_flops}
+            "tiled_kernel_flops": base_flops + expand_flops,
+            # the standalone pair: shrink reads x and A, writes v; expand reads v, B and y and
+            # writes y (v is fp32 [K][T][n_slices R])
+            "shrink_bytes": x_bytes + a_bytes + L.K * L.T * L.n_slices * L.R * 4 + meta,
+            "expand_bytes": 2 * y_bytes + b_bytes + L.K * L.T * L.n_slices * L.R * 4 + meta,
+            "bgmv_flops": shrink_flops + expand_flops}
 
 
 def committed_traffic(kernel: str):
@@ -134,9 +140,10 @@ def measured_ceilings(roof):
             "gemm_shape": [m, m, m], "achieved_over_probe": roof["achieved"] / probe}
 
 
-def cpu_baseline(layers, budget_s: float):
+def cpu_baseline(layers, budget_s: float, with_base: bool = True):
     """The oracle, as it stands, on the host cores, on a bounded sample of the workload's
-    tokens (whole batches while they take under the budget), scaled to tokens/s."""
+    tokens (whole batches while they take under the budget), scaled to tokens/s; without the
+    base product for the shrink/expand pair."""
     import numpy as np
     import oracle
     oracle.build(force=False)
@@ -148,11 +155,11 @@ def cpu_baseline(layers, budget_s: float):
     while True:
         for L in layers:
             if L.T <= 128:
-                oracle.linear(L)
+                oracle.linear(L, with_base=with_base)
                 n_tok += L.T / len(layers)
             else:
                 toks = np.sort(rng.choice(L.T, size=32, replace=False))
-                oracle.linear(L, tokens=toks)
+                oracle.linear(L, tokens=toks, with_base=with_base)
                 n_tok += 32 / len(layers)
         rounds += 1
         el = time.perf_counter() - t0
@@ -186,6 +193,9 @@ def main():
                          "batches, where it is faster, row-major for the tiled path")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured copy-bandwidth and bf16 GEMM ceilings")
+    ap.add_argument("--op", default="linear", choices=["linear", "bgmv"],
+                    help="linear: mlora_linear (the whole layer); bgmv: the standalone pair "
+                         "mlora_shrink + mlora_expand (y += LoRA delta), per layer")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -200,7 +210,9 @@ def main():
     if not isinstance(layers, list):
         layers = [layers]
     decode_like = all(L.T <= 512 for L in layers)
-    if args.w_layout == "auto":
+    if args.op == "bgmv":
+        args.w_layout = "unused"                     # the pair reads no base weight
+    elif args.w_layout == "auto":
         args.w_layout = "packed" if decode_like else "rowmajor"
     steps = args.steps or (2000 if decode_like else 20)
     warmup = args.warmup if args.warmup >= 0 else (100 if decode_like else 3)
@@ -221,17 +233,24 @@ def main():
                 x, W, A, B = D.x.clone(), D.W.clone(), D.A.clone(), D.B.clone()
             slots = mlora.Slots(A, B, D.factor, slice_start=[int(v) for v in D.L.slice_start],
                                 rank=D.rank)
-            y = torch.empty((D.L.T, D.L.n_out), dtype=torch.bfloat16, device="cuda")
-            if args.w_layout == "packed":
+            y = torch.zeros((D.L.T, D.L.n_out), dtype=torch.bfloat16, device="cuda")
+            if args.w_layout == "packed" and args.op == "linear":
                 W = mlora.mlora_pack_weight(W)
-            one.append((x, W, slots, y, D))
+            v = (torch.empty((D.L.K, D.L.T, D.L.n_slices * D.L.R), dtype=torch.float32,
+                             device="cuda") if args.op == "bgmv" else None)
+            one.append((x, W, slots, y, D, v))
         sets.append(one)
 
     wflag = mlora.MLORA_W_PACKED if args.w_layout == "packed" else 0
 
     def step(i):
-        for (x, W, slots, y, D) in sets[i % nsets]:
-            mlora.mlora_linear(x, W, slots, D.idx, D.scale, y, flags=args.flags | wflag, ws=D.ws)
+        for (x, W, slots, y, D, v) in sets[i % nsets]:
+            if args.op == "bgmv":
+                mlora.mlora_shrink(x, slots, D.idx, D.scale, v, ws=D.ws)
+                mlora.mlora_expand(v, slots, D.idx, y)
+            else:
+                mlora.mlora_linear(x, W, slots, D.idx, D.scale, y, flags=args.flags | wflag,
+                                   ws=D.ws)
 
     if args.calibrate_copy:
         # a plain elementwise copy of known size, for scaling the HBM byte counters
@@ -257,7 +276,10 @@ def main():
     # Main product kernel: HIP events that the library records on the launch stream around
     # each of its launches, over a second timed region of the same length (the event pairs
     # add a few microseconds per launch, so the step time above is taken without them).
-    launches_per_step = sum((L.T + 511) // 512 if decode_like else 1 for L in layers)
+    if args.op == "bgmv":
+        launches_per_step = 2 * len(layers)          # shrink, expand
+    else:
+        launches_per_step = sum((L.T + 511) // 512 if decode_like else 1 for L in layers)
     cap = steps * launches_per_step
     torch.cuda.synchronize()
     mlora.mlora_trace_start(cap)
@@ -268,6 +290,9 @@ def main():
     if len(kernel_ms) != cap:
         raise RuntimeError(f"expected {cap} traced launches, got {len(kernel_ms)}")
     k_avg_ms = sum(kernel_ms) / len(kernel_ms)
+    if args.op == "bgmv":
+        sh_ms = sum(kernel_ms[0::2]) / len(kernel_ms[0::2])
+        ex_ms = sum(kernel_ms[1::2]) / len(kernel_ms[1::2])
     # single-call latency: one input set, each call waited for (no rotation, launch included)
     lat = []
     for i in range(50 if decode_like else 5):
@@ -280,7 +305,26 @@ def main():
     tokens_per_s = T / (ms * 1e-3)
     tot_bytes = sum(a["bytes"] for a in algs)
     tot_flops = sum(a["flops"] for a in algs)
-    if decode_like:
+    if args.op == "bgmv":
+        # the pair's two kernels; the roofline object describes the longer one
+        sh_b = sum(a["shrink_bytes"] for a in algs) / len(layers)
+        ex_b = sum(a["expand_bytes"] for a in algs) / len(layers)
+        kern = [("mlora::shrink_rows_kernel (mlora_shrink)", sh_ms, sh_b),
+                ("mlora::expand_tokens_kernel (mlora_expand)", ex_ms, ex_b)]
+        kern.sort(key=lambda k: -k[1])
+        kname, k_avg_ms, k_bytes = kern[0]
+        achieved = k_bytes / (k_avg_ms * 1e-3) / 1e9
+        tot_bytes = sh_b * len(layers) + ex_b * len(layers)
+        tot_flops = sum(a["bgmv_flops"] for a in algs)
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                "kernel": kname, "kernel_avg_us": k_avg_ms * 1e3,
+                "algorithmic_bytes_per_launch": k_bytes,
+                "other_kernel": {"kernel": kern[1][0], "kernel_avg_us": kern[1][1] * 1e3,
+                                 "algorithmic_bytes_per_launch": kern[1][2],
+                                 "achieved_GBps": kern[1][2] / (kern[1][1] * 1e-3) / 1e9},
+                "step_achieved_GBps": tot_bytes / (ms * 1e-3) / 1e9}
+    elif decode_like:
         kname = "mlora::decode_gemm_kernel (base product + LoRA shrink)"
         k_bytes = sum(a["decode_kernel_bytes"] for a in algs) / launches_per_step
         achieved = k_bytes / (k_avg_ms * 1e-3) / 1e9
@@ -300,7 +344,7 @@ def main():
                 "algorithmic_flops_per_launch": k_flops,
                 "step_achieved_TFLOPs": tot_flops / (ms * 1e-3) / 1e12}
     out = {
-        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC_BGMV if args.op == "bgmv" else METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; random bf16 weights and adapters)",
@@ -308,7 +352,7 @@ def main():
                    "layers": [[L.n_in, L.n_out] for L in layers], "S": layers[0].S,
                    "R": layers[0].R, "K": layers[0].K,
                    "distinct_adapters": [a["distinct_adapters"] for a in algs],
-                   "rotating_sets": nsets, "w_layout": args.w_layout},
+                   "rotating_sets": nsets, "w_layout": args.w_layout, "op": args.op},
         "roofline": roof,
         "step_algorithmic": {"bytes": tot_bytes, "flops": tot_flops},
     }
@@ -316,7 +360,8 @@ def main():
     if not args.no_probes:
         out["probes"] = measured_ceilings(roof)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds,
+                                           with_base=args.op == "linear")
     print(json.dumps(out), flush=True)
 
 

@@ -374,8 +374,11 @@ mlora_status mlora_shrink(const void *x, int64_t T, int64_t n_in, const mlora_sl
         return MLORA_OK;
     if (x == nullptr || idx == nullptr || v == nullptr || !aligned16(x) || !aligned16(v))
         return MLORA_ERR_ARG;
-    return hip_status(launch_shrink_pairs((const uint16_t *)x, T, n_in, g, idx, K, scale, v,
-                                          stream));
+    trace_mark(stream, true);
+    const hipError_t e = launch_shrink_pairs((const uint16_t *)x, T, n_in, g, idx, K, scale, v,
+                                             stream);
+    trace_mark(stream, false);
+    return hip_status(e);
 }
 
 mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_slots *slots,
@@ -391,8 +394,11 @@ mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_
         return MLORA_OK;
     if (v == nullptr || idx == nullptr || y == nullptr || !aligned16(v) || !aligned16(y))
         return MLORA_ERR_ARG;
-    return hip_status(launch_expand_tokens(v, 1, 0, nullptr, T, n_out, g, idx, K, nullptr, 0,
-                                           (uint16_t *)y, stream));
+    trace_mark(stream, true);
+    const hipError_t e = launch_expand_tokens(v, 1, 0, nullptr, T, n_out, g, idx, K, nullptr, 0,
+                                              (uint16_t *)y, stream);
+    trace_mark(stream, false);
+    return hip_status(e);
 }
 
 mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in, int64_t n_out,
