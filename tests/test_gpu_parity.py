@@ -360,6 +360,38 @@ def test_large_workloads_sampled(oracle_mod, which):
         check_linear(oracle_mod, L, tokens=toks, label=f"{which}:{L.name}")
 
 
+@pytest.mark.parametrize("which", ["decode", "decode256", "lm_head", "mixed_qkv", "prefill",
+                                   "compose"])
+def test_workloads_in_bench_configuration(oracle_mod, which):
+    """Each bench workload called the way bench.py calls it: the slots carry the true-rank
+    table, decode-sized batches (T <= 512) take the packed base weight.  Whole output for the
+    decode batches, sampled tokens (segment edges and random ones) for the large ones."""
+    import torch
+    from lora_serving_amd import mlora
+    layers = synth.WORKLOADS[which]()
+    if not isinstance(layers, list):
+        layers = [layers]
+    packed = all(L.T <= 512 for L in layers)
+    for L in layers:
+        say(f"[bench-config] {which}:{L.name} T={L.T} n_in={L.n_in} n_out={L.n_out} "
+            f"packed={packed}")
+        D = DevLayer(L)
+        slots = mlora.Slots(D.A, D.B, D.factor, slice_start=[int(v) for v in L.slice_start],
+                            rank=D.rank)
+        W = mlora.mlora_pack_weight(D.W) if packed else D.W
+        y = torch.empty((L.T, L.n_out), dtype=torch.bfloat16, device="cuda")
+        mlora.mlora_linear(D.x, W, slots, D.idx, D.scale, y,
+                           flags=mlora.MLORA_W_PACKED if packed else 0, ws=D.ws)
+        yy = from_dev_bf16(y)
+        toks = None if L.T <= 512 and L.n_out <= 8192 else _sample_tokens(L)
+        y_ref = oracle_mod.linear(L, tokens=toks)
+        if toks is not None:
+            yy = yy[toks]
+        ok = tol_ok(yy, y_ref)
+        assert ok.all(), f"{which}: worst {worst(yy, y_ref):.3e}, {np.sum(~ok)} elements out"
+        del D, slots, W, y
+
+
 # ------------------------------------------------------------------------------------------
 # invariants
 # ------------------------------------------------------------------------------------------
