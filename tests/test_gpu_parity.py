@@ -337,16 +337,18 @@ def test_decode_workload_full(oracle_mod):
     check_delta(oracle_mod, L, D, label="decode")
 
 
-def _sample_tokens(L, n=48, seed=0):
+def _sample_tokens(L, n=1024, seed=0):
+    """At least n tokens (all of them when T <= n): the first and last token of every
+    segment, plus seeded random ones.  Tokens are independent, so each is checked exactly."""
     rng = np.random.default_rng(seed)
+    if L.T <= n:
+        return np.arange(L.T, dtype=np.int64)
     edges = set()
     for first, length in L.segments:
         edges.add(first)
         edges.add(first + length - 1)
-    edges = sorted(edges)
-    extra = rng.choice(L.T, size=min(n, L.T), replace=False)
-    toks = sorted(set(edges[:: max(1, len(edges) // n)]) | set(int(e) for e in extra)
-                  | {0, L.T - 1})
+    extra = rng.choice(L.T, size=n, replace=False)
+    toks = sorted(edges | set(int(e) for e in extra) | {0, L.T - 1})
     return np.array(toks, np.int64)
 
 
