@@ -63,7 +63,12 @@ __device__ __forceinline__ void df_vload(const float *upart, int sk, int64_t pst
     fa = *(a >= 0 ? factor + a : df_zero);
 }
 
-template <bool MC>
+// RC > 0 (slot width R = RC in {8, 16, 32}): the 16 lanes of a token read its adapter's 64-row
+// B block (contiguous, 128 R bytes) as consecutive 16-byte pieces, 256 bytes per instruction
+// (whole cache lines): piece c = g4 + 16 k is row c / (R / 8), columns 8 (c % (R / 8)) .. +8.
+// The R / 8 lanes holding one row add their parts with lane shuffles, and the rows' sums reach
+// the thread that stores them through LDS.  RC = 0: each thread reads its own 4 rows (any R).
+template <bool MC, int RC>
 __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
     const float *__restrict__ part, int sk, int n_tiles, const float *__restrict__ upart,
     const float *__restrict__ scale, int T_all, int n_out, SlotGeom g,
@@ -130,14 +135,45 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
         const bool pre = R <= DF_BPRE_R;
         const int a0 = tl < nt ? sidx[tl * K] : -1;
         u32x4 bp[4][DF_BPRE_R / 8];
+        // RC > 0: this lane's B pieces (rows crow(k), part cpart), their slices and sums
+        constexpr int CP = RC > 0 ? RC / 8 : 1;          // 16-byte parts of a row
+        constexpr int CN = RC > 0 ? RC / 2 : 1;          // pieces (rows) per lane
+        const int cpart = g4 % CP;
+        auto crow = [&](int k) { return g4 / CP + (16 / CP) * k; };
+        u32x4 bq[CN];
+        int csg[CN];
+        float cacc[CN];
+        auto cload = [&](int a) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint16_t *brow = g.B + ((int64_t)max(a0, 0) * n_out + min(n + i, n_out - 1)) * R;
+            for (int k = 0; k < CN; ++k) {
+                const int nn = row0 + crow(k);
+                bq[k] = *(const u32x4 *)(a >= 0 && nn < n_out
+                                             ? (const void *)(g.B + ((int64_t)a * n_out + nn) * RC +
+                                                              cpart * 8)
+                                             : (const void *)df_zero);
+            }
+        };
+        if constexpr (RC > 0) {
 #pragma unroll
-            for (int u = 0; u < DF_BPRE_R / 8; ++u)
-                bp[i][u] = *(const u32x4 *)((pre && a0 >= 0 && u * 8 < R)
-                                                ? (const void *)(brow + u * 8)
-                                                : (const void *)df_zero);
+            for (int k = 0; k < CN; ++k) {
+                const int ni = min(row0 + crow(k), n_out - 1);
+                int sg = 0;
+                while (sg + 1 < g.n_slices && ni >= g.slice_start[sg + 1])
+                    ++sg;
+                csg[k] = sg;
+                cacc[k] = 0.f;
+            }
+            cload(a0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint16_t *brow = g.B + ((int64_t)max(a0, 0) * n_out + min(n + i, n_out - 1)) * R;
+#pragma unroll
+                for (int u = 0; u < DF_BPRE_R / 8; ++u)
+                    bp[i][u] = *(const u32x4 *)((pre && a0 >= 0 && u * 8 < R)
+                                                    ? (const void *)(brow + u * 8)
+                                                    : (const void *)df_zero);
+            }
         }
         const int nv = nt * R;                     // a multiple of 8
         const int e0 = threadIdx.x * 4;
@@ -182,6 +218,23 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
                 }
                 lds_barrier();
                 const int a = tl < nt ? sidx[tl * K + j] : -1;
+                if constexpr (RC > 0) {
+                    if (j > 0 && sg == 0)
+                        cload(a);                  // this slot's pieces (slot 0's are in)
+                    if (a < 0)
+                        continue;
+                    const float *vv = vl + tl * RC + cpart * 8;
+#pragma unroll
+                    for (int k = 0; k < CN; ++k) {
+                        float sp = csg[k] == sg ? dot8(bq[k], vv) : 0.f;
+                        if constexpr (CP >= 2)
+                            sp += __shfl_xor(sp, 1, 64);
+                        if constexpr (CP >= 4)
+                            sp += __shfl_xor(sp, 2, 64);
+                        cacc[k] += sp;
+                    }
+                    continue;
+                }
                 if (a < 0)
                     continue;
                 const float *vv = vl + tl * R;
@@ -203,6 +256,19 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
                     d4[i] += dj;
                 }
             }
+        }
+        if constexpr (RC > 0) {
+            // the rows' sums to the threads that store them (4 consecutive rows each)
+            __shared__ float dl[DF_TOK * DF_ROWS];
+            if (cpart == 0) {
+#pragma unroll
+                for (int k = 0; k < CN; ++k)
+                    dl[tl * DF_ROWS + crow(k)] = cacc[k];
+            }
+            lds_barrier();
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                d4[i] = dl[tl * DF_ROWS + g4 * 4 + i];
         }
     }
 
@@ -251,12 +317,25 @@ hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, 
     const int64_t n_chunks = (T + DF_CHUNK - 1) / DF_CHUNK;
     const unsigned grid =
         (unsigned)(n_chunks * n_tiles * ((std::min<int64_t>(T, DF_CHUNK) + DF_TOK - 1) / DF_TOK));
-    if (n_chunks > 1)
-        hipLaunchKernelGGL(decode_finish_kernel<true>, dim3(grid), dim3(DF_THREADS), lds, stream,
-                           part, sk, n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y);
-    else
-        hipLaunchKernelGGL(decode_finish_kernel<false>, dim3(grid), dim3(DF_THREADS), lds, stream,
-                           part, sk, n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y);
+    const int rc = upart != nullptr && (gg.R == 8 || gg.R == 16 || gg.R == 32) ? gg.R : 0;
+    const bool mc = n_chunks > 1;
+#define DF_LAUNCH(M, C)                                                                            \
+    hipLaunchKernelGGL((decode_finish_kernel<M, C>), dim3(grid), dim3(DF_THREADS), lds, stream,  \
+                       part, sk, n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y)
+    switch (rc * 2 + (mc ? 1 : 0)) {
+    case 16: DF_LAUNCH(false, 8); break;
+    case 17: DF_LAUNCH(true, 8); break;
+    case 32: DF_LAUNCH(false, 16); break;
+    case 33: DF_LAUNCH(true, 16); break;
+    case 64: DF_LAUNCH(false, 32); break;
+    case 65: DF_LAUNCH(true, 32); break;
+    default:
+        if (mc)
+            DF_LAUNCH(true, 0);
+        else
+            DF_LAUNCH(false, 0);
+    }
+#undef DF_LAUNCH
     return hipGetLastError();
 }
 
