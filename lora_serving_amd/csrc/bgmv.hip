@@ -8,11 +8,11 @@
 // the K slots of a token inside one kernel pass, as both kernels here do.
 //
 // shrink: one workgroup (4 waves) per (pair, block of RB rows of the pair's n_slices * R rows),
-//   RB = 16, 8 or 4 so that small batches still give every CU a workgroup.  Lanes walk n_in in
-//   16-byte chunks (A rows read fully coalesced), two chunks of loads issued before any is
-//   used, keep the RB rows' partial dot products in registers, fold them with a wave
-//   "transpose reduction" (every lane ends with one row's sum) and then across the 4 waves
-//   through LDS in a fixed order (deterministic).
+//   RB = 16, 8, 4, 2 or 1 so that small batches still spread over many workgroups.  Lanes
+//   walk n_in in 16-byte chunks (A rows read fully coalesced), two chunks of loads issued
+//   before any is used, keep the RB rows' partial dot products in registers, fold them with a
+//   wave "transpose reduction" (every lane ends with one row's sum) and then across the 4
+//   waves through LDS in a fixed order (deterministic).
 // expand: one workgroup per (token, block of output rows).  Lanes walk the contiguous
 //   B[a][rows][0..R) block 16 bytes at a time, so each lane holds 8 rank entries of one row;
 //   the R/8 lanes of a row finish the dot product with xor shuffles over the rank dimension.
@@ -147,23 +147,42 @@ hipError_t launch_shrink_pairs(const uint16_t *x, int64_t T, int64_t n_in, const
     if (P == 0)
         return hipSuccess;
     const int wd = g.n_slices * g.R;
-    // rows per workgroup: 16 while that already gives 256 workgroups, else fewer
-    const int RB = P * ((wd + 15) / 16) >= 256 ? 16 : P * ((wd + 7) / 8) >= 256 ? 8 : 4;
+    // rows per workgroup: the most (16, 8, 4, 2, 1) that still gives SHRINK_MIN_WG workgroups,
+    // so small batches spread over many more workgroups than the chip has CUs
+    constexpr int64_t SHRINK_MIN_WG = 2048;
+    int RB = 16;
+    while (RB > 1 && P * ((wd + RB - 1) / RB) < SHRINK_MIN_WG)
+        RB >>= 1;
     const unsigned grid = (unsigned)(P * ((wd + RB - 1) / RB));
-    if (RB == 16)
+    switch (RB) {
+    case 16:
         hipLaunchKernelGGL(shrink_rows_kernel<16>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
                            g, idx, K, scale, v);
-    else if (RB == 8)
+        break;
+    case 8:
         hipLaunchKernelGGL(shrink_rows_kernel<8>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
                            g, idx, K, scale, v);
-    else
+        break;
+    case 4:
         hipLaunchKernelGGL(shrink_rows_kernel<4>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
                            g, idx, K, scale, v);
+        break;
+    case 2:
+        hipLaunchKernelGGL(shrink_rows_kernel<2>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
+                           g, idx, K, scale, v);
+        break;
+    default:
+        hipLaunchKernelGGL(shrink_rows_kernel<1>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
+                           g, idx, K, scale, v);
+        break;
+    }
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------
-constexpr int EXPAND_ROWS = 1024;   // output rows per workgroup (256 threads x 4)
+// output rows per workgroup: 1024 (256 threads x 4), or 256 when that leaves too few
+// workgroups for the chip (small batches)
+constexpr int EXPAND_MIN_WG = 1024;
 constexpr int EXPAND_GROUP = 8;     // 16-byte B loads a thread keeps in flight
 
 __device__ __forceinline__ int slice_of(const SlotGeom &g, int64_t n)
@@ -174,21 +193,22 @@ __device__ __forceinline__ int slice_of(const SlotGeom &g, int64_t n)
     return s;
 }
 
-// One workgroup per (token, block of EXPAND_ROWS output rows).
+// One workgroup per (token, block of ER output rows).
 //   v_j = coef_j * sum_{s < n_vsplit} vsrc[s][j][t][:]   (coef_j = scale*factor, or 1)
 //   delta[n] = sum_j sum_rho B[a_j][n][rho] v_j[slice(n)*R + rho]
 //   y[t][n] = bf16(base[n] + delta[n]),  base = sum of n_part fp32 partials, or y itself
+template <int ER>
 __global__ __launch_bounds__(256) void expand_tokens_kernel(
     const float *__restrict__ vsrc, int n_vsplit, int apply_coef, const float *__restrict__ scale,
     int64_t T, int64_t n_out, SlotGeom g, const int32_t *__restrict__ idx, int32_t K,
     const float *__restrict__ part, int32_t n_part, uint16_t *__restrict__ y)
 {
-    __shared__ float delta[EXPAND_ROWS];
+    __shared__ float delta[ER];
     __shared__ float vs[MLORA_MAX_SLICES_DEV * MLORA_MAX_RANK_DEV];
-    const int64_t nblk = (n_out + EXPAND_ROWS - 1) / EXPAND_ROWS;
+    const int64_t nblk = (n_out + ER - 1) / ER;
     const int64_t t = blockIdx.x / nblk;
-    const int64_t n0 = (blockIdx.x - t * nblk) * EXPAND_ROWS;
-    const int nrows = (int)min((int64_t)EXPAND_ROWS, n_out - n0);
+    const int64_t n0 = (blockIdx.x - t * nblk) * ER;
+    const int nrows = (int)min((int64_t)ER, n_out - n0);
     const int R = g.R;
     const int wd = g.n_slices * R;
     const int G = R >> 3;                 // lanes per output row (a power of two <= 64)
@@ -218,8 +238,12 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(
     if (!any && part == nullptr)
         return;   // accumulate mode: rows with no adapter are left untouched
 
-    for (int r = threadIdx.x; r < EXPAND_ROWS; r += blockDim.x)
-        delta[r] = 0.f;
+    // the first slot with an adapter stores its row sums, later ones add theirs (a row's sum
+    // is always written by the same thread); with no adapter at all delta stays zero
+    if (!any)
+        for (int r = threadIdx.x; r < ER; r += blockDim.x)
+            delta[r] = 0.f;
+    bool first = true;
 
     const int64_t total = (int64_t)nrows * R;          // bf16 elements of one B block
     const int64_t step = (int64_t)blockDim.x * 8;
@@ -268,10 +292,11 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(
                 for (int off = 1; off < G; off <<= 1)
                     ps += __shfl_xor(ps, off, 64);
                 if (e < total && (lane & (G - 1)) == 0)
-                    delta[row] += ps;
+                    delta[row] = first ? ps : delta[row] + ps;
             }
         }
-        lds_barrier();   // delta and vs are complete for this slot
+        first = false;
+        lds_barrier();   // vs is free again for the next slot
     }
     lds_barrier();
 
@@ -328,9 +353,17 @@ hipError_t launch_expand_tokens(const float *vsrc, int n_vsplit, int apply_coef,
 {
     if (T == 0 || n_out == 0)
         return hipSuccess;
-    const int64_t nblk = (n_out + EXPAND_ROWS - 1) / EXPAND_ROWS;
-    hipLaunchKernelGGL(expand_tokens_kernel, dim3((unsigned)(T * nblk)), dim3(256), 0, stream,
-                       vsrc, n_vsplit, apply_coef, scale, T, n_out, g, idx, K, part, n_part, y);
+    if (T * ((n_out + 1023) / 1024) >= EXPAND_MIN_WG) {
+        const int64_t nblk = (n_out + 1023) / 1024;
+        hipLaunchKernelGGL(expand_tokens_kernel<1024>, dim3((unsigned)(T * nblk)), dim3(256), 0,
+                           stream, vsrc, n_vsplit, apply_coef, scale, T, n_out, g, idx, K, part,
+                           n_part, y);
+    } else {
+        const int64_t nblk = (n_out + 255) / 256;
+        hipLaunchKernelGGL(expand_tokens_kernel<256>, dim3((unsigned)(T * nblk)), dim3(256), 0,
+                           stream, vsrc, n_vsplit, apply_coef, scale, T, n_out, g, idx, K, part,
+                           n_part, y);
+    }
     return hipGetLastError();
 }
 

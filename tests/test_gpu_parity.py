@@ -325,6 +325,44 @@ def test_shrink_matches_oracle(oracle_mod):
                 assert np.all(v[j, t] == 0)
 
 
+@pytest.mark.parametrize("T,K", [(1100, 1), (800, 1), (400, 1), (150, 2), (100, 1), (1, 3)])
+def test_shrink_every_row_block(oracle_mod, T, K):
+    """The standalone shrink takes the most rows of v per workgroup (16, 8, 4, 2, 1) that still
+    give 2048 workgroups; with 24 rows per pair (3 slices of rank 8) these pair counts reach
+    each choice in turn, 16 rows with a ragged last block.  n_in = 2056 leaves one 8-element
+    chunk past the lanes' first two passes."""
+    L = synth.random_layer(71 + T, T=T, n_in=2056, n_out=48, S=5, R=8, K=K,
+                           slice_sizes=[16, 16, 16], p_sentinel=0.2)
+    say(f"[shrink-rb] T={T} K={K}")
+    v = DevLayer(L).shrink().cpu().numpy().astype(np.float64)
+    v_ref = oracle_mod.shrink(L)
+    scale = np.abs(v_ref).max()
+    assert np.all(np.abs(v - v_ref) <= 1e-4 * (scale + np.abs(v_ref)))
+    for j in range(L.K):
+        assert np.all(v[j][L.idx[:, j] == -1] == 0)
+
+
+@pytest.mark.parametrize("T,n_out,K", [(300, 4100, 2), (40, 1030, 3), (1, 4096, 1)])
+def test_expand_both_row_blocks(oracle_mod, T, n_out, K):
+    """The standalone expand covers 1024 output rows per workgroup when that gives at least
+    1024 workgroups (T = 300 here, with a 4-row last block), else 256 (the others; 1030 rows
+    is not a multiple of 4, so the last rows go one at a time).  Slots without an adapter sit
+    before and between used ones, so the first slot to store is not always slot 0."""
+    L = synth.random_layer(90 + T, T=T, n_in=512, n_out=n_out, S=6, R=16, K=K,
+                           p_sentinel=0.35)
+    check_delta(oracle_mod, L, label=f"expand T={T} n_out={n_out} K={K}")
+    # accumulate mode: rows whose slots are all empty keep y's bits
+    import torch
+    from lora_serving_amd import mlora
+    D = DevLayer(L)
+    v = D.shrink()
+    y0 = torch.randn((L.T, L.n_out), device=D.device).to(torch.bfloat16)
+    y = y0.clone()
+    mlora.mlora_expand(v, D.slots, D.idx, y)
+    empty = torch.as_tensor(np.where((L.idx == -1).all(axis=1))[0], device=D.device)
+    assert torch.equal(y[empty].view(torch.int16), y0[empty].view(torch.int16))
+
+
 def test_tiny_workload(oracle_mod):
     L = synth.workload_tiny()
     D, _ = check_linear(oracle_mod, L, label="tiny")
