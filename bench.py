@@ -29,6 +29,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 METRIC = "multi-LoRA layer tokens/s + % HBM GB/s (decode) / % MFMA peak (prefill)"
 METRIC_BGMV = "BGMV shrink + expand tokens/s + % HBM GB/s (the standalone mlora_shrink / mlora_expand pair)"
+METRIC_PLAN = "mapping plan tokens/s + % HBM GB/s (mlora_plan: stable sort of the (token, slot) pairs by slot)"
 
 DESCRIPTIONS = {
     "tiny": "tiny: T=16, 256->256, 4 adapters rank 8 alpha 16, P(-1)=0.25, K=1",
@@ -175,6 +176,24 @@ def cpu_baseline(layers, budget_s: float, with_base: bool = True):
                       f"{total_tokens:.0f} per step, {el:.1f} s, fp64 oracle, OpenMP over tokens)"}
 
 
+def cpu_baseline_plan(L, budget_s: float):
+    """The oracle's plan (a plain stable counting sort in C, one thread) on the host, repeated
+    on the batch's whole index map until the budget is spent, scaled to tokens/s."""
+    import oracle
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    rounds = 0
+    while True:
+        oracle.plan(L.idx, L.S)
+        rounds += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": rounds * L.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rounds} plans of the whole index map ({L.T} tokens x {L.K} slots, "
+                      f"{el:.1f} s, one thread)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,9 +212,10 @@ def main():
                          "batches, where it is faster, row-major for the tiled path")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured copy-bandwidth and bf16 GEMM ceilings")
-    ap.add_argument("--op", default="linear", choices=["linear", "bgmv"],
+    ap.add_argument("--op", default="linear", choices=["linear", "bgmv", "plan"],
                     help="linear: mlora_linear (the whole layer); bgmv: the standalone pair "
-                         "mlora_shrink + mlora_expand (y += LoRA delta), per layer")
+                         "mlora_shrink + mlora_expand (y += LoRA delta), per layer; plan: "
+                         "mlora_plan on the batch's index map (shared by its layers)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -210,8 +230,8 @@ def main():
     if not isinstance(layers, list):
         layers = [layers]
     decode_like = all(L.T <= 512 for L in layers)
-    if args.op == "bgmv":
-        args.w_layout = "unused"                     # the pair reads no base weight
+    if args.op in ("bgmv", "plan"):
+        args.w_layout = "unused"                     # neither reads the base weight
     elif args.w_layout == "auto":
         args.w_layout = "packed" if decode_like else "rowmajor"
     steps = args.steps or (2000 if decode_like else 20)
@@ -223,6 +243,12 @@ def main():
     per_set = sum((D.x.numel() + D.W.numel() + D.A.numel() + D.B.numel()) * 2 +
                   D.L.T * D.L.n_out * 2 for D in devs)
     nsets = args.sets or (max(2, -(-600 * 2 ** 20 // per_set)) if per_set < 256 * 2 ** 20 else 1)
+    if args.op == "plan":
+        nsets = 1                                    # reads only the index map
+        L0 = layers[0]
+        P0 = L0.T * L0.K
+        i32 = lambda n: torch.empty((max(n, 1),), dtype=torch.int32, device="cuda")
+        plan_out = (i32(P0), i32(L0.S), i32(L0.S), i32(L0.S), i32(2))
     sets = []
     for i in range(nsets):
         one = []
@@ -245,7 +271,10 @@ def main():
 
     def step(i):
         for (x, W, slots, y, D, v) in sets[i % nsets]:
-            if args.op == "bgmv":
+            if args.op == "plan":
+                mlora.mlora_plan(D.idx, D.L.S, *plan_out, D.ws)
+                break                                # one plan per batch
+            elif args.op == "bgmv":
                 mlora.mlora_shrink(x, slots, D.idx, D.scale, v, ws=D.ws)
                 mlora.mlora_expand(v, slots, D.idx, y)
             else:
@@ -276,7 +305,9 @@ def main():
     # Main product kernel: HIP events that the library records on the launch stream around
     # each of its launches, over a second timed region of the same length (the event pairs
     # add a few microseconds per launch, so the step time above is taken without them).
-    if args.op == "bgmv":
+    if args.op == "plan":
+        launches_per_step = 1                        # the three sort kernels, traced as one
+    elif args.op == "bgmv":
         launches_per_step = 2 * len(layers)          # shrink, expand
     else:
         launches_per_step = sum((L.T + 511) // 512 if decode_like else 1 for L in layers)
@@ -305,7 +336,22 @@ def main():
     tokens_per_s = T / (ms * 1e-3)
     tot_bytes = sum(a["bytes"] for a in algs)
     tot_flops = sum(a["flops"] for a in algs)
-    if args.op == "bgmv":
+    if args.op == "plan":
+        # bytes the sort must move: idx read, perm written, segment table and counts written
+        import numpy as np
+        L0 = layers[0]
+        n_used = int(np.count_nonzero(L0.idx >= 0))
+        n_seg = int(len(np.unique(L0.idx[L0.idx >= 0])))
+        k_bytes = 4.0 * L0.T * L0.K + 4.0 * n_used + 12.0 * n_seg + 8.0
+        achieved = k_bytes / (k_avg_ms * 1e-3) / 1e9
+        tot_bytes, tot_flops = k_bytes, 0.0
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                "kernel": "mlora_plan (sort_count + sort_scan + sort_scatter, one region)",
+                "kernel_avg_us": k_avg_ms * 1e3, "algorithmic_bytes_per_launch": k_bytes,
+                "pairs": L0.T * L0.K, "used_pairs": n_used, "segments": n_seg,
+                "step_achieved_GBps": tot_bytes / (ms * 1e-3) / 1e9}
+    elif args.op == "bgmv":
         # the pair's two kernels; the roofline object describes the longer one
         sh_b = sum(a["shrink_bytes"] for a in algs) / len(layers)
         ex_b = sum(a["expand_bytes"] for a in algs) / len(layers)
@@ -344,7 +390,8 @@ def main():
                 "algorithmic_flops_per_launch": k_flops,
                 "step_achieved_TFLOPs": tot_flops / (ms * 1e-3) / 1e12}
     out = {
-        "metric": METRIC_BGMV if args.op == "bgmv" else METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "metric": {"bgmv": METRIC_BGMV, "plan": METRIC_PLAN}.get(args.op, METRIC),
+        "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; random bf16 weights and adapters)",
@@ -360,8 +407,11 @@ def main():
     if not args.no_probes:
         out["probes"] = measured_ceilings(roof)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds,
-                                           with_base=args.op == "linear")
+        if args.op == "plan":
+            out["cpu_baseline"] = cpu_baseline_plan(layers[0], args.cpu_seconds)
+        else:
+            out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds,
+                                               with_base=args.op == "linear")
     print(json.dumps(out), flush=True)
 
 

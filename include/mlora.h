@@ -229,8 +229,9 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
  * Profiling hook (not part of the computation).  mlora_trace_start creates 2*capacity HIP
  * events (no device memory); from then on every mlora_linear call records one event on its
  * stream right before and one right after each launch of its main product kernel (the decode
- * GEMM or the tiled GEMM), and every mlora_shrink / mlora_expand call around its one kernel,
- * for the first `capacity` launches.
+ * GEMM or the tiled GEMM), every mlora_shrink / mlora_expand call around its one kernel, and
+ * every mlora_plan call around its three kernels (one duration for the three), for the first
+ * `capacity` launches.
  * mlora_trace_stop waits for the recorded events, writes the duration of launch i in
  * milliseconds to ms[i] (host array of `capacity` floats; NULL discards them), releases the
  * events and returns the number of durations written (-1 on a HIP error).

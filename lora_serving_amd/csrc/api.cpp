@@ -345,8 +345,11 @@ mlora_status mlora_plan(const int32_t *idx, int64_t T, int32_t K, int32_t S, int
     const size_t need = sort_workspace_bytes(T * K, S);
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return MLORA_ERR_WORKSPACE;
-    return hip_status(launch_stable_sort(idx, T * K, S, perm, seg_slot, seg_start, seg_len,
-                                         counts, (int32_t *)ws, stream));
+    trace_mark(stream, true);
+    const hipError_t e = launch_stable_sort(idx, T * K, S, perm, seg_slot, seg_start, seg_len,
+                                            counts, (int32_t *)ws, stream);
+    trace_mark(stream, false);
+    return hip_status(e);
 }
 
 mlora_status mlora_shrink(const void *x, int64_t T, int64_t n_in, const mlora_slots *slots,

@@ -6,7 +6,8 @@
 // tile plan), -1 entries are dropped, and ties keep their input order.  Exactly one output is
 // correct, so the result is bit-exact.
 //
-// Three launches:
+// Small maps (up to 8192 entries, up to 1000 keys): one launch, sort_small (below).  Otherwise
+// three launches:
 //   sort_count   one wave per unit of SORT_UNIT consecutive entries: per-key counts (LDS)
 //   sort_scan    one workgroup: exclusive scan of the counts in key-major order, which gives
 //                every (key, unit) its first output position; then the segment table
@@ -137,6 +138,109 @@ __global__ __launch_bounds__(64) void sort_scatter(const int32_t *__restrict__ k
     }
 }
 
+// One-workgroup form for small index maps (n <= SORT_SMALL_MAX_N, nkeys <= SORT_SMALL_MAX_KEYS),
+// one launch instead of three: wave w owns the contiguous range [w U, (w + 1) U) of the entries
+// (U a multiple of 64), its keys held in registers.  The per-(key, wave) counts sit in LDS (each
+// wave adds one ballot-matched group of equal keys at a time to its own column); their
+// exclusive scan in key-major, wave-minor order gives every (key, wave) its first output
+// position, which is the stable order because the waves' ranges follow each other.  Each wave
+// then walks its range 64 entries at a time, ranking equal keys with ballots, and advances its
+// own positions (a column of the table no other wave touches).
+constexpr int SORT_SMALL_WAVES = 16;
+constexpr int SORT_SMALL_PER_LANE = 8;    // beyond 8 steps per wave the three kernels are faster
+constexpr int64_t SORT_SMALL_MAX_N = (int64_t)SORT_SMALL_WAVES * 64 * SORT_SMALL_PER_LANE;
+constexpr int SORT_SMALL_MAX_KEYS = 1000;   // the table fits the 64 KB of static LDS
+
+__global__ __launch_bounds__(1024) void sort_small(const int32_t *__restrict__ keys, int32_t n,
+                                                   int32_t nkeys, int32_t nbits,
+                                                   int32_t *__restrict__ perm,
+                                                   int32_t *__restrict__ seg_key,
+                                                   int32_t *__restrict__ seg_start,
+                                                   int32_t *__restrict__ seg_len,
+                                                   int32_t *__restrict__ counts)
+{
+    __shared__ int32_t tab[SORT_SMALL_MAX_KEYS * SORT_SMALL_WAVES];   // [key][wave]
+    __shared__ int wsum[16];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int len = nkeys * SORT_SMALL_WAVES;
+    for (int i = threadIdx.x; i < len; i += blockDim.x)
+        tab[i] = 0;
+    const int U = ((n + 1023) >> 10) * 64;          // entries per wave, a multiple of 64
+    const int p0 = w * U;
+    int kk[SORT_SMALL_PER_LANE];
+#pragma unroll
+    for (int i = 0; i < SORT_SMALL_PER_LANE; ++i) {
+        const int p = p0 + i * 64 + lane;
+        kk[i] = (i * 64 < U && p < n) ? keys[p] : -1;
+    }
+    __syncthreads();
+    // counts: the first lane of each group of equal keys adds the group's size (runs of one
+    // key, as in prefill batches, would otherwise make 64 atomics on one address per step)
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < SORT_SMALL_PER_LANE; ++i) {
+        if (i * 64 >= U)
+            break;                                   // the same for every wave
+        const int k = kk[i];
+        const uint64_t same = match_key((uint32_t)(k + 1), nbits) & ballot64(k >= 0);
+        if (k >= 0 && __popcll(same & below) == 0)
+            tab[k * SORT_SMALL_WAVES + w] += __popcll(same);
+    }
+    __syncthreads();
+
+    int carry = 0;
+    for (int base = 0; base < len; base += blockDim.x) {
+        const int i = base + threadIdx.x;
+        const int v = i < len ? tab[i] : 0;
+        int tot;
+        const int ex = block_exclusive_scan(v, &tot, wsum);
+        if (i < len)
+            tab[i] = carry + ex;
+        carry += tot;
+    }
+    const int total = carry;
+    __syncthreads();
+    int g = 0;
+    for (int base = 0; base < nkeys; base += blockDim.x) {
+        const int k = base + threadIdx.x;
+        int start = 0, cnt = 0;
+        if (k < nkeys) {
+            start = tab[k * SORT_SMALL_WAVES];
+            const int end = k + 1 < nkeys ? tab[(k + 1) * SORT_SMALL_WAVES] : total;
+            cnt = end - start;
+        }
+        const int flag = cnt > 0;
+        int tot;
+        const int ex = block_exclusive_scan(flag, &tot, wsum);
+        if (flag) {
+            seg_key[g + ex] = k;
+            seg_start[g + ex] = start;
+            seg_len[g + ex] = cnt;
+        }
+        g += tot;
+    }
+    if (threadIdx.x == 0) {
+        counts[0] = g;
+        counts[1] = total;
+    }
+
+#pragma unroll
+    for (int i = 0; i < SORT_SMALL_PER_LANE; ++i) {
+        if (i * 64 >= U)
+            break;
+        const int k = kk[i];
+        const bool part = k >= 0;
+        const uint64_t same = match_key((uint32_t)(k + 1), nbits) & ballot64(part);
+        const int rank = __popcll(same & below);
+        if (part) {
+            const int at = tab[k * SORT_SMALL_WAVES + w];
+            perm[at + rank] = p0 + i * 64 + lane;
+            if (rank == 0)
+                tab[k * SORT_SMALL_WAVES + w] = at + __popcll(same);
+        }
+    }
+}
+
 static int key_bits(int32_t nkeys)
 {
     int b = 0;
@@ -155,6 +259,11 @@ hipError_t launch_stable_sort(const int32_t *keys, int64_t n, int32_t nkeys, int
                               int32_t *seg_key, int32_t *seg_start, int32_t *seg_len,
                               int32_t *counts, int32_t *cnt_ws, hipStream_t stream)
 {
+    if (n <= SORT_SMALL_MAX_N && nkeys <= SORT_SMALL_MAX_KEYS) {
+        hipLaunchKernelGGL(sort_small, dim3(1), dim3(1024), 0, stream, keys, (int32_t)n, nkeys,
+                           key_bits(nkeys), perm, seg_key, seg_start, seg_len, counts);
+        return hipGetLastError();
+    }
     const int64_t nu64 = (n + SORT_UNIT - 1) / SORT_UNIT;
     const int32_t nu = (int32_t)nu64;
     const size_t lds = (size_t)nkeys * sizeof(int32_t);

@@ -489,8 +489,12 @@ def test_t_zero_is_noop():
 # ------------------------------------------------------------------------------------------
 # plan
 # ------------------------------------------------------------------------------------------
+# maps up to 8192 pairs over up to 1000 slots take the one-workgroup sort, larger ones the
+# three-kernel sort: cases 9-11 and 13 sit on both sides of both limits
 PLAN_CASES = [(0, 1, 1, 1), (1, 6, 1, 4), (2, 64, 1, 100), (3, 1000, 3, 7), (4, 16384, 1, 100),
-              (5, 8192, 3, 32), (6, 3000, 2, 16384), (7, 0, 1, 5), (8, 5000, 8, 1)]
+              (5, 8192, 3, 32), (6, 3000, 2, 16384), (7, 0, 1, 5), (8, 5000, 8, 1),
+              (9, 8192, 1, 1000), (10, 8193, 1, 1000), (11, 4096, 1, 1001), (12, 1500, 2, 50),
+              (13, 1170, 7, 3), (14, 32768, 1, 1000)]
 
 
 @pytest.mark.parametrize("case", PLAN_CASES, ids=[f"p{c[0]}" for c in PLAN_CASES])
