@@ -240,6 +240,32 @@ def test_packed_weight_same_bits(oracle_mod, case):
     assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
 
 
+@pytest.mark.parametrize("T", [9, 40])
+def test_decode_wide_output(oracle_mod, T):
+    """A vocabulary-wide decode product: n_out = 65600 (1025 row tiles of 64) with n_in = 2056
+    split in 3 (the last split 8 columns wide); two slices of rank 32 and K = 3 make every
+    pair need shrink pieces beyond the first.  Row-major and packed W against the oracle, and
+    bit-identical to each other."""
+    import torch
+    from lora_serving_amd import mlora
+    L = synth.random_layer(64 + T, T=T, n_in=2056, n_out=65600, S=6, R=32, K=3,
+                           slice_sizes=[40000, 25600], p_sentinel=0.2)
+    say(f"[wide-decode] T={T} n_in={L.n_in} n_out={L.n_out} K={L.K}")
+    D = DevLayer(L)
+    y0 = D.linear(flags=mlora.MLORA_PATH_DECODE).clone()
+    toks = (np.arange(L.T, dtype=np.int64) if L.T <= 12
+            else np.array(sorted({0, L.T - 1, *range(1, L.T - 1, 4)}), np.int64))
+    y_ref = oracle_mod.linear(L, tokens=toks)
+    yy = from_dev_bf16(y0)[toks]
+    ok = tol_ok(yy, y_ref)
+    assert ok.all(), f"worst {worst(yy, y_ref):.3e}, {np.sum(~ok)} out"
+    Wp = mlora.mlora_pack_weight(D.W)
+    y1 = torch.empty_like(y0)
+    mlora.mlora_linear(D.x, Wp, D.slots, D.idx, D.scale, y1,
+                       flags=mlora.MLORA_PATH_DECODE | mlora.MLORA_W_PACKED, ws=D.ws)
+    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
+
+
 @pytest.mark.parametrize("path", ["decode", "tiled"])
 def test_limits_rank_slots_slices(oracle_mod, path):
     """The widest slots (R = 512), the most slots per token (K = 8) and the most slices (4)."""
