@@ -1224,12 +1224,15 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
     c.grp_stride = PF_BM * K / 16 + c.list_stride;   // 16-token groups of a scattered tile
     c.sc_cap = (int)std::min<int64_t>(
         c.n_mtiles, std::max<int64_t>(1, (64ll << 20) / ((int64_t)PF_BM * n_out * 4)));
+    // a tile holds at most list_stride adapters: when even that many stay within the
+    // scattered-tile limit (tile_scattered), no tile is scattered and the expand launches
+    // after the GEMM would find no work
+    c.may_scatter = (int64_t)c.list_stride * 2 * R > n_in / 2;
     // fp32 partial blocks of the dense shrink items: within 64 MiB, and no more than the most
     // the launch can use (every tile dense with list_stride adapters, SD_KS_MAX parts)
     const int64_t rbs_max = ((int64_t)c.list_stride * n_slices * R + SD_ROWS - 1) / SD_ROWS;
     c.sd_cap_slots = (int)std::min<int64_t>(
         (64ll << 20) / ((int64_t)SD_PART_ELEMS * 4), (int64_t)c.n_mtiles * rbs_max * SD_KS_MAX);
-    (void)n_in;
     return c;
 }
 
@@ -1391,7 +1394,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
                            dim3(512), lds, stream, a);
     hipError_t e = hipGetLastError();
     trace_mark(stream, false);
-    if (e == hipSuccess && g != nullptr) {
+    if (e == hipSuccess && g != nullptr && c.may_scatter) {
         ScArgs x2{};
         x2.T = (int)T;
         x2.n_out = (int)n_out;

@@ -89,6 +89,7 @@ struct PrefillCfg {
     int tok_stride;           // bytes of a tile's per-adapter token lists (256 K)
     int sd_cap_slots;         // fp32 partial blocks of the dense shrink items (256 x 128 each)
     int grp_stride;           // group records per tile (scattered tiles' 16-token groups)
+    bool may_scatter;         // some tile could be scattered (else no expand launches)
 };
 PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t R,
                           int32_t n_slices);
