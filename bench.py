@@ -212,6 +212,10 @@ def main():
                          "batches, where it is faster, row-major for the tiled path")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured copy-bandwidth and bf16 GEMM ceilings")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as replays of a HIP graph holding whole passes over "
+                         "the rotating input sets, at least 16 steps (the host's cost per call "
+                         "paid once per replay)")
     ap.add_argument("--op", default="linear", choices=["linear", "bgmv", "plan"],
                     help="linear: mlora_linear (the whole layer); bgmv: the standalone pair "
                          "mlora_shrink + mlora_expand (y += LoRA delta), per layer; plan: "
@@ -295,11 +299,38 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()     # the stream the library launches on
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(steps):
-        step(i)
-    ev1.record(stream)
+    if args.graph:
+        # whole passes over the input sets, at least 16 steps (a replay costs several
+        # microseconds of its own), captured once after a warm-up pass on a side stream, as
+        # capture asks; the timed region replays it, so steps round up to whole replays
+        per_graph = nsets * -(-16 // nsets)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(per_graph):
+                step(i)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(per_graph):
+                step(i)
+        torch.cuda.synchronize()
+        reps = -(-steps // per_graph)
+        steps = reps * per_graph
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        ev1.record(stream)
+    else:
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(steps):
+            step(i)
+        ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / steps
     # Main product kernel: HIP events that the library records on the launch stream around
@@ -399,7 +430,8 @@ def main():
                    "layers": [[L.n_in, L.n_out] for L in layers], "S": layers[0].S,
                    "R": layers[0].R, "K": layers[0].K,
                    "distinct_adapters": [a["distinct_adapters"] for a in algs],
-                   "rotating_sets": nsets, "w_layout": args.w_layout, "op": args.op},
+                   "rotating_sets": nsets, "w_layout": args.w_layout, "op": args.op,
+                   "graph": args.graph},
         "roofline": roof,
         "step_algorithmic": {"bytes": tot_bytes, "flops": tot_flops},
     }
