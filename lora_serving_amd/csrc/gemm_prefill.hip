@@ -268,6 +268,7 @@ struct ShrinkArgs {
     int32_t *tile_pbase;  // out: first partial slot / SD block of a dense tile, -1 otherwise
     int32_t *sd_ks;       // out: ks of this launch
     int stages;           // dense item stages in LDS (2 or 3)
+    int skip_groups;      // 1: the GEMM's helper workgroups run the group items instead
 };
 
 // Coefficient of adapter a for token t: the sum of s[t][j] * f[a] over the slots j holding a.
@@ -486,11 +487,14 @@ __device__ __forceinline__ void sg_load(const uint16_t *const (&ap)[2], const bo
     xf = *(const u32x4 *)(ok && xok ? (const void *)(xp + col) : (const void *)pf_zero16);
 }
 
-__device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int local, float4 *red)
+// tid: the thread's index among the item's 256 threads (its wave is tid / 64); red: 8 KB of
+// LDS for the item.  Every thread of the workgroup meets exactly two barriers.
+__device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int local, float4 *red,
+                                              int tid)
 {
     const SlotGeom &g = P.g;
     const int R = g.R, wd = g.n_slices * R;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, gq = lane >> 4;
     const int RB = (wd + SG_ROWS - 1) / SG_ROWS;
     const int gidx = local / RB, rb = local - gidx * RB;
@@ -540,7 +544,7 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
         red[(wave * 2 + f) * 64 + lane] = float4{acc[f][0], acc[f][1], acc[f][2], acc[f][3]};
     __syncthreads();
     // thread: gathered token j = tid % 16, rows 2 * (tid / 16) and the next
-    const int j = threadIdx.x & 15, rp = (threadIdx.x >> 4) * 2;
+    const int j = tid & 15, rp = (tid >> 4) * 2;
     if (j < ng) {
         const int tl = tk[j];
         const float cf = sh_coef(P, m * PF_BM + tl, a);
@@ -626,7 +630,9 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
         int cnt = 0;
         if (m < P.n_mtiles) {
             const int Dm = P.tile_D[m];
-            cnt = grouped[m] ? P.tile_gpre[(int64_t)m * (P.list_stride + 1) + Dm] * RBg
+            cnt = grouped[m] ? (P.skip_groups ? 0
+                                              : P.tile_gpre[(int64_t)m * (P.list_stride + 1) + Dm] *
+                                                    RBg)
                              : ((Dm * wd + SD_ROWS - 1) / SD_ROWS) * ks;
         }
         int ex, all, u0, u1;
@@ -650,7 +656,7 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
         }
         const int local = item - pre[lo];
         if (grouped[lo]) {
-            sh_group_item(P, lo, local, red);
+            sh_group_item(P, lo, local, red, threadIdx.x);
         } else {
             const int rb = local / ks, kp = local - rb * ks;
             sh_dense_item(P, lo, rb, kp, ks, kc, (pbase[lo] + rb) * ks + kp, stages);
@@ -759,7 +765,45 @@ struct GemmArgs {
     const int32_t *tile_ord;   // scattered tile ordinal (sgmv_shrink_kernel), or -1
     float *part_sc;            // fp32 [sc_cap][256][n_out] sums of scattered tiles
     int n_rg, n_kb;            // packed W: row groups of 16, column blocks of 32
+    ShrinkArgs sh;             // for the helper workgroups (group items of scattered tiles)
 };
+
+// Workgroups past the GEMM's tiles (launched only while the tiles leave CUs idle) run the
+// scattered tiles' shrink group items, which the shrink kernel then skips: nothing in the GEMM
+// reads a scattered tile's V, only the expand after it.  Two items at a time, waves 0-3 and
+// 4-7, each half with 8 KB of the stage LDS; a half without an item meets the other half's
+// two barriers.
+__device__ void pf_group_helper(const GemmArgs &P, int n_tiles, uint16_t *lds)
+{
+    const ShrinkArgs &S = P.sh;
+    const int n_sc = S.sc_tiles[S.sc_cap];
+    const int wd = S.g.n_slices * S.g.R;
+    const int RBg = (wd + SG_ROWS - 1) / SG_ROWS;
+    auto items_of = [&](int o) {
+        const int m = S.sc_tiles[o];
+        return S.tile_gpre[(int64_t)m * (S.list_stride + 1) + S.tile_D[m]] * RBg;
+    };
+    int total = 0;
+    for (int o = 0; o < n_sc; ++o)
+        total += items_of(o);
+    const int h = blockIdx.x - n_tiles, nh = gridDim.x - n_tiles;
+    const int half = threadIdx.x >> 8, tid = threadIdx.x & 255;
+    float4 *red = (float4 *)lds + half * 512;
+    for (int base = 0; base < total; base += 2 * nh) {
+        const int item = base + 2 * h + half;
+        if (item < total) {
+            int o = 0, pre = 0;
+            while (item >= pre + items_of(o)) {
+                pre += items_of(o);
+                ++o;
+            }
+            sh_group_item(S, S.sc_tiles[o], item - pre, red, tid);
+        } else {
+            __syncthreads();
+            __syncthreads();
+        }
+    }
+}
 
 // GEMM: 256 W rows x 256 tokens per workgroup, 8 waves (4 along W rows x 2 along tokens,
 // 64 x 128 each), k-steps of 64 columns.  Operand tiles go from global memory straight into
@@ -889,12 +933,16 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t pf_lds[];
     // [stage][W 256 x 32 | X 256 x 32], then the tile's adapter list
+    const int nwg = P.n_mtiles * P.n_ntiles;
+    if ((int)blockIdx.x >= nwg) {
+        pf_group_helper(P, nwg, pf_lds);
+        return;
+    }
 
     // Workgroups are dealt to the 8 XCDs round robin (their own L2 each): give every XCD a
     // contiguous run of logical tiles, ordered in groups of 8 n-tiles per m-tile, so the
     // tiles an XCD runs together share their x and W panels in its L2.  Any bijection is
     // correct; this one only decides which tiles meet in which cache.
-    const int nwg = gridDim.x;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int lt = xcd * (nwg >> 3) + min(xcd, nwg & 7) + slot;
     const int GN = 8;
@@ -1297,6 +1345,15 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
 
     if (g != nullptr && c.n_mtiles > SH_MAX_TILES)
         return hipErrorInvalidValue;   // callers split larger batches
+    // helper workgroups after the GEMM's tiles take the scattered tiles' shrink group items
+    // while the tiles leave CUs idle (one workgroup per CU: 128 KB of LDS each)
+    const int n_tiles = c.n_mtiles * c.n_ntiles;
+    int n_cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        n_cus = 0;
+    const int n_helpers = g != nullptr && c.may_scatter && n_tiles < n_cus ? n_cus - n_tiles : 0;
+    ShrinkArgs s{};
     if (g != nullptr) {
         const size_t lds = (size_t)((g->S + 31) / 32) * 4 + (size_t)g->S * 4 + (size_t)c.list_stride * 4;
         static size_t lds_allowed = 64 * 1024;
@@ -1311,7 +1368,6 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
                            (int)T, K, g->S, g->R, g->n_slices, (int)n_in, c.list_stride, tile_D,
                            tile_list, tile_toff, tile_gpre, tile_tok, c.tok_stride, tile_grp,
                            c.grp_stride, vcat, c.vcat_tile_elems);
-        ShrinkArgs s{};
         s.x = x;
         s.T = (int)T;
         s.n_in = (int)n_in;
@@ -1338,6 +1394,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         s.sd_cap_slots = c.sd_cap_slots;
         s.tile_pbase = tile_pbase;
         s.sd_ks = sd_ks;
+        s.skip_groups = n_helpers > 0 ? 1 : 0;
         // three dense stages while the item tables leave room in the 160 KB of LDS, else two
         const size_t tables = (size_t)c.n_mtiles * SD_TABLE_BYTES;
         s.stages = 3 * (size_t)SD_STAGE_BYTES + tables <= 160 * 1024 ? 3 : 2;
@@ -1375,6 +1432,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     a.part_sc = part_sc;
     a.n_rg = (int)((n_out + 15) / 16);
     a.n_kb = (int)((n_in + 31) / 32);
+    a.sh = s;
     const size_t lds = (size_t)PF_STAGES * PF_STAGE_BYTES;                // 128 KB of stages
     const void *kfn = packed ? (const void *)prefill_gemm_kernel<true>
                              : (const void *)prefill_gemm_kernel<false>;
@@ -1387,10 +1445,10 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     }
     trace_mark(stream, true);
     if (packed)
-        hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3((unsigned)(c.n_mtiles * c.n_ntiles)),
+        hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3((unsigned)(n_tiles + n_helpers)),
                            dim3(512), lds, stream, a);
     else
-        hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3((unsigned)(c.n_mtiles * c.n_ntiles)),
+        hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3((unsigned)(n_tiles + n_helpers)),
                            dim3(512), lds, stream, a);
     hipError_t e = hipGetLastError();
     trace_mark(stream, false);
