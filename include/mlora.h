@@ -180,6 +180,9 @@ mlora_status mlora_validate(const int32_t *idx, int64_t T, int32_t K, const mlor
  *   seg_len    int32 [S]    its length
  *   counts     int32 [2]    {n_seg, n_pairs}
  * Exactly one result is correct, so the outputs are bit-exact.  T = 0 writes counts {0, 0}.
+ * ws: at least the plan's part of mlora_workspace_size for T, K and S (MLORA_ERR_WORKSPACE
+ * otherwise; maps of up to 8192 pairs over up to 1000 slots are sorted in one launch that
+ * leaves it untouched).
  */
 mlora_status mlora_plan(const int32_t *idx, int64_t T, int32_t K, int32_t S, int32_t *perm,
                         int32_t *seg_slot, int32_t *seg_start, int32_t *seg_len,
@@ -230,7 +233,7 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
  * events (no device memory); from then on every mlora_linear call records one event on its
  * stream right before and one right after each launch of its main product kernel (the decode
  * GEMM or the tiled GEMM), every mlora_shrink / mlora_expand call around its one kernel, and
- * every mlora_plan call around its three kernels (one duration for the three), for the first
+ * every mlora_plan call around its kernels (one duration for the one or three), for the first
  * `capacity` launches.
  * mlora_trace_stop waits for the recorded events, writes the duration of launch i in
  * milliseconds to ms[i] (host array of `capacity` floats; NULL discards them), releases the
