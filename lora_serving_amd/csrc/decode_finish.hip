@@ -109,10 +109,15 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
     const int32_t my_idx = *(has_idx ? idx + t0 * K + threadIdx.x : (const int32_t *)df_zero);
     const float *psrc = part + ((int64_t)tile * T + min(t, T - 1)) * DF_ROWS + g4 * 4;
     const int64_t sstride = (int64_t)n_tiles * T * DF_ROWS;
+    // the partials are read exactly once: non-temporal loads (nt), which leave the caches to
+    // the B rows and v (the step at T = 64 went 16.65 -> 16.55 us)
     float4 pq[DF_PQ];
 #pragma unroll
-    for (int sp = 0; sp < DF_PQ; ++sp)
-        pq[sp] = *(const float4 *)(sp < sk ? psrc + sp * sstride : df_zero);
+    for (int sp = 0; sp < DF_PQ; ++sp) {
+        const f32x4 q =
+            __builtin_nontemporal_load((const f32x4 *)(sp < sk ? psrc + sp * sstride : df_zero));
+        pq[sp] = float4{q[0], q[1], q[2], q[3]};
+    }
     asm volatile("" ::: "memory");
 
     float d4[4] = {0.f, 0.f, 0.f, 0.f};

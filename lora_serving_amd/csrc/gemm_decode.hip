@@ -46,6 +46,14 @@ __device__ __forceinline__ u32x4 dec_ld16(const uint16_t *row, int c, bool ok)
     return *(const u32x4 *)(ok ? row + c : (const uint16_t *)dec_zero16);
 }
 
+// The same for W, which every launch reads exactly once: a non-temporal load (nt), so the
+// stream does not displace x, A and the split partials from the caches.  Measured: the
+// T = 64 step 17.8 -> 16.6 us, the LM head 252 -> 243 us.
+__device__ __forceinline__ u32x4 dec_ld16_stream(const uint16_t *p, bool ok)
+{
+    return __builtin_nontemporal_load((const u32x4 *)(ok ? p : (const uint16_t *)dec_zero16));
+}
+
 // Shrink piece of pair p, A rows r0..r0+15: D[16 rows][16 tokens] = A rows x (the token tile
 // holding t), one MFMA per 32 columns on fragments already in registers; the pair's token
 // column is summed over the 8 waves (fixed order) and written to upart[s][j][t][r0..].
@@ -202,12 +210,12 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
                 const int rg = tile * 4 + rt, kb = (kw >> 5) + ks;
                 const bool ok = wave_on && rg < P.n_rg && kb < P.n_kb;
                 const uint16_t *wp = W + (((int64_t)min(rg, P.n_rg - 1) * P.n_kb + min(kb, P.n_kb - 1)) * 64 + lane) * 8;
-                wf[rt][ks] = *(const u32x4 *)(ok ? (const void *)wp : (const void *)dec_zero16);
+                wf[rt][ks] = dec_ld16_stream(wp, ok);
             } else {
                 const int row = tile * DEC_ROWS + rt * 16 + r;
                 const uint16_t *wrow = W + (int64_t)min(row, n_out - 1) * n_in;
                 const int c = col(ks);
-                wf[rt][ks] = dec_ld16(wrow, c, wave_on && c < n_in && row < n_out);
+                wf[rt][ks] = dec_ld16_stream(wrow + c, wave_on && c < n_in && row < n_out);
             }
         }
     }
