@@ -124,6 +124,31 @@ def test_tiled_scattered_tiles_beyond_capacity(oracle_mod):
     assert ok.all(), f"worst {worst(y[toks], y_ref):.3e}, {np.sum(~ok)} out"
 
 
+def test_scattered_shrink_in_gemm_helpers_same_bits(oracle_mod):
+    """The scattered tiles' shrink group items run in helper workgroups of the GEMM launch when
+    its output tiles leave CUs idle, else in the shrink kernel.  The same layer at n_out = 32768
+    (256 output tiles: no helper) and cut to its first 32512 outputs (254 tiles: helpers) gives
+    the same bits on the shared outputs, and the cut one matches the oracle."""
+    import dataclasses
+    import torch
+    from lora_serving_amd import mlora
+    L = synth.random_layer(47, T=300, n_in=256, n_out=32768, S=40, R=16, K=2, p_sentinel=0.2)
+    n_cut = 32512
+    Lc = dataclasses.replace(L, n_out=n_cut, W=np.ascontiguousarray(L.W[:n_cut]),
+                             B=np.ascontiguousarray(L.B[:, :n_cut]),
+                             slice_start=np.array([0, n_cut], np.int32))
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say(f"[helpers] T={L.T} n_out {L.n_out} vs {n_cut}, {n_cus} CUs")
+    if n_cus != 256:
+        pytest.skip("tile counts chosen for 256 CUs")
+    y_full = from_dev_bf16(DevLayer(L).linear(flags=mlora.MLORA_PATH_TILED))
+    y_cut = from_dev_bf16(DevLayer(Lc).linear(flags=mlora.MLORA_PATH_TILED))
+    assert np.array_equal(y_cut, y_full[:, :n_cut])
+    toks = np.arange(0, L.T, 7, dtype=np.int64)
+    y_ref = oracle_mod.linear(Lc, tokens=toks)
+    assert tol_ok(y_cut[toks], y_ref).all()
+
+
 def test_slot_load_rebuilds_padded_slots():
     """Slot activation: every adapter loaded at its true rank (host pinned sources and device
     sources) over slots filled with NaN bits gives back the zero-padded slots bit for bit, and
