@@ -1,7 +1,9 @@
 """CPU oracle for the multi-LoRA adapted linear layer (TEST INFRASTRUCTURE ONLY).
 
 Loads ``oracle.c`` compiled with gcc (fp64 sums, -ffp-contract=off, OpenMP over tokens) and
-marshals numpy arrays into it.  Only tests, the smoke check and the benchmark's CPU-baseline leg
+marshals numpy arrays into it.  The same source is also built with fp32 sums (-DORACLE_ACC=float,
+``liboracle_f32.so``): the plain fp32 CPU loop timed as the benchmark's CPU baseline.  Parity
+and every pin use the fp64 build.  Only tests, the smoke check and the benchmark's CPU-baseline leg
 may import this package; the GPU library never does.  The two sides share nothing but the seeded
 inputs, which callers draw from the synthetic-input module and hand to each side.
 """
@@ -17,30 +19,34 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _BUILD = os.path.join(_HERE, "_build")
 _LIB = os.path.join(_BUILD, "liboracle.so")
+_LIB_F32 = os.path.join(_BUILD, "liboracle_f32.so")
 
 CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
           "-shared", "-Wall", "-Wextra"]
 
 
 def build(force: bool = True) -> str:
-    """Compile oracle.c into oracle/_build/liboracle.so with gcc."""
+    """Compile oracle.c into oracle/_build/liboracle.so (fp64 sums) and liboracle_f32.so (fp32
+    sums) with gcc."""
     os.makedirs(_BUILD, exist_ok=True)
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + f".tmp{os.getpid()}"
-        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, _LIB)
+    for lib, extra in ((_LIB, []), (_LIB_F32, ["-DORACLE_ACC=float"])):
+        if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+            tmp = lib + f".tmp{os.getpid()}"
+            subprocess.run(["gcc", *CFLAGS, *extra, _SRC, "-o", tmp, "-lm"], check=True)
+            os.replace(tmp, lib)
     return _LIB
 
 
-_lib = None
+_libs = {}
 
 
-def _load():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+def _load(acc: str = "f64"):
+    """The fp64 build (acc="f64", every pin and parity check) or the fp32 one (acc="f32")."""
+    if acc not in _libs:
+        path = {"f64": _LIB, "f32": _LIB_F32}[acc]
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
             build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int32
         lib.oracle_lora_factor.restype = ctypes.c_double
@@ -56,8 +62,8 @@ def _load():
                                       i32, P, i32, P, i64, P]
         lib.oracle_slot_bytes.restype = i64
         lib.oracle_slot_bytes.argtypes = [i32, i32, i64, i64, i32]
-        _lib = lib
-    return _lib
+        _libs[acc] = lib
+    return _libs[acc]
 
 
 def _ptr(a: np.ndarray | None):
@@ -123,8 +129,9 @@ def expand(L, v: np.ndarray, y: np.ndarray | None = None) -> np.ndarray:
     return y
 
 
-def linear(L, tokens=None, with_base: bool = True) -> np.ndarray:
-    """y rows (fp64) for the listed tokens (all when None): base + every slot's delta."""
+def linear(L, tokens=None, with_base: bool = True, acc: str = "f64") -> np.ndarray:
+    """y rows for the listed tokens (all when None): base + every slot's delta, summed in fp64
+    (acc="f64") or in fp32 (acc="f32", the timed CPU baseline); returned as float64."""
     alpha, rank, rs = _slot_args(L)
     if tokens is None:
         tok = None
@@ -134,7 +141,7 @@ def linear(L, tokens=None, with_base: bool = True) -> np.ndarray:
         nt = tok.shape[0]
     y = np.zeros((nt, L.n_out), np.float64)
     scale = _c(L.scale, np.float32)
-    _load().oracle_linear(_ptr(_c(L.x, np.uint16)), _ptr(_c(L.W, np.uint16)), L.T, L.n_in,
+    _load(acc).oracle_linear(_ptr(_c(L.x, np.uint16)), _ptr(_c(L.W, np.uint16)), L.T, L.n_in,
                           L.n_out, _ptr(_c(L.A, np.uint16)), _ptr(_c(L.B, np.uint16)), L.S, L.R,
                           L.n_slices, _ptr(_c(L.slice_start, np.int32)), _ptr(alpha), _ptr(rank),
                           _ptr(rs), _ptr(_c(L.idx, np.int32)), L.K, _ptr(scale),

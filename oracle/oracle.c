@@ -7,7 +7,10 @@
  *
  * Arithmetic: every bfloat16 input is decoded exactly and all sums run in fp64 (the pages'
  * worked examples are NumPy float64 scripts), in plain ascending loops, compiled with
- * -ffp-contract=off so no fused multiply-add changes the rounding.
+ * -ffp-contract=off so no fused multiply-add changes the rounding.  Parity is checked against
+ * this fp64 build.  Built with -DORACLE_ACC=float, the same loops accumulate in fp32 instead
+ * (the plain fp32 CPU loop that serves as the timed CPU baseline; results still returned as
+ * double); nothing else changes.
  *
  * What it computes, for token t with adapter slots idx[t][0..K-1] (-1 = none):
  *
@@ -38,12 +41,17 @@
 #include <stdlib.h>
 #include <string.h>
 
-static double bf16_value(uint16_t bits)
+#ifndef ORACLE_ACC
+#define ORACLE_ACC double
+#endif
+typedef ORACLE_ACC acc_t;   /* type of every product and running sum */
+
+static acc_t bf16_value(uint16_t bits)
 {
     uint32_t u = (uint32_t)bits << 16;
     float f;
     memcpy(&f, &u, sizeof f);
-    return (double)f;
+    return (acc_t)f;
 }
 
 /* Scale factor of one adapter: alpha/r, or alpha/sqrt(r) with rsLoRA ("[vLLM] LoRA",
@@ -96,12 +104,12 @@ static double pair_coef(const float *scale, int64_t p, int32_t a, const double *
 
 /* Shrink for one pair: u[sigma*R + rho] = c * sum_i A[a][sigma][rho][i] * x_t[i]. */
 static void shrink_one(const uint16_t *xt, int64_t n_in, const uint16_t *A, int32_t a, int32_t R,
-                       int32_t n_slices, double c, double *u)
+                       int32_t n_slices, acc_t c, acc_t *u)
 {
     for (int32_t sg = 0; sg < n_slices; ++sg)
         for (int32_t rho = 0; rho < R; ++rho) {
             const uint16_t *arow = A + (((int64_t)a * n_slices + sg) * R + rho) * n_in;
-            double acc = 0.0;
+            acc_t acc = 0;
             for (int64_t i = 0; i < n_in; ++i)
                 acc += bf16_value(arow[i]) * bf16_value(xt[i]);
             u[sg * R + rho] = c * acc;
@@ -117,13 +125,13 @@ static int32_t slice_of(int64_t n, int32_t n_slices, const int32_t *slice_start)
 }
 
 /* Expand for one pair: yt[n] += sum_rho B[a][n][rho] * u[sigma(n)*R + rho]. */
-static void expand_one(const double *u, int64_t n_out, const uint16_t *B, int32_t a, int32_t R,
-                       int32_t n_slices, const int32_t *slice_start, double *yt)
+static void expand_one(const acc_t *u, int64_t n_out, const uint16_t *B, int32_t a, int32_t R,
+                       int32_t n_slices, const int32_t *slice_start, acc_t *yt)
 {
     for (int64_t n = 0; n < n_out; ++n) {
         const int32_t sg = slice_of(n, n_slices, slice_start);
         const uint16_t *brow = B + ((int64_t)a * n_out + n) * R;
-        double d = 0.0;
+        acc_t d = 0;
         for (int32_t rho = 0; rho < R; ++rho)
             d += bf16_value(brow[rho]) * u[sg * R + rho];
         yt[n] += d;
@@ -139,20 +147,27 @@ void oracle_shrink(const uint16_t *x, int64_t T, int64_t n_in, const uint16_t *A
 {
     (void)S;
     const int64_t w = (int64_t)n_slices * R;
-#pragma omp parallel for schedule(dynamic)
-    for (int64_t t = 0; t < T; ++t) {
-        for (int32_t j = 0; j < K; ++j) {
-            const int64_t p = t * K + j;
-            double *u = v + ((int64_t)j * T + t) * w;
-            const int32_t a = idx[p];
-            if (a == -1) {
+#pragma omp parallel
+    {
+        acc_t *u = (acc_t *)malloc((size_t)w * sizeof(acc_t));
+#pragma omp for schedule(dynamic)
+        for (int64_t t = 0; t < T; ++t) {
+            for (int32_t j = 0; j < K; ++j) {
+                const int64_t p = t * K + j;
+                double *vt = v + ((int64_t)j * T + t) * w;
+                const int32_t a = idx[p];
+                if (a == -1) {
+                    for (int64_t q = 0; q < w; ++q)
+                        vt[q] = 0.0;
+                    continue;
+                }
+                shrink_one(x + t * n_in, n_in, A, a, R, n_slices,
+                           (acc_t)pair_coef(scale, p, a, alpha, rank, rslora), u);
                 for (int64_t q = 0; q < w; ++q)
-                    u[q] = 0.0;
-                continue;
+                    vt[q] = (double)u[q];
             }
-            shrink_one(x + t * n_in, n_in, A, a, R, n_slices,
-                       pair_coef(scale, p, a, alpha, rank, rslora), u);
         }
+        free(u);
     }
 }
 
@@ -164,15 +179,28 @@ void oracle_expand(const double *v, int64_t T, int64_t n_out, const uint16_t *B,
 {
     (void)S;
     const int64_t w = (int64_t)n_slices * R;
-#pragma omp parallel for schedule(dynamic)
-    for (int64_t t = 0; t < T; ++t)
-        for (int32_t j = 0; j < K; ++j) {
-            const int32_t a = idx[t * K + j];
-            if (a == -1)
-                continue;
-            expand_one(v + ((int64_t)j * T + t) * w, n_out, B, a, R, n_slices, slice_start,
-                       y + t * n_out);
+#pragma omp parallel
+    {
+        acc_t *u = (acc_t *)malloc((size_t)w * sizeof(acc_t));
+        acc_t *yt = (acc_t *)malloc((size_t)n_out * sizeof(acc_t));
+#pragma omp for schedule(dynamic)
+        for (int64_t t = 0; t < T; ++t) {
+            for (int64_t n = 0; n < n_out; ++n)
+                yt[n] = (acc_t)y[t * n_out + n];
+            for (int32_t j = 0; j < K; ++j) {
+                const int32_t a = idx[t * K + j];
+                if (a == -1)
+                    continue;
+                for (int64_t q = 0; q < w; ++q)
+                    u[q] = (acc_t)v[((int64_t)j * T + t) * w + q];
+                expand_one(u, n_out, B, a, R, n_slices, slice_start, yt);
+            }
+            for (int64_t n = 0; n < n_out; ++n)
+                y[t * n_out + n] = (double)yt[n];
         }
+        free(yt);
+        free(u);
+    }
 }
 
 /* The whole layer for the tokens listed in tokens[0..n_tokens) (all tokens when tokens is
@@ -190,14 +218,14 @@ void oracle_linear(const uint16_t *x, const uint16_t *W, int64_t T, int64_t n_in
     const int64_t w = (int64_t)n_slices * R;
 #pragma omp parallel
     {
-        double *u = (double *)malloc((size_t)w * sizeof(double));
+        acc_t *u = (acc_t *)malloc((size_t)w * sizeof(acc_t));
+        acc_t *yt = (acc_t *)malloc((size_t)n_out * sizeof(acc_t));
 #pragma omp for schedule(dynamic)
         for (int64_t q = 0; q < n_tokens; ++q) {
             const int64_t t = tokens ? tokens[q] : q;
             const uint16_t *xt = x + t * n_in;
-            double *yt = y + q * n_out;
             for (int64_t n = 0; n < n_out; ++n) {
-                double acc = 0.0;
+                acc_t acc = 0;
                 if (with_base) {
                     const uint16_t *wrow = W + n * n_in;
                     for (int64_t i = 0; i < n_in; ++i)
@@ -211,10 +239,13 @@ void oracle_linear(const uint16_t *x, const uint16_t *W, int64_t T, int64_t n_in
                 if (a == -1)
                     continue;
                 shrink_one(xt, n_in, A, a, R, n_slices,
-                           pair_coef(scale, p, a, alpha, rank, rslora), u);
+                           (acc_t)pair_coef(scale, p, a, alpha, rank, rslora), u);
                 expand_one(u, n_out, B, a, R, n_slices, slice_start, yt);
             }
+            for (int64_t n = 0; n < n_out; ++n)
+                y[q * n_out + n] = (double)yt[n];
         }
+        free(yt);
         free(u);
     }
 }
