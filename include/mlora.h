@@ -229,6 +229,25 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
                           hipStream_t stream);
 
 /*
+ * mlora_linear for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation, kernels and
+ * output bits as mlora_linear with the same arguments, but its scratch space is a fixed array
+ * of MLORA_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held until the process ends)
+ * instead of a caller-provided workspace.  The caller still passes inputs and outputs.  It
+ * calls no hipMalloc, hipFree or allocating routine.  A call whose path needs more scratch than
+ * the fixed size (e.g. large tiled batches, very wide outputs) returns MLORA_ERR_WORKSPACE
+ * before launching anything, with the needed size in mlora_last_error().  All calls on one GPU
+ * share its array: calls that may overlap on one GPU (other streams, other threads) race and
+ * must not be issued.  The array belongs to the device of `stream` (the current device for the
+ * null stream).
+ */
+#define MLORA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mlora_status mlora_linear_noalloc(const void *x, const void *W, int64_t T, int64_t n_in,
+                                  int64_t n_out, const mlora_slots *slots, const int32_t *idx,
+                                  int32_t K, const float *scale, void *y, uint32_t flags,
+                                  hipStream_t stream);
+
+/*
  * Profiling hook (not part of the computation).  mlora_trace_start creates 2*capacity HIP
  * events (no device memory); from then on every mlora_linear call records one event on its
  * stream right before and one right after each launch of its main product kernel (the decode

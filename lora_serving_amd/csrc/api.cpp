@@ -404,10 +404,18 @@ mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_
     return hip_status(e);
 }
 
-mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in, int64_t n_out,
-                          const mlora_slots *slots, const int32_t *idx, int32_t K,
-                          const float *scale, void *y, uint32_t flags, void *ws, size_t ws_bytes,
-                          hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// mlora_linear and mlora_linear_noalloc: checks, scratch regions and kernel dispatch.  With
+// noalloc the scratch is the library's fixed per-device array (ws and ws_bytes unused) and holds
+// only the regions of the path the call takes, from offset 0; otherwise it is the caller's
+// workspace laid out as mlora_workspace_size() counts it (either path).
+mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in, int64_t n_out,
+                           const mlora_slots *slots, const int32_t *idx, int32_t K,
+                           const float *scale, void *y, uint32_t flags, void *ws, size_t ws_bytes,
+                           bool noalloc, hipStream_t stream)
 {
     if (T < 0 || n_in <= 0 || n_out <= 0 || K < 1 || K > MLORA_MAX_K)
         return MLORA_ERR_ARG;
@@ -436,20 +444,54 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
         return MLORA_ERR_ARG;
     if (lora && idx == nullptr)
         return MLORA_ERR_ARG;
-    const Layout L = make_layout(T, K, n_in, n_out, S, R, n_slices);
-    if (ws == nullptr || ws_bytes < L.total)
-        return MLORA_ERR_WORKSPACE;
-    uint8_t *wsb = (uint8_t *)ws;
-    if (!aligned16(wsb))
-        return MLORA_ERR_ARG;
-    float *upart = (float *)(wsb + L.off_v);
-    float *part = (float *)(wsb + L.off_part);
-    const uint16_t *xb = (const uint16_t *)x;
-    uint16_t *yb = (uint16_t *)y;
     const bool force_decode = (flags & MLORA_PATH_DECODE) != 0;
     const bool force_tiled = (flags & MLORA_PATH_TILED) != 0;
     const bool packed = (flags & MLORA_W_PACKED) != 0;
-    if (force_tiled || (!force_decode && prefill_worth_it(T, n_out))) {
+    const bool tiled = force_tiled || (!force_decode && prefill_worth_it(T, n_out));
+    size_t off_v, off_part, off_pre, need;
+    if (!noalloc) {
+        const Layout L = make_layout(T, K, n_in, n_out, S, R, n_slices);
+        off_v = L.off_v;
+        off_part = L.off_part;
+        off_pre = L.off_pre;
+        need = L.total;
+    } else if (tiled) {
+        off_v = off_part = off_pre = 0;
+        need = prefill_workspace_bytes(
+            prefill_config(std::min<int64_t>(T, PREFILL_MAX_T), K, n_in, n_out, S, R, n_slices));
+    } else {
+        const int64_t Tc = std::min<int64_t>(T, DECODE_MAX_T);
+        const int64_t sk = decode_config(Tc, n_in, n_out).sk;
+        const int64_t chunks = (Tc + 63) / 64, per = chunks > 1 ? 64 : Tc;
+        off_v = off_pre = 0;
+        off_part = align_up((size_t)chunks * sk * K * per * n_slices * R * sizeof(float));
+        need = off_part + decode_partial_bytes(Tc, n_in, n_out);
+    }
+    uint8_t *wsb;
+    if (noalloc) {
+        if (need > MLORA_NOALLOC_SCRATCH_BYTES) {
+            std::snprintf(g_last_error, sizeof g_last_error,
+                          "mlora_linear_noalloc: this call needs %zu bytes of scratch, above the "
+                          "fixed %zu",
+                          need, (size_t)MLORA_NOALLOC_SCRATCH_BYTES);
+            return MLORA_ERR_WORKSPACE;
+        }
+        void *p = nullptr;
+        if (hipError_t e = noalloc_scratch(stream, &p); e != hipSuccess)
+            return hip_status(e, "scratch address");
+        wsb = (uint8_t *)p;
+    } else {
+        if (ws == nullptr || ws_bytes < need)
+            return MLORA_ERR_WORKSPACE;
+        wsb = (uint8_t *)ws;
+        if (!aligned16(wsb))
+            return MLORA_ERR_ARG;
+    }
+    float *upart = (float *)(wsb + off_v);
+    float *part = (float *)(wsb + off_part);
+    const uint16_t *xb = (const uint16_t *)x;
+    uint16_t *yb = (uint16_t *)y;
+    if (tiled) {
         // chunks of at most PREFILL_MAX_T tokens (the shrink's tile table lives in LDS)
         for (int64_t t0 = 0; t0 < T; t0 += PREFILL_MAX_T) {
             const int64_t Tc = std::min<int64_t>(PREFILL_MAX_T, T - t0);
@@ -458,7 +500,7 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
                 launch_prefill(xb + t0 * n_in, (const uint16_t *)W, packed, Tc, n_in, n_out,
                                lora ? &g : nullptr, lora ? idx + t0 * K : nullptr, K,
                                (lora && scale) ? scale + t0 * K : nullptr, yb + t0 * n_out, pc,
-                               wsb + L.off_pre, stream),
+                               wsb + off_pre, stream),
                 "prefill launch");
             if (st != MLORA_OK)
                 return st;
@@ -485,6 +527,28 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
             return hip_status(e, "decode finish launch");
     }
     return MLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in, int64_t n_out,
+                          const mlora_slots *slots, const int32_t *idx, int32_t K,
+                          const float *scale, void *y, uint32_t flags, void *ws, size_t ws_bytes,
+                          hipStream_t stream)
+{
+    return linear_common(x, W, T, n_in, n_out, slots, idx, K, scale, y, flags, ws, ws_bytes,
+                         false, stream);
+}
+
+mlora_status mlora_linear_noalloc(const void *x, const void *W, int64_t T, int64_t n_in,
+                                  int64_t n_out, const mlora_slots *slots, const int32_t *idx,
+                                  int32_t K, const float *scale, void *y, uint32_t flags,
+                                  hipStream_t stream)
+{
+    return linear_common(x, W, T, n_in, n_out, slots, idx, K, scale, y, flags, nullptr, 0, true,
+                         stream);
 }
 
 }  // extern "C"

@@ -104,4 +104,9 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
                           int32_t K, const float *scale, uint16_t *y, const PrefillCfg &c,
                           void *ws, hipStream_t stream);
 
+// ---- noalloc.hip: the fixed per-device scratch of mlora_linear_noalloc ----------------------
+// Device address of this library's scratch array on the stream's device (looked up once per
+// device with hipGetSymbolAddress), MLORA_NOALLOC_SCRATCH_BYTES long.
+hipError_t noalloc_scratch(hipStream_t stream, void **ptr);
+
 }  // namespace mlora

@@ -31,12 +31,13 @@ MLORA_NO_ADAPTERS = 1
 MLORA_PATH_DECODE = 2
 MLORA_PATH_TILED = 4
 MLORA_W_PACKED = 8
+MLORA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("mlora_status_string", "mlora_last_error", "mlora_factor", "mlora_slot_bytes",
            "mlora_workspace_size", "mlora_slot_load", "mlora_packed_weight_bytes",
            "mlora_pack_weight",
            "mlora_validate", "mlora_plan", "mlora_shrink", "mlora_expand", "mlora_linear",
-           "mlora_trace_start", "mlora_trace_stop")
+           "mlora_linear_noalloc", "mlora_trace_start", "mlora_trace_stop")
 
 _P = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -80,6 +81,9 @@ _lib.mlora_expand.argtypes = [_P, _i64, _i64, _SLOTS_P, _P, _i32, _P, _P]
 _lib.mlora_linear.restype = ctypes.c_int
 _lib.mlora_linear.argtypes = [_P, _P, _i64, _i64, _i64, _SLOTS_P, _P, _i32, _P, _P, ctypes.c_uint32,
                               _P, ctypes.c_size_t, _P]
+_lib.mlora_linear_noalloc.restype = ctypes.c_int
+_lib.mlora_linear_noalloc.argtypes = [_P, _P, _i64, _i64, _i64, _SLOTS_P, _P, _i32, _P, _P,
+                                      ctypes.c_uint32, _P]
 _lib.mlora_trace_start.restype = ctypes.c_int
 _lib.mlora_trace_start.argtypes = [_i32]
 _lib.mlora_trace_stop.restype = _i32
@@ -290,6 +294,27 @@ def mlora_linear(x, W, slots: Slots | None, idx, scale, y, flags: int = 0, ws=No
                              _ptr(y), flags, _ptr(ws),
                              0 if ws is None else ws.numel() * ws.element_size(),
                              _stream(stream)), "mlora_linear")
+
+
+def mlora_linear_noalloc(x, W, slots: Slots | None, idx, scale, y, flags: int = 0,
+                         stream=None):
+    """mlora_linear with the library's fixed per-device scratch instead of a workspace."""
+    import torch
+    _bf16(x, "x")
+    _bf16(W, "W")
+    _bf16(y, "y")
+    T, n_in = x.shape
+    n_out = y.shape[1]
+    K = 1
+    if idx is not None:
+        _need(idx, (torch.int32,), "idx")
+        K = idx.shape[1]
+    if scale is not None:
+        _need(scale, (torch.float32,), "scale")
+    _check(_lib.mlora_linear_noalloc(_ptr(x), _ptr(W), T, n_in, n_out,
+                                     None if slots is None else slots.ref, _ptr(idx), K,
+                                     _ptr(scale), _ptr(y), flags, _stream(stream)),
+           "mlora_linear_noalloc")
 
 
 def mlora_trace_start(capacity: int):
