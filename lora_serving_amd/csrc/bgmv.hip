@@ -1,11 +1,12 @@
 // BGMV ("batched gather matrix-vector") shrink and expand: every (token, slot) pair fetches its
 // own adapter's rows by slot index.
 //
-// "Multi-LoRA Serving Explained" (sevydevy.com), six-token batching script: the gather method
-// picks each token's A and B by its id (-1 = base only) and multiplies; the learning book's
-// chapter "04. LoRA Serving", section 6, names the two steps shrink (x A, scaled, rank-wide)
-// and expand (y += v B).  The vLLM RFC on per-request composition (Proposed Change, step 4) runs
-// the K slots of a token inside one kernel pass, as both kernels here do.
+// Sources: "Multi-LoRA Serving Explained" (sevydevy.com), six-token batching example, gather
+// variant (the slot id of a token selects the matrices it is multiplied with; -1 selects
+// none); vLLM learning book, chapter "04. LoRA Serving", section 6 (the shrink to a rank-wide
+// scaled intermediate and the expand that adds it back through B); "[RFC]: Per-request
+// activation of multiple LoRA adapters with static scales", Proposed Change, step 4 (a token's
+// K slots handled in one kernel pass, as both kernels here do).
 //
 // shrink: one workgroup (4 waves) per (pair, block of RB rows of the pair's n_slices * R rows),
 //   RB = 16, 8, 4, 2 or 1 so that small batches still spread over many workgroups.  Lanes

@@ -63,52 +63,48 @@ def test_rslora_delta_is_exactly_four_times(oracle_mod):
 # ------------------------------------------------------------------------------------------
 # The pages' worked examples
 # ------------------------------------------------------------------------------------------
-def test_merge_identity_page_script(oracle_mod):
+def test_merge_identity_within_page_residual(oracle_mod):
+    """The page's merge example (512 x 512 layer, one rank-8 adapter, alpha 16): running the
+    adapter beside the base weight gives the merged-weight result, the page printing a float64
+    residual of about 4.3e-14.  The inputs here are this repository's own seeded draws at those
+    sizes; the oracle (fp64) must agree with the merged-weight route to the same order."""
     g = golden("merge_identity.json")
-    s = g["script"]
-    rng = np.random.default_rng(s["seed"])
-    W = rng.standard_normal((s["d_out"], s["d_in"]))
-    A = rng.standard_normal((s["r"], s["d_in"])) * 0.01
-    B = rng.standard_normal((s["d_out"], s["r"])) * 0.01
-    x = rng.standard_normal(s["d_in"])
-    assert A.size + B.size == g["printed"]["adapter_numbers"]
-    assert W.size == g["printed"]["base_numbers"]
-    L = single_layer(x[None], W, A[None], B[None], [[0]], alpha=[s["alpha"]], rank=[s["r"]],
-                     R=s["r"])
+    e = g["example"]
+    rng = np.random.default_rng(3001)
+    x, W, A, B = synth.draw_weights(rng, 1, e["d_in"], e["d_out"], 1, e["r"], 1,
+                                    np.array([e["r"]]))
+    assert e["r"] * (e["d_in"] + e["d_out"]) == g["printed"]["adapter_numbers"]
+    assert e["d_in"] * e["d_out"] == g["printed"]["base_numbers"]
+    L = make_layer("merge", 3001, rng, np.zeros((1, 1), np.int32), n_in=e["d_in"],
+                   n_out=e["d_out"], S=1, R=e["r"], ranks=e["r"], alpha=e["alpha"])
+    L.x, L.W, L.A, L.B = x, W, A, B
     y = oracle_mod.linear(L)[0]
     merged, mag = cf.merged_linear(L)
-    # the page's fp64 unmerged-vs-merged residual is about 4.3e-14 at this size; the oracle,
-    # also fp64, must agree with the merged route to the same order
     diff = np.abs(y - merged[0]).max()
     assert diff <= 50 * g["printed"]["max_difference_about"], diff
     assert np.allclose(y, merged[0]) == g["printed"]["same_result"]
+    # the adapter's delta is not negligible next to that residual
+    assert np.abs(y - cf.f64(L.W) @ cf.f64(L.x)[0]).max() > 1e6 * diff
 
 
 def _six_token_layer():
+    """The page's six-token batch: four slots of width 16 holding ranks 8, 16, 4, 16, token
+    slot ids 2, 0, -1, 2, 3, 0, B A applied with no alpha/r factor (alpha = r gives factor 1).
+    Inputs are this repository's own seeded draws at those sizes."""
     g = golden("six_token_batch.json")
-    s = g["script"]
-    rng = np.random.default_rng(s["seed"])
-    d, R, S = s["d"], s["max_rank"], s["n_slots"]
-    W = rng.standard_normal((d, d))
-    A = np.zeros((S, R, d))
-    B = np.zeros((S, d, R))
-    for slot, r in enumerate(s["slot_ranks"]):
-        A[slot, :r] = rng.standard_normal((r, d)) * s["weight_scale"]
-        B[slot, :, :r] = rng.standard_normal((d, r)) * s["weight_scale"]
-    ids = np.array(s["ids"])
-    X = rng.standard_normal((len(ids), d))
-    # the script applies B A with no alpha/r factor: alpha = r gives factor 1
-    ranks = np.array(s["slot_ranks"])
-    return g, make_explicit(X, W, A, B, ids, ranks, R)
+    e = g["example"]
+    ids = np.array(e["ids"], np.int32)
+    ranks = np.array(e["slot_ranks"], np.int32)
+    rng = np.random.default_rng(3002)
+    L = make_layer("six_token", 3002, rng, ids[:, None], n_in=e["d"], n_out=e["d"],
+                   S=e["n_slots"], R=e["max_rank"], ranks=ranks,
+                   alpha=ranks.astype(np.float64))
+    return g, L
 
 
-def make_explicit(X, W, A, B, ids, ranks, R):
-    return single_layer(X, W, A, B, ids[:, None], alpha=ranks.astype(float), rank=ranks, R=R)
-
-
-def test_six_token_page_script(oracle_mod):
+def test_six_token_page_example(oracle_mod):
     g, L = _six_token_layer()
-    ids = np.array(g["script"]["ids"])
+    ids = np.array(g["example"]["ids"])
     y = oracle_mod.linear(L)
     merged, _ = cf.merged_linear(L)
     assert np.allclose(y, merged) == g["printed"]["batched_matches_per_request"]
@@ -122,23 +118,26 @@ def test_six_token_page_script(oracle_mod):
     assert list(seg_start) == [0, 2, 4]
 
 
-def test_padding_page_script(oracle_mod):
+def test_padding_page_example(oracle_mod):
+    """The page's padding example (a rank-8 adapter in a width-64 slot, d = 128): the padded
+    slot gives exactly the unpadded result, and holds 16384 numbers against 2048."""
     g = golden("padding.json")
-    s = g["script"]
-    rng = np.random.default_rng(s["seed"])
-    d, r, R = s["d"], s["r"], s["R"]
-    A = rng.standard_normal((r, d))
-    B = rng.standard_normal((d, r))
-    x = rng.standard_normal(d)
-    A_pad = np.zeros((R, d)); A_pad[:r] = A
-    B_pad = np.zeros((d, R)); B_pad[:, :r] = B
-    assert A.size + B.size == g["printed"]["numbers_rank_r"]
-    assert A_pad.size + B_pad.size == g["printed"]["numbers_rank_R_slot"]
-    W = np.zeros((d, d))
-    Lr = single_layer(x[None], W, A[None], B[None], [[0]], alpha=[r], rank=[r], R=r)
-    LR = single_layer(x[None], W, A_pad[None], B_pad[None], [[0]], alpha=[r], rank=[r], R=R)
+    e = g["example"]
+    d, r, R = e["d"], e["r"], e["R"]
+    assert r * 2 * d == g["printed"]["numbers_rank_r"]
+    assert R * 2 * d == g["printed"]["numbers_rank_R_slot"]
+    rng = np.random.default_rng(3003)
+    Lr = make_layer("pad_r", 3003, rng, np.zeros((1, 1), np.int32), n_in=d, n_out=d, S=1, R=r,
+                    ranks=r, alpha=float(r))
+    LR = make_layer("pad_R", 3003, rng, np.zeros((1, 1), np.int32), n_in=d, n_out=d, S=1, R=R,
+                    ranks=r, alpha=float(r))
+    A = np.zeros((1, 1, R, d), np.uint16); A[:, :, :r] = Lr.A
+    B = np.zeros((1, d, R), np.uint16); B[:, :, :r] = Lr.B
+    LR.x, LR.W, LR.A, LR.B = Lr.x, Lr.W, A, B
+    assert int(np.count_nonzero(synth.bf16_to_f32(LR.A)[0, 0, r:])) == 0
     yr = oracle_mod.linear(Lr, with_base=False)
     yR = oracle_mod.linear(LR, with_base=False)
+    assert np.any(yr != 0)
     assert np.array_equal(yr, yR) == g["printed"]["padded_equals_unpadded"]
 
 
@@ -340,3 +339,23 @@ def test_plan_rejects_out_of_range(oracle_mod):
         oracle_mod.plan(np.array([[0], [3]], np.int32), 3)
     with pytest.raises(ValueError):
         oracle_mod.plan(np.array([[-2]], np.int32), 3)
+
+
+# ------------------------------------------------------------------------------------------
+# The fp32 build (timed as the CPU baseline) against the pinned fp64 build
+# ------------------------------------------------------------------------------------------
+def test_fp32_build_within_fp32_rounding_of_fp64(oracle_mod):
+    """The same loops summed in fp32: each output within a few fp32 roundings per term of the
+    fp64 result (bound: n terms x 2^-23 x the sum of the absolute products), and exactly the
+    fp64 result where every product and partial sum is exact (all-zero deltas of sentinel
+    tokens)."""
+    L = synth.random_layer(13, T=10, n_in=256, n_out=64, S=4, R=16, K=2, p_sentinel=0.3)
+    y64 = oracle_mod.linear(L)
+    y32 = oracle_mod.linear(L, acc="f32")
+    _, mag = cf.merged_linear(L)
+    n_terms = L.n_in + L.K * L.R
+    assert np.all(np.abs(y32 - y64) <= n_terms * 2.0 ** -23 * mag)
+    assert np.any(y32 != y64)                  # it really sums in fp32
+    d32 = oracle_mod.linear(L, with_base=False, acc="f32")
+    rows = np.where(np.all(L.idx == -1, axis=1))[0]
+    assert np.all(d32[rows] == 0)
