@@ -352,9 +352,10 @@ DecodeCfg decode_config(int64_t T, int64_t n_in, int64_t n_out)
     c.n_tiles = (int)((n_out + DEC_ROWS - 1) / DEC_ROWS);
     const int64_t wblocks = (n_in + DEC_WK - 1) / DEC_WK;          // 128-column blocks
     // each workgroup takes up to 8 blocks (one per wave); split further while the grid is
-    // smaller than the 256 CUs
+    // smaller than the device's CUs
+    const int n_cus = device_cu_count();
     int per = DEC_WAVES;
-    while (per > 1 && c.n_tiles * ((wblocks + per - 1) / per) < 256)
+    while (per > 1 && c.n_tiles * ((wblocks + per - 1) / per) < n_cus)
         per >>= 1;
     c.kr = per * DEC_WK;
     c.sk = (int)((n_in + c.kr - 1) / c.kr);
@@ -373,14 +374,9 @@ template <int TT, bool PW, bool MC>
 static hipError_t launch_tfm(DecodeArgs &a, const DecodeCfg &c, hipStream_t stream)
 {
     const size_t lds = (size_t)DEC_WAVES * 4 * TT * 64 * sizeof(float4);
-    static size_t lds_allowed = 64 * 1024;
-    if (lds > lds_allowed) {
-        hipError_t e = hipFuncSetAttribute((const void *)decode_gemm_kernel<TT, PW, MC>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess)
-            return e;
-        lds_allowed = lds;
-    }
+    if (hipError_t e = ensure_dynamic_lds((const void *)decode_gemm_kernel<TT, PW, MC>, lds);
+        e != hipSuccess)
+        return e;
     const dim3 grid((unsigned)(a.n_chunks * c.n_tiles * c.sk)), block(512);
     hipLaunchKernelGGL((decode_gemm_kernel<TT, PW, MC>), grid, block, lds, stream, a);
     return hipGetLastError();

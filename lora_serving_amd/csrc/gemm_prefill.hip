@@ -1348,22 +1348,13 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     // helper workgroups after the GEMM's tiles take the scattered tiles' shrink group items
     // while the tiles leave CUs idle (one workgroup per CU: 128 KB of LDS each)
     const int n_tiles = c.n_mtiles * c.n_ntiles;
-    int n_cus = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        n_cus = 0;
+    const int n_cus = device_cu_count();
     const int n_helpers = g != nullptr && c.may_scatter && n_tiles < n_cus ? n_cus - n_tiles : 0;
     ShrinkArgs s{};
     if (g != nullptr) {
         const size_t lds = (size_t)((g->S + 31) / 32) * 4 + (size_t)g->S * 4 + (size_t)c.list_stride * 4;
-        static size_t lds_allowed = 64 * 1024;
-        if (lds > lds_allowed) {
-            hipError_t e = hipFuncSetAttribute((const void *)tile_plan_kernel,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess)
-                return e;
-            lds_allowed = lds;
-        }
+        if (hipError_t e = ensure_dynamic_lds((const void *)tile_plan_kernel, lds); e != hipSuccess)
+            return e;
         hipLaunchKernelGGL(tile_plan_kernel, dim3(c.n_mtiles), dim3(256), lds, stream, idx,
                            (int)T, K, g->S, g->R, g->n_slices, (int)n_in, c.list_stride, tile_D,
                            tile_list, tile_toff, tile_gpre, tile_tok, c.tok_stride, tile_grp,
@@ -1395,18 +1386,17 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         s.tile_pbase = tile_pbase;
         s.sd_ks = sd_ks;
         s.skip_groups = n_helpers > 0 ? 1 : 0;
-        // three dense stages while the item tables leave room in the 160 KB of LDS, else two
+        // three dense stages while the item tables and the kernel's own __shared__ arrays
+        // leave room in the 160 KB of LDS, else two
         const size_t tables = (size_t)c.n_mtiles * SD_TABLE_BYTES;
-        s.stages = 3 * (size_t)SD_STAGE_BYTES + tables <= 160 * 1024 ? 3 : 2;
+        const size_t st_lds = kernel_static_lds((const void *)sgmv_shrink_kernel);
+        s.stages = 3 * (size_t)SD_STAGE_BYTES + tables + st_lds <= LDS_BYTES ? 3 : 2;
         const size_t sh_lds = (size_t)s.stages * SD_STAGE_BYTES + tables;
-        static size_t sh_allowed = 64 * 1024;
-        if (sh_lds > sh_allowed) {
-            hipError_t e = hipFuncSetAttribute((const void *)sgmv_shrink_kernel,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh_lds);
-            if (e != hipSuccess)
-                return e;
-            sh_allowed = sh_lds;
-        }
+        if (sh_lds + st_lds > LDS_BYTES)
+            return hipErrorInvalidValue;   // more tiles than SH_MAX_TILES allows
+        if (hipError_t e = ensure_dynamic_lds((const void *)sgmv_shrink_kernel, sh_lds);
+            e != hipSuccess)
+            return e;
         hipLaunchKernelGGL(sgmv_shrink_kernel, dim3(1024), dim3(SH_THREADS), sh_lds, stream, s);
         hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)c.n_mtiles * (PF_BM / SR_TOK)),
                            dim3(256), 0, stream, s);
@@ -1436,13 +1426,8 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     const size_t lds = (size_t)PF_STAGES * PF_STAGE_BYTES;                // 128 KB of stages
     const void *kfn = packed ? (const void *)prefill_gemm_kernel<true>
                              : (const void *)prefill_gemm_kernel<false>;
-    static size_t lds_allowed[2] = {0, 0};
-    if (lds > lds_allowed[packed ? 1 : 0]) {
-        hipError_t e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess)
-            return e;
-        lds_allowed[packed ? 1 : 0] = lds;
-    }
+    if (hipError_t e = ensure_dynamic_lds(kfn, lds); e != hipSuccess)
+        return e;
     trace_mark(stream, true);
     if (packed)
         hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3((unsigned)(n_tiles + n_helpers)),

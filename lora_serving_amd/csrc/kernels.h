@@ -7,6 +7,16 @@
 namespace mlora {
 
 constexpr int SORT_UNIT = 1024;   // entries per wave in the counting sort
+constexpr int MI355X_CUS = 256;   // CUs assumed when no device can be asked (host-only callers)
+constexpr size_t LDS_BYTES = 160 * 1024;   // LDS per CU on gfx950
+
+// ---- device_props.hip: per-device facts, cached under a lock ------------------------------
+// CUs of the current device (MI355X_CUS when there is no device to ask).
+int device_cu_count();
+// Static (__shared__) LDS of a kernel.
+size_t kernel_static_lds(const void *fn);
+// Raises the kernel's dynamic-LDS limit on the current device to at least `bytes` (once).
+hipError_t ensure_dynamic_lds(const void *fn, size_t bytes);
 constexpr int MLORA_MAX_SLICES_DEV = 4;
 constexpr int MLORA_MAX_RANK_DEV = 512;
 constexpr int MLORA_MAX_K_DEV = 8;

@@ -244,6 +244,14 @@ def workload_decode256(seed: int = 1006) -> Layer:
     return L
 
 
+def workload_mixed_qkv_prefill_first(seed: int = 1003) -> Layer:
+    """The mixed merged-QKV batch with its 2048-token segment ahead of the 256 one-token
+    requests (same draws otherwise): the result must not depend on the order of the parts."""
+    L = workload_mixed_qkv(seed=seed, prefill_first=True)
+    L.name = "mixed_qkv_prefill_first"
+    return L
+
+
 WORKLOADS = {
     "tiny": workload_tiny,
     "decode256": workload_decode256,
@@ -251,6 +259,7 @@ WORKLOADS = {
     "decode": workload_decode,
     "prefill": workload_prefill,
     "mixed_qkv": workload_mixed_qkv,
+    "mixed_qkv_prefill_first": workload_mixed_qkv_prefill_first,
     "compose": workload_compose,
 }
 

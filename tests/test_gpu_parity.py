@@ -324,19 +324,23 @@ def test_tiled_path_chunks_past_a_million_tokens(oracle_mod):
     assert tol_ok(y[toks], y_ref).all(), f"worst {worst(y[toks], y_ref):.3e}"
 
 
-def test_tiled_many_tiles_two_stage_shrink(oracle_mod):
-    """1821 tiles: the dense shrink items' LDS then holds two 48 KB stages (the tiles' item
-    tables take the rest), over three 64-column stages of n_in; tokens of the first, middle and
-    last tiles and the ragged end are checked against the oracle."""
+@pytest.mark.parametrize("n_tiles,extra", [(1816, 0), (1820, 0), (1820, 77)])
+def test_tiled_many_tiles_shrink_stages(oracle_mod, n_tiles, extra):
+    """The dense shrink items keep three 48 KB stages in LDS while those, the tiles' item tables
+    (9 bytes per tile) and the kernel's own __shared__ arrays fit in 160 KB, else two:
+    1816 tiles is the last count with three (8 bytes to spare), 1820 tiles (and 1821, with a
+    ragged last tile) take two.  Over three 64-column stages of n_in; tokens of the first,
+    middle and last tiles and the ragged end are checked against the oracle."""
     from lora_serving_amd import mlora
-    T = 1820 * 256 + 77
-    L = synth.random_layer(72, T=T, n_in=192, n_out=96, S=6, R=16, K=2, p_sentinel=0.25,
-                           contiguous=True)
-    say(f"[two-stage] T={T} n_in={L.n_in}")
+    T = n_tiles * 256 + extra
+    L = synth.random_layer(72 + n_tiles + extra, T=T, n_in=192, n_out=96, S=6, R=16, K=2,
+                           p_sentinel=0.25, contiguous=True)
+    say(f"[shrink stages] T={T} tiles={-(-T // 256)} n_in={L.n_in}")
     D = DevLayer(L)
     y = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_TILED))
-    toks = np.unique(np.array([0, 1, 255, 256, 511, T // 2, T // 2 + 1, T - 78, T - 77, T - 2,
-                               T - 1] + list(range(333, T, 9973)), np.int64))
+    toks = np.unique(np.array([0, 1, 255, 256, 511, T // 2, T // 2 + 1, T - 257, T - 256,
+                               T - 78, T - 77, T - 2, T - 1] + list(range(333, T, 9973)),
+                              np.int64))
     y_ref = oracle_mod.linear(L, tokens=toks)
     assert tol_ok(y[toks], y_ref).all(), f"worst {worst(y[toks], y_ref):.3e}"
 
@@ -451,8 +455,8 @@ def test_large_workloads_sampled(oracle_mod, which):
         check_linear(oracle_mod, L, tokens=toks, label=f"{which}:{L.name}")
 
 
-@pytest.mark.parametrize("which", ["decode", "decode256", "lm_head", "mixed_qkv", "prefill",
-                                   "compose"])
+@pytest.mark.parametrize("which", ["decode", "decode256", "lm_head", "mixed_qkv",
+                                   "mixed_qkv_prefill_first", "prefill", "compose"])
 def test_workloads_in_bench_configuration(oracle_mod, which):
     """Each bench workload called the way bench.py calls it: the slots carry the true-rank
     table, decode-sized batches (T <= 512) take the packed base weight.  Whole output for the
@@ -592,3 +596,43 @@ def test_validate_rejects_bad_index_and_rank():
     code, val = mlora.mlora_validate(D.idx, D.slots, rank=rk)
     assert code == mlora.MLORA_ERR_RANK and val == 32
     del torch
+
+
+def _mlora_kernels_launched(fn):
+    """Names of the library's kernels that fn() launches, from torch's profiler (kernel
+    activity of the device, whoever launched it)."""
+    import torch
+    from torch.profiler import ProfilerActivity, profile
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        fn()
+        torch.cuda.synchronize()
+    names = set()
+    for e in prof.events():
+        n = e.name
+        if "mlora::" in n:
+            names.add(n.split("mlora::", 1)[1].split("<", 1)[0].split("(", 1)[0])
+    return names
+
+
+@pytest.mark.parametrize("path", ["decode", "tiled"])
+def test_no_adapters_flag_launches_base_kernels_only(path):
+    """With MLORA_NO_ADAPTERS no LoRA kernel is launched ("Multi-LoRA Serving Explained": the
+    LoRA kernels are skipped when no token uses an adapter): the decode path runs its GEMM and
+    the split-K finish only, the tiled path its GEMM only.  Without the flag the same call
+    launches the shrink / plan kernels as well (so the profiler does see them)."""
+    from lora_serving_amd import mlora
+    L = synth.random_layer(77, T=300, n_in=512, n_out=768, S=6, R=16, K=2, p_sentinel=0.2,
+                           contiguous=(path == "tiled"))
+    D = DevLayer(L)
+    pf = mlora.MLORA_PATH_DECODE if path == "decode" else mlora.MLORA_PATH_TILED
+    D.linear(flags=pf)
+    with_lora = _mlora_kernels_launched(lambda: D.linear(flags=pf))
+    base_only = _mlora_kernels_launched(lambda: D.linear(flags=pf | mlora.MLORA_NO_ADAPTERS))
+    say(f"[no-adapters] {path}: with adapters {sorted(with_lora)}, flag {sorted(base_only)}")
+    if path == "decode":
+        assert base_only == {"decode_gemm_kernel", "decode_finish_kernel"}
+        assert with_lora == base_only            # the shrink rides in the GEMM pass
+    else:
+        assert base_only == {"prefill_gemm_kernel"}
+        assert {"tile_plan_kernel", "sgmv_shrink_kernel"} <= with_lora
