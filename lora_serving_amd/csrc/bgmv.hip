@@ -89,13 +89,28 @@ __global__ __launch_bounds__(256) void shrink_rows_kernel(const uint16_t *__rest
     const int64_t t = p / K;
     const int j = (int)(p - t * K);
     float *out = v + ((int64_t)j * T + t) * wd + r0;
+    const uint16_t *xt = x + t * n_in;
+    const int64_t step = (int64_t)blockDim.x * 8;
+    // the first round's x chunks do not depend on the slot id: in flight before it is read
+    u32x4 xv0[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t k = (int64_t)threadIdx.x * 8 + h * step;
+        xv0[h] = k < n_in ? *(const u32x4 *)(xt + k) : u32x4{0u, 0u, 0u, 0u};
+    }
     const int a = idx[p];
-    if (a < 0) {
+    // rows of this block below the adapter's rank (rounded to 8); the others are zero padding,
+    // neither read nor multiplied
+    const int r8 = a >= 0 ? slot_rank8(g.rank, a, g.R) : 0;
+    uint32_t live = 0;
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+        live |= (r < nr && (r0 + r) % g.R < r8 ? 1u : 0u) << r;
+    if (live == 0) {
         if ((int)threadIdx.x < nr)
             out[threadIdx.x] = 0.f;
         return;
     }
-    const uint16_t *xt = x + t * n_in;
     const uint16_t *Aa = g.A + ((int64_t)a * wd + r0) * n_in;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -104,19 +119,21 @@ __global__ __launch_bounds__(256) void shrink_rows_kernel(const uint16_t *__rest
 #pragma unroll
     for (int r = 0; r < RB; ++r)
         acc[r] = 0.f;
-    // two 16-byte chunks per lane in flight: x and the RB rows of both, then their products
-    const int64_t step = (int64_t)blockDim.x * 8;
+    // two 16-byte chunks per lane in flight: x and the live rows of both, then their products
     for (int64_t k0 = (int64_t)threadIdx.x * 8; k0 < n_in; k0 += 2 * step) {
         u32x4 xv[2], av[2][RB];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t k = k0 + h * step;
             const bool ok = k < n_in;
-            xv[h] = ok ? *(const u32x4 *)(xt + k) : u32x4{0u, 0u, 0u, 0u};
+            if (k0 == (int64_t)threadIdx.x * 8)
+                xv[h] = xv0[h];
+            else
+                xv[h] = ok ? *(const u32x4 *)(xt + k) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int r = 0; r < RB; ++r)
-                av[h][r] = ok && r < nr ? *(const u32x4 *)(Aa + (int64_t)r * n_in + k)
-                                        : u32x4{0u, 0u, 0u, 0u};
+                av[h][r] = ok && (live >> r & 1u) ? *(const u32x4 *)(Aa + (int64_t)r * n_in + k)
+                                                  : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -212,7 +229,6 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(
     const int nrows = (int)min((int64_t)ER, n_out - n0);
     const int R = g.R;
     const int wd = g.n_slices * R;
-    const int G = R >> 3;                 // lanes per output row (a power of two <= 64)
     const int lane = threadIdx.x & 63;
     const int r4 = threadIdx.x * 4;       // first of this thread's 4 output rows
     const bool vec = ((n_out & 3) == 0) && r4 + 3 < nrows;
@@ -246,20 +262,30 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(
             delta[r] = 0.f;
     bool first = true;
 
-    const int64_t total = (int64_t)nrows * R;          // bf16 elements of one B block
     const int64_t step = (int64_t)blockDim.x * 8;
     for (int j = 0; j < K; ++j) {
         const int a = idx[t * K + j];
         if (a < 0)
             continue;
+        // this adapter's columns: the smallest power of two at or above its rank (rounded to
+        // 8), never above R; the columns past it are zero padding and are not read
+        const int r8 = slot_rank8(g.rank, a, R);
+        int lw = 3;                                     // log2 of the columns walked per row
+        while ((1 << lw) < r8)
+            ++lw;
+        const int RW = 1 << lw;
+        const int G = RW >> 3;                          // lanes per output row
+        const int total = nrows << lw;                  // elements of the block walked
         const uint16_t *Bb = g.B + ((int64_t)a * n_out + n0) * R;
-        for (int64_t e0 = 0; e0 < total; e0 += step * EXPAND_GROUP) {
+        for (int e0 = 0; e0 < total; e0 += (int)step * EXPAND_GROUP) {
             // B loads of this group first, then (first group only) v of this slot into LDS
             u32x4 bv[EXPAND_GROUP];
 #pragma unroll
             for (int u = 0; u < EXPAND_GROUP; ++u) {
-                const int64_t e = e0 + u * step + (int64_t)threadIdx.x * 8;
-                bv[u] = e < total ? *(const u32x4 *)(Bb + e) : u32x4{0u, 0u, 0u, 0u};
+                const int e = e0 + u * (int)step + (int)threadIdx.x * 8;
+                const int row = e >> lw;
+                bv[u] = e < total ? *(const u32x4 *)(Bb + (int64_t)row * R + (e & (RW - 1)))
+                                  : u32x4{0u, 0u, 0u, 0u};
             }
             if (e0 == 0) {
                 const float coef =
@@ -274,12 +300,12 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(
             }
 #pragma unroll
             for (int u = 0; u < EXPAND_GROUP; ++u) {
-                const int64_t e = e0 + u * step + (int64_t)threadIdx.x * 8;
+                const int e = e0 + u * (int)step + (int)threadIdx.x * 8;
                 float ps = 0.f;
                 int row = 0;
                 if (e < total) {
-                    row = (int)(e / R);
-                    const int rho0 = (int)(e - (int64_t)row * R);
+                    row = e >> lw;
+                    const int rho0 = e & (RW - 1);
                     const float *vv = vs + slice_of(g, n0 + row) * R + rho0;
                     ps += bf16_lo(bv[u].x) * vv[0];
                     ps += bf16_hi(bv[u].x) * vv[1];

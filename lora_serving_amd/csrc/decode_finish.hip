@@ -254,8 +254,11 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
                             if (u * 8 < R)
                                 dj += dot8(bp[i][u], vv + u * 8);
                     } else {
+                        // the row's columns up to the adapter's rank (rounded to 8; the rest
+                        // multiply zero padding)
                         const uint16_t *brow = g.B + ((int64_t)a * n_out + min(n + i, n_out - 1)) * R;
-                        for (int rho = 0; rho < R; rho += 8)
+                        const int r8 = slot_rank8(g.rank, a, R);
+                        for (int rho = 0; rho < r8; rho += 8)
                             dj += dot8(*(const u32x4 *)(brow + rho), vv + rho);
                     }
                     d4[i] += dj;

@@ -325,7 +325,15 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
             const int a = idx[p];
             if (a < 0)
                 continue;
+            const int r8 = slot_rank8(g.rank, a, g.R);
             for (int r0 = (p == tile ? 16 : 0); r0 < wd; r0 += 16) {
+                if (g.R >= 16 && r0 % g.R >= r8) {
+                    // all 16 rows of the piece past the adapter's rank: exact zeros, no loads
+                    const int t = p / K;
+                    if (threadIdx.x < 16)
+                        upart[(((int64_t)s * K + (p - t * K)) * T + t) * wd + r0 + threadIdx.x] = 0.f;
+                    continue;
+                }
                 if (!synced) {
                     lds_barrier();
                     synced = true;
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
                 const int arow = r0 + r;
                 const uint16_t *ap = g.A + ((int64_t)a * wd + min(arow, wd - 1)) * n_in;
                 // rows past the adapter's rank (zero padding) come from the zero block
-                const bool rok = arow < wd && arow % g.R < slot_rank8(g.rank, a, g.R);
+                const bool rok = arow < wd && arow % g.R < r8;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int c = col(ks);

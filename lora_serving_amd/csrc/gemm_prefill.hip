@@ -62,6 +62,17 @@ __device__ __forceinline__ bool tile_scattered(int D, int R, int n_in)
     return D > 0 && (int64_t)D * 2 * R > n_in / 2;
 }
 
+// Width of one adapter's half of a tile's V block: the smallest power of two at or above the
+// largest true rank (rounded to 8) among the tile's adapters, never above R.  Columns past an
+// adapter's rank would multiply its zero padding, so they are left out of the extra k-steps.
+__device__ __forceinline__ int tile_vwidth(int r8max, int R)
+{
+    int w = 8;
+    while (w < r8max)
+        w <<= 1;
+    return min(w, R);
+}
+
 // Exclusive scan of two values over the 256 threads of a workgroup; ws holds 8 ints.
 __device__ __forceinline__ void block_scan2(int v1, int v2, int *ws, int &ex1, int &ex2, int &all1,
                                             int &all2)
@@ -95,12 +106,13 @@ __device__ __forceinline__ void block_scan2(int v1, int v2, int *ws, int &ex1, i
 // tokens inside a list is whatever the atomics give; each token's results do not depend on it.
 __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restrict__ idx, int T,
                                                         int K, int S, int R, int n_slices, int n_in,
+                                                        const int32_t *__restrict__ rank,
                                                         int list_stride, int32_t *tile_D,
+                                                        int32_t *tile_w,
                                                         int32_t *tile_list, int32_t *tile_toff,
                                                         int32_t *tile_gpre, uint8_t *tile_tok,
                                                         int tok_stride, int4 *tile_grp,
-                                                        int grp_stride, uint16_t *vcat,
-                                                        int64_t vcat_tile_elems)
+                                                        int grp_stride)
 {
     extern __shared__ uint32_t plan_lds[];         // bits[(S+31)/32], cnt[S], lst[list_stride]
     const int nw = (S + 31) / 32;
@@ -154,8 +166,22 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
     if (threadIdx.x == 0)
         tile_D[m] = base;
     const int D = base;
+    __syncthreads();                              // lst complete
+    // the tile's V width: largest rounded rank among its adapters (block maximum via wsum)
+    int r8max = 0;
+    for (int d = threadIdx.x; d < D; d += blockDim.x)
+        r8max = max(r8max, slot_rank8(rank, lst[d], R));
+    for (int off = 32; off >= 1; off >>= 1)
+        r8max = max(r8max, __shfl_xor(r8max, off, 64));
+    if ((threadIdx.x & 63) == 0)
+        wsum[threadIdx.x >> 6] = r8max;
+    __syncthreads();
+    r8max = max(max(wsum[0], wsum[1]), max(wsum[2], wsum[3]));
+    const int VW = tile_vwidth(r8max, R);
+    if (threadIdx.x == 0)
+        tile_w[m] = VW;
+    __syncthreads();                              // wsum free again
     if (tile_scattered(D, R, n_in)) {
-        __syncthreads();                          // lst complete
         int32_t *toff = tile_toff + (int64_t)m * (list_stride + 1);
         int32_t *gpre = tile_gpre + (int64_t)m * (list_stride + 1);
         int obase = 0, gbase = 0;
@@ -199,21 +225,8 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
             }
         }
     }
-    // zero the padding columns [2*D*R, KXs) of every slice block of this tile's V
-    const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
-    const int pad = kxs - D * 2 * R;
-    if (pad > 0) {
-        const int pitch = n_slices * kxs;
-        uint16_t *vt = vcat + (int64_t)m * vcat_tile_elems;
-        const int per_row = n_slices * pad;
-        for (int e = threadIdx.x; e < PF_BM * per_row; e += blockDim.x) {
-            const int row = e / per_row;
-            const int rem = e - row * per_row;
-            const int sg = rem / pad;
-            const int c = D * 2 * R + (rem - sg * pad);
-            vt[(int64_t)row * pitch + sg * kxs + c] = 0;
-        }
-    }
+    // (the V block's columns past 2 D VW, up to the 64-column k-step, are never written: the
+    // GEMM copies zeros in their place)
 }
 
 // ------------------------------------------------------------------------------------------
@@ -253,6 +266,7 @@ struct ShrinkArgs {
     const float *scale;
     int n_mtiles, list_stride;
     const int32_t *tile_D, *tile_list;
+    const int32_t *tile_w;   // V width of each tile (tile plan)
     uint16_t *vcat;
     int64_t vcat_tile_elems;
     int32_t *tile_ord;    // out: ordinal of a scattered tile (< sc_cap), else -1
@@ -441,7 +455,8 @@ __device__ __forceinline__ void sh_dense_item(const ShrinkArgs &P, int m, int rb
         }
         return;
     }
-    const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
+    const int VW = P.tile_w[m];
+    const int kxs = ((D * 2 * VW + PF_BK - 1) / PF_BK) * PF_BK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int tl = wave * 64 + j * 16 + r;
@@ -464,7 +479,8 @@ __device__ __forceinline__ void sh_dense_item(const ShrinkArgs &P, int m, int rb
                     dprev = d;
                 }
                 const int rin = a_row - d * wd, sg = rin / R, rho = rin - sg * R;
-                sh_store_v(vrow + sg * kxs + d * 2 * R + rho, R, cf * acc[i][j][e]);
+                if (rho < VW)   // rows past VW are past the rank: zeros, not in the V block
+                    sh_store_v(vrow + sg * kxs + d * 2 * VW + rho, VW, cf * acc[i][j][e]);
             }
         }
     }
@@ -548,9 +564,10 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
     if (j < ng) {
         const int tl = tk[j];
         const float cf = sh_coef(P, m * PF_BM + tl, a);
-        const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
+        const int VW = P.tile_w[m];
+        const int kxs = ((D * 2 * VW + PF_BK - 1) / PF_BK) * PF_BK;
         uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems + (int64_t)tl * (g.n_slices * kxs) +
-                         d * 2 * R;
+                         d * 2 * VW;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int rl = rp + e, row = rb * SG_ROWS + rl;
@@ -565,7 +582,8 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
                 sum += comp == 0 ? v4.x : comp == 1 ? v4.y : comp == 2 ? v4.z : v4.w;
             }
             const int sg = row / R, rho = row - sg * R;
-            sh_store_v(vrow + sg * kxs + rho, R, cf * sum);
+            if (rho < VW)
+                sh_store_v(vrow + sg * kxs + rho, VW, cf * sum);
         }
     }
     __syncthreads();
@@ -703,7 +721,8 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(ShrinkArgs P)
     }
     __syncthreads();
     const int rows4 = D * wd / 4;                  // groups of 4 rows
-    const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
+    const int VW = P.tile_w[m];
+    const int kxs = ((D * 2 * VW + PF_BK - 1) / PF_BK) * PF_BK;
     for (int e = threadIdx.x; e < nt * rows4; e += 256) {
         const int tt = e / rows4, a_row = (e - tt * rows4) * 4;
         const int tl = t0l + tt;
@@ -732,8 +751,10 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(ShrinkArgs P)
             if (s_idx[tt * K + j] == a)
                 cf += s_sc[tt * K + j] * f;
         const int rin = a_row - d * wd, sg = rin / R, rho = rin - sg * R;
+        if (rho >= VW)
+            continue;   // past the rank (the 4 rows share it: VW is a multiple of 8)
         uint16_t *vp = P.vcat + (int64_t)m * P.vcat_tile_elems + (int64_t)tl * (g.n_slices * kxs) +
-                       sg * kxs + d * 2 * R + rho;
+                       sg * kxs + d * 2 * VW + rho;
         const float v[4] = {cf * sum.x, cf * sum.y, cf * sum.z, cf * sum.w};
         uint16_t hi[4], lo[4];
 #pragma unroll
@@ -743,7 +764,7 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(ShrinkArgs P)
         }
         *(u32x2 *)vp = u32x2{(uint32_t)hi[0] | (uint32_t)hi[1] << 16,
                              (uint32_t)hi[2] | (uint32_t)hi[3] << 16};
-        *(u32x2 *)(vp + R) = u32x2{(uint32_t)lo[0] | (uint32_t)lo[1] << 16,
+        *(u32x2 *)(vp + VW) = u32x2{(uint32_t)lo[0] | (uint32_t)lo[1] << 16,
                                    (uint32_t)lo[2] | (uint32_t)lo[3] << 16};
     }
 }
@@ -761,6 +782,7 @@ struct GemmArgs {
     const uint16_t *vcat;
     int64_t vcat_tile_elems;
     const int32_t *tile_D, *tile_list;
+    const int32_t *tile_w;     // V width of each tile
     int list_stride;
     const int32_t *tile_ord;   // scattered tile ordinal (sgmv_shrink_kernel), or -1
     float *part_sc;            // fp32 [sc_cap][256][n_out] sums of scattered tiles
@@ -827,7 +849,7 @@ constexpr int PF_STAGE_BYTES = 2 * 256 * PF_KS * 2;
 template <bool PW>
 __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q, int nk_main,
                                          int nk_extra, int m0, int n0, const uint16_t *vtile,
-                                         int D, int kxs, int sg_lo, int kb_per_slice,
+                                         int D, int kxs, int VW, int sg_lo, int kb_per_slice,
                                          const int *slist, int wave, int lane)
 {
     const int rr = lane >> 3;                       // row within the 8-row block
@@ -858,12 +880,12 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
         const int sg = sg_lo + ke / kb_per_slice;
         const int kk0 = (ke % kb_per_slice) * PF_KS;          // first column of the step
         const int kk = kk0 + c * 8;                           // column within the slice block
-        const int dd = kk / (2 * R);
-        const int rho = (kk - dd * 2 * R) & (R - 1);
-        // the step's 64 columns meet at most four adapters (2R >= 16): dd0 .. dd0 + 3.  Their
+        const int dd = kk / (2 * VW);
+        const int rho = (kk - dd * 2 * VW) & (VW - 1);
+        // the step's 64 columns meet at most four adapters (2 VW >= 16): dd0 .. dd0 + 3.  Their
         // ids are read with scalar loads (constant address space), which wait on the scalar
         // counter only: a vector load here would also wait for every copy in flight.
-        const int dd0 = __builtin_amdgcn_readfirstlane(kk0 / (2 * R));
+        const int dd0 = __builtin_amdgcn_readfirstlane(kk0 / (2 * VW));
         const __attribute__((address_space(4))) int *cl =
             (const __attribute__((address_space(4))) int *)slist;
         const int a0 = cl[min(dd0, D - 1)];
@@ -881,8 +903,8 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
                 const int f = wave * 4 + b;
                 const int bn = n0 + (f >> 1) * 16 + (lane & 15);
                 const int bkk = kk0 + ((f & 1) * 4 + (lane >> 4)) * 8;
-                const int bdd = bkk / (2 * R);
-                const int brho = (bkk - bdd * 2 * R) & (R - 1);
+                const int bdd = bkk / (2 * VW);
+                const int brho = (bkk - bdd * 2 * VW) & (VW - 1);
                 const int be = bdd - dd0;
                 const int ba = be == 0 ? a0 : be == 1 ? a1 : be == 2 ? a2 : a3;
                 const bool bok = bdd < D && bn >= s_lo && bn < s_hi;
@@ -895,7 +917,9 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
                 pf_dma(ok ? (const void *)gb : (const void *)pf_zero16, sw + (wave * 4 + b) * 8 * PF_KS);
             }
             const uint16_t *gv = vtile + (int64_t)row * (P.g.n_slices * kxs) + sg * kxs + kk;
-            pf_dma((const void *)gv, sx + (wave * 4 + b) * 8 * PF_KS);
+            // columns past the tile's adapters (up to the step's end) are not written: zeros
+            pf_dma(kk < D * 2 * VW ? (const void *)gv : (const void *)pf_zero16,
+                   sx + (wave * 4 + b) * 8 * PF_KS);
         }
     }
 }
@@ -959,12 +983,13 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
     const int r = lane & 15, gq = lane >> 4;
 
     const int nk_main = (P.n_in + PF_KS - 1) / PF_KS;
-    int D = 0, kxs = 0, sg_lo = 0, sg_hi = -1, kb_per_slice = 1;
+    int D = 0, kxs = 0, VW = 8, sg_lo = 0, sg_hi = -1, kb_per_slice = 1;
     // a scattered tile gets no extra k-steps: its fp32 sums go to part_sc for the expand kernel
     const int ord = P.lora ? P.tile_ord[mt] : -1;
     if (P.lora && ord < 0) {
         D = P.tile_D[mt];
-        kxs = ((D * 2 * P.g.R + PF_BK - 1) / PF_BK) * PF_BK;
+        VW = P.tile_w[mt];
+        kxs = ((D * 2 * VW + PF_BK - 1) / PF_BK) * PF_BK;
         if (D > 0) {
             kb_per_slice = kxs / PF_KS;
             const int nlast = min(n0 + PF_BN, P.n_out) - 1;
@@ -992,7 +1017,7 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
 #pragma unroll
     for (int q = 0; q < PF_STAGES; ++q)
         pf_issue<PW>(P, pf_lds + q * (PF_STAGE_BYTES / 2), min(q, nk - 1), nk_main, nk_extra, m0, n0,
-                 vtile, D, kxs, sg_lo, kb_per_slice, slist, wave, lane);
+                 vtile, D, kxs, VW, sg_lo, kb_per_slice, slist, wave, lane);
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");    // stage 0 (8 copies per stage)
     lds_barrier();
     for (int q = 0; q < nk; ++q) {
@@ -1001,7 +1026,7 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stage q+1
         lds_barrier();                                      // also: stage q fully read
         pf_issue<PW>(P, st, min(q + PF_STAGES, nk - 1), nk_main, nk_extra, m0, n0, vtile, D, kxs,
-                 sg_lo, kb_per_slice, slist, wave, lane);
+                 VW, sg_lo, kb_per_slice, slist, wave, lane);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no copy outlives the workgroup
 
@@ -1064,6 +1089,7 @@ struct ScArgs {
     SlotGeom g;
     const int32_t *idx;
     const int32_t *tile_D, *tile_list;
+    const int32_t *tile_w;
     int list_stride;
     const int32_t *tile_toff, *tile_gpre;
     const uint8_t *tile_tok;
@@ -1124,9 +1150,10 @@ __device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int m, 
     const bool last = below == n_dist - 1;
     const int rk = slot_rank8(g.rank, a, R);
 
-    const int kxs = ((D * 2 * R + PF_BK - 1) / PF_BK) * PF_BK;
+    const int VW = P.tile_w[m];
+    const int kxs = ((D * 2 * VW + PF_BK - 1) / PF_BK) * PF_BK;
     const uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems + (int64_t)tl * (g.n_slices * kxs) +
-                           d * 2 * R + gq * 8;
+                           d * 2 * VW + gq * 8;
     const uint16_t *brow0 = g.B + (int64_t)a * P.n_out * R + gq * 8;
     float *po = P.part_sc + ((int64_t)ord * PF_BM + tl) * P.n_out;
 
@@ -1165,7 +1192,7 @@ __device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int m, 
                 const bool kok = k + gq * 8 < rk;
                 const uint16_t *vp = vrow + sg * kxs + k;
                 vh[h] = *(const u32x4 *)(tok_ok && kok ? (const void *)vp : (const void *)pf_zero16);
-                vl[h] = *(const u32x4 *)(tok_ok && kok ? (const void *)(vp + R) : (const void *)pf_zero16);
+                vl[h] = *(const u32x4 *)(tok_ok && kok ? (const void *)(vp + VW) : (const void *)pf_zero16);
 #pragma unroll
                 for (int f = 0; f < 4; ++f)
                     bv[f][h] = *(const u32x4 *)(sgb[f] == sg && kok
@@ -1286,7 +1313,7 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
 
 // Workspace regions of the tiled path, each 256-byte aligned, in this order.
 struct PrefillLayout {
-    size_t tile_D, tile_list, tile_toff, tile_gpre, tile_tok, tile_ord, sc_tiles, part_sc, vcat,
+    size_t tile_w, tile_D, tile_list, tile_toff, tile_gpre, tile_tok, tile_ord, sc_tiles, part_sc, vcat,
         tile_pbase, sd_ks, sd_part, tile_grp, total;
 };
 
@@ -1297,7 +1324,8 @@ static PrefillLayout prefill_layout(const PrefillCfg &c)
     PrefillLayout L;
     const size_t lists = al256((size_t)c.n_mtiles * c.list_stride * sizeof(int32_t));
     const size_t offs = al256((size_t)c.n_mtiles * (c.list_stride + 1) * sizeof(int32_t));
-    L.tile_D = 0;
+    L.tile_w = 0;
+    L.tile_D = L.tile_w + al256((size_t)c.n_mtiles * sizeof(int32_t));
     L.tile_list = L.tile_D + al256((size_t)c.n_mtiles * sizeof(int32_t));
     L.tile_toff = L.tile_list + lists;
     L.tile_gpre = L.tile_toff + offs;
@@ -1330,6 +1358,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     uint8_t *p = (uint8_t *)ws;
     const PrefillLayout WL = prefill_layout(c);
     int32_t *tile_D = (int32_t *)(p + WL.tile_D);
+    int32_t *tile_w = (int32_t *)(p + WL.tile_w);
     int32_t *tile_list = (int32_t *)(p + WL.tile_list);
     int32_t *tile_toff = (int32_t *)(p + WL.tile_toff);
     int32_t *tile_gpre = (int32_t *)(p + WL.tile_gpre);
@@ -1356,9 +1385,9 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         if (hipError_t e = ensure_dynamic_lds((const void *)tile_plan_kernel, lds); e != hipSuccess)
             return e;
         hipLaunchKernelGGL(tile_plan_kernel, dim3(c.n_mtiles), dim3(256), lds, stream, idx,
-                           (int)T, K, g->S, g->R, g->n_slices, (int)n_in, c.list_stride, tile_D,
-                           tile_list, tile_toff, tile_gpre, tile_tok, c.tok_stride, tile_grp,
-                           c.grp_stride, vcat, c.vcat_tile_elems);
+                           (int)T, K, g->S, g->R, g->n_slices, (int)n_in, g->rank, c.list_stride,
+                           tile_D, tile_w, tile_list, tile_toff, tile_gpre, tile_tok, c.tok_stride, tile_grp,
+                           c.grp_stride);
         s.x = x;
         s.T = (int)T;
         s.n_in = (int)n_in;
@@ -1369,6 +1398,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         s.n_mtiles = c.n_mtiles;
         s.list_stride = c.list_stride;
         s.tile_D = tile_D;
+        s.tile_w = tile_w;
         s.tile_list = tile_list;
         s.vcat = vcat;
         s.vcat_tile_elems = c.vcat_tile_elems;
@@ -1416,6 +1446,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     a.vcat = vcat;
     a.vcat_tile_elems = c.vcat_tile_elems;
     a.tile_D = tile_D;
+    a.tile_w = tile_w;
     a.tile_list = tile_list;
     a.list_stride = c.list_stride;
     a.tile_ord = tile_ord;
@@ -1445,6 +1476,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         x2.g = *g;
         x2.idx = idx;
         x2.tile_D = tile_D;
+        x2.tile_w = tile_w;
         x2.tile_list = tile_list;
         x2.list_stride = c.list_stride;
         x2.tile_toff = tile_toff;
