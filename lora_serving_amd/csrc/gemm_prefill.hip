@@ -925,31 +925,59 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
 }
 
 // MFMAs of one stage (two k-steps of 32): wave (wn, wm) owns W rows wn*64 .. +64 and tokens
-// wm*128 .. +128.
+// wm*128 .. +128.  The operand reads run one group ahead of the MFMAs (a group: one k-step's two
+// 16-token fragments against the four W fragments), so a wave never waits for the LDS right
+// after issuing its reads; each accumulator still takes k-step 0, then 1.
 template <bool PW>
 __device__ __forceinline__ void pf_compute(const uint16_t *st, int wn, int wm, int r, int gq,
                                            f32x4 (&acc)[4][8])
 {
     const uint16_t *sw = st, *sx = st + 256 * PF_KS;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    auto rd_a = [&](int ks, int i) -> bf16x8 {
         const int pos = (ks * 4 + gq) ^ (r & 7);
-        bf16x8 af[4];
+        if constexpr (PW)
+            return *(const bf16x8 *)(sw + (((wn * 4 + i) * 2 + ks) * 64 + gq * 16 + r) * 8);
+        else
+            return *(const bf16x8 *)(sw + ((wn * 64 + i * 16 + r) * 8 + pos) * 8);
+    };
+    auto rd_b = [&](int ks, int j) -> bf16x8 {
+        const int pos = (ks * 4 + gq) ^ (r & 7);
+        return *(const bf16x8 *)(sx + ((wm * 128 + j * 16 + r) * 8 + pos) * 8);
+    };
+    bf16x8 af[2][4], bv[2][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (PW)
-                af[i] = *(const bf16x8 *)(sw + (((wn * 4 + i) * 2 + ks) * 64 + gq * 16 + r) * 8);
-            else
-                af[i] = *(const bf16x8 *)(sw + ((wn * 64 + i * 16 + r) * 8 + pos) * 8);
+    for (int i = 0; i < 4; ++i)
+        af[0][i] = rd_a(0, i);
+    bv[0][0] = rd_b(0, 0);
+    bv[0][1] = rd_b(0, 1);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {              // group g: k-step g / 4, fragments 2 (g % 4) + 0, 1
+        const int ks = g >> 2, jp = g & 3, cur = g & 1;
+        if (g + 1 < 8) {
+            const int nks = (g + 1) >> 2, njp = (g + 1) & 3;
+            if (njp == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    af[nks][i] = rd_a(nks, i);
+            }
+            bv[cur ^ 1][0] = rd_b(nks, 2 * njp);
+            bv[cur ^ 1][1] = rd_b(nks, 2 * njp + 1);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bf16x8 bv = *(const bf16x8 *)(sx + ((wm * 128 + j * 16 + r) * 8 + pos) * 8);
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv, acc[i][j], 0, 0, 0);
-        }
+                acc[i][2 * jp + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    af[ks][i], bv[cur][jj], acc[i][2 * jp + jj], 0, 0, 0);
     }
+    // keep that order in the schedule: the first group's 6 reads, then for every group the
+    // next group's reads (2, or 6 where the next k-step's W fragments start) before its 8 MFMAs
+#define PF_SG(ds) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0); \
+                  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    PF_SG(2) PF_SG(2) PF_SG(2) PF_SG(6) PF_SG(2) PF_SG(2) PF_SG(2)
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+#undef PF_SG
 }
 
 template <bool PW>
