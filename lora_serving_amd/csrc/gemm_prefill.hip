@@ -846,7 +846,7 @@ constexpr int PF_STAGE_BYTES = 2 * 256 * PF_KS * 2;
 // the LoRA extra steps) into buffer `st`: 4 blocks of 8 W rows and 4 of 8 tokens per wave.
 // With a packed W (PW) the W side of a stage is 32 fragments of 16 rows x 32 columns in lane
 // order instead (4 per wave), for the base steps and the LoRA steps alike.
-template <bool PW>
+template <bool PW, bool BASE_ONLY = false>
 __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q, int nk_main,
                                          int nk_extra, int m0, int n0, const uint16_t *vtile,
                                          int D, int kxs, int VW, int sg_lo, int kb_per_slice,
@@ -855,7 +855,7 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
     const int rr = lane >> 3;                       // row within the 8-row block
     const int c = (lane & 7) ^ rr;                  // chunk this lane's position holds
     uint16_t *sw = st, *sx = st + 256 * PF_KS;
-    if (q < nk_main) {
+    if (BASE_ONLY || q < nk_main) {
         const int k = q * PF_KS + c * 8;
         const bool ok = k < P.n_in;
 #pragma unroll
@@ -874,7 +874,7 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
             const uint16_t *gx = P.x + (int64_t)min(m0 + row, P.T - 1) * P.n_in + k;
             pf_dma(ok ? (const void *)gx : (const void *)pf_zero16, sx + (wave * 4 + b) * 8 * PF_KS);
         }
-    } else {
+    } else if constexpr (!BASE_ONLY) {
         const int R = P.g.R;
         const int ke = min(q - nk_main, nk_extra - 1);
         const int sg = sg_lo + ke / kb_per_slice;
@@ -929,27 +929,52 @@ __device__ __forceinline__ void pf_issue(const GemmArgs &P, uint16_t *st, int q,
 // 16-token fragments against the four W fragments), so a wave never waits for the LDS right
 // after issuing its reads; each accumulator still takes k-step 0, then 1.
 template <bool PW>
+__device__ __forceinline__ bf16x8 pf_rd_a(const uint16_t *st, int wn, int r, int gq, int ks, int i)
+{
+    const uint16_t *sw = st;
+    const int pos = (ks * 4 + gq) ^ (r & 7);
+    if constexpr (PW)
+        return *(const bf16x8 *)(sw + (((wn * 4 + i) * 2 + ks) * 64 + gq * 16 + r) * 8);
+    else
+        return *(const bf16x8 *)(sw + ((wn * 64 + i * 16 + r) * 8 + pos) * 8);
+}
+
+__device__ __forceinline__ bf16x8 pf_rd_b(const uint16_t *st, int wm, int r, int gq, int ks, int j)
+{
+    const uint16_t *sx = st + 256 * PF_KS;
+    const int pos = (ks * 4 + gq) ^ (r & 7);
+    return *(const bf16x8 *)(sx + ((wm * 128 + j * 16 + r) * 8 + pos) * 8);
+}
+
+// The first MFMA group's operands of a stage (k-step 0: the four W fragments and token
+// fragments 0, 1), read as soon as the stage is published, ahead of the copy issue.
+template <bool PW>
+__device__ __forceinline__ void pf_prefetch(const uint16_t *st, int wn, int wm, int r, int gq,
+                                            bf16x8 (&a0)[4], bf16x8 (&b0)[2])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        a0[i] = pf_rd_a<PW>(st, wn, r, gq, 0, i);
+    b0[0] = pf_rd_b(st, wm, r, gq, 0, 0);
+    b0[1] = pf_rd_b(st, wm, r, gq, 0, 1);
+}
+
+// MFMAs of one stage (two k-steps of 32): wave (wn, wm) owns W rows wn*64 .. +64 and tokens
+// wm*128 .. +128.  The operand reads run one group ahead of the MFMAs (a group: one k-step's two
+// 16-token fragments against the four W fragments; the first group's come from pf_prefetch), so
+// a wave never waits for the LDS right after issuing its reads; each accumulator still takes
+// k-step 0, then 1.
+template <bool PW>
 __device__ __forceinline__ void pf_compute(const uint16_t *st, int wn, int wm, int r, int gq,
+                                           const bf16x8 (&a0)[4], const bf16x8 (&b0)[2],
                                            f32x4 (&acc)[4][8])
 {
-    const uint16_t *sw = st, *sx = st + 256 * PF_KS;
-    auto rd_a = [&](int ks, int i) -> bf16x8 {
-        const int pos = (ks * 4 + gq) ^ (r & 7);
-        if constexpr (PW)
-            return *(const bf16x8 *)(sw + (((wn * 4 + i) * 2 + ks) * 64 + gq * 16 + r) * 8);
-        else
-            return *(const bf16x8 *)(sw + ((wn * 64 + i * 16 + r) * 8 + pos) * 8);
-    };
-    auto rd_b = [&](int ks, int j) -> bf16x8 {
-        const int pos = (ks * 4 + gq) ^ (r & 7);
-        return *(const bf16x8 *)(sx + ((wm * 128 + j * 16 + r) * 8 + pos) * 8);
-    };
     bf16x8 af[2][4], bv[2][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        af[0][i] = rd_a(0, i);
-    bv[0][0] = rd_b(0, 0);
-    bv[0][1] = rd_b(0, 1);
+        af[0][i] = a0[i];
+    bv[0][0] = b0[0];
+    bv[0][1] = b0[1];
 #pragma unroll
     for (int g = 0; g < 8; ++g) {              // group g: k-step g / 4, fragments 2 (g % 4) + 0, 1
         const int ks = g >> 2, jp = g & 3, cur = g & 1;
@@ -958,10 +983,10 @@ __device__ __forceinline__ void pf_compute(const uint16_t *st, int wn, int wm, i
             if (njp == 0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    af[nks][i] = rd_a(nks, i);
+                    af[nks][i] = pf_rd_a<PW>(st, wn, r, gq, nks, i);
             }
-            bv[cur ^ 1][0] = rd_b(nks, 2 * njp);
-            bv[cur ^ 1][1] = rd_b(nks, 2 * njp + 1);
+            bv[cur ^ 1][0] = pf_rd_b(st, wm, r, gq, nks, 2 * njp);
+            bv[cur ^ 1][1] = pf_rd_b(st, wm, r, gq, nks, 2 * njp + 1);
         }
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
@@ -970,11 +995,10 @@ __device__ __forceinline__ void pf_compute(const uint16_t *st, int wn, int wm, i
                 acc[i][2 * jp + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     af[ks][i], bv[cur][jj], acc[i][2 * jp + jj], 0, 0, 0);
     }
-    // keep that order in the schedule: the first group's 6 reads, then for every group the
-    // next group's reads (2, or 6 where the next k-step's W fragments start) before its 8 MFMAs
+    // keep that order in the schedule: for every group the next group's reads (2, or 6 where
+    // the next k-step's W fragments start) before its 8 MFMAs
 #define PF_SG(ds) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0); \
                   __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
     PF_SG(2) PF_SG(2) PF_SG(2) PF_SG(6) PF_SG(2) PF_SG(2) PF_SG(2)
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 #undef PF_SG
@@ -1048,13 +1072,29 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
                  vtile, D, kxs, VW, sg_lo, kb_per_slice, slist, wave, lane);
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");    // stage 0 (8 copies per stage)
     lds_barrier();
-    for (int q = 0; q < nk; ++q) {
+    bf16x8 a0[4], b0[2];
+    pf_prefetch<PW>(pf_lds, wn, wm, r, gq, a0, b0);
+    // two loops: while the stage after next is a base stage the copies need no adapter ids
+    // (no scalar loads in the loop, so the LDS waits can count exactly); then the rest
+    int q = 0;
+    for (; q + PF_STAGES < nk_main; ++q) {
         uint16_t *st = pf_lds + (q & 1) * (PF_STAGE_BYTES / 2);
-        pf_compute<PW>(st, wn, wm, r, gq, acc);
+        pf_compute<PW>(st, wn, wm, r, gq, a0, b0, acc);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stage q+1
         lds_barrier();                                      // also: stage q fully read
+        // stage q+1's first operands, then the copies into the buffer stage q used
+        pf_prefetch<PW>(pf_lds + ((q + 1) & 1) * (PF_STAGE_BYTES / 2), wn, wm, r, gq, a0, b0);
+        pf_issue<PW, true>(P, st, q + PF_STAGES, nk_main, nk_extra, m0, n0, vtile, D, kxs, VW,
+                           sg_lo, kb_per_slice, slist, wave, lane);
+    }
+    for (; q < nk; ++q) {
+        uint16_t *st = pf_lds + (q & 1) * (PF_STAGE_BYTES / 2);
+        pf_compute<PW>(st, wn, wm, r, gq, a0, b0, acc);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        pf_prefetch<PW>(pf_lds + ((q + 1) & 1) * (PF_STAGE_BYTES / 2), wn, wm, r, gq, a0, b0);
         pf_issue<PW>(P, st, min(q + PF_STAGES, nk - 1), nk_main, nk_extra, m0, n0, vtile, D, kxs,
-                 VW, sg_lo, kb_per_slice, slist, wave, lane);
+                     VW, sg_lo, kb_per_slice, slist, wave, lane);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no copy outlives the workgroup
 
