@@ -73,6 +73,14 @@ __device__ __forceinline__ int tile_vwidth(int r8max, int R)
     return min(w, R);
 }
 
+// Token i (0..15) of a group record's token bytes.
+__device__ __forceinline__ int grp_token(const int4 &gt, int i)
+{
+    const int w = i >> 2;
+    const uint32_t v = (uint32_t)(w == 0 ? gt.x : w == 1 ? gt.y : w == 2 ? gt.z : gt.w);
+    return (int)((v >> ((i & 3) * 8)) & 255u);
+}
+
 // Exclusive scan of two values over the 256 threads of a workgroup; ws holds 8 ints.
 __device__ __forceinline__ void block_scan2(int v1, int v2, int *ws, int &ex1, int &ex2, int &all1,
                                             int &all2)
@@ -101,24 +109,28 @@ __device__ __forceinline__ void block_scan2(int v1, int v2, int *ws, int &ex1, i
 }
 
 // One workgroup of 256 threads per tile.  For a scattered tile it also lists, per adapter of
-// the tile (list order), the tile-local tokens that use it: tile_tok[toff[d] ..toff[d+1]), in
-// groups of 16 numbered by gpre[d] = sum over d' < d of ceil(count / 16).  The order of the
-// tokens inside a list is whatever the atomics give; each token's results do not depend on it.
+// the tile (list order), the tile-local tokens that use it (entries toff[d] .. toff[d+1] of the
+// tile's list, built in LDS), in groups of 16 numbered by gpre[d] = sum over d' < d of
+// ceil(count / 16), and writes one record per group: {position d, adapter, first list entry,
+// tokens}, then the group's up to 16 tile-local token numbers as bytes, so that a consumer has
+// the group's tokens after one load.  The order of the tokens inside a list is whatever the
+// atomics give; each token's results do not depend on it.
 __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restrict__ idx, int T,
                                                         int K, int S, int R, int n_slices, int n_in,
                                                         const int32_t *__restrict__ rank,
                                                         int list_stride, int32_t *tile_D,
                                                         int32_t *tile_w,
                                                         int32_t *tile_list, int32_t *tile_toff,
-                                                        int32_t *tile_gpre, uint8_t *tile_tok,
-                                                        int tok_stride, int4 *tile_grp,
+                                                        int32_t *tile_gpre, int4 *tile_grp,
                                                         int grp_stride)
 {
-    extern __shared__ uint32_t plan_lds[];         // bits[(S+31)/32], cnt[S], lst[list_stride]
+    // bits[(S+31)/32], cnt[S], lst[list_stride], tok[256 K] bytes
+    extern __shared__ uint32_t plan_lds[];
     const int nw = (S + 31) / 32;
     uint32_t *bits = plan_lds;
     int *cnt = (int *)(plan_lds + nw);
     int *lst = cnt + S;
+    uint8_t *tok = (uint8_t *)(lst + list_stride);
     __shared__ int wsum[8];
     const int m = blockIdx.x;
     const int t0 = m * PF_BM;
@@ -203,14 +215,6 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
             gpre[D] = gbase;
         }
         __syncthreads();
-        // one record per 16-token group: {position d, adapter, first list entry, tokens}
-        int4 *grp = tile_grp + (int64_t)m * grp_stride;
-        for (int d = threadIdx.x; d < D; d += blockDim.x) {
-            const int o0 = toff[d], o1 = toff[d + 1], g0 = gpre[d];
-            for (int o = o0; o < o1; o += 16)
-                grp[g0 + (o - o0) / 16] = int4{d, lst[d], o, min(16, o1 - o)};
-        }
-        uint8_t *tok = tile_tok + (int64_t)m * tok_stride;
         for (int tl = threadIdx.x; tl < nt; tl += blockDim.x) {
             const int32_t *it = idx + (int64_t)(t0 + tl) * K;
             for (int j = 0; j < K; ++j) {
@@ -224,6 +228,20 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
                     tok[atomicAdd(&cnt[a], 1)] = (uint8_t)tl;
             }
         }
+        __syncthreads();                          // the lists complete
+        int4 *grp = tile_grp + (int64_t)m * grp_stride * 2;
+        for (int d = threadIdx.x; d < D; d += blockDim.x) {
+            const int o0 = toff[d], o1 = toff[d + 1], g0 = gpre[d];
+            for (int o = o0; o < o1; o += 16) {
+                const int n = min(16, o1 - o);
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+                for (int i = 0; i < n; ++i)
+                    w[i >> 2] |= (uint32_t)tok[o + i] << ((i & 3) * 8);
+                const int gi = g0 + (o - o0) / 16;
+                grp[2 * gi] = int4{d, lst[d], o, n};
+                grp[2 * gi + 1] = int4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+            }
+        }
     }
     // (the V block's columns past 2 D VW, up to the 64-column k-step, are never written: the
     // GEMM copies zeros in their place)
@@ -232,9 +250,11 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
 // ------------------------------------------------------------------------------------------
 // 2. SGMV shrink into V
 // ------------------------------------------------------------------------------------------
-// The tile's D adapters are stacked into one "cat" matrix A_cat (D * n_slices * R rows), so the
-// shrink of a tile is one dense product V_tile = X_tile A_cat^T; a token that does not use
-// adapter d gets coefficient 0 for d's columns (the zeros the GEMM's extra K-steps expect).
+// The tile's D adapters are stacked into one "cat" matrix A_cat (D * n_slices * VW rows: each
+// slice's first VW rows, VW the tile's V width, the power of two at or above its largest rank),
+// so the shrink of a tile is one dense product V_tile = X_tile A_cat^T; a token that does not
+// use adapter d gets coefficient 0 for d's columns (the zeros the GEMM's extra K-steps expect).
+// Rows past an adapter's own rank are copied from the zero block, not read.
 //
 // Dense item = (tile m, 128-row block rb of A_cat, part kp of n_in split in ks parts): all 256
 // tokens of the tile against the block's rows over the part's columns.  Operands are copied
@@ -253,7 +273,7 @@ constexpr int SD_ROWS = 128;         // A_cat rows of a dense item
 constexpr int SD_KS = 64;            // columns per stage
 constexpr int SD_STAGE_ELEMS = (PF_BM + SD_ROWS) * SD_KS;   // bf16: 256 x rows, then A rows
 constexpr int SD_STAGE_BYTES = SD_STAGE_ELEMS * 2;          // 48 KB
-constexpr int SD_KS_MAX = 8;         // most parts of n_in
+constexpr int SD_KS_MAX = 16;        // most parts of n_in
 constexpr int SD_TARGET = 256;       // dense items aimed for
 constexpr int SD_PART_ELEMS = PF_BM * SD_ROWS;              // fp32 partial block of an item
 constexpr int SD_TABLE_BYTES = 9;    // LDS per tile for the item tables (pre, pbase, grouped)
@@ -272,11 +292,11 @@ struct ShrinkArgs {
     int32_t *tile_ord;    // out: ordinal of a scattered tile (< sc_cap), else -1
     int32_t *sc_tiles;    // out: [sc_cap] tile of each ordinal, then their count
     int sc_cap;
-    const int32_t *tile_toff, *tile_gpre;   // scattered tiles: token lists (tile plan)
-    const uint8_t *tile_tok;
-    int tok_stride;
-    const int4 *tile_grp;                   // scattered tiles: group records (tile plan)
+    const int32_t *tile_toff, *tile_gpre;   // scattered tiles: list offsets (tile plan)
+    const int4 *tile_grp;                   // scattered tiles: group records, 2 x int4 each
     int grp_stride;
+    int32_t *sc_pre;      // out: [sc_cap + 1] expand items before each scattered ordinal, total
+    int n_chunks;         // output row chunks of an expand item
     float *sd_part;       // [sd_cap_slots][256][128] fp32 partial blocks (ks > 1)
     int sd_cap_slots;
     int32_t *tile_pbase;  // out: first partial slot / SD block of a dense tile, -1 otherwise
@@ -386,7 +406,8 @@ __device__ __forceinline__ void sh_dense_item(const ShrinkArgs &P, int m, int rb
     const int r = lane & 15, gq = lane >> 4;
     const int D = P.tile_D[m];
     const int32_t *list = P.tile_list + (int64_t)m * P.list_stride;
-    const int rows_cat = D * wd;
+    const int VW = P.tile_w[m], wv = g.n_slices * VW;   // A_cat rows per adapter
+    const int rows_cat = D * wv;
     const int row0 = rb * SD_ROWS;
     const int ni = min(8, (rows_cat - row0 + 15) / 16);   // row groups with a row of A_cat
     const int kbeg = kp * kc, kend = min(P.n_in, kbeg + kc);
@@ -407,10 +428,10 @@ __device__ __forceinline__ void sh_dense_item(const ShrinkArgs &P, int m, int rb
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int a_row = row0 + wave * 32 + i * 8 + rr;
-        const int d = min(a_row, rows_cat - 1) / wd;
-        const int rin = min(a_row, rows_cat - 1) - d * wd;
-        const bool ok = a_row < rows_cat && rin % R < slot_rank8(g.rank, list[d], R);
-        ar[i] = g.A + ((int64_t)list[d] * wd + rin) * P.n_in;
+        const int ac = min(a_row, rows_cat - 1);
+        const int d = ac / wv, rin = ac - d * wv, sg = rin / VW, rho = rin - sg * VW;
+        const bool ok = a_row < rows_cat && rho < slot_rank8(g.rank, list[d], R);
+        ar[i] = g.A + ((int64_t)list[d] * wd + sg * R + rho) * P.n_in;
         rmask |= (ok ? 1u : 0u) << (8 + i);
     }
 
@@ -455,7 +476,6 @@ __device__ __forceinline__ void sh_dense_item(const ShrinkArgs &P, int m, int rb
         }
         return;
     }
-    const int VW = P.tile_w[m];
     const int kxs = ((D * 2 * VW + PF_BK - 1) / PF_BK) * PF_BK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -473,14 +493,13 @@ __device__ __forceinline__ void sh_dense_item(const ShrinkArgs &P, int m, int rb
                 const int a_row = row0 + i * 16 + gq * 4 + e;
                 if (i >= ni || a_row >= rows_cat)
                     continue;
-                const int d = a_row / wd;
+                const int d = a_row / wv;
                 if (d != dprev) {
                     cf = sh_coef(P, t, list[d]);
                     dprev = d;
                 }
-                const int rin = a_row - d * wd, sg = rin / R, rho = rin - sg * R;
-                if (rho < VW)   // rows past VW are past the rank: zeros, not in the V block
-                    sh_store_v(vrow + sg * kxs + d * 2 * VW + rho, VW, cf * acc[i][j][e]);
+                const int rin = a_row - d * wv, sg = rin / VW, rho = rin - sg * VW;
+                sh_store_v(vrow + sg * kxs + d * 2 * VW + rho, VW, cf * acc[i][j][e]);
             }
         }
     }
@@ -515,9 +534,9 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
     const int RB = (wd + SG_ROWS - 1) / SG_ROWS;
     const int gidx = local / RB, rb = local - gidx * RB;
     const int D = P.tile_D[m];
-    const int4 gr = P.tile_grp[(int64_t)m * P.grp_stride + gidx];   // {d, adapter, s0, tokens}
-    const int d = gr.x, a = gr.y, s0 = gr.z, ng = gr.w;
-    const uint8_t *tk = P.tile_tok + (int64_t)m * P.tok_stride + s0;
+    const int4 *rec = P.tile_grp + ((int64_t)m * P.grp_stride + gidx) * 2;
+    const int4 gr = rec[0], gt = rec[1];   // {d, adapter, first entry, tokens}, token bytes
+    const int d = gr.x, a = gr.y, ng = gr.w;
     // rows past the adapter's rank (zero padding) are neither read nor multiplied: their
     // fragments come from the zero block, and a block with no row below the rank skips the loop
     const int rk = slot_rank8(g.rank, a, R);
@@ -531,7 +550,7 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
     }
     const bool any_row = __ballot(aok[0] || aok[1]) != 0ull;
     const bool xok = r < ng && any_row;
-    const uint16_t *xp = P.x + ((int64_t)m * PF_BM + (r < ng ? tk[r] : 0)) * P.n_in + gq * 8;
+    const uint16_t *xp = P.x + ((int64_t)m * PF_BM + (r < ng ? grp_token(gt, r) : 0)) * P.n_in + gq * 8;
     int kb, kend, nsteps;
     sh_wave_cols(P.n_in, wave, kb, kend, nsteps);
     if (!any_row)
@@ -562,7 +581,7 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
     // thread: gathered token j = tid % 16, rows 2 * (tid / 16) and the next
     const int j = tid & 15, rp = (tid >> 4) * 2;
     if (j < ng) {
-        const int tl = tk[j];
+        const int tl = grp_token(gt, j);
         const float cf = sh_coef(P, m * PF_BM + tl, a);
         const int VW = P.tile_w[m];
         const int kxs = ((D * 2 * VW + PF_BK - 1) / PF_BK) * PF_BK;
@@ -589,6 +608,12 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
     __syncthreads();
 }
 
+// 128-row blocks of tile m's A_cat (D adapters, n_slices * VW rows each)
+__device__ __forceinline__ int sd_row_blocks(const ShrinkArgs &P, int m, int D)
+{
+    return (D * P.g.n_slices * P.tile_w[m] + SD_ROWS - 1) / SD_ROWS;
+}
+
 __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
 {
     extern __shared__ __attribute__((aligned(16))) float sh_lds[];
@@ -605,7 +630,7 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
 
     // Pass 1: which tiles take group items (a scattered tile whose ordinal is below sc_cap),
     // and the 128-row blocks of the others; workgroup 0 also numbers the scattered tiles.
-    int rb_base = 0, sc_base = 0;
+    int rb_base = 0, sc_base = 0, ei_base = 0;
     for (int m0 = 0; m0 < P.n_mtiles; m0 += SH_THREADS) {
         const int m = m0 + threadIdx.x;
         const int Dm = m < P.n_mtiles ? P.tile_D[m] : 0;
@@ -614,23 +639,30 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
         block_scan2(scm, 0, wsum, sc_ex, u0, sc_all, u1);
         const int ord = sc_base + sc_ex;
         const bool kept = scm && ord < P.sc_cap;
-        const int rbs = kept ? 0 : (Dm * wd + SD_ROWS - 1) / SD_ROWS;
-        int rb_ex, rb_all;
-        block_scan2(rbs, 0, wsum, rb_ex, u0, rb_all, u1);
+        const int rbs = kept || m >= P.n_mtiles ? 0 : sd_row_blocks(P, m, Dm);
+        // expand items of a kept scattered tile (its 16-token groups x the row chunks)
+        const int eit = kept ? P.tile_gpre[(int64_t)m * (P.list_stride + 1) + Dm] * P.n_chunks : 0;
+        int rb_ex, rb_all, ei_ex, ei_all;
+        block_scan2(rbs, eit, wsum, rb_ex, ei_ex, rb_all, ei_all);
         if (m < P.n_mtiles) {
             grouped[m] = kept ? 1 : 0;
             pbase[m] = rbs > 0 ? rb_base + rb_ex : -1;
         }
         if (blockIdx.x == 0 && m < P.n_mtiles) {
             P.tile_ord[m] = kept ? ord : -1;
-            if (kept)
+            if (kept) {
                 P.sc_tiles[ord] = m;
+                P.sc_pre[ord] = ei_base + ei_ex;
+            }
         }
         rb_base += rb_all;
         sc_base += sc_all;
+        ei_base += ei_all;
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0)
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         P.sc_tiles[P.sc_cap] = min(sc_base, P.sc_cap);
+        P.sc_pre[P.sc_cap] = ei_base;
+    }
     int ks, kc;
     sd_split(rb_base, P.n_in, P.sd_cap_slots, ks, kc);
     __syncthreads();
@@ -651,7 +683,7 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
             cnt = grouped[m] ? (P.skip_groups ? 0
                                               : P.tile_gpre[(int64_t)m * (P.list_stride + 1) + Dm] *
                                                     RBg)
-                             : ((Dm * wd + SD_ROWS - 1) / SD_ROWS) * ks;
+                             : sd_row_blocks(P, m, Dm) * ks;
         }
         int ex, all, u0, u1;
         block_scan2(cnt, 0, wsum, ex, u0, all, u1);
@@ -706,7 +738,7 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(ShrinkArgs P)
     if (ks <= 1 || pb < 0 || nt <= 0)
         return;
     const SlotGeom &g = P.g;
-    const int R = g.R, wd = g.n_slices * R, K = P.K;
+    const int K = P.K;
     const int D = P.tile_D[m];
     const int32_t *list = P.tile_list + (int64_t)m * P.list_stride;
     const int64_t tb = (int64_t)m * PF_BM + t0l;   // first token of the block
@@ -720,8 +752,8 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(ShrinkArgs P)
         s_f[d] = g.factor[a];
     }
     __syncthreads();
-    const int rows4 = D * wd / 4;                  // groups of 4 rows
-    const int VW = P.tile_w[m];
+    const int VW = P.tile_w[m], wv = g.n_slices * VW;   // A_cat rows per adapter
+    const int rows4 = D * wv / 4;                  // groups of 4 rows
     const int kxs = ((D * 2 * VW + PF_BK - 1) / PF_BK) * PF_BK;
     for (int e = threadIdx.x; e < nt * rows4; e += 256) {
         const int tt = e / rows4, a_row = (e - tt * rows4) * 4;
@@ -743,16 +775,14 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(ShrinkArgs P)
                 sum.w += pv[kp].w;
             }
         }
-        const int d = a_row / wd;
+        const int d = a_row / wv;
         const int a = d < SR_D ? s_a[d] : list[d];
         const float f = d < SR_D ? s_f[d] : g.factor[a];
         float cf = 0.f;
         for (int j = 0; j < K; ++j)
             if (s_idx[tt * K + j] == a)
                 cf += s_sc[tt * K + j] * f;
-        const int rin = a_row - d * wd, sg = rin / R, rho = rin - sg * R;
-        if (rho >= VW)
-            continue;   // past the rank (the 4 rows share it: VW is a multiple of 8)
+        const int rin = a_row - d * wv, sg = rin / VW, rho = rin - sg * VW;
         uint16_t *vp = P.vcat + (int64_t)m * P.vcat_tile_elems + (int64_t)tl * (g.n_slices * kxs) +
                        sg * kxs + d * 2 * VW + rho;
         const float v[4] = {cf * sum.x, cf * sum.y, cf * sum.z, cf * sum.w};
@@ -1159,14 +1189,12 @@ struct ScArgs {
     const int32_t *tile_D, *tile_list;
     const int32_t *tile_w;
     int list_stride;
-    const int32_t *tile_toff, *tile_gpre;
-    const uint8_t *tile_tok;
-    int tok_stride;
-    const int4 *tile_grp;
+    const int4 *tile_grp;     // group records, 2 x int4 each (tile plan)
     int grp_stride;
     const uint16_t *vcat;
     int64_t vcat_tile_elems;
-    const int32_t *sc_tiles;
+    const int32_t *sc_tiles;  // [sc_cap] tile of each scattered ordinal, then their count
+    const int32_t *sc_pre;    // [sc_cap] first item of each ordinal, then the item total
     int sc_cap, n_chunks;
     float *part_sc;
     uint16_t *y;
@@ -1193,15 +1221,18 @@ __device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int m, 
     if (n0 >= P.n_out)
         return;
     const int D = P.tile_D[m];
-    const int4 gr = P.tile_grp[(int64_t)m * P.grp_stride + gidx];   // {d, adapter, s0, tokens}
-    const int d = gr.x, a = gr.y, s0 = gr.z, ng = gr.w;
+    const int4 *rec = P.tile_grp + ((int64_t)m * P.grp_stride + gidx) * 2;
+    const int4 gr = rec[0], gt = rec[1];   // {d, adapter, first entry, tokens}, token bytes
+    const int d = gr.x, a = gr.y, ng = gr.w;
     const bool tok_ok = r < ng;
-    const int tl = tok_ok ? P.tile_tok[(int64_t)m * P.tok_stride + s0 + r] : 0;
+    const int tl = tok_ok ? grp_token(gt, r) : 0;
     const int t = m * PF_BM + tl;
 
-    // this pass's adapter of the token: its rank among the token's distinct ids, and their count
-    int below = 0, n_dist = 0;
-    if (tok_ok) {
+    // this pass's adapter of the token: its rank among the token's distinct ids, and their
+    // count (one slot per token: the group's adapter is the token's only one)
+    int below = 0, n_dist = 1;
+    if (tok_ok && P.K > 1) {
+        n_dist = 0;
         const int32_t *it = P.idx + (int64_t)t * P.K;
         for (int j = 0; j < P.K; ++j) {
             const int b = it[j];
@@ -1317,27 +1348,16 @@ __device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int m, 
 
 __global__ __launch_bounds__(256) void sc_expand_kernel(ScArgs P)
 {
+    // the scattered tiles and their first items (numbered by sgmv_shrink_kernel), in LDS
     extern __shared__ int sc_pre[];           // [sc_cap] item prefix, then [sc_cap] tiles
     int *sc_m = sc_pre + P.sc_cap;
-    __shared__ int wsum[8];
     const int n_sc = P.sc_tiles[P.sc_cap];
-    int base = 0;
-    for (int o0 = 0; o0 < n_sc; o0 += 256) {
-        const int o = o0 + threadIdx.x;
-        int cnt = 0;
-        if (o < n_sc) {
-            const int m = P.sc_tiles[o];
-            sc_m[o] = m;
-            cnt = P.tile_gpre[(int64_t)m * (P.list_stride + 1) + P.tile_D[m]] * P.n_chunks;
-        }
-        int ex, all, u0, u1;
-        block_scan2(cnt, 0, wsum, ex, u0, all, u1);
-        if (o < n_sc)
-            sc_pre[o] = base + ex;
-        base += all;
+    const int total = P.sc_pre[P.sc_cap];
+    for (int o = threadIdx.x; o < n_sc; o += 256) {
+        sc_pre[o] = P.sc_pre[o];
+        sc_m[o] = P.sc_tiles[o];
     }
     __syncthreads();
-    const int total = base;
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
         int lo = 0, hi = n_sc - 1;            // scattered tile: last o with sc_pre[o] <= item
         while (lo < hi) {
@@ -1381,7 +1401,7 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
 
 // Workspace regions of the tiled path, each 256-byte aligned, in this order.
 struct PrefillLayout {
-    size_t tile_w, tile_D, tile_list, tile_toff, tile_gpre, tile_tok, tile_ord, sc_tiles, part_sc, vcat,
+    size_t tile_w, tile_D, tile_list, tile_toff, tile_gpre, sc_pre, tile_ord, sc_tiles, part_sc, vcat,
         tile_pbase, sd_ks, sd_part, tile_grp, total;
 };
 
@@ -1397,8 +1417,8 @@ static PrefillLayout prefill_layout(const PrefillCfg &c)
     L.tile_list = L.tile_D + al256((size_t)c.n_mtiles * sizeof(int32_t));
     L.tile_toff = L.tile_list + lists;
     L.tile_gpre = L.tile_toff + offs;
-    L.tile_tok = L.tile_gpre + offs;
-    L.tile_ord = L.tile_tok + al256((size_t)c.n_mtiles * c.tok_stride);
+    L.sc_pre = L.tile_gpre + offs;
+    L.tile_ord = L.sc_pre + al256(((size_t)c.sc_cap + 1) * sizeof(int32_t));
     L.sc_tiles = L.tile_ord + al256((size_t)c.n_mtiles * sizeof(int32_t));
     L.part_sc = L.sc_tiles + al256(((size_t)c.sc_cap + 1) * sizeof(int32_t));
     L.vcat = L.part_sc + al256((size_t)c.sc_cap * PF_BM * (size_t)c.n_out * sizeof(float));
@@ -1406,7 +1426,7 @@ static PrefillLayout prefill_layout(const PrefillCfg &c)
     L.sd_ks = L.tile_pbase + al256((size_t)c.n_mtiles * sizeof(int32_t));
     L.sd_part = L.sd_ks + 256;
     L.tile_grp = L.sd_part + al256((size_t)c.sd_cap_slots * SD_PART_ELEMS * sizeof(float));
-    L.total = L.tile_grp + (size_t)c.n_mtiles * c.grp_stride * sizeof(int4);
+    L.total = L.tile_grp + (size_t)c.n_mtiles * c.grp_stride * 2 * sizeof(int4);
     return L;
 }
 
@@ -1430,7 +1450,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     int32_t *tile_list = (int32_t *)(p + WL.tile_list);
     int32_t *tile_toff = (int32_t *)(p + WL.tile_toff);
     int32_t *tile_gpre = (int32_t *)(p + WL.tile_gpre);
-    uint8_t *tile_tok = p + WL.tile_tok;
+    int32_t *sc_pre = (int32_t *)(p + WL.sc_pre);
     int32_t *tile_ord = (int32_t *)(p + WL.tile_ord);
     int32_t *sc_tiles = (int32_t *)(p + WL.sc_tiles);
     float *part_sc = (float *)(p + WL.part_sc);
@@ -1449,13 +1469,13 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     const int n_helpers = g != nullptr && c.may_scatter && n_tiles < n_cus ? n_cus - n_tiles : 0;
     ShrinkArgs s{};
     if (g != nullptr) {
-        const size_t lds = (size_t)((g->S + 31) / 32) * 4 + (size_t)g->S * 4 + (size_t)c.list_stride * 4;
+        const size_t lds = (size_t)((g->S + 31) / 32) * 4 + (size_t)g->S * 4 +
+                           (size_t)c.list_stride * 4 + (size_t)c.tok_stride;
         if (hipError_t e = ensure_dynamic_lds((const void *)tile_plan_kernel, lds); e != hipSuccess)
             return e;
         hipLaunchKernelGGL(tile_plan_kernel, dim3(c.n_mtiles), dim3(256), lds, stream, idx,
                            (int)T, K, g->S, g->R, g->n_slices, (int)n_in, g->rank, c.list_stride,
-                           tile_D, tile_w, tile_list, tile_toff, tile_gpre, tile_tok, c.tok_stride, tile_grp,
-                           c.grp_stride);
+                           tile_D, tile_w, tile_list, tile_toff, tile_gpre, tile_grp, c.grp_stride);
         s.x = x;
         s.T = (int)T;
         s.n_in = (int)n_in;
@@ -1475,8 +1495,8 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         s.sc_cap = c.sc_cap;
         s.tile_toff = tile_toff;
         s.tile_gpre = tile_gpre;
-        s.tile_tok = tile_tok;
-        s.tok_stride = c.tok_stride;
+        s.sc_pre = sc_pre;
+        s.n_chunks = (int)((n_out + SC_ROWS - 1) / SC_ROWS);
         s.tile_grp = tile_grp;
         s.grp_stride = c.grp_stride;
         s.sd_part = sd_part;
@@ -1495,7 +1515,10 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         if (hipError_t e = ensure_dynamic_lds((const void *)sgmv_shrink_kernel, sh_lds);
             e != hipSuccess)
             return e;
-        hipLaunchKernelGGL(sgmv_shrink_kernel, dim3(1024), dim3(SH_THREADS), sh_lds, stream, s);
+        // one workgroup per CU (the stages take most of its LDS), items shared out in the kernel:
+        // every workgroup then runs the kernel's item numbering once, all in one round
+        hipLaunchKernelGGL(sgmv_shrink_kernel, dim3((unsigned)n_cus), dim3(SH_THREADS), sh_lds,
+                           stream, s);
         hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)c.n_mtiles * (PF_BM / SR_TOK)),
                            dim3(256), 0, stream, s);
     }
@@ -1547,10 +1570,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
         x2.tile_w = tile_w;
         x2.tile_list = tile_list;
         x2.list_stride = c.list_stride;
-        x2.tile_toff = tile_toff;
-        x2.tile_gpre = tile_gpre;
-        x2.tile_tok = tile_tok;
-        x2.tok_stride = c.tok_stride;
+        x2.sc_pre = sc_pre;
         x2.tile_grp = tile_grp;
         x2.grp_stride = c.grp_stride;
         x2.vcat = vcat;

@@ -190,7 +190,7 @@ RANKED = [
     # seed, T, contiguous, path, ranks
     (50, 300, False, "decode", [8, 16, 64, 24, 8, 40, 16, 5, 64]),
     (51, 300, False, "tiled", [8, 16, 64, 24, 8, 40, 16, 5, 64]),   # the scattered route
-    (52, 600, True, "tiled", [8, 16, 64, 24, 8, 40, 16, 5, 64]),    # stacked (dense) tiles
+    (52, 600, True, "tiled", [8, 16, 64, 24, 8, 40, 16, 5, 64]),    # prefill-like runs
     (53, 600, True, "tiled", [8, 16, 8, 24, 8, 5, 16, 5, 12]),      # narrower V blocks
     (54, 90, False, "decode", [8, 16, 8, 24, 8, 5, 16, 5, 12]),
 ]
@@ -225,6 +225,40 @@ def test_rank_table_skips_padding_exactly(oracle_mod, case):
         assert tol_ok(from_dev_bf16(y0), y_ref).all()
     yy = from_dev_bf16(y1)
     assert tol_ok(yy, y_ref).all(), f"worst {worst(yy, y_ref):.3e}"
+
+
+DENSE_RANKED = [
+    # seed, n_in, R, K, ranks: every 256-token tile dense (2 D R <= n_in / 2), ranks below R
+    (58, 2048, 64, 2, [8, 16, 24, 8, 5, 16, 5, 12, 8]),   # n_in in parts: partials + reduce
+    (59, 448, 16, 1, [8, 5, 8]),                          # n_in whole: the items write V
+]
+
+
+@pytest.mark.parametrize("seed,n_in,R,K,ranks", DENSE_RANKED,
+                         ids=[f"d{c[0]}" for c in DENSE_RANKED])
+def test_rank_table_dense_tiles(oracle_mod, seed, n_in, R, K, ranks):
+    """Dense tiles with the rank table: A_cat stacks only the first VW rows of each slice of each
+    adapter (VW from the tile's largest rank, here below R), on both routes of the dense shrink
+    (n_in split in parts with a reduce after, or whole); against the oracle, as is the
+    rank-blind run."""
+    import torch
+    from lora_serving_amd import mlora
+    L = synth.random_layer(seed, T=768, n_in=n_in, n_out=384, S=len(ranks), R=R, K=K,
+                           slice_sizes=[256, 64, 64], ranks=ranks, p_sentinel=0.2,
+                           contiguous=True)
+    for m in range(L.T // 256):                 # the case really takes the dense route
+        ids = L.idx[m * 256:(m + 1) * 256]
+        assert 2 * len(np.unique(ids[ids >= 0])) * R <= n_in // 2
+    say(f"[dense ranked] seed={seed} n_in={n_in} R={R} K={K} ranks={ranks}")
+    D = DevLayer(L)
+    y_ref = oracle_mod.linear(L)
+    y0 = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_TILED))
+    assert tol_ok(y0, y_ref).all(), f"rank-blind: worst {worst(y0, y_ref):.3e}"
+    rank_dev = torch.tensor(ranks, dtype=torch.int32, device="cuda")
+    D.slots = mlora.Slots(D.A, D.B, D.factor, slice_start=[int(v) for v in L.slice_start],
+                          rank=rank_dev)
+    y1 = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_TILED))
+    assert tol_ok(y1, y_ref).all(), f"worst {worst(y1, y_ref):.3e}"
 
 
 @pytest.mark.parametrize("seed,T,K", [(55, 64, 1), (56, 37, 3)])
