@@ -115,6 +115,7 @@ __device__ __forceinline__ void block_scan2(int v1, int v2, int *ws, int &ex1, i
 // tokens}, then the group's up to 16 tile-local token numbers as bytes, so that a consumer has
 // the group's tokens after one load.  The order of the tokens inside a list is whatever the
 // atomics give; each token's results do not depend on it.
+static_assert(PF_BM == 256, "tile_plan_kernel: one thread per token of a tile");
 __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restrict__ idx, int T,
                                                         int K, int S, int R, int n_slices, int n_in,
                                                         const int32_t *__restrict__ rank,
@@ -124,33 +125,46 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
                                                         int32_t *tile_gpre, int4 *tile_grp,
                                                         int grp_stride)
 {
-    // bits[(S+31)/32], cnt[S], lst[list_stride], tok[256 K] bytes
+    // bits[(S+31)/32], cnt[S], r8[S], lst[list_stride], tok[256 K] bytes
     extern __shared__ uint32_t plan_lds[];
     const int nw = (S + 31) / 32;
     uint32_t *bits = plan_lds;
     int *cnt = (int *)(plan_lds + nw);
-    int *lst = cnt + S;
+    int *r8 = cnt + S;
+    int *lst = r8 + S;
     uint8_t *tok = (uint8_t *)(lst + list_stride);
     __shared__ int wsum[8];
     const int m = blockIdx.x;
     const int t0 = m * PF_BM;
     const int nt = min(PF_BM, T - t0);
+    // thread tl holds token tl's slot ids (256 threads, 256 tokens a tile), distinct ids only
+    // (a repeated id is -1 here), loaded before the LDS is cleared so that the slot map and
+    // the slots' ranks are read in one round trip
+    const int tl = threadIdx.x;
+    int ids[MLORA_MAX_K_DEV];
+#pragma unroll
+    for (int j = 0; j < MLORA_MAX_K_DEV; ++j)
+        ids[j] = j < K && tl < nt ? idx[(int64_t)(t0 + tl) * K + j] : -1;
     for (int i = threadIdx.x; i < nw; i += blockDim.x)
         bits[i] = 0u;
-    for (int i = threadIdx.x; i < S; i += blockDim.x)
+    for (int i = threadIdx.x; i < S; i += blockDim.x) {
         cnt[i] = 0;
+        r8[i] = slot_rank8(rank, i, R);
+    }
+#pragma unroll
+    for (int j = 1; j < MLORA_MAX_K_DEV; ++j) {
+        bool dup = false;
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj)
+            dup |= ids[jj] == ids[j];
+        if (dup)
+            ids[j] = -1;
+    }
     __syncthreads();
-    for (int tl = threadIdx.x; tl < nt; tl += blockDim.x) {
-        const int32_t *it = idx + (int64_t)(t0 + tl) * K;
-        for (int j = 0; j < K; ++j) {
-            const int a = it[j];
-            if (a < 0)
-                continue;
-            bool dup = false;
-            for (int jj = 0; jj < j; ++jj)
-                dup |= it[jj] == a;
-            if (dup)
-                continue;
+#pragma unroll
+    for (int j = 0; j < MLORA_MAX_K_DEV; ++j) {
+        const int a = ids[j];
+        if (a >= 0) {
             atomicOr(&bits[a >> 5], 1u << (a & 31));
             atomicAdd(&cnt[a], 1);
         }
@@ -182,7 +196,7 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
     // the tile's V width: largest rounded rank among its adapters (block maximum via wsum)
     int r8max = 0;
     for (int d = threadIdx.x; d < D; d += blockDim.x)
-        r8max = max(r8max, slot_rank8(rank, lst[d], R));
+        r8max = max(r8max, r8[lst[d]]);
     for (int off = 32; off >= 1; off >>= 1)
         r8max = max(r8max, __shfl_xor(r8max, off, 64));
     if ((threadIdx.x & 63) == 0)
@@ -215,19 +229,10 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
             gpre[D] = gbase;
         }
         __syncthreads();
-        for (int tl = threadIdx.x; tl < nt; tl += blockDim.x) {
-            const int32_t *it = idx + (int64_t)(t0 + tl) * K;
-            for (int j = 0; j < K; ++j) {
-                const int a = it[j];
-                if (a < 0)
-                    continue;
-                bool dup = false;
-                for (int jj = 0; jj < j; ++jj)
-                    dup |= it[jj] == a;
-                if (!dup)
-                    tok[atomicAdd(&cnt[a], 1)] = (uint8_t)tl;
-            }
-        }
+#pragma unroll
+        for (int j = 0; j < MLORA_MAX_K_DEV; ++j)
+            if (ids[j] >= 0)
+                tok[atomicAdd(&cnt[ids[j]], 1)] = (uint8_t)tl;
         __syncthreads();                          // the lists complete
         int4 *grp = tile_grp + (int64_t)m * grp_stride * 2;
         for (int d = threadIdx.x; d < D; d += blockDim.x) {
@@ -1469,7 +1474,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     const int n_helpers = g != nullptr && c.may_scatter && n_tiles < n_cus ? n_cus - n_tiles : 0;
     ShrinkArgs s{};
     if (g != nullptr) {
-        const size_t lds = (size_t)((g->S + 31) / 32) * 4 + (size_t)g->S * 4 +
+        const size_t lds = (size_t)((g->S + 31) / 32) * 4 + (size_t)g->S * 8 +
                            (size_t)c.list_stride * 4 + (size_t)c.tok_stride;
         if (hipError_t e = ensure_dynamic_lds((const void *)tile_plan_kernel, lds); e != hipSuccess)
             return e;
