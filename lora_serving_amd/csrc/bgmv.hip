@@ -268,8 +268,10 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(
         if (a < 0)
             continue;
         // this adapter's columns: the smallest power of two at or above its rank (rounded to
-        // 8), never above R; the columns past it are zero padding and are not read
-        const int r8 = slot_rank8(g.rank, a, R);
+        // 8), never above R; the columns past it are zero padding and are not read.  Up to
+        // R = 32 a row is at most 64 bytes, inside one cache line that is fetched whole either
+        // way: all R columns are walked then, and the rank's load stays off the B loads' path
+        const int r8 = R <= 32 ? R : slot_rank8(g.rank, a, R);
         int lw = 3;                                     // log2 of the columns walked per row
         while ((1 << lw) < r8)
             ++lw;
