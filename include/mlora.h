@@ -68,6 +68,7 @@ typedef enum {
 #define MLORA_PATH_DECODE 2u      /* force the decode kernels (token chunks of 64)             */
 #define MLORA_PATH_TILED 4u       /* force the tiled prefill kernels (256-token tiles)         */
 #define MLORA_W_PACKED 8u         /* W is in the packed layout of mlora_pack_weight            */
+#define MLORA_PATH_GROUPED 16u    /* force the grouped decode: decode base, LoRA per adapter   */
 
 /*
  * The adapter slot set of ONE layer: S slots, each R wide (R = max_lora_rank), an adapter of
@@ -219,9 +220,17 @@ mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_
  * With flags & MLORA_NO_ADAPTERS no LoRA kernel is launched (y = bf16(W x)); without it, an
  * all-sentinel map gives the same values.  T = 0 is a no-op.  By default the library picks
  * the decode kernels for small batches and the tiled kernels when the batch fills the GPU
- * with 256 x 256 output tiles; MLORA_PATH_DECODE / MLORA_PATH_TILED force one (both set:
- * MLORA_ERR_ARG).  mlora_workspace_size() covers either path.  With MLORA_W_PACKED, W points
- * to the packed layout written by mlora_pack_weight (same output bits).
+ * with 256 x 256 output tiles.  Between them, a decode-sized batch whose per-token adapter
+ * reads (each (token, slot) pair's A rows and B columns) would exceed four times W's bytes
+ * takes the grouped decode ("Multi-LoRA Serving Explained", the segmented method: tokens
+ * sorted by adapter so that each adapter is read once per group): the decode kernels' base
+ * product, the LoRA terms computed per adapter over its tokens.  MLORA_PATH_DECODE /
+ * MLORA_PATH_TILED / MLORA_PATH_GROUPED force one (more than one set: MLORA_ERR_ARG;
+ * MLORA_PATH_GROUPED where the fp32 sums of one launch's up to 512 tokens exceed what the
+ * grouped expand keeps, 64 MiB or one 256-token tile: MLORA_ERR_UNSUPPORTED).
+ * mlora_workspace_size() covers every path.  With
+ * MLORA_W_PACKED, W points to the packed layout written by mlora_pack_weight (same output
+ * bits).
  */
 mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in, int64_t n_out,
                           const mlora_slots *slots, const int32_t *idx, int32_t K,

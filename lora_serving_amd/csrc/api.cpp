@@ -419,8 +419,11 @@ mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in
 {
     if (T < 0 || n_in <= 0 || n_out <= 0 || K < 1 || K > MLORA_MAX_K)
         return MLORA_ERR_ARG;
-    if ((flags & MLORA_PATH_DECODE) && (flags & MLORA_PATH_TILED))
-        return MLORA_ERR_ARG;
+    {
+        const uint32_t path = flags & (MLORA_PATH_DECODE | MLORA_PATH_TILED | MLORA_PATH_GROUPED);
+        if (path & (path - 1))
+            return MLORA_ERR_ARG;   // more than one path forced
+    }
     if (n_in % 8 != 0)
         return MLORA_ERR_SHAPE;
     if (n_in > INT32_MAX / 2 || n_out > INT32_MAX / 2)
@@ -446,8 +449,25 @@ mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in
         return MLORA_ERR_ARG;
     const bool force_decode = (flags & MLORA_PATH_DECODE) != 0;
     const bool force_tiled = (flags & MLORA_PATH_TILED) != 0;
+    const bool force_grouped = (flags & MLORA_PATH_GROUPED) != 0;
     const bool packed = (flags & MLORA_W_PACKED) != 0;
-    const bool tiled = force_tiled || (!force_decode && prefill_worth_it(T, n_out));
+    const bool tiled =
+        force_tiled || (!force_decode && !force_grouped && prefill_worth_it(T, n_out));
+    // grouped decode: the decode kernels' base product, the LoRA terms per adapter group
+    bool grouped = false;
+    if (!tiled && lora && !force_decode) {
+        const int64_t Tc = std::min<int64_t>(T, DECODE_MAX_T);
+        const bool fits = grouped_decode_fits(grouped_config(Tc, K, n_in, n_out, S, R, n_slices));
+        if (force_grouped && !fits) {
+            std::snprintf(g_last_error, sizeof g_last_error,
+                          "MLORA_PATH_GROUPED: the fp32 sums of %lld tokens x %lld outputs exceed "
+                          "the grouped expand's 64 MiB",
+                          (long long)Tc, (long long)n_out);
+            return MLORA_ERR_UNSUPPORTED;
+        }
+        grouped = fits && (force_grouped || grouped_decode_worth_it(Tc, K, n_in, n_out,
+                                                                     n_slices * R, R));
+    }
     size_t off_v, off_part, off_pre, need;
     if (!noalloc) {
         const Layout L = make_layout(T, K, n_in, n_out, S, R, n_slices);
@@ -459,6 +479,11 @@ mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in
         off_v = off_part = off_pre = 0;
         need = prefill_workspace_bytes(
             prefill_config(std::min<int64_t>(T, PREFILL_MAX_T), K, n_in, n_out, S, R, n_slices));
+    } else if (grouped) {
+        const int64_t Tc = std::min<int64_t>(T, DECODE_MAX_T);
+        off_v = off_part = 0;
+        off_pre = align_up(decode_partial_bytes(Tc, n_in, n_out));
+        need = off_pre + prefill_workspace_bytes(grouped_config(Tc, K, n_in, n_out, S, R, n_slices));
     } else {
         const int64_t Tc = std::min<int64_t>(T, DECODE_MAX_T);
         const int64_t sk = decode_config(Tc, n_in, n_out).sk;
@@ -508,12 +533,36 @@ mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in
         return MLORA_OK;
     }
     // Launches of at most DECODE_MAX_T tokens (chunks of 64 inside): base GEMM + shrink pieces,
-    // then the finish kernel.
+    // then the finish kernel.  Grouped: the group shrink first, the GEMM and the finish on the
+    // base alone (the finish also keeps the fp32 sums), then the grouped expand.
     for (int64_t t0 = 0; t0 < T; t0 += DECODE_MAX_T) {
         const int64_t Tc = std::min<int64_t>(DECODE_MAX_T, T - t0);
         const DecodeCfg cfg = decode_config(Tc, n_in, n_out);
         const int32_t *idx_c = lora ? idx + t0 * K : nullptr;
         const float *scale_c = (lora && scale) ? scale + t0 * K : nullptr;
+        if (grouped) {
+            const PrefillCfg pc = grouped_config(Tc, K, n_in, n_out, S, R, n_slices);
+            void *wpre = wsb + off_pre;
+            hipError_t e = launch_grouped_shrink(xb + t0 * n_in, Tc, n_in, n_out, g, idx_c, K,
+                                                 scale_c, pc, wpre, stream);
+            if (e != hipSuccess)
+                return hip_status(e, "grouped shrink launch");
+            trace_mark(stream, true);
+            e = launch_decode_gemm(xb + t0 * n_in, (const uint16_t *)W, packed, Tc, n_in, n_out,
+                                   part, cfg, nullptr, nullptr, K, nullptr, stream);
+            trace_mark(stream, false);
+            if (e != hipSuccess)
+                return hip_status(e, "decode gemm launch");
+            e = launch_decode_finish(part, cfg.sk, cfg.n_tiles, nullptr, nullptr, Tc, n_out,
+                                     nullptr, nullptr, 1, yb + t0 * n_out,
+                                     grouped_base_sums(pc, wpre), stream);
+            if (e != hipSuccess)
+                return hip_status(e, "decode finish launch");
+            e = launch_grouped_expand(Tc, n_out, g, idx_c, K, yb + t0 * n_out, pc, wpre, stream);
+            if (e != hipSuccess)
+                return hip_status(e, "grouped expand launch");
+            continue;
+        }
         trace_mark(stream, true);
         hipError_t e = launch_decode_gemm(xb + t0 * n_in, (const uint16_t *)W, packed, Tc, n_in,
                                           n_out, part, cfg, lora ? &g : nullptr, idx_c, K,
@@ -522,7 +571,8 @@ mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in
         if (e != hipSuccess)
             return hip_status(e, "decode gemm launch");
         e = launch_decode_finish(part, cfg.sk, cfg.n_tiles, lora ? upart : nullptr, scale_c, Tc,
-                                 n_out, lora ? &g : nullptr, idx_c, K, yb + t0 * n_out, stream);
+                                 n_out, lora ? &g : nullptr, idx_c, K, yb + t0 * n_out, nullptr,
+                                 stream);
         if (e != hipSuccess)
             return hip_status(e, "decode finish launch");
     }

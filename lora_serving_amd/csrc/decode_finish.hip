@@ -72,7 +72,7 @@ template <bool MC, int RC>
 __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
     const float *__restrict__ part, int sk, int n_tiles, const float *__restrict__ upart,
     const float *__restrict__ scale, int T_all, int n_out, SlotGeom g,
-    const int32_t *__restrict__ idx, int K, uint16_t *__restrict__ y)
+    const int32_t *__restrict__ idx, int K, uint16_t *__restrict__ y, float *__restrict__ ysum)
 {
     extern __shared__ __attribute__((aligned(16))) float vl[];   // [DF_TOK][R] of one (slot, slice)
     __shared__ int sidx[DF_TOK * MLORA_MAX_K_DEV];
@@ -92,6 +92,8 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
         if (scale != nullptr)
             scale += (int64_t)chunk * DF_CHUNK * K;
         y += (int64_t)chunk * DF_CHUNK * n_out;
+        if (ysum != nullptr)
+            ysum += (int64_t)chunk * DF_CHUNK * n_out;
     }
     const int tile = bl / n_tg;
     const int t0 = (bl - tile * n_tg) * DF_TOK;
@@ -300,18 +302,26 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
         return;
     const float o4[4] = {base.x + d4[0], base.y + d4[1], base.z + d4[2], base.w + d4[3]};
     uint16_t *yo = y + (int64_t)t * n_out + n;
+    float *so = ysum != nullptr ? ysum + (int64_t)t * n_out + n : nullptr;
     if (n + 3 < n_out && (n_out & 3) == 0) {
         *(u32x2 *)yo = u32x2{pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3])};
+        if (so != nullptr)
+            *(float4 *)so = float4{o4[0], o4[1], o4[2], o4[3]};
     } else {
-        for (int i = 0; i < 4; ++i)
-            if (n + i < n_out)
+        for (int i = 0; i < 4; ++i) {
+            if (n + i < n_out) {
                 yo[i] = f32_to_bf16(o4[i]);
+                if (so != nullptr)
+                    so[i] = o4[i];
+            }
+        }
     }
 }
 
 hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, const float *upart,
                                 const float *scale, int64_t T, int64_t n_out, const SlotGeom *g,
-                                const int32_t *idx, int32_t K, uint16_t *y, hipStream_t stream)
+                                const int32_t *idx, int32_t K, uint16_t *y, float *ysum,
+                                hipStream_t stream)
 {
     SlotGeom gg{};
     size_t lds = 0;
@@ -329,7 +339,7 @@ hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, 
     const bool mc = n_chunks > 1;
 #define DF_LAUNCH(M, C)                                                                            \
     hipLaunchKernelGGL((decode_finish_kernel<M, C>), dim3(grid), dim3(DF_THREADS), lds, stream,  \
-                       part, sk, n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y)
+                       part, sk, n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y, ysum)
     switch (rc * 2 + (mc ? 1 : 0)) {
     case 16: DF_LAUNCH(false, 8); break;
     case 17: DF_LAUNCH(true, 8); break;

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
                                                         int32_t *tile_w,
                                                         int32_t *tile_list, int32_t *tile_toff,
                                                         int32_t *tile_gpre, int4 *tile_grp,
-                                                        int grp_stride)
+                                                        int grp_stride, int force_scatter)
 {
     // bits[(S+31)/32], cnt[S], r8[S], lst[list_stride], tok[256 K] bytes
     extern __shared__ uint32_t plan_lds[];
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
     if (threadIdx.x == 0)
         tile_w[m] = VW;
     __syncthreads();                              // wsum free again
-    if (tile_scattered(D, R, n_in)) {
+    if (force_scatter || tile_scattered(D, R, n_in)) {
         int32_t *toff = tile_toff + (int64_t)m * (list_stride + 1);
         int32_t *gpre = tile_gpre + (int64_t)m * (list_stride + 1);
         int obase = 0, gbase = 0;
@@ -308,6 +308,7 @@ struct ShrinkArgs {
     int32_t *sd_ks;       // out: ks of this launch
     int stages;           // dense item stages in LDS (2 or 3)
     int skip_groups;      // 1: the GEMM's helper workgroups run the group items instead
+    int force_scatter;    // 1: every tile takes the scattered route (grouped decode)
 };
 
 // Coefficient of adapter a for token t: the sum of s[t][j] * f[a] over the slots j holding a.
@@ -639,7 +640,8 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
     for (int m0 = 0; m0 < P.n_mtiles; m0 += SH_THREADS) {
         const int m = m0 + threadIdx.x;
         const int Dm = m < P.n_mtiles ? P.tile_D[m] : 0;
-        const int scm = m < P.n_mtiles && tile_scattered(Dm, P.g.R, P.n_in) ? 1 : 0;
+        const int scm =
+            m < P.n_mtiles && (P.force_scatter || tile_scattered(Dm, P.g.R, P.n_in)) ? 1 : 0;
         int sc_ex, sc_all, u0, u1;
         block_scan2(scm, 0, wsum, sc_ex, u0, sc_all, u1);
         const int ord = sc_base + sc_ex;
@@ -1437,10 +1439,161 @@ static PrefillLayout prefill_layout(const PrefillCfg &c)
 
 size_t prefill_workspace_bytes(const PrefillCfg &c) { return prefill_layout(c).total; }
 
+// Grouping pays where the per-(token, slot) reads of the decode kernels (each pair's A rows
+// and B columns, padded slot width) would dwarf the base weight: at least 128 tokens and that
+// gather above four times W's bytes.  Below it the group items (a few tokens each, bound by
+// their latency) lose to the gather, e.g. 256 tokens of rank 16 at 4096 -> 4096.
+bool grouped_decode_worth_it(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t wd,
+                             int32_t R)
+{
+    const double gather = (double)T * K * ((double)wd * n_in + (double)n_out * R);
+    return T >= 128 && gather > 4.0 * (double)n_out * n_in;
+}
+
 bool prefill_worth_it(int64_t T, int64_t n_out)
 {
     const int64_t tiles = ((T + PF_BM - 1) / PF_BM) * ((n_out + PF_BN - 1) / PF_BN);
     return T >= 512 && tiles >= 128;
+}
+
+// The tiled path's workspace regions of one call.
+struct PrefillPtrs {
+    int32_t *tile_D, *tile_w, *tile_list, *tile_toff, *tile_gpre, *sc_pre, *tile_ord, *sc_tiles;
+    float *part_sc;
+    uint16_t *vcat;
+    int32_t *tile_pbase, *sd_ks;
+    float *sd_part;
+    int4 *tile_grp;
+};
+
+static PrefillPtrs prefill_ptrs(const PrefillCfg &c, void *ws)
+{
+    uint8_t *p = (uint8_t *)ws;
+    const PrefillLayout WL = prefill_layout(c);
+    PrefillPtrs q;
+    q.tile_D = (int32_t *)(p + WL.tile_D);
+    q.tile_w = (int32_t *)(p + WL.tile_w);
+    q.tile_list = (int32_t *)(p + WL.tile_list);
+    q.tile_toff = (int32_t *)(p + WL.tile_toff);
+    q.tile_gpre = (int32_t *)(p + WL.tile_gpre);
+    q.sc_pre = (int32_t *)(p + WL.sc_pre);
+    q.tile_ord = (int32_t *)(p + WL.tile_ord);
+    q.sc_tiles = (int32_t *)(p + WL.sc_tiles);
+    q.part_sc = (float *)(p + WL.part_sc);
+    q.vcat = (uint16_t *)(p + WL.vcat);
+    q.tile_pbase = (int32_t *)(p + WL.tile_pbase);
+    q.sd_ks = (int32_t *)(p + WL.sd_ks);
+    q.sd_part = (float *)(p + WL.sd_part);
+    q.tile_grp = (int4 *)(p + WL.tile_grp);
+    return q;
+}
+
+// Tile plan, then the shrink kernels into the tiles' V blocks.  skip_groups: the GEMM's helper
+// workgroups take the scattered tiles' group items; force_scatter: every tile is scattered.
+static hipError_t plan_and_shrink(const uint16_t *x, int64_t T, int64_t n_in, int64_t n_out,
+                                  const SlotGeom &g, const int32_t *idx, int32_t K,
+                                  const float *scale, const PrefillCfg &c, const PrefillPtrs &q,
+                                  int skip_groups, int force_scatter, hipStream_t stream,
+                                  ShrinkArgs &s)
+{
+    if (c.n_mtiles > SH_MAX_TILES)
+        return hipErrorInvalidValue;   // callers split larger batches
+    const size_t lds = (size_t)((g.S + 31) / 32) * 4 + (size_t)g.S * 8 +
+                       (size_t)c.list_stride * 4 + (size_t)c.tok_stride;
+    if (hipError_t e = ensure_dynamic_lds((const void *)tile_plan_kernel, lds); e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(tile_plan_kernel, dim3(c.n_mtiles), dim3(256), lds, stream, idx, (int)T,
+                       K, g.S, g.R, g.n_slices, (int)n_in, g.rank, c.list_stride, q.tile_D,
+                       q.tile_w, q.tile_list, q.tile_toff, q.tile_gpre, q.tile_grp, c.grp_stride,
+                       force_scatter);
+    s = ShrinkArgs{};
+    s.x = x;
+    s.T = (int)T;
+    s.n_in = (int)n_in;
+    s.K = K;
+    s.g = g;
+    s.idx = idx;
+    s.scale = scale;
+    s.n_mtiles = c.n_mtiles;
+    s.list_stride = c.list_stride;
+    s.tile_D = q.tile_D;
+    s.tile_w = q.tile_w;
+    s.tile_list = q.tile_list;
+    s.vcat = q.vcat;
+    s.vcat_tile_elems = c.vcat_tile_elems;
+    s.tile_ord = q.tile_ord;
+    s.sc_tiles = q.sc_tiles;
+    s.sc_cap = c.sc_cap;
+    s.tile_toff = q.tile_toff;
+    s.tile_gpre = q.tile_gpre;
+    s.sc_pre = q.sc_pre;
+    s.n_chunks = (int)((n_out + SC_ROWS - 1) / SC_ROWS);
+    s.tile_grp = q.tile_grp;
+    s.grp_stride = c.grp_stride;
+    s.sd_part = q.sd_part;
+    s.sd_cap_slots = c.sd_cap_slots;
+    s.tile_pbase = q.tile_pbase;
+    s.sd_ks = q.sd_ks;
+    s.skip_groups = skip_groups;
+    s.force_scatter = force_scatter;
+    // three dense stages while the item tables and the kernel's own __shared__ arrays leave
+    // room in the 160 KB of LDS, else two
+    const size_t tables = (size_t)c.n_mtiles * SD_TABLE_BYTES;
+    const size_t st_lds = kernel_static_lds((const void *)sgmv_shrink_kernel);
+    s.stages = 3 * (size_t)SD_STAGE_BYTES + tables + st_lds <= LDS_BYTES ? 3 : 2;
+    const size_t sh_lds = (size_t)s.stages * SD_STAGE_BYTES + tables;
+    if (sh_lds + st_lds > LDS_BYTES)
+        return hipErrorInvalidValue;   // more tiles than SH_MAX_TILES allows
+    if (hipError_t e = ensure_dynamic_lds((const void *)sgmv_shrink_kernel, sh_lds);
+        e != hipSuccess)
+        return e;
+    // one workgroup per CU (the stages take most of its LDS), items shared out in the kernel:
+    // every workgroup then runs the kernel's item numbering once, all in one round
+    hipLaunchKernelGGL(sgmv_shrink_kernel, dim3((unsigned)device_cu_count()), dim3(SH_THREADS),
+                       sh_lds, stream, s);
+    if (!force_scatter)   // (no dense tile then: nothing to reduce)
+        hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)c.n_mtiles * (PF_BM / SR_TOK)),
+                           dim3(256), 0, stream, s);
+    return hipGetLastError();
+}
+
+// The scattered tiles' LoRA delta per adapter group, added to their fp32 sums and rounded
+// into y, one launch per slot rank (K).
+static hipError_t expand_scattered(int64_t T, int64_t n_out, const SlotGeom &g,
+                                   const int32_t *idx, int32_t K, uint16_t *y,
+                                   const PrefillCfg &c, const PrefillPtrs &q, hipStream_t stream)
+{
+    ScArgs x2{};
+    x2.T = (int)T;
+    x2.n_out = (int)n_out;
+    x2.K = K;
+    x2.g = g;
+    x2.idx = idx;
+    x2.tile_D = q.tile_D;
+    x2.tile_w = q.tile_w;
+    x2.tile_list = q.tile_list;
+    x2.list_stride = c.list_stride;
+    x2.sc_pre = q.sc_pre;
+    x2.tile_grp = q.tile_grp;
+    x2.grp_stride = c.grp_stride;
+    x2.vcat = q.vcat;
+    x2.vcat_tile_elems = c.vcat_tile_elems;
+    x2.sc_tiles = q.sc_tiles;
+    x2.sc_cap = c.sc_cap;
+    x2.n_chunks = (int)((n_out + SC_ROWS - 1) / SC_ROWS);
+    x2.part_sc = q.part_sc;
+    x2.y = y;
+    const size_t xl = (size_t)2 * c.sc_cap * sizeof(int32_t);
+    // items per scattered tile: at most (256 K / 16 + list_stride) groups x n_chunks
+    const int64_t items = (int64_t)c.sc_cap * (PF_BM * K / 16 + c.list_stride) * x2.n_chunks;
+    const unsigned grid = (unsigned)std::min<int64_t>(items, 1024);
+    hipError_t e = hipSuccess;
+    for (int pass = 0; pass < K && e == hipSuccess; ++pass) {
+        x2.pass = pass;
+        hipLaunchKernelGGL(sc_expand_kernel, dim3(grid), dim3(256), xl, stream, x2);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int64_t T,
@@ -1448,25 +1601,7 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
                           int32_t K, const float *scale, uint16_t *y, const PrefillCfg &c,
                           void *ws, hipStream_t stream)
 {
-    uint8_t *p = (uint8_t *)ws;
-    const PrefillLayout WL = prefill_layout(c);
-    int32_t *tile_D = (int32_t *)(p + WL.tile_D);
-    int32_t *tile_w = (int32_t *)(p + WL.tile_w);
-    int32_t *tile_list = (int32_t *)(p + WL.tile_list);
-    int32_t *tile_toff = (int32_t *)(p + WL.tile_toff);
-    int32_t *tile_gpre = (int32_t *)(p + WL.tile_gpre);
-    int32_t *sc_pre = (int32_t *)(p + WL.sc_pre);
-    int32_t *tile_ord = (int32_t *)(p + WL.tile_ord);
-    int32_t *sc_tiles = (int32_t *)(p + WL.sc_tiles);
-    float *part_sc = (float *)(p + WL.part_sc);
-    uint16_t *vcat = (uint16_t *)(p + WL.vcat);
-    int32_t *tile_pbase = (int32_t *)(p + WL.tile_pbase);
-    int32_t *sd_ks = (int32_t *)(p + WL.sd_ks);
-    float *sd_part = (float *)(p + WL.sd_part);
-    int4 *tile_grp = (int4 *)(p + WL.tile_grp);
-
-    if (g != nullptr && c.n_mtiles > SH_MAX_TILES)
-        return hipErrorInvalidValue;   // callers split larger batches
+    const PrefillPtrs q = prefill_ptrs(c, ws);
     // helper workgroups after the GEMM's tiles take the scattered tiles' shrink group items
     // while the tiles leave CUs idle (one workgroup per CU: 128 KB of LDS each)
     const int n_tiles = c.n_mtiles * c.n_ntiles;
@@ -1474,58 +1609,10 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     const int n_helpers = g != nullptr && c.may_scatter && n_tiles < n_cus ? n_cus - n_tiles : 0;
     ShrinkArgs s{};
     if (g != nullptr) {
-        const size_t lds = (size_t)((g->S + 31) / 32) * 4 + (size_t)g->S * 8 +
-                           (size_t)c.list_stride * 4 + (size_t)c.tok_stride;
-        if (hipError_t e = ensure_dynamic_lds((const void *)tile_plan_kernel, lds); e != hipSuccess)
-            return e;
-        hipLaunchKernelGGL(tile_plan_kernel, dim3(c.n_mtiles), dim3(256), lds, stream, idx,
-                           (int)T, K, g->S, g->R, g->n_slices, (int)n_in, g->rank, c.list_stride,
-                           tile_D, tile_w, tile_list, tile_toff, tile_gpre, tile_grp, c.grp_stride);
-        s.x = x;
-        s.T = (int)T;
-        s.n_in = (int)n_in;
-        s.K = K;
-        s.g = *g;
-        s.idx = idx;
-        s.scale = scale;
-        s.n_mtiles = c.n_mtiles;
-        s.list_stride = c.list_stride;
-        s.tile_D = tile_D;
-        s.tile_w = tile_w;
-        s.tile_list = tile_list;
-        s.vcat = vcat;
-        s.vcat_tile_elems = c.vcat_tile_elems;
-        s.tile_ord = tile_ord;
-        s.sc_tiles = sc_tiles;
-        s.sc_cap = c.sc_cap;
-        s.tile_toff = tile_toff;
-        s.tile_gpre = tile_gpre;
-        s.sc_pre = sc_pre;
-        s.n_chunks = (int)((n_out + SC_ROWS - 1) / SC_ROWS);
-        s.tile_grp = tile_grp;
-        s.grp_stride = c.grp_stride;
-        s.sd_part = sd_part;
-        s.sd_cap_slots = c.sd_cap_slots;
-        s.tile_pbase = tile_pbase;
-        s.sd_ks = sd_ks;
-        s.skip_groups = n_helpers > 0 ? 1 : 0;
-        // three dense stages while the item tables and the kernel's own __shared__ arrays
-        // leave room in the 160 KB of LDS, else two
-        const size_t tables = (size_t)c.n_mtiles * SD_TABLE_BYTES;
-        const size_t st_lds = kernel_static_lds((const void *)sgmv_shrink_kernel);
-        s.stages = 3 * (size_t)SD_STAGE_BYTES + tables + st_lds <= LDS_BYTES ? 3 : 2;
-        const size_t sh_lds = (size_t)s.stages * SD_STAGE_BYTES + tables;
-        if (sh_lds + st_lds > LDS_BYTES)
-            return hipErrorInvalidValue;   // more tiles than SH_MAX_TILES allows
-        if (hipError_t e = ensure_dynamic_lds((const void *)sgmv_shrink_kernel, sh_lds);
+        if (hipError_t e = plan_and_shrink(x, T, n_in, n_out, *g, idx, K, scale, c, q,
+                                           n_helpers > 0 ? 1 : 0, 0, stream, s);
             e != hipSuccess)
             return e;
-        // one workgroup per CU (the stages take most of its LDS), items shared out in the kernel:
-        // every workgroup then runs the kernel's item numbering once, all in one round
-        hipLaunchKernelGGL(sgmv_shrink_kernel, dim3((unsigned)n_cus), dim3(SH_THREADS), sh_lds,
-                           stream, s);
-        hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)c.n_mtiles * (PF_BM / SR_TOK)),
-                           dim3(256), 0, stream, s);
     }
     GemmArgs a{};
     a.x = x;
@@ -1539,14 +1626,14 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
     a.lora = g != nullptr;
     if (g != nullptr)
         a.g = *g;
-    a.vcat = vcat;
+    a.vcat = q.vcat;
     a.vcat_tile_elems = c.vcat_tile_elems;
-    a.tile_D = tile_D;
-    a.tile_w = tile_w;
-    a.tile_list = tile_list;
+    a.tile_D = q.tile_D;
+    a.tile_w = q.tile_w;
+    a.tile_list = q.tile_list;
     a.list_stride = c.list_stride;
-    a.tile_ord = tile_ord;
-    a.part_sc = part_sc;
+    a.tile_ord = q.tile_ord;
+    a.part_sc = q.part_sc;
     a.n_rg = (int)((n_out + 15) / 16);
     a.n_kb = (int)((n_in + 31) / 32);
     a.sh = s;
@@ -1564,38 +1651,48 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
                            dim3(512), lds, stream, a);
     hipError_t e = hipGetLastError();
     trace_mark(stream, false);
-    if (e == hipSuccess && g != nullptr && c.may_scatter) {
-        ScArgs x2{};
-        x2.T = (int)T;
-        x2.n_out = (int)n_out;
-        x2.K = K;
-        x2.g = *g;
-        x2.idx = idx;
-        x2.tile_D = tile_D;
-        x2.tile_w = tile_w;
-        x2.tile_list = tile_list;
-        x2.list_stride = c.list_stride;
-        x2.sc_pre = sc_pre;
-        x2.tile_grp = tile_grp;
-        x2.grp_stride = c.grp_stride;
-        x2.vcat = vcat;
-        x2.vcat_tile_elems = c.vcat_tile_elems;
-        x2.sc_tiles = sc_tiles;
-        x2.sc_cap = c.sc_cap;
-        x2.n_chunks = (int)((n_out + SC_ROWS - 1) / SC_ROWS);
-        x2.part_sc = part_sc;
-        x2.y = y;
-        const size_t xl = (size_t)2 * c.sc_cap * sizeof(int32_t);
-        // items per scattered tile: at most (256 K / 16 + list_stride) groups x n_chunks
-        const int64_t items = (int64_t)c.sc_cap * (PF_BM * K / 16 + c.list_stride) * x2.n_chunks;
-        const unsigned grid = (unsigned)std::min<int64_t>(items, 1024);
-        for (int pass = 0; pass < K && e == hipSuccess; ++pass) {
-            x2.pass = pass;
-            hipLaunchKernelGGL(sc_expand_kernel, dim3(grid), dim3(256), xl, stream, x2);
-            e = hipGetLastError();
-        }
-    }
+    if (e == hipSuccess && g != nullptr && c.may_scatter)
+        e = expand_scattered(T, n_out, *g, idx, K, y, c, q, stream);
     return e;
+}
+
+PrefillCfg grouped_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t R,
+                          int32_t n_slices)
+{
+    PrefillCfg c = prefill_config(T, K, n_in, n_out, S, R, n_slices);
+    c.sd_cap_slots = 0;   // every tile scattered: no dense item, no partial blocks
+    return c;
+}
+
+bool grouped_decode_fits(const PrefillCfg &c)
+{
+    return c.n_mtiles <= c.sc_cap && c.n_mtiles <= SH_MAX_TILES;
+}
+
+hipError_t launch_grouped_shrink(const uint16_t *x, int64_t T, int64_t n_in, int64_t n_out,
+                                 const SlotGeom &g, const int32_t *idx, int32_t K,
+                                 const float *scale, const PrefillCfg &c, void *ws,
+                                 hipStream_t stream)
+{
+    if (!grouped_decode_fits(c))
+        return hipErrorInvalidValue;
+    ShrinkArgs s;
+    return plan_and_shrink(x, T, n_in, n_out, g, idx, K, scale, c, prefill_ptrs(c, ws), 0, 1,
+                           stream, s);
+}
+
+float *grouped_base_sums(const PrefillCfg &c, void *ws)
+{
+    return prefill_ptrs(c, ws).part_sc;
+}
+
+hipError_t launch_grouped_expand(int64_t T, int64_t n_out, const SlotGeom &g, const int32_t *idx,
+                                 int32_t K, uint16_t *y, const PrefillCfg &c, void *ws,
+                                 hipStream_t stream)
+{
+    if (!grouped_decode_fits(c))
+        return hipErrorInvalidValue;
+    return expand_scattered(T, n_out, g, idx, K, y, c, prefill_ptrs(c, ws), stream);
 }
 
 }  // namespace mlora

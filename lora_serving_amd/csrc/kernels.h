@@ -72,10 +72,12 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed,
                               hipStream_t stream);
 // ---- decode_finish.hip: y = bf16(sum of the split partials + LoRA delta), T <= 64 ----------
 // part: fp32 [sk][n_tiles][T][64] (launch_decode_gemm); upart: fp32 [sk][K][T][wd] unscaled
-// shrink pieces (nullptr: base only, g unused)
+// shrink pieces (nullptr: base only, g unused); ysum: fp32 [T][n_out], the same sums before
+// rounding, or nullptr
 hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, const float *upart,
                                 const float *scale, int64_t T, int64_t n_out, const SlotGeom *g,
-                                const int32_t *idx, int32_t K, uint16_t *y, hipStream_t stream);
+                                const int32_t *idx, int32_t K, uint16_t *y, float *ysum,
+                                hipStream_t stream);
 
 // ---- pack.hip: W in the matrix cores' fragment order ------------------------------------------
 // Wp[rg][kb][lane][8] = W[16 rg + lane % 16][32 kb + 8 (lane / 16) + e], zero padded.
@@ -105,6 +107,8 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
                           int32_t n_slices);
 size_t prefill_workspace_bytes(const PrefillCfg &c);
 bool prefill_worth_it(int64_t T, int64_t n_out);
+bool grouped_decode_worth_it(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t wd,
+                             int32_t R);
 // y = bf16(x W^T + LoRA delta); g == nullptr: base only.  ws: prefill_workspace_bytes(c).
 // Profiling hook (mlora_trace_start): records the begin/end event of the main product kernel.
 void trace_mark(hipStream_t stream, bool begin);
@@ -113,6 +117,26 @@ hipError_t launch_prefill(const uint16_t *x, const uint16_t *W, bool packed, int
                           int64_t n_in, int64_t n_out, const SlotGeom *g, const int32_t *idx,
                           int32_t K, const float *scale, uint16_t *y, const PrefillCfg &c,
                           void *ws, hipStream_t stream);
+
+// Grouped decode: the decode kernels' base product with the LoRA terms computed per adapter
+// group by the tiled path's scattered-tile kernels (every 256-token tile scattered).  Order:
+// launch_grouped_shrink (tile plan, group items into V), the decode GEMM and finish without
+// LoRA (the finish also leaves the fp32 sums in grouped_base_sums(c, ws), [T][n_out]), then
+// launch_grouped_expand (adds each token's delta, rounds y).  Only while
+// grouped_decode_fits(c) (every tile's fp32 sums kept); c: grouped_config(T, ...), ws:
+// prefill_workspace_bytes(c).
+// the tiled path's configuration for a grouped-decode launch of T tokens (no dense regions)
+PrefillCfg grouped_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t S, int32_t R,
+                          int32_t n_slices);
+bool grouped_decode_fits(const PrefillCfg &c);
+hipError_t launch_grouped_shrink(const uint16_t *x, int64_t T, int64_t n_in, int64_t n_out,
+                                 const SlotGeom &g, const int32_t *idx, int32_t K,
+                                 const float *scale, const PrefillCfg &c, void *ws,
+                                 hipStream_t stream);
+float *grouped_base_sums(const PrefillCfg &c, void *ws);
+hipError_t launch_grouped_expand(int64_t T, int64_t n_out, const SlotGeom &g, const int32_t *idx,
+                                 int32_t K, uint16_t *y, const PrefillCfg &c, void *ws,
+                                 hipStream_t stream);
 
 // ---- noalloc.hip: the fixed per-device scratch of mlora_linear_noalloc ----------------------
 // Device address of this library's scratch array on the stream's device (looked up once per

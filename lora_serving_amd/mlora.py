@@ -31,6 +31,7 @@ MLORA_NO_ADAPTERS = 1
 MLORA_PATH_DECODE = 2
 MLORA_PATH_TILED = 4
 MLORA_W_PACKED = 8
+MLORA_PATH_GROUPED = 16
 MLORA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("mlora_status_string", "mlora_last_error", "mlora_factor", "mlora_slot_bytes",

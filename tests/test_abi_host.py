@@ -100,6 +100,8 @@ def test_linear_argument_checks(m):
     assert call_linear(m, s, ws=0x50000, ws_bytes=16) == m.MLORA_ERR_WORKSPACE
     assert call_linear(m, s, T=0) == m.MLORA_OK                # T = 0 is a no-op
     assert call_linear(m, s, flags=m.MLORA_PATH_DECODE | m.MLORA_PATH_TILED) == m.MLORA_ERR_ARG
+    assert call_linear(m, s, flags=m.MLORA_PATH_GROUPED | m.MLORA_PATH_TILED) == m.MLORA_ERR_ARG
+    assert call_linear(m, s, flags=m.MLORA_PATH_GROUPED | m.MLORA_PATH_DECODE) == m.MLORA_ERR_ARG
     # base-only hint needs no slots and no index map, but still a workspace
     assert call_linear(m, None, idx=0, flags=m.MLORA_NO_ADAPTERS) == m.MLORA_ERR_WORKSPACE
 

@@ -1,8 +1,8 @@
 """HIP graph capture of the library's calls.
 
 A serving loop captures its decode steps in a graph so that the host's cost per call is paid
-once per replay.  mlora_linear (decode path; tiled path with stacked and with scattered
-tiles), the mlora_shrink / mlora_expand pair and mlora_plan are captured together on torch's
+once per replay.  mlora_linear (decode path; grouped decode; tiled path with stacked and with
+scattered tiles), the mlora_shrink / mlora_expand pair and mlora_plan are captured together on torch's
 capture stream, then the graph is replayed several times with the program's own eager work
 and synchronizations between the replays; every replay must reproduce the eager results bit
 for bit (the kernels are deterministic, and no call allocates memory or records a memset).
@@ -47,12 +47,13 @@ def test_graph_replays_match_eager():
     yd = torch.empty((Ld.T, Ld.n_out), dtype=bf, device=dev)
     yt = torch.empty((Lt.T, Lt.n_out), dtype=bf, device=dev)
     ys = torch.empty((Ls.T, Ls.n_out), dtype=bf, device=dev)
+    yg = torch.empty((Ld.T, Ld.n_out), dtype=bf, device=dev)
     v = torch.empty((Ld.K, Ld.T, Ld.n_slices * Ld.R), dtype=torch.float32, device=dev)
     y_base = torch.randn((Ld.T, Ld.n_out), device=dev).to(bf)      # expand accumulates onto it
     ye = torch.empty_like(y_base)
     i32 = lambda n: torch.empty((n,), dtype=torch.int32, device=dev)
     perm, ss, st, sl, cnt = i32(Ld.T * Ld.K), i32(Ld.S), i32(Ld.S), i32(Ld.S), i32(2)
-    outs = [yd, yt, ys, v, ye, perm, ss, st, sl, cnt]
+    outs = [yd, yt, ys, yg, v, ye, perm, ss, st, sl, cnt]
 
     def work():
         mlora.mlora_linear(Dd.x, Dd.W, Dd.slots, Dd.idx, Dd.scale, yd,
@@ -61,6 +62,8 @@ def test_graph_replays_match_eager():
                            flags=mlora.MLORA_PATH_TILED, ws=Dt.ws)
         mlora.mlora_linear(Ds.x, Ds.W, Ds.slots, Ds.idx, Ds.scale, ys,
                            flags=mlora.MLORA_PATH_TILED, ws=Ds.ws)
+        mlora.mlora_linear(Dd.x, Dd.W, Dd.slots, Dd.idx, Dd.scale, yg,
+                           flags=mlora.MLORA_PATH_GROUPED, ws=Dd.ws)
         mlora.mlora_shrink(Dd.x, Dd.slots, Dd.idx, Dd.scale, v, ws=Dd.ws)
         torch.mul(y_base, 1.0, out=ye)         # a kernel, not a copy or memset node
         mlora.mlora_expand(v, Dd.slots, Dd.idx, ye)

@@ -109,6 +109,83 @@ def test_tiled_path_small(oracle_mod, case):
         assert tol_ok(y2, y_ref).all()
 
 
+GROUPED = [
+    # seed, T, n_in, n_out, S, R, K, slices   (grouped decode forced)
+    (60, 1, 64, 48, 3, 8, 1, None),
+    (61, 37, 256, 200, 5, 16, 2, None),
+    (62, 300, 512, 520, 30, 32, 3, [260, 130, 130]),   # two tiles, the second ragged
+    (63, 600, 392, 136, 9, 64, 1, [64, 72]),           # two launches: 512 + 88 tokens
+    (64, 256, 1024, 1000, 40, 16, 2, None),
+]
+
+
+@pytest.mark.parametrize("case", GROUPED, ids=[f"g{c[0]}" for c in GROUPED])
+def test_grouped_decode_small(oracle_mod, case):
+    """The grouped decode (decode kernels' base product, LoRA terms per adapter group with
+    every 256-token tile on the scattered route) against the oracle, on maps with runs of one
+    adapter and on scattered ones; and the plain decode path within the same bound."""
+    from lora_serving_amd import mlora
+    seed, T, n_in, n_out, S, R, K, slices = case
+    for contiguous in (False, True):
+        L = synth.random_layer(seed, T=T, n_in=n_in, n_out=n_out, S=S, R=R, K=K,
+                               slice_sizes=slices, p_sentinel=0.25, contiguous=contiguous)
+        say(f"[grouped] seed={seed} T={T} n_in={n_in} n_out={n_out} K={K} R={R} "
+            f"contiguous={contiguous}")
+        D = DevLayer(L)
+        y = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_GROUPED))
+        y_ref = oracle_mod.linear(L)
+        ok = tol_ok(y, y_ref)
+        assert ok.all(), f"grouped {seed}: worst {worst(y, y_ref):.3e}, {np.sum(~ok)} out"
+        y2 = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_DECODE))
+        assert tol_ok(y2, y_ref).all()
+
+
+def test_grouped_decode_rank_table_and_sentinels(oracle_mod):
+    """Grouped decode with the slots' true ranks (V blocks and expand walks sized by the
+    tile's largest rank), and an all-sentinel map (y = W x exactly as with MLORA_NO_ADAPTERS)."""
+    import torch
+    from lora_serving_amd import mlora
+    ranks = [8, 16, 64, 24, 8, 40, 16, 5, 12]
+    L = synth.random_layer(65, T=400, n_in=512, n_out=384, S=9, R=64, K=2,
+                           slice_sizes=[256, 64, 64], ranks=ranks, p_sentinel=0.2)
+    say(f"[grouped ranked] T={L.T} ranks={ranks}")
+    D = DevLayer(L)
+    D.slots = mlora.Slots(D.A, D.B, D.factor, slice_start=[int(v) for v in L.slice_start],
+                          rank=torch.tensor(ranks, dtype=torch.int32, device="cuda"))
+    y = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_GROUPED))
+    y_ref = oracle_mod.linear(L)
+    assert tol_ok(y, y_ref).all(), f"worst {worst(y, y_ref):.3e}"
+    D.idx.fill_(-1)
+    y_all = D.linear(flags=mlora.MLORA_PATH_GROUPED).clone()
+    y_base = D.linear(flags=mlora.MLORA_PATH_DECODE | mlora.MLORA_NO_ADAPTERS)
+    assert torch.equal(y_all.view(torch.int16), y_base.view(torch.int16))
+
+
+def test_grouped_decode_chosen_for_heavy_gather(oracle_mod):
+    """The mixed batch's 256 one-token requests alone (merged QKV, ranks up to 64 padded to
+    64): their per-pair A and B reads are about 12 times W, so the library takes the grouped
+    decode by itself (the group shrink and the grouped expand around the decode GEMM and
+    finish); the result matches the oracle on every third token and the last."""
+    import dataclasses
+    L0 = synth.workload_mixed_qkv()
+    nd = sum(1 for (_s, n) in L0.segments if n == 1)
+    L = dataclasses.replace(L0, T=nd, x=L0.x[:nd].copy(), idx=L0.idx[:nd].copy(),
+                            scale=L0.scale[:nd].copy(), segments=L0.segments[:nd])
+    say(f"[grouped auto] T={L.T} {L.n_in}->{L.n_out} R={L.R}")
+    D = DevLayer(L)
+    names = _mlora_kernels_launched(lambda: D.linear())
+    assert {"tile_plan_kernel", "sgmv_shrink_kernel", "decode_gemm_kernel",
+            "decode_finish_kernel", "sc_expand_kernel"} <= names, sorted(names)
+    y = from_dev_bf16(D.linear())
+    toks = np.unique(np.r_[np.arange(0, L.T, 3), L.T - 1]).astype(np.int64)
+    y_ref = oracle_mod.linear(L, tokens=toks)
+    assert tol_ok(y[toks], y_ref).all(), f"worst {worst(y[toks], y_ref):.3e}"
+    # the decode batch of the headline workload keeps the per-pair path
+    Dd = DevLayer(synth.workload_decode())
+    names_d = _mlora_kernels_launched(lambda: Dd.linear())
+    assert names_d == {"decode_gemm_kernel", "decode_finish_kernel"}, sorted(names_d)
+
+
 def test_tiled_scattered_tiles_beyond_capacity(oracle_mod):
     """Wide n_out keeps the fp32 sums of only one scattered tile: the first takes the per-adapter
     shrink/expand route, the other two the extra-k-step route; both against the oracle."""

@@ -52,6 +52,16 @@ def test_noalloc_tiled_then_smaller_decode():
 
 
 @pytest.mark.gpu
+def test_noalloc_grouped_decode_then_smaller():
+    from lora_serving_amd import mlora
+    _check(synth.random_layer(7106, T=300, n_in=512, n_out=768, S=20, R=32, K=2,
+                              slice_sizes=[512, 128, 128], p_sentinel=0.2),
+           flags=mlora.MLORA_PATH_GROUPED)
+    _check(synth.random_layer(7107, T=33, n_in=256, n_out=264, S=5, R=16, K=3, p_sentinel=0.3),
+           flags=mlora.MLORA_PATH_GROUPED)
+
+
+@pytest.mark.gpu
 def test_noalloc_rejects_calls_beyond_the_fixed_scratch():
     """A 4096 -> 100,000 decode call needs about 100 MB of split partials: refused before any
     launch, y untouched, the needed size named; the next call that fits still works."""
