@@ -49,6 +49,8 @@ DESCRIPTIONS = {
                  "alpha 32, 26 tokens base-only, K=1",
     "lm_head": "lm_head: T=64 one-token requests, 4096->100000 (vocabulary) bf16, 100 adapters "
                "rank 16 alpha 32, 6 tokens base-only, K=1",
+    "mixed_qkv_decode": "mixed_qkv_decode: the mixed batch's 256 one-token requests alone, merged "
+                        "QKV 4096->(4096,1024,1024), 64 adapters ranks {8,16,64} padded to 64",
 }
 # the workloads of the `configs` list, in this order, when the headline is the decode batch
 CONFIG_ORDER = ["tiny", "prefill", "mixed_qkv", "compose"]
@@ -75,6 +77,7 @@ def algorithmic(L):
             "distinct_adapters": int(len(used)),
             # the part of the call done by the main product kernel, per path
             "decode_kernel_bytes": w_bytes + x_bytes + a_bytes + meta,
+            "grouped_kernel_bytes": w_bytes + x_bytes,         # the decode GEMM on the base alone
             "decode_kernel_flops": base_flops + shrink_flops,
             "tiled_kernel_bytes": w_bytes + x_bytes + y_bytes + b_bytes + meta,
             "tiled_kernel_flops": base_flops + expand_flops,
@@ -244,6 +247,12 @@ class Prepared:
         self.w_layout = w_layout
         self.algs = [algorithmic(L) for L in self.layers]
         self.devs = [DevLayer(L) for L in self.layers]
+        # the kernels mlora_linear runs for each layer (the library's own host-side choice)
+        names = {mlora.MLORA_PATH_DECODE: "decode", mlora.MLORA_PATH_TILED: "tiled",
+                 mlora.MLORA_PATH_GROUPED: "grouped"}
+        self.paths = [names.get(mlora.mlora_linear_path(D.L.T, D.L.n_in, D.L.n_out, D.slots,
+                                                        D.L.K, flags), "?")
+                      for D in self.devs]
         # rotating copies so that decode-sized steps read HBM, not the Infinity Cache (a
         # workload under 1 MB is latency-bound and keeps one copy)
         per_set = sum((D.x.numel() + D.W.numel() + D.A.numel() + D.B.numel()) * 2 +
@@ -403,11 +412,15 @@ def linear_roofline(P: Prepared, kernel_ms, only_layer=None):
     k_avg_ms = sum(kernel_ms) / len(kernel_ms)
     per_step = P.launches_per_step(only_layer)
     if P.decode_like:
-        k_bytes = sum(a["decode_kernel_bytes"] for a in algs) / per_step
+        paths = [P.paths[i] for i in idxs]
+        k_bytes = sum(a["grouped_kernel_bytes" if p == "grouped" else "decode_kernel_bytes"]
+                      for a, p in zip(algs, paths)) / per_step
         achieved = k_bytes / (k_avg_ms * 1e-3) / 1e9
+        what = ("base product (grouped decode: the LoRA terms in the group kernels)"
+                if all(p == "grouped" for p in paths) else "base product + LoRA shrink")
         return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                "kernel": "mlora::decode_gemm_kernel (base product + LoRA shrink)",
+                "kernel": f"mlora::decode_gemm_kernel ({what})",
                 "kernel_avg_us": k_avg_ms * 1e3, "algorithmic_bytes_per_launch": k_bytes}
     k_flops = sum(a["tiled_kernel_flops"] for a in algs) / per_step
     achieved = k_flops / (k_avg_ms * 1e-3) / 1e12
@@ -433,7 +446,8 @@ def config_entry(name, steps, warmup, cpu_s, with_cpu, graph=False):
          "layers": [[L.n_in, L.n_out] for L in P.layers],
          "distinct_adapters": [a["distinct_adapters"] for a in P.algs],
          "steps": steps_done, "warmup": warmup, "rotating_sets": P.nsets,
-         "w_layout": P.w_layout, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+         "w_layout": P.w_layout, "path": P.paths, "ms_per_step": ms,
+         "tokens_per_s": T / (ms * 1e-3),
          "roofline": roof,
          "step_algorithmic": {"bytes": tot_bytes, "flops": tot_flops},
          "step_achieved": {"GBps": tot_bytes / (ms * 1e-3) / 1e9,
@@ -607,7 +621,8 @@ def main():
                    "layers": [[L.n_in, L.n_out] for L in layers], "S": layers[0].S,
                    "R": layers[0].R, "K": layers[0].K,
                    "distinct_adapters": [a["distinct_adapters"] for a in algs],
-                   "rotating_sets": P.nsets, "w_layout": P.w_layout, "op": args.op,
+                   "rotating_sets": P.nsets, "w_layout": P.w_layout, "path": P.paths,
+                   "op": args.op,
                    "graph": args.graph},
         "roofline": roof,
         "step_algorithmic": {"bytes": tot_bytes, "flops": tot_flops},

@@ -238,6 +238,16 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
                           hipStream_t stream);
 
 /*
+ * Which kernels mlora_linear runs for these sizes, slots and flags: MLORA_PATH_DECODE,
+ * MLORA_PATH_TILED or MLORA_PATH_GROUPED (the choice is made on the host from the shapes and
+ * flags alone, as described above; idx is not read).  Host only, no GPU call; slots' data
+ * pointers are not checked.  Returns 0 where mlora_linear would fail its checks on these
+ * arguments (sizes, slot geometry, conflicting flags, MLORA_PATH_GROUPED that does not fit).
+ */
+uint32_t mlora_linear_path(int64_t T, int64_t n_in, int64_t n_out, const mlora_slots *slots,
+                           int32_t K, uint32_t flags);
+
+/*
  * mlora_linear for callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the same computation, kernels and
  * output bits as mlora_linear with the same arguments, but its scratch space is a fixed array

@@ -408,6 +408,39 @@ mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_
 
 namespace {
 
+// The kernels mlora_linear runs for these sizes and flags (a host-side choice from the shapes):
+// MLORA_PATH_TILED when forced or when the batch fills the GPU with 256 x 256 output tiles;
+// else MLORA_PATH_GROUPED when forced or when the per-pair adapter reads of the decode kernels
+// would exceed four times W's bytes (and the grouped expand keeps a launch's fp32 sums);
+// else MLORA_PATH_DECODE.  MLORA_ERR_UNSUPPORTED: grouped forced where it does not fit.
+mlora_status choose_path(int64_t T, int64_t n_in, int64_t n_out, int32_t S, int32_t R,
+                         int32_t n_slices, int32_t K, uint32_t flags, bool lora, uint32_t *path)
+{
+    const bool force_decode = (flags & MLORA_PATH_DECODE) != 0;
+    const bool force_tiled = (flags & MLORA_PATH_TILED) != 0;
+    const bool force_grouped = (flags & MLORA_PATH_GROUPED) != 0;
+    if (force_tiled || (!force_decode && !force_grouped && prefill_worth_it(T, n_out))) {
+        *path = MLORA_PATH_TILED;
+        return MLORA_OK;
+    }
+    *path = MLORA_PATH_DECODE;
+    if (!lora || force_decode)
+        return MLORA_OK;
+    const int64_t Tc = std::min<int64_t>(std::max<int64_t>(T, 1), DECODE_MAX_T);
+    const bool fits = grouped_decode_fits(grouped_config(Tc, K, n_in, n_out, S, R, n_slices));
+    if (force_grouped && !fits) {
+        std::snprintf(g_last_error, sizeof g_last_error,
+                      "MLORA_PATH_GROUPED: the fp32 sums of %lld tokens x %lld outputs exceed "
+                      "what the grouped expand keeps",
+                      (long long)Tc, (long long)n_out);
+        return MLORA_ERR_UNSUPPORTED;
+    }
+    if (fits && (force_grouped ||
+                 grouped_decode_worth_it(Tc, K, n_in, n_out, n_slices * R, R)))
+        *path = MLORA_PATH_GROUPED;
+    return MLORA_OK;
+}
+
 // mlora_linear and mlora_linear_noalloc: checks, scratch regions and kernel dispatch.  With
 // noalloc the scratch is the library's fixed per-device array (ws and ws_bytes unused) and holds
 // only the regions of the path the call takes, from offset 0; otherwise it is the caller's
@@ -447,27 +480,14 @@ mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in
         return MLORA_ERR_ARG;
     if (lora && idx == nullptr)
         return MLORA_ERR_ARG;
-    const bool force_decode = (flags & MLORA_PATH_DECODE) != 0;
-    const bool force_tiled = (flags & MLORA_PATH_TILED) != 0;
-    const bool force_grouped = (flags & MLORA_PATH_GROUPED) != 0;
     const bool packed = (flags & MLORA_W_PACKED) != 0;
-    const bool tiled =
-        force_tiled || (!force_decode && !force_grouped && prefill_worth_it(T, n_out));
+    uint32_t path = 0;
+    if (mlora_status st = choose_path(T, n_in, n_out, S, R, n_slices, K, flags, lora, &path);
+        st != MLORA_OK)
+        return st;
+    const bool tiled = path == MLORA_PATH_TILED;
     // grouped decode: the decode kernels' base product, the LoRA terms per adapter group
-    bool grouped = false;
-    if (!tiled && lora && !force_decode) {
-        const int64_t Tc = std::min<int64_t>(T, DECODE_MAX_T);
-        const bool fits = grouped_decode_fits(grouped_config(Tc, K, n_in, n_out, S, R, n_slices));
-        if (force_grouped && !fits) {
-            std::snprintf(g_last_error, sizeof g_last_error,
-                          "MLORA_PATH_GROUPED: the fp32 sums of %lld tokens x %lld outputs exceed "
-                          "the grouped expand's 64 MiB",
-                          (long long)Tc, (long long)n_out);
-            return MLORA_ERR_UNSUPPORTED;
-        }
-        grouped = fits && (force_grouped || grouped_decode_worth_it(Tc, K, n_in, n_out,
-                                                                     n_slices * R, R));
-    }
+    const bool grouped = path == MLORA_PATH_GROUPED;
     size_t off_v, off_part, off_pre, need;
     if (!noalloc) {
         const Layout L = make_layout(T, K, n_in, n_out, S, R, n_slices);
@@ -590,6 +610,31 @@ mlora_status mlora_linear(const void *x, const void *W, int64_t T, int64_t n_in,
 {
     return linear_common(x, W, T, n_in, n_out, slots, idx, K, scale, y, flags, ws, ws_bytes,
                          false, stream);
+}
+
+uint32_t mlora_linear_path(int64_t T, int64_t n_in, int64_t n_out, const mlora_slots *slots,
+                           int32_t K, uint32_t flags)
+{
+    if (T < 0 || n_in <= 0 || n_out <= 0 || K < 1 || K > MLORA_MAX_K)
+        return 0;
+    {
+        const uint32_t p = flags & (MLORA_PATH_DECODE | MLORA_PATH_TILED | MLORA_PATH_GROUPED);
+        if (p & (p - 1))
+            return 0;
+    }
+    const bool lora = (flags & MLORA_NO_ADAPTERS) == 0;
+    SlotGeom g;
+    int32_t S = 1, R = 8, n_slices = 1;
+    if (lora || slots != nullptr) {
+        if (check_slots(slots, n_out, false, &g) != MLORA_OK)
+            return 0;
+        S = g.S;
+        R = g.R;
+        n_slices = g.n_slices;
+    }
+    uint32_t path = 0;
+    return choose_path(T, n_in, n_out, S, R, n_slices, K, flags, lora, &path) == MLORA_OK ? path
+                                                                                         : 0;
 }
 
 mlora_status mlora_linear_noalloc(const void *x, const void *W, int64_t T, int64_t n_in,

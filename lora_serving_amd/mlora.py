@@ -38,7 +38,7 @@ EXPORTS = ("mlora_status_string", "mlora_last_error", "mlora_factor", "mlora_slo
            "mlora_workspace_size", "mlora_slot_load", "mlora_packed_weight_bytes",
            "mlora_pack_weight",
            "mlora_validate", "mlora_plan", "mlora_shrink", "mlora_expand", "mlora_linear",
-           "mlora_linear_noalloc", "mlora_trace_start", "mlora_trace_stop")
+           "mlora_linear_path", "mlora_linear_noalloc", "mlora_trace_start", "mlora_trace_stop")
 
 _P = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -82,6 +82,8 @@ _lib.mlora_expand.argtypes = [_P, _i64, _i64, _SLOTS_P, _P, _i32, _P, _P]
 _lib.mlora_linear.restype = ctypes.c_int
 _lib.mlora_linear.argtypes = [_P, _P, _i64, _i64, _i64, _SLOTS_P, _P, _i32, _P, _P, ctypes.c_uint32,
                               _P, ctypes.c_size_t, _P]
+_lib.mlora_linear_path.restype = ctypes.c_uint32
+_lib.mlora_linear_path.argtypes = [_i64, _i64, _i64, _SLOTS_P, _i32, ctypes.c_uint32]
 _lib.mlora_linear_noalloc.restype = ctypes.c_int
 _lib.mlora_linear_noalloc.argtypes = [_P, _P, _i64, _i64, _i64, _SLOTS_P, _P, _i32, _P, _P,
                                       ctypes.c_uint32, _P]
@@ -295,6 +297,14 @@ def mlora_linear(x, W, slots: Slots | None, idx, scale, y, flags: int = 0, ws=No
                              _ptr(y), flags, _ptr(ws),
                              0 if ws is None else ws.numel() * ws.element_size(),
                              _stream(stream)), "mlora_linear")
+
+
+def mlora_linear_path(T: int, n_in: int, n_out: int, slots: Slots | None, K: int = 1,
+                      flags: int = 0) -> int:
+    """The path mlora_linear takes for these sizes and flags (MLORA_PATH_DECODE, _TILED or
+    _GROUPED), or 0 where its checks would fail."""
+    return int(_lib.mlora_linear_path(T, n_in, n_out, None if slots is None else slots.ref, K,
+                                      flags))
 
 
 def mlora_linear_noalloc(x, W, slots: Slots | None, idx, scale, y, flags: int = 0,

@@ -252,6 +252,16 @@ def workload_mixed_qkv_prefill_first(seed: int = 1003) -> Layer:
     return L
 
 
+def workload_mixed_qkv_decode(seed: int = 1003) -> Layer:
+    """The mixed merged-QKV batch's one-token requests alone (same draws): the decode part of
+    that batch as a call of its own."""
+    L = workload_mixed_qkv(seed=seed)
+    nd = sum(1 for (_s, n) in L.segments if n == 1)
+    return dataclasses.replace(L, name="mixed_qkv_decode", T=nd, x=L.x[:nd].copy(),
+                               idx=L.idx[:nd].copy(), scale=L.scale[:nd].copy(),
+                               segments=L.segments[:nd])
+
+
 WORKLOADS = {
     "tiny": workload_tiny,
     "decode256": workload_decode256,
@@ -260,6 +270,7 @@ WORKLOADS = {
     "prefill": workload_prefill,
     "mixed_qkv": workload_mixed_qkv,
     "mixed_qkv_prefill_first": workload_mixed_qkv_prefill_first,
+    "mixed_qkv_decode": workload_mixed_qkv_decode,
     "compose": workload_compose,
 }
 

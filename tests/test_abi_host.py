@@ -106,6 +106,31 @@ def test_linear_argument_checks(m):
     assert call_linear(m, None, idx=0, flags=m.MLORA_NO_ADAPTERS) == m.MLORA_ERR_WORKSPACE
 
 
+def test_linear_path_choice(m):
+    """The host-side choice of mlora_linear's kernels for the workloads' shapes and the
+    forcing flags (no GPU call)."""
+    L = m._lib
+    dec, til, grp = m.MLORA_PATH_DECODE, m.MLORA_PATH_TILED, m.MLORA_PATH_GROUPED
+    s16 = slots_struct(m, S=100, R=16)
+    qkv = slots_struct(m, S=64, R=64, n_slices=3, starts=[0, 4096, 5120, 6144, 0])
+    path = lambda T, n_in, n_out, s, K=1, flags=0: L.mlora_linear_path(T, n_in, n_out,
+                                                                        ctypes.byref(s), K, flags)
+    assert path(64, 4096, 4096, s16) == dec            # decode batch
+    assert path(256, 4096, 4096, s16) == dec           # 256 tokens at rank 16: gather ~2x W
+    assert path(64, 4096, 100_000, s16) == dec         # LM head
+    assert path(16384, 4096, 11008, slots_struct(m, S=100, R=64)) == til   # prefill
+    assert path(2304, 4096, 6144, qkv) == til          # the mixed batch
+    assert path(256, 4096, 6144, qkv) == grp           # its 256 one-token requests: ~12x W
+    assert path(256, 4096, 6144, qkv, flags=dec) == dec
+    assert path(256, 4096, 6144, qkv, flags=til) == til
+    assert path(64, 4096, 4096, s16, flags=grp) == grp
+    assert path(256, 4096, 6144, qkv, flags=m.MLORA_NO_ADAPTERS) == dec   # base only
+    assert path(512, 4096, 100_000, s16, flags=grp) == 0   # 2 tiles of fp32 sums: too wide
+    assert path(64, 4096, 4096, s16, flags=dec | grp) == 0
+    assert path(64, 4096, 4096, slots_struct(m, R=24)) == 0
+    assert path(-1, 4096, 4096, s16) == 0
+
+
 def test_other_entry_points_argument_checks(m):
     s = slots_struct(m)
     L = m._lib

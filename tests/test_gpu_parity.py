@@ -166,11 +166,7 @@ def test_grouped_decode_chosen_for_heavy_gather(oracle_mod):
     64): their per-pair A and B reads are about 12 times W, so the library takes the grouped
     decode by itself (the group shrink and the grouped expand around the decode GEMM and
     finish); the result matches the oracle on every third token and the last."""
-    import dataclasses
-    L0 = synth.workload_mixed_qkv()
-    nd = sum(1 for (_s, n) in L0.segments if n == 1)
-    L = dataclasses.replace(L0, T=nd, x=L0.x[:nd].copy(), idx=L0.idx[:nd].copy(),
-                            scale=L0.scale[:nd].copy(), segments=L0.segments[:nd])
+    L = synth.workload_mixed_qkv_decode()
     say(f"[grouped auto] T={L.T} {L.n_in}->{L.n_out} R={L.R}")
     D = DevLayer(L)
     names = _mlora_kernels_launched(lambda: D.linear())
@@ -600,7 +596,8 @@ def test_large_workloads_sampled(oracle_mod, which):
 
 
 @pytest.mark.parametrize("which", ["decode", "decode256", "lm_head", "mixed_qkv",
-                                   "mixed_qkv_prefill_first", "prefill", "compose"])
+                                   "mixed_qkv_prefill_first", "mixed_qkv_decode", "prefill",
+                                   "compose"])
 def test_workloads_in_bench_configuration(oracle_mod, which):
     """Each bench workload called the way bench.py calls it: the slots carry the true-rank
     table, decode-sized batches (T <= 512) take the packed base weight.  Whole output for the
