@@ -116,6 +116,15 @@ int64_t mlora_slot_bytes(int32_t S, int32_t R, int64_t n_in, int64_t n_out, int3
 /*
  * Bytes of workspace that mlora_plan / mlora_shrink / mlora_linear need for these sizes
  * (an upper bound over every index map of this shape).  Returns 0 on invalid arguments.
+ * The largest part is the tiled path's V blocks, about T x n_slices x 4 R x min(256 K, S)
+ * bytes (T up to 1,048,576 tokens a launch): each 256-token tile's block is sized for a tile
+ * that holds min(256 K, S) adapters, since a tile with too many adapters for the extra
+ * k-steps takes the per-adapter route only while its fp32 sums fit the 64 MiB kept for them
+ * (else the extra k-steps).  The rest: at most 64 MiB each of those fp32 sums and of the
+ * shrink's partial blocks, and the decode kernels' split partials (16 n_out bytes a token of a
+ * launch of up to 512).  For example 605 MiB at T = 16384, 4096 -> 11008, S = 100, R = 64;
+ * 36 MiB for the 64-token decode batch at 4096 -> 4096; 3.2 GiB for a merged QKV layer with
+ * S = 1000, R = 64 at T = 16384 (the size is linear in T: such callers can split the batch).
  */
 size_t mlora_workspace_size(int64_t T, int32_t K, int64_t n_in, int64_t n_out,
                             const mlora_slots *slots);
