@@ -68,6 +68,7 @@ SMALL = [
     (7, 300, 2056, 136, 11, 8, 1, None),
     (8, 20, 512, 4096, 5, 16, 3, [2048, 1024, 1024]),   # 60 pairs over 5 slots: grouped shrink
     (9, 64, 256, 4096, 40, 32, 1, None),                # 64 pairs, wd > 16: grouped + per pair
+    (10, 45, 256, 203, 5, 16, 2, [101, 102]),           # n_out not a multiple of 4
 ]
 
 
@@ -87,6 +88,7 @@ TILED = [
     (43, 700, 1032, 600, 9, 8, 2, [300, 300]),
     (44, 64, 128, 136, 3, 32, 1, None),
     (45, 520, 512, 1024, 40, 16, 3, [512, 256, 256]),
+    (46, 300, 256, 301, 6, 16, 2, [150, 151]),          # n_out not a multiple of 4
 ]
 
 
@@ -116,6 +118,7 @@ GROUPED = [
     (62, 300, 512, 520, 30, 32, 3, [260, 130, 130]),   # two tiles, the second ragged
     (63, 600, 392, 136, 9, 64, 1, [64, 72]),           # two launches: 512 + 88 tokens
     (64, 256, 1024, 1000, 40, 16, 2, None),
+    (66, 140, 256, 202, 6, 16, 2, [101, 101]),          # n_out not a multiple of 4
 ]
 
 
