@@ -434,7 +434,7 @@ def test_decode_wide_output(oracle_mod, T):
     assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
 
 
-@pytest.mark.parametrize("path", ["decode", "tiled"])
+@pytest.mark.parametrize("path", ["decode", "tiled", "grouped"])
 def test_limits_rank_slots_slices(oracle_mod, path):
     """The widest slots (R = 512), the most slots per token (K = 8) and the most slices (4)."""
     from lora_serving_amd import mlora
@@ -442,7 +442,8 @@ def test_limits_rank_slots_slices(oracle_mod, path):
                            R=512, K=8, slice_sizes=[160, 160, 160, 160], p_sentinel=0.3,
                            contiguous=(path == "tiled"))
     say(f"[limits] path={path} T={L.T} R={L.R} K={L.K} slices={L.n_slices}")
-    flags = mlora.MLORA_PATH_DECODE if path == "decode" else mlora.MLORA_PATH_TILED
+    flags = {"decode": mlora.MLORA_PATH_DECODE, "tiled": mlora.MLORA_PATH_TILED,
+             "grouped": mlora.MLORA_PATH_GROUPED}[path]
     D = DevLayer(L)
     y = from_dev_bf16(D.linear(flags=flags))
     y_ref = oracle_mod.linear(L)
