@@ -635,7 +635,8 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
     const int RBg = (wd + SG_ROWS - 1) / SG_ROWS;
 
     // Pass 1: which tiles take group items (a scattered tile whose ordinal is below sc_cap),
-    // and the 128-row blocks of the others; workgroup 0 also numbers the scattered tiles.
+    // and the 128-row blocks of the others; workgroup 0 also numbers the scattered tiles and
+    // the expand's items (each kept tile's 16-token groups x the output row chunks).
     int rb_base = 0, sc_base = 0, ei_base = 0;
     for (int m0 = 0; m0 < P.n_mtiles; m0 += SH_THREADS) {
         const int m = m0 + threadIdx.x;

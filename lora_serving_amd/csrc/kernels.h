@@ -98,7 +98,7 @@ struct PrefillCfg {
     int64_t vcat_tile_elems;  // bf16 elements of one tile's V block
     int sc_cap;               // scattered tiles whose expand runs outside the GEMM
     int64_t n_out;
-    int tok_stride;           // bytes of a tile's per-adapter token lists (256 K)
+    int tok_stride;           // bytes of a tile's per-adapter token lists in the tile plan's LDS (256 K)
     int sd_cap_slots;         // fp32 partial blocks of the dense shrink items (256 x 128 each)
     int grp_stride;           // group records per tile (scattered tiles' 16-token groups)
     bool may_scatter;         // some tile could be scattered (else no expand launches)
