@@ -430,6 +430,22 @@ def linear_roofline(P: Prepared, kernel_ms, only_layer=None):
             "kernel_avg_us": k_avg_ms * 1e3, "algorithmic_flops_per_launch": k_flops}
 
 
+def binding(nbytes, nflops, ms):
+    """A call against both roofs: its algorithmic bytes at the HBM peak and flops at the bf16
+    MFMA peak, as times, and the longer of the two over the measured time."""
+    t_b = nbytes / (HBM_PEAK_GBPS * 1e9)
+    t_f = nflops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    return {"t_bytes_us": t_b * 1e6, "t_flops_us": t_f * 1e6,
+            "bound": "hbm" if t_b >= t_f else "mfma", "frac": max(t_b, t_f) / (ms * 1e-3)}
+
+
+def part_layer(L, sl):
+    """The tokens sl of layer L as a layer of their own (for the algorithmic work of a part)."""
+    import dataclasses
+    return dataclasses.replace(L, T=sl.stop - sl.start, x=L.x[sl], idx=L.idx[sl],
+                               scale=L.scale[sl], segments=[])
+
+
 def config_entry(name, steps, warmup, cpu_s, with_cpu, graph=False):
     """One entry of the `configs` list: the workload's mlora_linear step timed like the
     headline, its main kernel's roofline, per-layer or per-part times where the workload has
@@ -451,7 +467,10 @@ def config_entry(name, steps, warmup, cpu_s, with_cpu, graph=False):
          "roofline": roof,
          "step_algorithmic": {"bytes": tot_bytes, "flops": tot_flops},
          "step_achieved": {"GBps": tot_bytes / (ms * 1e-3) / 1e9,
-                           "TFLOPs": tot_flops / (ms * 1e-3) / 1e12}}
+                           "TFLOPs": tot_flops / (ms * 1e-3) / 1e12},
+         # the step against both roofs: the longer of its bytes at 8 TB/s and its flops at the
+         # bf16 MFMA peak, over the measured step time
+         "step_binding": binding(tot_bytes, tot_flops, ms)}
     if name == "tiny":
         e["roofline"]["note"] = ("latency-bound (about 0.2 MB and 2 MFLOP per call, far below "
                                  "both roofs): reported, no roofline claim")
@@ -490,8 +509,15 @@ def config_entry(name, steps, warmup, cpu_s, with_cpu, graph=False):
             ev1.record()
             torch.cuda.synchronize()
             pms = ev0.elapsed_time(ev1) / steps
+            Lp = part_layer(L, sl)
+            ap = algorithmic(Lp)
             parts[pname] = {"T": sl.stop - sl.start, "ms_per_call": pms,
-                            "tokens_per_s": (sl.stop - sl.start) / (pms * 1e-3)}
+                            "tokens_per_s": (sl.stop - sl.start) / (pms * 1e-3),
+                            "path": {m.MLORA_PATH_DECODE: "decode", m.MLORA_PATH_TILED: "tiled",
+                                     m.MLORA_PATH_GROUPED: "grouped"}.get(
+                                m.mlora_linear_path(Lp.T, Lp.n_in, Lp.n_out, slots, Lp.K,
+                                                    P.flags & ~m.MLORA_W_PACKED), "?"),
+                            "binding": binding(ap["bytes"], ap["flops"], pms)}
         e["split"] = parts
     if with_cpu:
         e["cpu_baseline"] = cpu_baseline(P.layers, cpu_s)
