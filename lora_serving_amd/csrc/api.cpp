@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -408,6 +409,49 @@ mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_
 
 namespace {
 
+// A second stream per device for the grouped decode's LoRA kernels (tile plan and group shrink),
+// which do not depend on the base product: forked from the caller's stream and joined back
+// before the expand with events, so the group shrink runs beside the decode GEMM.  Both are
+// created once per device, at the device's first grouped call, with the default priority.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;                 // guards g_side and each fork / join sequence
+std::map<int, SideStream> g_side;
+
+hipError_t side_stream(hipStream_t caller, SideStream **out)
+{
+    int dev = -1;
+    hipError_t e = caller != nullptr ? hipStreamGetDevice(caller, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    SideStream &ss = g_side[dev];
+    if (ss.s == nullptr) {
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return e;
+        SideStream n;
+        e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess)
+                e = e2;
+        }
+        if (e != hipSuccess)
+            return e;
+        ss = n;
+    }
+    *out = &ss;
+    return hipSuccess;
+}
+
 // The kernels mlora_linear runs for these sizes and flags (a host-side choice from the shapes):
 // MLORA_PATH_TILED when forced or when the batch fills the GPU with 256 x 256 output tiles;
 // else MLORA_PATH_GROUPED when forced or when the per-pair adapter reads of the decode kernels
@@ -563,21 +607,52 @@ mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in
         if (grouped) {
             const PrefillCfg pc = grouped_config(Tc, K, n_in, n_out, S, R, n_slices);
             void *wpre = wsb + off_pre;
-            hipError_t e = launch_grouped_shrink(xb + t0 * n_in, Tc, n_in, n_out, g, idx_c, K,
-                                                 scale_c, pc, wpre, stream);
-            if (e != hipSuccess)
-                return hip_status(e, "grouped shrink launch");
+            // the tile plan and the group shrink on the side stream, forked before the GEMM is
+            // enqueued and joined before the expand; the GEMM's launch goes in first so that
+            // its workgroups are dispatched from the start (the no-allocation variant creates
+            // nothing and runs all of it on the caller's stream)
+            std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
+            SideStream *ss = nullptr;
+            hipError_t e = hipSuccess;
+            if (!noalloc) {
+                lk.lock();
+                e = side_stream(stream, &ss);
+                if (e == hipSuccess)
+                    e = hipEventRecord(ss->fork, stream);
+                if (e != hipSuccess)
+                    return hip_status(e, "side stream fork");
+            } else {
+                e = launch_grouped_shrink(xb + t0 * n_in, Tc, n_in, n_out, g, idx_c, K, scale_c,
+                                          pc, wpre, stream);
+                if (e != hipSuccess)
+                    return hip_status(e, "grouped shrink launch");
+            }
             trace_mark(stream, true);
             e = launch_decode_gemm(xb + t0 * n_in, (const uint16_t *)W, packed, Tc, n_in, n_out,
                                    part, cfg, nullptr, nullptr, K, nullptr, stream);
             trace_mark(stream, false);
             if (e != hipSuccess)
                 return hip_status(e, "decode gemm launch");
+            if (ss != nullptr) {
+                e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+                if (e == hipSuccess)
+                    e = launch_grouped_shrink(xb + t0 * n_in, Tc, n_in, n_out, g, idx_c, K,
+                                              scale_c, pc, wpre, ss->s);
+                if (e == hipSuccess)
+                    e = hipEventRecord(ss->join, ss->s);
+                if (e != hipSuccess)
+                    return hip_status(e, "grouped shrink launch");
+            }
             e = launch_decode_finish(part, cfg.sk, cfg.n_tiles, nullptr, nullptr, Tc, n_out,
                                      nullptr, nullptr, 1, yb + t0 * n_out,
                                      grouped_base_sums(pc, wpre), stream);
             if (e != hipSuccess)
                 return hip_status(e, "decode finish launch");
+            if (ss != nullptr) {
+                if ((e = hipStreamWaitEvent(stream, ss->join, 0)) != hipSuccess)
+                    return hip_status(e, "side stream join");
+                lk.unlock();
+            }
             e = launch_grouped_expand(Tc, n_out, g, idx_c, K, yb + t0 * n_out, pc, wpre, stream);
             if (e != hipSuccess)
                 return hip_status(e, "grouped expand launch");

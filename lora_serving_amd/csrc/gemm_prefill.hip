@@ -620,6 +620,11 @@ __device__ __forceinline__ int sd_row_blocks(const ShrinkArgs &P, int m, int D)
     return (D * P.g.n_slices * P.tile_w[m] + SD_ROWS - 1) / SD_ROWS;
 }
 
+constexpr int SG_RED_BYTES = 4 * 2 * 64 * 16;   // a group item's reduction space (8 KB)
+
+// GO (groups only): every tile scattered (the grouped decode), so no dense item code, few
+// registers and 8 KB of LDS: the kernel can share CUs with the decode GEMM it runs beside.
+template <bool GO>
 __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
 {
     extern __shared__ __attribute__((aligned(16))) float sh_lds[];
@@ -627,7 +632,8 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
     // the item tables
     uint16_t *stages = (uint16_t *)sh_lds;
     float4 *red = (float4 *)sh_lds;                           // [4 waves][16][64] float4
-    int *pre = (int *)((uint8_t *)sh_lds + (size_t)P.stages * SD_STAGE_BYTES);   // item prefix
+    const size_t tbl_off = GO ? (size_t)SG_RED_BYTES : (size_t)P.stages * SD_STAGE_BYTES;
+    int *pre = (int *)((uint8_t *)sh_lds + tbl_off);          // item prefix
     int *pbase = pre + P.n_mtiles;                            // first 128-row block of a tile
     uint8_t *grouped = (uint8_t *)(pbase + P.n_mtiles);       // 1: group items
     __shared__ int wsum[8];
@@ -691,7 +697,7 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
             cnt = grouped[m] ? (P.skip_groups ? 0
                                               : P.tile_gpre[(int64_t)m * (P.list_stride + 1) + Dm] *
                                                     RBg)
-                             : sd_row_blocks(P, m, Dm) * ks;
+                             : (GO ? 0 : sd_row_blocks(P, m, Dm) * ks);
         }
         int ex, all, u0, u1;
         block_scan2(cnt, 0, wsum, ex, u0, all, u1);
@@ -715,7 +721,7 @@ __global__ __launch_bounds__(SH_THREADS) void sgmv_shrink_kernel(ShrinkArgs P)
         const int local = item - pre[lo];
         if (grouped[lo]) {
             sh_group_item(P, lo, local, red, threadIdx.x);
-        } else {
+        } else if constexpr (!GO) {
             const int rb = local / ks, kp = local - rb * ks;
             sh_dense_item(P, lo, rb, kp, ks, kc, (pbase[lo] + rb) * ks + kp, stages);
         }
@@ -1537,24 +1543,40 @@ static hipError_t plan_and_shrink(const uint16_t *x, int64_t T, int64_t n_in, in
     s.sd_ks = q.sd_ks;
     s.skip_groups = skip_groups;
     s.force_scatter = force_scatter;
+    const size_t tables = (size_t)c.n_mtiles * SD_TABLE_BYTES;
+    if (force_scatter) {
+        // group items only: 8 KB of reduction space and the tables; up to two workgroups per CU
+        // (the items are bound by their latency), fewer when there are fewer items
+        const void *kf = (const void *)sgmv_shrink_kernel<true>;
+        const size_t sh_lds = (size_t)SG_RED_BYTES + tables;
+        if (sh_lds + kernel_static_lds(kf) > LDS_BYTES)
+            return hipErrorInvalidValue;
+        if (hipError_t e = ensure_dynamic_lds(kf, sh_lds); e != hipSuccess)
+            return e;
+        const int wd = g.n_slices * g.R;
+        const int64_t items = (int64_t)c.n_mtiles * c.grp_stride * ((wd + SG_ROWS - 1) / SG_ROWS);
+        const unsigned grid = (unsigned)std::max<int64_t>(
+            1, std::min<int64_t>(items, 2 * (int64_t)device_cu_count()));
+        hipLaunchKernelGGL(sgmv_shrink_kernel<true>, dim3(grid), dim3(SH_THREADS), sh_lds, stream,
+                           s);
+        return hipGetLastError();
+    }
     // three dense stages while the item tables and the kernel's own __shared__ arrays leave
     // room in the 160 KB of LDS, else two
-    const size_t tables = (size_t)c.n_mtiles * SD_TABLE_BYTES;
-    const size_t st_lds = kernel_static_lds((const void *)sgmv_shrink_kernel);
+    const void *kf = (const void *)sgmv_shrink_kernel<false>;
+    const size_t st_lds = kernel_static_lds(kf);
     s.stages = 3 * (size_t)SD_STAGE_BYTES + tables + st_lds <= LDS_BYTES ? 3 : 2;
     const size_t sh_lds = (size_t)s.stages * SD_STAGE_BYTES + tables;
     if (sh_lds + st_lds > LDS_BYTES)
         return hipErrorInvalidValue;   // more tiles than SH_MAX_TILES allows
-    if (hipError_t e = ensure_dynamic_lds((const void *)sgmv_shrink_kernel, sh_lds);
-        e != hipSuccess)
+    if (hipError_t e = ensure_dynamic_lds(kf, sh_lds); e != hipSuccess)
         return e;
     // one workgroup per CU (the stages take most of its LDS), items shared out in the kernel:
     // every workgroup then runs the kernel's item numbering once, all in one round
-    hipLaunchKernelGGL(sgmv_shrink_kernel, dim3((unsigned)device_cu_count()), dim3(SH_THREADS),
-                       sh_lds, stream, s);
-    if (!force_scatter)   // (no dense tile then: nothing to reduce)
-        hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)c.n_mtiles * (PF_BM / SR_TOK)),
-                           dim3(256), 0, stream, s);
+    hipLaunchKernelGGL(sgmv_shrink_kernel<false>, dim3((unsigned)device_cu_count()),
+                       dim3(SH_THREADS), sh_lds, stream, s);
+    hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)c.n_mtiles * (PF_BM / SR_TOK)),
+                       dim3(256), 0, stream, s);
     return hipGetLastError();
 }
 
