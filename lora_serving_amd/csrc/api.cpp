@@ -420,14 +420,23 @@ struct SideStream {
 std::mutex g_side_mu;                 // guards g_side and each fork / join sequence
 std::map<int, SideStream> g_side;
 
+// *out: the device's side stream, or nullptr when it does not exist yet and may not be created
+// now (the caller's stream is being captured into a graph: creating a stream then could
+// invalidate the capture; that call runs on the caller's stream alone).
 hipError_t side_stream(hipStream_t caller, SideStream **out)
 {
+    *out = nullptr;
     int dev = -1;
     hipError_t e = caller != nullptr ? hipStreamGetDevice(caller, &dev) : hipGetDevice(&dev);
     if (e != hipSuccess)
         return e;
     SideStream &ss = g_side[dev];
     if (ss.s == nullptr) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if ((e = hipStreamIsCapturing(caller, &cs)) != hipSuccess)
+            return e;
+        if (cs != hipStreamCaptureStatusNone)
+            return hipSuccess;
         int cur = -1;
         if ((e = hipGetDevice(&cur)) != hipSuccess)
             return e;
@@ -617,11 +626,12 @@ mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in
             if (!noalloc) {
                 lk.lock();
                 e = side_stream(stream, &ss);
-                if (e == hipSuccess)
+                if (e == hipSuccess && ss != nullptr)
                     e = hipEventRecord(ss->fork, stream);
                 if (e != hipSuccess)
                     return hip_status(e, "side stream fork");
-            } else {
+            }
+            if (ss == nullptr) {
                 e = launch_grouped_shrink(xb + t0 * n_in, Tc, n_in, n_out, g, idx_c, K, scale_c,
                                           pc, wpre, stream);
                 if (e != hipSuccess)
