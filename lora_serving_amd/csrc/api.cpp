@@ -399,8 +399,7 @@ mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_
     if (v == nullptr || idx == nullptr || y == nullptr || !aligned16(v) || !aligned16(y))
         return MLORA_ERR_ARG;
     trace_mark(stream, true);
-    const hipError_t e = launch_expand_tokens(v, 1, 0, nullptr, T, n_out, g, idx, K, nullptr, 0,
-                                              (uint16_t *)y, stream);
+    const hipError_t e = launch_expand_tokens(v, T, n_out, g, idx, K, (uint16_t *)y, stream);
     trace_mark(stream, false);
     return hip_status(e);
 }

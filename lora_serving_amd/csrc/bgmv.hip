@@ -71,7 +71,14 @@ __device__ __forceinline__ int transpose_row(int lane)
     return row;
 }
 
-// Workgroup = (pair p, rows r0 .. r0 + RB - 1 of the pair's n_slices * R rows of v).
+// Masked loads read this static block instead: the choice is made on the address, so a load
+// is always issued and no branch or select waits for anything when it is.
+__device__ __attribute__((aligned(16))) float vzero[4];   // never written: zeros
+
+// Workgroup = (pair p = (token blockIdx.x, slot blockIdx.z), rows r0 .. r0 + RB - 1 of the
+// pair's n_slices * R rows of v, r0 = RB blockIdx.y).  The loads that do not depend on the slot id (x, the pair's scale)
+// are issued before it is read, the adapter's factor right after it, so the chain of dependent
+// round trips is the slot id, the rank (only with a rank table) and the A rows.
 template <int RB>
 __global__ __launch_bounds__(256) void shrink_rows_kernel(const uint16_t *__restrict__ x,
                                                           int64_t T, int64_t n_in, SlotGeom g,
@@ -81,31 +88,31 @@ __global__ __launch_bounds__(256) void shrink_rows_kernel(const uint16_t *__rest
                                                           float *__restrict__ v)
 {
     __shared__ float red[4 * RB];
+    const u32x4 *zero = (const u32x4 *)vzero;
     const int wd = g.n_slices * g.R;
-    const int nrb = (wd + RB - 1) / RB;
-    const int64_t p = blockIdx.x / nrb;
-    const int r0 = (int)(blockIdx.x - p * nrb) * RB;
+    const int64_t t = blockIdx.x;
+    const int j = blockIdx.z;
+    const int64_t p = t * K + j;
+    const int r0 = (int)blockIdx.y * RB;
     const int nr = min(RB, wd - r0);
-    const int64_t t = p / K;
-    const int j = (int)(p - t * K);
     float *out = v + ((int64_t)j * T + t) * wd + r0;
     const uint16_t *xt = x + t * n_in;
     const int64_t step = (int64_t)blockDim.x * 8;
-    // the first round's x chunks do not depend on the slot id: in flight before it is read
+    const int64_t kt = (int64_t)threadIdx.x * 8;
     u32x4 xv0[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int64_t k = (int64_t)threadIdx.x * 8 + h * step;
-        xv0[h] = k < n_in ? *(const u32x4 *)(xt + k) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int h = 0; h < 2; ++h)
+        xv0[h] = *(kt + h * step < n_in ? (const u32x4 *)(xt + kt + h * step) : zero);
+    const float sc = scale ? scale[p] : 1.f;
     const int a = idx[p];
+    const float fa = a >= 0 ? g.factor[a] : 0.f;
     // rows of this block below the adapter's rank (rounded to 8); the others are zero padding,
-    // neither read nor multiplied
+    // neither read nor multiplied (R is a power of two)
     const int r8 = a >= 0 ? slot_rank8(g.rank, a, g.R) : 0;
     uint32_t live = 0;
 #pragma unroll
     for (int r = 0; r < RB; ++r)
-        live |= (r < nr && (r0 + r) % g.R < r8 ? 1u : 0u) << r;
+        live |= (r < nr && ((r0 + r) & (g.R - 1)) < r8 ? 1u : 0u) << r;
     if (live == 0) {
         if ((int)threadIdx.x < nr)
             out[threadIdx.x] = 0.f;
@@ -119,21 +126,18 @@ __global__ __launch_bounds__(256) void shrink_rows_kernel(const uint16_t *__rest
 #pragma unroll
     for (int r = 0; r < RB; ++r)
         acc[r] = 0.f;
-    // two 16-byte chunks per lane in flight: x and the live rows of both, then their products
-    for (int64_t k0 = (int64_t)threadIdx.x * 8; k0 < n_in; k0 += 2 * step) {
-        u32x4 xv[2], av[2][RB];
+    // one round: two 16-byte chunks per lane, the live rows' A chunks all in flight, then the
+    // products in chunk order
+    auto round = [&](int64_t k0, const u32x4 (&xv)[2]) {
+        u32x4 av[2][RB];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t k = k0 + h * step;
-            const bool ok = k < n_in;
-            if (k0 == (int64_t)threadIdx.x * 8)
-                xv[h] = xv0[h];
-            else
-                xv[h] = ok ? *(const u32x4 *)(xt + k) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int r = 0; r < RB; ++r)
-                av[h][r] = ok && (live >> r & 1u) ? *(const u32x4 *)(Aa + (int64_t)r * n_in + k)
-                                                  : u32x4{0u, 0u, 0u, 0u};
+                av[h][r] = *(k < n_in && (live >> r & 1u)
+                                 ? (const u32x4 *)(Aa + (int64_t)r * n_in + k)
+                                 : zero);
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -144,6 +148,14 @@ __global__ __launch_bounds__(256) void shrink_rows_kernel(const uint16_t *__rest
             for (int r = 0; r < RB; ++r)
                 acc[r] += dot8_bf16(av[h][r], xf);
         }
+    };
+    round(kt, xv0);
+    for (int64_t k0 = kt + 2 * step; k0 < n_in; k0 += 2 * step) {
+        u32x4 xv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            xv[h] = *(k0 + h * step < n_in ? (const u32x4 *)(xt + k0 + h * step) : zero);
+        round(k0, xv);
     }
     const float s = transpose_reduce<RB>(acc);
     if ((lane & (64 / RB - 1)) == 0)
@@ -151,9 +163,8 @@ __global__ __launch_bounds__(256) void shrink_rows_kernel(const uint16_t *__rest
     __syncthreads();
     if ((int)threadIdx.x < nr) {
         const int rr = threadIdx.x;
-        const float coef = (scale ? scale[p] : 1.f) * g.factor[a];
         const float tot = ((red[rr] + red[RB + rr]) + red[2 * RB + rr]) + red[3 * RB + rr];
-        out[rr] = coef * tot;
+        out[rr] = (sc * fa) * tot;
     }
 }
 
@@ -164,6 +175,8 @@ hipError_t launch_shrink_pairs(const uint16_t *x, int64_t T, int64_t n_in, const
     const int64_t P = T * K;
     if (P == 0)
         return hipSuccess;
+    if (T >= 2147483647LL)                 // tokens along the grid's x dimension
+        return hipErrorInvalidValue;
     const int wd = g.n_slices * g.R;
     // rows per workgroup: the most (16, 8, 4, 2, 1) that still gives SHRINK_MIN_WG workgroups,
     // so small batches spread over many more workgroups than the chip has CUs
@@ -171,27 +184,27 @@ hipError_t launch_shrink_pairs(const uint16_t *x, int64_t T, int64_t n_in, const
     int RB = 16;
     while (RB > 1 && P * ((wd + RB - 1) / RB) < SHRINK_MIN_WG)
         RB >>= 1;
-    const unsigned grid = (unsigned)(P * ((wd + RB - 1) / RB));
+    const dim3 grid((unsigned)T, (unsigned)((wd + RB - 1) / RB), (unsigned)K);
     switch (RB) {
     case 16:
-        hipLaunchKernelGGL(shrink_rows_kernel<16>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
-                           g, idx, K, scale, v);
+        hipLaunchKernelGGL(shrink_rows_kernel<16>, grid, dim3(256), 0, stream, x, T, n_in, g,
+                           idx, K, scale, v);
         break;
     case 8:
-        hipLaunchKernelGGL(shrink_rows_kernel<8>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
-                           g, idx, K, scale, v);
+        hipLaunchKernelGGL(shrink_rows_kernel<8>, grid, dim3(256), 0, stream, x, T, n_in, g, idx,
+                           K, scale, v);
         break;
     case 4:
-        hipLaunchKernelGGL(shrink_rows_kernel<4>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
-                           g, idx, K, scale, v);
+        hipLaunchKernelGGL(shrink_rows_kernel<4>, grid, dim3(256), 0, stream, x, T, n_in, g, idx,
+                           K, scale, v);
         break;
     case 2:
-        hipLaunchKernelGGL(shrink_rows_kernel<2>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
-                           g, idx, K, scale, v);
+        hipLaunchKernelGGL(shrink_rows_kernel<2>, grid, dim3(256), 0, stream, x, T, n_in, g, idx,
+                           K, scale, v);
         break;
     default:
-        hipLaunchKernelGGL(shrink_rows_kernel<1>, dim3(grid), dim3(256), 0, stream, x, T, n_in,
-                           g, idx, K, scale, v);
+        hipLaunchKernelGGL(shrink_rows_kernel<1>, grid, dim3(256), 0, stream, x, T, n_in, g, idx,
+                           K, scale, v);
         break;
     }
     return hipGetLastError();
@@ -211,21 +224,22 @@ __device__ __forceinline__ int slice_of(const SlotGeom &g, int64_t n)
     return s;
 }
 
-// One workgroup per (token, block of ER output rows).
-//   v_j = coef_j * sum_{s < n_vsplit} vsrc[s][j][t][:]   (coef_j = scale*factor, or 1)
-//   delta[n] = sum_j sum_rho B[a_j][n][rho] v_j[slice(n)*R + rho]
-//   y[t][n] = bf16(base[n] + delta[n]),  base = sum of n_part fp32 partials, or y itself
+// One workgroup per (token t = blockIdx.x, block of ER output rows from ER blockIdx.y):
+//   delta[n] = sum_j sum_rho B[a_j][n][rho] v[j][t][slice(n)*R+rho],  y[t][n] = bf16(y + delta)
+// Rows of a token whose slots are all -1 are left untouched.  The loads that do not depend on
+// the slot ids (this thread's rows of y, v of the token's first slot, the ids themselves) are
+// issued first, so the only dependent round trip before the products is the B rows (and the
+// rank, with a rank table and R above 32).
 template <int ER>
-__global__ __launch_bounds__(256) void expand_tokens_kernel(
-    const float *__restrict__ vsrc, int n_vsplit, int apply_coef, const float *__restrict__ scale,
-    int64_t T, int64_t n_out, SlotGeom g, const int32_t *__restrict__ idx, int32_t K,
-    const float *__restrict__ part, int32_t n_part, uint16_t *__restrict__ y)
+__global__ __launch_bounds__(256) void expand_tokens_kernel(const float *__restrict__ v,
+                                                            int64_t T, int64_t n_out, SlotGeom g,
+                                                            const int32_t *__restrict__ idx,
+                                                            int32_t K, uint16_t *__restrict__ y)
 {
     __shared__ float delta[ER];
     __shared__ float vs[MLORA_MAX_SLICES_DEV * MLORA_MAX_RANK_DEV];
-    const int64_t nblk = (n_out + ER - 1) / ER;
-    const int64_t t = blockIdx.x / nblk;
-    const int64_t n0 = (blockIdx.x - t * nblk) * ER;
+    const int64_t t = blockIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.y * ER;
     const int nrows = (int)min((int64_t)ER, n_out - n0);
     const int R = g.R;
     const int wd = g.n_slices * R;
@@ -233,38 +247,26 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(
     const int r4 = threadIdx.x * 4;       // first of this thread's 4 output rows
     const bool vec = ((n_out & 3) == 0) && r4 + 3 < nrows;
 
-    // base of this thread's rows, loaded first and only used at the end, so its latency
-    // overlaps the slot map and the B loads: the first EXPAND_PQ partials, or y itself
-    constexpr int EXPAND_PQ = 8;
-    float4 pq[EXPAND_PQ];
-    const bool use_pq = part != nullptr && vec;
-    if (use_pq) {
-#pragma unroll
-        for (int sp = 0; sp < EXPAND_PQ; ++sp)
-            if (sp < n_part)
-                pq[sp] = *(const float4 *)(part + ((int64_t)sp * T + t) * n_out + n0 + r4);
-    }
-    const bool use_y = part == nullptr && vec;
+    // lane j of every wave holds slot j's id
+    const int my = lane < K ? idx[t * K + lane] : -1;
     u32x2 yv = {0u, 0u};
-    if (use_y)
+    if (vec)
         yv = *(const u32x2 *)(y + t * n_out + n0 + r4);
-
-    bool any = false;
-    for (int j = 0; j < K; ++j)
-        any |= idx[t * K + j] >= 0;
-    if (!any && part == nullptr)
-        return;   // accumulate mode: rows with no adapter are left untouched
+    // slot 0's v, 4 entries a thread (wd is a multiple of 8; up to 2048 entries)
+    constexpr int VPRE = MLORA_MAX_SLICES_DEV * MLORA_MAX_RANK_DEV / 1024;
+    f32x4 vpre[VPRE];
+#pragma unroll
+    for (int q = 0; q < VPRE; ++q)
+        vpre[q] = *(const f32x4 *)(r4 + q * 1024 < wd ? v + t * wd + r4 + q * 1024 : vzero);
+    if (__ballot(my >= 0) == 0)
+        return;   // no adapter: the rows are left untouched (the same test in every wave)
 
     // the first slot with an adapter stores its row sums, later ones add theirs (a row's sum
-    // is always written by the same thread); with no adapter at all delta stays zero
-    if (!any)
-        for (int r = threadIdx.x; r < ER; r += blockDim.x)
-            delta[r] = 0.f;
+    // is always written by the same thread)
     bool first = true;
-
     const int64_t step = (int64_t)blockDim.x * 8;
     for (int j = 0; j < K; ++j) {
-        const int a = idx[t * K + j];
+        const int a = __builtin_amdgcn_readlane(my, j);
         if (a < 0)
             continue;
         // this adapter's columns: the smallest power of two at or above its rank (rounded to
@@ -290,13 +292,14 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(
                                   : u32x4{0u, 0u, 0u, 0u};
             }
             if (e0 == 0) {
-                const float coef =
-                    apply_coef ? (scale ? scale[t * K + j] : 1.f) * g.factor[a] : 1.f;
-                for (int c = threadIdx.x; c < wd; c += blockDim.x) {
-                    float sum = 0.f;
-                    for (int sp = 0; sp < n_vsplit; ++sp)
-                        sum += vsrc[(((int64_t)sp * K + j) * T + t) * wd + c];
-                    vs[c] = coef * sum;
+                if (!first)
+                    lds_barrier();                      // the previous slot's reads are done
+#pragma unroll
+                for (int q = 0; q < VPRE; ++q) {
+                    const int c = r4 + q * 1024;
+                    if (c < wd)
+                        *(f32x4 *)(vs + c) =
+                            j == 0 ? vpre[q] : *(const f32x4 *)(v + ((int64_t)j * T + t) * wd + c);
                 }
                 lds_barrier();
             }
@@ -325,74 +328,158 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(
             }
         }
         first = false;
-        lds_barrier();   // vs is free again for the next slot
     }
     lds_barrier();
 
     if (r4 < nrows) {
-        float base[4] = {0.f, 0.f, 0.f, 0.f};
-        if (use_pq) {
-#pragma unroll
-            for (int sp = 0; sp < EXPAND_PQ; ++sp)
-                if (sp < n_part) {
-                    base[0] += pq[sp].x;
-                    base[1] += pq[sp].y;
-                    base[2] += pq[sp].z;
-                    base[3] += pq[sp].w;
-                }
-            for (int sp = EXPAND_PQ; sp < n_part; ++sp) {
-                const float4 q4 = *(const float4 *)(part + ((int64_t)sp * T + t) * n_out + n0 + r4);
-                base[0] += q4.x;
-                base[1] += q4.y;
-                base[2] += q4.z;
-                base[3] += q4.w;
-            }
-        } else if (part != nullptr) {
-            for (int sp = 0; sp < n_part; ++sp) {
-                const float *pp = part + ((int64_t)sp * T + t) * n_out + n0 + r4;
-                for (int q = 0; q < 4 && r4 + q < nrows; ++q)
-                    base[q] += pp[q];
-            }
-        } else if (use_y) {
-            base[0] = bf16_lo(yv.x);
-            base[1] = bf16_hi(yv.x);
-            base[2] = bf16_lo(yv.y);
-            base[3] = bf16_hi(yv.y);
-        } else {
-            const uint16_t *yy = y + t * n_out + n0 + r4;
-            for (int q = 0; q < 4 && r4 + q < nrows; ++q)
-                base[q] = bf16_to_f32(yy[q]);
-        }
         uint16_t *yo = y + t * n_out + n0 + r4;
         if (vec) {
-            const uint32_t lo = pack_bf16x2(base[0] + delta[r4], base[1] + delta[r4 + 1]);
-            const uint32_t hi = pack_bf16x2(base[2] + delta[r4 + 2], base[3] + delta[r4 + 3]);
+            const uint32_t lo = pack_bf16x2(bf16_lo(yv.x) + delta[r4], bf16_hi(yv.x) + delta[r4 + 1]);
+            const uint32_t hi =
+                pack_bf16x2(bf16_lo(yv.y) + delta[r4 + 2], bf16_hi(yv.y) + delta[r4 + 3]);
             *(u32x2 *)yo = u32x2{lo, hi};
         } else {
             for (int q = 0; q < 4 && r4 + q < nrows; ++q)
-                yo[q] = f32_to_bf16(base[q] + delta[r4 + q]);
+                yo[q] = f32_to_bf16(bf16_to_f32(yo[q]) + delta[r4 + q]);
         }
     }
 }
 
-hipError_t launch_expand_tokens(const float *vsrc, int n_vsplit, int apply_coef,
-                                const float *scale, int64_t T, int64_t n_out, const SlotGeom &g,
-                                const int32_t *idx, int32_t K, const float *part, int32_t n_part,
-                                uint16_t *y, hipStream_t stream)
+// Slot width R = RC in {8, 16, 32}: every row of B is at most 64 bytes, one cache line read
+// whole either way, so the rank table is not consulted and the row width is known at compile
+// time.  One workgroup per (token t = blockIdx.x, 256 output rows from 256 blockIdx.y); lane
+// pieces of 8 columns as in the kernel above (RC / 8 lanes per row, RC / 8 pieces a thread),
+// the v rows of all K slots staged in LDS at once, the row sums kept in registers across the
+// slots, then gathered in LDS so that each thread rounds 4 consecutive rows.  The only
+// dependent round trip before the products is the B rows.
+template <int RC>
+__global__ __launch_bounds__(256) void expand_narrow_kernel(const float *__restrict__ v,
+                                                            int64_t T, int n_out, SlotGeom g,
+                                                            const int32_t *__restrict__ idx,
+                                                            int32_t K, uint16_t *__restrict__ y)
+{
+    constexpr int U = RC / 8;             // 16-byte pieces a thread (and lanes a row)
+    __shared__ float vs[MLORA_MAX_K_DEV * MLORA_MAX_SLICES_DEV * RC];
+    __shared__ float delta[256];
+    const u32x4 *zero = (const u32x4 *)vzero;
+    const int64_t t = blockIdx.x;
+    const int n0 = (int)blockIdx.y * 256;
+    const int nrows = min(256, n_out - n0);
+    const int wd = g.n_slices * RC;
+    const int lane = threadIdx.x & 63;
+    const int r4 = threadIdx.x * 4;
+    uint16_t *yt = y + t * n_out + n0;
+    const bool vec = ((n_out & 3) == 0) && r4 + 3 < nrows;
+
+    // independent loads first: the slot ids (lane j of every wave holds slot j's), v of every
+    // slot (wave w loads slots w and w + 4, 4 entries a lane; wd <= 128), this thread's rows
+    // of y
+    const int my = lane < K ? idx[t * K + lane] : -1;
+    const int wave = threadIdx.x >> 6;
+    const int l4 = lane * 4;
+    const bool vl0 = wave < K && l4 < wd, vl1 = wave + 4 < K && l4 < wd;
+    const float *vrow = v + ((int64_t)wave * T + t) * wd + l4;
+    const f32x4 vq0 = *(const f32x4 *)(vl0 ? vrow : vzero);
+    const f32x4 vq1 = *(const f32x4 *)(vl1 ? vrow + 4 * T * wd : vzero);
+    u32x2 yv = {0u, 0u};
+    if (vec)
+        yv = *(const u32x2 *)(yt + r4);
+    if (vl0)
+        *(f32x4 *)(vs + wave * wd + l4) = vq0;
+    if (vl1)
+        *(f32x4 *)(vs + (wave + 4) * wd + l4) = vq1;
+    if (__ballot(my >= 0) == 0)
+        return;   // no adapter: the rows are left untouched (the same test in every wave)
+    lds_barrier();
+
+    // piece u of this thread: element e = 2048 u + 8 threadIdx.x of the block's [256][RC]
+    // B rows (row e / RC, columns e % RC .. + 8)
+    const int total = nrows * RC;
+    const int rho0 = ((int)threadIdx.x * 8) % RC;
+    int sg[U] = {};
+    if (g.n_slices > 1) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int n = n0 + (u * 2048 + (int)threadIdx.x * 8) / RC;
+            sg[u] = (n >= g.slice_start[1]) + (n >= g.slice_start[2]) + (n >= g.slice_start[3]);
+        }
+    }
+    float acc[U] = {};
+    bool first = true;
+    for (int j = 0; j < K; ++j) {
+        const int a = __builtin_amdgcn_readlane(my, j);
+        if (a < 0)
+            continue;
+        const uint16_t *Bb = g.B + ((int64_t)a * n_out + n0) * RC;
+        u32x4 bv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = u * 2048 + (int)threadIdx.x * 8;
+            bv[u] = *(e < total ? (const u32x4 *)(Bb + e) : zero);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float *vv = vs + j * wd + sg[u] * RC + rho0;
+            float ps = 0.f;
+            ps += bf16_lo(bv[u].x) * vv[0];
+            ps += bf16_hi(bv[u].x) * vv[1];
+            ps += bf16_lo(bv[u].y) * vv[2];
+            ps += bf16_hi(bv[u].y) * vv[3];
+            ps += bf16_lo(bv[u].z) * vv[4];
+            ps += bf16_hi(bv[u].z) * vv[5];
+            ps += bf16_lo(bv[u].w) * vv[6];
+            ps += bf16_hi(bv[u].w) * vv[7];
+#pragma unroll
+            for (int off = 1; off < U; off <<= 1)
+                ps += __shfl_xor(ps, off, 64);
+            acc[u] = first ? ps : acc[u] + ps;
+        }
+        first = false;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int e = u * 2048 + (int)threadIdx.x * 8;
+        if (e < total && (lane & (U - 1)) == 0)
+            delta[e / RC] = acc[u];
+    }
+    lds_barrier();
+
+    if (vec) {
+        const uint32_t lo = pack_bf16x2(bf16_lo(yv.x) + delta[r4], bf16_hi(yv.x) + delta[r4 + 1]);
+        const uint32_t hi = pack_bf16x2(bf16_lo(yv.y) + delta[r4 + 2], bf16_hi(yv.y) + delta[r4 + 3]);
+        *(u32x2 *)(yt + r4) = u32x2{lo, hi};
+    } else {
+        for (int q = 0; q < 4 && r4 + q < nrows; ++q)
+            yt[r4 + q] = f32_to_bf16(bf16_to_f32(yt[r4 + q]) + delta[r4 + q]);
+    }
+}
+
+hipError_t launch_expand_tokens(const float *v, int64_t T, int64_t n_out, const SlotGeom &g,
+                                const int32_t *idx, int32_t K, uint16_t *y, hipStream_t stream)
 {
     if (T == 0 || n_out == 0)
         return hipSuccess;
-    if (T * ((n_out + 1023) / 1024) >= EXPAND_MIN_WG) {
-        const int64_t nblk = (n_out + 1023) / 1024;
-        hipLaunchKernelGGL(expand_tokens_kernel<1024>, dim3((unsigned)(T * nblk)), dim3(256), 0,
-                           stream, vsrc, n_vsplit, apply_coef, scale, T, n_out, g, idx, K, part,
-                           n_part, y);
-    } else {
-        const int64_t nblk = (n_out + 255) / 256;
-        hipLaunchKernelGGL(expand_tokens_kernel<256>, dim3((unsigned)(T * nblk)), dim3(256), 0,
-                           stream, vsrc, n_vsplit, apply_coef, scale, T, n_out, g, idx, K, part,
-                           n_part, y);
-    }
+    // grid: tokens along x (up to 2^31 - 1), row blocks along y (up to 65535)
+    const int64_t nblk1k = (n_out + 1023) / 1024, nblk256 = (n_out + 255) / 256;
+    if (T >= 2147483647LL || nblk256 > 65535)
+        return hipErrorInvalidValue;
+    if (g.R <= 32) {
+        const dim3 grid((unsigned)T, (unsigned)nblk256);
+        if (g.R == 8)
+            hipLaunchKernelGGL(expand_narrow_kernel<8>, grid, dim3(256), 0, stream, v, T,
+                               (int)n_out, g, idx, K, y);
+        else if (g.R == 16)
+            hipLaunchKernelGGL(expand_narrow_kernel<16>, grid, dim3(256), 0, stream, v, T,
+                               (int)n_out, g, idx, K, y);
+        else
+            hipLaunchKernelGGL(expand_narrow_kernel<32>, grid, dim3(256), 0, stream, v, T,
+                               (int)n_out, g, idx, K, y);
+    } else if (T * nblk1k >= EXPAND_MIN_WG)
+        hipLaunchKernelGGL(expand_tokens_kernel<1024>, dim3((unsigned)T, (unsigned)nblk1k),
+                           dim3(256), 0, stream, v, T, n_out, g, idx, K, y);
+    else
+        hipLaunchKernelGGL(expand_tokens_kernel<256>, dim3((unsigned)T, (unsigned)nblk256),
+                           dim3(256), 0, stream, v, T, n_out, g, idx, K, y);
     return hipGetLastError();
 }
 

@@ -42,15 +42,12 @@ struct SlotGeom {
 hipError_t launch_shrink_pairs(const uint16_t *x, int64_t T, int64_t n_in, const SlotGeom &g,
                                const int32_t *idx, int32_t K, const float *scale, float *v,
                                hipStream_t stream);
-// One workgroup per (token, 1024 output rows):
-//   v_j = coef_j * sum_{s < n_vsplit} vsrc[s][j][t][:], coef_j = scale[t][j]*factor[a] if
-//   apply_coef else 1;  y[t][n] = bf16(base + sum_j B[a_j][n][:] . v_j[slice(n)]), where
-//   base = y[t][n] (accumulate mode, part == nullptr; rows with no adapter untouched) or the sum
-//   of n_part fp32 partials part[s][t][n].
-hipError_t launch_expand_tokens(const float *vsrc, int n_vsplit, int apply_coef,
-                                const float *scale, int64_t T, int64_t n_out, const SlotGeom &g,
-                                const int32_t *idx, int32_t K, const float *part, int32_t n_part,
-                                uint16_t *y, hipStream_t stream);
+// One workgroup per (token, block of output rows):
+//   y[t][n] = bf16(y[t][n] + sum_j B[a_j][n][:] . v[j][t][slice(n)*R ..]); rows of a token whose
+//   slots are all -1 are left untouched.  hipErrorInvalidValue past the grid's limits
+//   (T >= 2^31, more than 65535 blocks of 256 rows).
+hipError_t launch_expand_tokens(const float *v, int64_t T, int64_t n_out, const SlotGeom &g,
+                                const int32_t *idx, int32_t K, uint16_t *y, hipStream_t stream);
 
 // ---- gemm_decode.hip: skinny base GEMM for T <= 64 -------------------------------------------
 struct DecodeCfg {
