@@ -6,12 +6,13 @@
 // the expand adds B v into y.  The first kernel (gemm_decode.hip) leaves the base product as
 // split-K partial sums and the shrink as split-K pieces; this one finishes both.
 //
-// One workgroup per (64-row tile, 16 tokens); each thread finishes 4 consecutive rows of one
-// token.  Every load that does not depend on another is issued at once: the slot map, the base
-// partials (stored tile-contiguous by the GEMM: 4 KB contiguous per split and workgroup) and
-// the shrink pieces; v = s * f * (pieces summed in split order) is staged in LDS, then the B
-// rows of each (token, slot) are read (4 rows x 2R contiguous bytes) and the expand added.
-// Sums run in a fixed order, so the output bits do not depend on scheduling.
+// The base partials are stored tile-contiguous by the GEMM ([split][64-row tile][token][64]).
+// Two kernels: slots up to 32 wide and the base alone take one workgroup per (tile, 8 tokens),
+// two rows a thread; wider slots one workgroup per (tile, 16 tokens), four rows a thread.  In
+// both, every load that does not depend on another is issued at once, v = s * f * (pieces
+// summed in split order) is staged in LDS, then the B rows of each (token, slot) are read and
+// the expand added.  Sums run in a fixed order, so the output bits do not depend on
+// scheduling.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,7 +21,6 @@ namespace mlora {
 constexpr int DF_ROWS = 64;       // rows of a tile (the GEMM's tile)
 constexpr int DF_TOK = 16;        // tokens per workgroup
 constexpr int DF_THREADS = 256;   // 16 tokens x 16 groups of 4 rows
-constexpr int DF_BPRE_R = 16;     // ranks up to which slot 0's B rows are prefetched
 constexpr int DF_CHUNK = 64;      // tokens of one chunk of the GEMM (one launch may hold several)
 
 // Masked loads read this static block instead (the choice is made on the address, so no
@@ -63,13 +63,10 @@ __device__ __forceinline__ void df_vload(const float *upart, int sk, int64_t pst
     fa = *(a >= 0 ? factor + a : df_zero);
 }
 
-// RC > 0 (slot width R = RC in {8, 16, 32}): the 16 lanes of a token read its adapter's 64-row
-// B block (contiguous, 128 R bytes) as consecutive 16-byte pieces, 256 bytes per instruction
-// (whole cache lines): piece c = g4 + 16 k is row c / (R / 8), columns 8 (c % (R / 8)) .. +8.
-// The R / 8 lanes holding one row add their parts with lane shuffles, and the rows' sums reach
-// the thread that stores them through LDS.  RC = 0: each thread reads its own 4 rows (any R).
-template <bool MC, int RC>
-__global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
+// Slots wider than 32 (R >= 64): each thread reads its own 4 rows of B, the columns up to the
+// adapter's rank (rounded to 8).
+template <bool MC>
+__global__ __launch_bounds__(DF_THREADS) void decode_finish_wide_kernel(
     const float *__restrict__ part, int sk, int n_tiles, const float *__restrict__ upart,
     const float *__restrict__ scale, int T_all, int n_out, SlotGeom g,
     const int32_t *__restrict__ idx, int K, uint16_t *__restrict__ y, float *__restrict__ ysum)
@@ -128,8 +125,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
         if (has_idx)
             sidx[threadIdx.x] = my_idx;
         lds_barrier();
-        // ---- phase 3: slot 0's B rows for this thread (small ranks) and the first round's
-        //      pieces, all in flight before anything waits
+        // ---- phase 3: the first round's pieces
         int rsg[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -138,49 +134,6 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
             while (sg + 1 < g.n_slices && ni >= g.slice_start[sg + 1])
                 ++sg;
             rsg[i] = sg;
-        }
-        const bool pre = R <= DF_BPRE_R;
-        const int a0 = tl < nt ? sidx[tl * K] : -1;
-        u32x4 bp[4][DF_BPRE_R / 8];
-        // RC > 0: this lane's B pieces (rows crow(k), part cpart), their slices and sums
-        constexpr int CP = RC > 0 ? RC / 8 : 1;          // 16-byte parts of a row
-        constexpr int CN = RC > 0 ? RC / 2 : 1;          // pieces (rows) per lane
-        const int cpart = g4 % CP;
-        auto crow = [&](int k) { return g4 / CP + (16 / CP) * k; };
-        u32x4 bq[CN];
-        int csg[CN];
-        float cacc[CN];
-        auto cload = [&](int a) {
-#pragma unroll
-            for (int k = 0; k < CN; ++k) {
-                const int nn = row0 + crow(k);
-                bq[k] = *(const u32x4 *)(a >= 0 && nn < n_out
-                                             ? (const void *)(g.B + ((int64_t)a * n_out + nn) * RC +
-                                                              cpart * 8)
-                                             : (const void *)df_zero);
-            }
-        };
-        if constexpr (RC > 0) {
-#pragma unroll
-            for (int k = 0; k < CN; ++k) {
-                const int ni = min(row0 + crow(k), n_out - 1);
-                int sg = 0;
-                while (sg + 1 < g.n_slices && ni >= g.slice_start[sg + 1])
-                    ++sg;
-                csg[k] = sg;
-                cacc[k] = 0.f;
-            }
-            cload(a0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint16_t *brow = g.B + ((int64_t)max(a0, 0) * n_out + min(n + i, n_out - 1)) * R;
-#pragma unroll
-                for (int u = 0; u < DF_BPRE_R / 8; ++u)
-                    bp[i][u] = *(const u32x4 *)((pre && a0 >= 0 && u * 8 < R)
-                                                    ? (const void *)(brow + u * 8)
-                                                    : (const void *)df_zero);
-            }
         }
         const int nv = nt * R;                     // a multiple of 8
         const int e0 = threadIdx.x * 4;
@@ -225,23 +178,6 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
                 }
                 lds_barrier();
                 const int a = tl < nt ? sidx[tl * K + j] : -1;
-                if constexpr (RC > 0) {
-                    if (j > 0 && sg == 0)
-                        cload(a);                  // this slot's pieces (slot 0's are in)
-                    if (a < 0)
-                        continue;
-                    const float *vv = vl + tl * RC + cpart * 8;
-#pragma unroll
-                    for (int k = 0; k < CN; ++k) {
-                        float sp = csg[k] == sg ? dot8(bq[k], vv) : 0.f;
-                        if constexpr (CP >= 2)
-                            sp += __shfl_xor(sp, 1, 64);
-                        if constexpr (CP >= 4)
-                            sp += __shfl_xor(sp, 2, 64);
-                        cacc[k] += sp;
-                    }
-                    continue;
-                }
                 if (a < 0)
                     continue;
                 const float *vv = vl + tl * R;
@@ -249,36 +185,16 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
                 for (int i = 0; i < 4; ++i) {
                     if (rsg[i] != sg)
                         continue;
+                    // the row's columns up to the adapter's rank (rounded to 8; the rest
+                    // multiply zero padding)
                     float dj = 0.f;
-                    if (pre && j == 0) {
-#pragma unroll
-                        for (int u = 0; u < DF_BPRE_R / 8; ++u)
-                            if (u * 8 < R)
-                                dj += dot8(bp[i][u], vv + u * 8);
-                    } else {
-                        // the row's columns up to the adapter's rank (rounded to 8; the rest
-                        // multiply zero padding)
-                        const uint16_t *brow = g.B + ((int64_t)a * n_out + min(n + i, n_out - 1)) * R;
-                        const int r8 = slot_rank8(g.rank, a, R);
-                        for (int rho = 0; rho < r8; rho += 8)
-                            dj += dot8(*(const u32x4 *)(brow + rho), vv + rho);
-                    }
+                    const uint16_t *brow = g.B + ((int64_t)a * n_out + min(n + i, n_out - 1)) * R;
+                    const int r8 = slot_rank8(g.rank, a, R);
+                    for (int rho = 0; rho < r8; rho += 8)
+                        dj += dot8(*(const u32x4 *)(brow + rho), vv + rho);
                     d4[i] += dj;
                 }
             }
-        }
-        if constexpr (RC > 0) {
-            // the rows' sums to the threads that store them (4 consecutive rows each)
-            __shared__ float dl[DF_TOK * DF_ROWS];
-            if (cpart == 0) {
-#pragma unroll
-                for (int k = 0; k < CN; ++k)
-                    dl[tl * DF_ROWS + crow(k)] = cacc[k];
-            }
-            lds_barrier();
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                d4[i] = dl[tl * DF_ROWS + g4 * 4 + i];
         }
     }
 
@@ -318,6 +234,155 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
     }
 }
 
+// Two rows a thread, 8 tokens a workgroup (twice the workgroups of the kernel above, each
+// thread with half the rows: more loads in flight per CU and shorter per-wave chains), for
+// slot widths R = RC in {8, 16, 32} and for the base alone (RC = 0, no LoRA).  Every load that
+// does not depend on a slot id is issued first: the split partials, this thread's token's
+// first slot id, and (threads that own a 4-entry quad of v) the quad's shrink pieces, scale
+// and slot id.  Then the B rows of the thread's 2 rows and the quad's factor; v = s * f *
+// (pieces summed in split order) goes through LDS, one barrier per slot.  The row sums follow
+// the kernel above's order (8-column dot products, pieces added pairwise, slots in order).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+constexpr int DF2_TOK = 8;
+
+template <bool MC, int RC>
+__global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
+    const float *__restrict__ part, int sk, int n_tiles, const float *__restrict__ upart,
+    const float *__restrict__ scale, int T_all, int n_out, SlotGeom g,
+    const int32_t *__restrict__ idx, int K, uint16_t *__restrict__ y, float *__restrict__ ysum)
+{
+    __shared__ __attribute__((aligned(16))) float vl[DF2_TOK * MLORA_MAX_SLICES_DEV * (RC > 0 ? RC : 4)];
+    const int n_tg = ((MC ? DF_CHUNK : T_all) + DF2_TOK - 1) / DF2_TOK;
+    const int chunk = MC ? blockIdx.x / (n_tiles * n_tg) : 0;
+    const unsigned bl = blockIdx.x - chunk * (n_tiles * n_tg);
+    const int T = MC ? min(DF_CHUNK, T_all - chunk * DF_CHUNK) : T_all;
+    if constexpr (MC) {
+        const int wd0 = g.n_slices * RC;
+        part += (int64_t)chunk * sk * n_tiles * DF_CHUNK * DF_ROWS;
+        if (RC > 0) {
+            upart += (int64_t)chunk * sk * K * DF_CHUNK * wd0;
+            idx += (int64_t)chunk * DF_CHUNK * K;
+            if (scale != nullptr)
+                scale += (int64_t)chunk * DF_CHUNK * K;
+        }
+        y += (int64_t)chunk * DF_CHUNK * n_out;
+        if (ysum != nullptr)
+            ysum += (int64_t)chunk * DF_CHUNK * n_out;
+    }
+    const int tile = bl / n_tg;
+    const int t0 = (bl - tile * n_tg) * DF2_TOK;
+    const int nt = min(DF2_TOK, T - t0);
+    const int tl = threadIdx.x >> 5, g2 = threadIdx.x & 31;
+    const int t = t0 + tl;
+    const int n = tile * DF_ROWS + g2 * 2;          // first of this thread's 2 rows
+
+    // ---- independent loads: the split partials (read once: non-temporal)
+    const float *psrc = part + ((int64_t)tile * T + min(t, T - 1)) * DF_ROWS + g2 * 2;
+    const int64_t sstride = (int64_t)n_tiles * T * DF_ROWS;
+    f32x2 pq[DF_PQ];
+#pragma unroll
+    for (int sp = 0; sp < DF_PQ; ++sp)
+        pq[sp] = __builtin_nontemporal_load((const f32x2 *)(sp < sk ? psrc + sp * sstride : df_zero));
+
+    float acc[2] = {0.f, 0.f};
+    if constexpr (RC > 0) {
+        constexpr int CP = RC / 8;                  // 16-byte pieces of a row
+        const int wd = g.n_slices * RC, wq = wd / 4;
+        const int64_t pstride = (int64_t)K * T * wd;
+        // this thread's quad of v: token tq, entries e4 .. e4 + 3 (nt * wd / 4 <= 256 quads)
+        const int tq = threadIdx.x / wq, e4 = (threadIdx.x - tq * wq) * 4;
+        const bool has_q = tq < nt;
+        int my_a = *(tl < nt ? idx + (int64_t)t * K : (const int32_t *)df_zero);
+        int sg[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ni = min(n + i, n_out - 1);
+            sg[i] = (ni >= g.slice_start[1]) + (ni >= g.slice_start[2]) + (ni >= g.slice_start[3]);
+        }
+        for (int j = 0; j < K; ++j) {
+            // pieces, scale and slot id of this thread's quad (no slot id needed to load them)
+            f32x4 pv[DF_PQ];
+            const float *qsrc = upart + ((int64_t)j * T + t0 + tq) * wd + e4;
+#pragma unroll
+            for (int sp = 0; sp < DF_PQ; ++sp)
+                pv[sp] = *(const f32x4 *)(has_q && sp < sk ? qsrc + sp * pstride : df_zero);
+            const int aq = has_q ? idx[(int64_t)(t0 + tq) * K + j] : -1;
+            const float sc = has_q && scale ? scale[(int64_t)(t0 + tq) * K + j] : 1.f;
+            if (j > 0) {
+                my_a = tl < nt ? idx[(int64_t)t * K + j] : -1;
+                lds_barrier();                      // the previous slot's reads of vl are done
+            }
+            const int a = tl < nt ? my_a : -1;
+            // this thread's 2 rows of B[a] (RC columns each), then the quad's factor
+            u32x4 bq[2][CP];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint16_t *brow = g.B + ((int64_t)max(a, 0) * n_out + min(n + i, n_out - 1)) * RC;
+#pragma unroll
+                for (int c = 0; c < CP; ++c)
+                    bq[i][c] = *(const u32x4 *)(a >= 0 ? (const void *)(brow + c * 8) : (const void *)df_zero);
+            }
+            const float fa = *(aq >= 0 ? g.factor + aq : df_zero);
+            if (has_q) {
+                f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sp = 0; sp < DF_PQ; ++sp)
+                    sum += pv[sp];
+                for (int sp = DF_PQ; sp < sk; ++sp)
+                    sum += *(const f32x4 *)(qsrc + sp * pstride);
+                const float cf = aq >= 0 ? (scale ? sc : 1.f) * fa : 0.f;
+                *(f32x4 *)(vl + tq * wd + e4) = sum * cf;
+            }
+            lds_barrier();
+            if (a < 0)
+                continue;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float *vv = vl + tl * wd + sg[i] * RC;
+                float d[CP];
+#pragma unroll
+                for (int c = 0; c < CP; ++c)
+                    d[c] = dot8(bq[i][c], vv + c * 8);
+                float sp;
+                if constexpr (CP == 1)
+                    sp = d[0];
+                else if constexpr (CP == 2)
+                    sp = d[0] + d[1];
+                else
+                    sp = (d[0] + d[1]) + (d[2] + d[3]);
+                acc[i] += sp;
+            }
+        }
+    }
+
+    // ---- base: the split partials in split order
+    f32x2 base = {0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < DF_PQ; ++sp)
+        base += pq[sp];
+    for (int sp = DF_PQ; sp < sk; ++sp)
+        base += *(const f32x2 *)(psrc + sp * sstride);
+    if (t >= t0 + nt || n >= n_out)
+        return;
+    const float o0 = base[0] + acc[0], o1 = base[1] + acc[1];
+    uint16_t *yo = y + (int64_t)t * n_out + n;
+    float *so = ysum != nullptr ? ysum + (int64_t)t * n_out + n : nullptr;
+    if (n + 1 < n_out && (n_out & 1) == 0) {
+        *(uint32_t *)yo = pack_bf16x2(o0, o1);
+        if (so != nullptr)
+            *(f32x2 *)so = f32x2{o0, o1};
+    } else {
+        yo[0] = f32_to_bf16(o0);
+        if (so != nullptr)
+            so[0] = o0;
+        if (n + 1 < n_out) {
+            yo[1] = f32_to_bf16(o1);
+            if (so != nullptr)
+                so[1] = o1;
+        }
+    }
+}
+
 hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, const float *upart,
                                 const float *scale, int64_t T, int64_t n_out, const SlotGeom *g,
                                 const int32_t *idx, int32_t K, uint16_t *y, float *ysum,
@@ -333,26 +398,38 @@ hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, 
         K = 1;
     }
     const int64_t n_chunks = (T + DF_CHUNK - 1) / DF_CHUNK;
+    const int rc = upart != nullptr ? (gg.R == 8 || gg.R == 16 || gg.R == 32 ? gg.R : -1) : 0;
+    const bool mc = n_chunks > 1;
+    if (rc >= 0) {
+        // two rows a thread: the base alone, or LoRA with slots up to 32 wide
+        const unsigned grid2 = (unsigned)(n_chunks * n_tiles *
+                                          ((std::min<int64_t>(T, DF_CHUNK) + DF2_TOK - 1) / DF2_TOK));
+#define DF2_LAUNCH(M, C)                                                                           \
+    hipLaunchKernelGGL((decode_finish_kernel<M, C>), dim3(grid2), dim3(DF_THREADS), 0, stream,   \
+                       part, sk, n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y, ysum)
+        switch (rc * 2 + (mc ? 1 : 0)) {
+        case 0: DF2_LAUNCH(false, 0); break;
+        case 1: DF2_LAUNCH(true, 0); break;
+        case 16: DF2_LAUNCH(false, 8); break;
+        case 17: DF2_LAUNCH(true, 8); break;
+        case 32: DF2_LAUNCH(false, 16); break;
+        case 33: DF2_LAUNCH(true, 16); break;
+        case 64: DF2_LAUNCH(false, 32); break;
+        default: DF2_LAUNCH(true, 32); break;
+        }
+#undef DF2_LAUNCH
+        return hipGetLastError();
+    }
+    // wider slots: four rows a thread, each thread reading its own rows of B
     const unsigned grid =
         (unsigned)(n_chunks * n_tiles * ((std::min<int64_t>(T, DF_CHUNK) + DF_TOK - 1) / DF_TOK));
-    const int rc = upart != nullptr && (gg.R == 8 || gg.R == 16 || gg.R == 32) ? gg.R : 0;
-    const bool mc = n_chunks > 1;
-#define DF_LAUNCH(M, C)                                                                            \
-    hipLaunchKernelGGL((decode_finish_kernel<M, C>), dim3(grid), dim3(DF_THREADS), lds, stream,  \
+#define DF_LAUNCH(M)                                                                               \
+    hipLaunchKernelGGL((decode_finish_wide_kernel<M>), dim3(grid), dim3(DF_THREADS), lds, stream,   \
                        part, sk, n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y, ysum)
-    switch (rc * 2 + (mc ? 1 : 0)) {
-    case 16: DF_LAUNCH(false, 8); break;
-    case 17: DF_LAUNCH(true, 8); break;
-    case 32: DF_LAUNCH(false, 16); break;
-    case 33: DF_LAUNCH(true, 16); break;
-    case 64: DF_LAUNCH(false, 32); break;
-    case 65: DF_LAUNCH(true, 32); break;
-    default:
-        if (mc)
-            DF_LAUNCH(true, 0);
-        else
-            DF_LAUNCH(false, 0);
-    }
+    if (mc)
+        DF_LAUNCH(true);
+    else
+        DF_LAUNCH(false);
 #undef DF_LAUNCH
     return hipGetLastError();
 }
