@@ -1,6 +1,7 @@
 // Per-device facts the launchers need, looked up once per device and cached under a lock:
-// the CU count, each kernel's static LDS, and the dynamic-LDS limit already granted to a kernel
-// (hipFuncSetAttribute is called again only when a launch needs more).
+// the CU count, each kernel's static LDS, how many of a kernel's workgroups a CU holds at once,
+// and the dynamic-LDS limit already granted to a kernel (hipFuncSetAttribute is called again
+// only when a launch needs more).
 #include <map>
 #include <mutex>
 #include <utility>
@@ -14,6 +15,7 @@ std::mutex g_mu;
 std::map<int, int> g_cus;                                    // device -> CUs
 std::map<std::pair<int, const void *>, size_t> g_lds_granted; // (device, kernel) -> bytes
 std::map<std::pair<int, const void *>, size_t> g_lds_static;  // (device, kernel) -> bytes
+std::map<std::pair<int, const void *>, int> g_resident;       // (device, kernel) -> workgroups
 
 int current_device()
 {
@@ -55,6 +57,22 @@ size_t kernel_static_lds(const void *fn)
         s = 1024;   // unknown: assume a little, so that budgets stay on the safe side
     g_lds_static[key] = s;
     return s;
+}
+
+int kernel_resident_blocks(const void *fn, int threads, size_t dyn_lds)
+{
+    const int dev = current_device();
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto key = std::make_pair(dev, fn);
+    auto it = g_resident.find(key);
+    if (it != g_resident.end())
+        return it->second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, dyn_lds) != hipSuccess ||
+        n < 1)
+        n = 1;
+    g_resident[key] = n;
+    return n;
 }
 
 hipError_t ensure_dynamic_lds(const void *fn, size_t bytes)

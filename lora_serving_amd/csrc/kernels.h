@@ -15,6 +15,9 @@ constexpr size_t LDS_BYTES = 160 * 1024;   // LDS per CU on gfx950
 int device_cu_count();
 // Static (__shared__) LDS of a kernel.
 size_t kernel_static_lds(const void *fn);
+// Workgroups of a kernel (threads each, dyn_lds bytes of dynamic LDS) that one CU holds at once
+// (its register and LDS use; looked up on the first call per device and kernel, at least 1).
+int kernel_resident_blocks(const void *fn, int threads, size_t dyn_lds);
 // Raises the kernel's dynamic-LDS limit on the current device to at least `bytes` (once).
 hipError_t ensure_dynamic_lds(const void *fn, size_t bytes);
 constexpr int MLORA_MAX_SLICES_DEV = 4;
