@@ -614,8 +614,11 @@ def main():
         ex_ms = sum(kernel_ms[1::2]) / len(kernel_ms[1::2])
         sh_b = sum(a["shrink_bytes"] for a in algs) / len(layers)
         ex_b = sum(a["expand_bytes"] for a in algs) / len(layers)
+        # the expand kernel the library picks: slot widths up to 32 have their own
+        ex_name = ("mlora::expand_narrow_kernel" if layers[0].R <= 32 else
+                   "mlora::expand_tokens_kernel")
         kern = [("mlora::shrink_rows_kernel (mlora_shrink)", sh_ms, sh_b),
-                ("mlora::expand_tokens_kernel (mlora_expand)", ex_ms, ex_b)]
+                (ex_name + " (mlora_expand)", ex_ms, ex_b)]
         kern.sort(key=lambda k: -k[1])
         kname, k_avg_ms, k_bytes = kern[0]
         achieved = k_bytes / (k_avg_ms * 1e-3) / 1e9
