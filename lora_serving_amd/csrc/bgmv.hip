@@ -17,6 +17,12 @@
 // expand: one workgroup per (token, block of output rows).  Lanes walk the contiguous
 //   B[a][rows][0..R) block 16 bytes at a time, so each lane holds 8 rank entries of one row;
 //   the R/8 lanes of a row finish the dot product with xor shuffles over the rank dimension.
+//   Slot widths up to 32 have a kernel of their own with the row width fixed at compile time.
+// These kernels are bound by latency at decode sizes: a launch and one round trip to HBM that
+// waits for a slot id are most of their time, and every instruction on a wave's path counts,
+// so everything that does not depend on a slot id is loaded before it is read, masked loads
+// read a static zero block instead of branching, and the index arithmetic stays 32-bit where
+// the grid allows.
 #include "common.h"
 #include "kernels.h"
 
