@@ -342,6 +342,44 @@ def test_rank_table_dense_tiles(oracle_mod, seed, n_in, R, K, ranks):
     assert tol_ok(y1, y_ref).all(), f"worst {worst(y1, y_ref):.3e}"
 
 
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_decode_more_splits_than_loads_in_flight(oracle_mod, path):
+    """n_in = 9224 gives the decode GEMM 10 splits of n_in (the last one ragged), more than the
+    finish keeps in flight at once (8): splits 8 and 9 are added in a second round, for the
+    partials and the shrink pieces alike.  Decode path with LoRA, the grouped decode (its
+    finish keeps only the base), and the base alone."""
+    from lora_serving_amd import mlora
+    L = synth.random_layer(81, T=40, n_in=9224, n_out=136, S=6, R=16, K=2,
+                           slice_sizes=[72, 64], p_sentinel=0.25)
+    say(f"[splits] path={path} T={L.T} n_in={L.n_in} n_out={L.n_out}")
+    flags = mlora.MLORA_PATH_DECODE if path == "decode" else mlora.MLORA_PATH_GROUPED
+    D = DevLayer(L)
+    y = from_dev_bf16(D.linear(flags=flags))
+    y_ref = oracle_mod.linear(L)
+    assert tol_ok(y, y_ref).all(), f"worst {worst(y, y_ref):.3e}"
+    if path == "decode":
+        import dataclasses
+        y0 = from_dev_bf16(D.linear(flags=flags | mlora.MLORA_NO_ADAPTERS))
+        y0_ref = oracle_mod.linear(dataclasses.replace(L, idx=np.full_like(L.idx, -1)))
+        assert tol_ok(y0, y0_ref).all(), f"base: worst {worst(y0, y0_ref):.3e}"
+
+
+def test_narrow_slots_at_the_limits(oracle_mod):
+    """Slot width 32 with the most slots per token (8) and slices (4): the decode finish's v
+    block (8 tokens x 4 slices x 32 entries, one quad a thread) and its slot loop, and the
+    standalone expand's v staging of slots 4..7 (the second row of each wave).  Decode path
+    and the standalone pair against the oracle."""
+    L = synth.random_layer(82, T=37, n_in=512, n_out=520, S=9, R=32, K=8,
+                           slice_sizes=[136, 128, 128, 128], p_sentinel=0.3)
+    say(f"[narrow limits] T={L.T} R={L.R} K={L.K} slices={L.n_slices}")
+    from lora_serving_amd import mlora
+    D = DevLayer(L)
+    y = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_DECODE))
+    y_ref = oracle_mod.linear(L)
+    assert tol_ok(y, y_ref).all(), f"worst {worst(y, y_ref):.3e}"
+    check_delta(oracle_mod, L, D=D, label="narrow limits")
+
+
 @pytest.mark.parametrize("seed,T,K", [(55, 64, 1), (56, 37, 3)])
 def test_rank_table_standalone_pair(oracle_mod, seed, T, K):
     """mlora_shrink / mlora_expand with the slots' true ranks: the rows of A and the columns of B
