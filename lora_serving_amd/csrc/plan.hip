@@ -6,8 +6,8 @@
 // tile plan), -1 entries are dropped, and ties keep their input order.  Exactly one output is
 // correct, so the result is bit-exact.
 //
-// Small maps (up to 8192 entries, up to 1000 keys): one launch, sort_small (below).  Otherwise
-// three launches:
+// Small maps (up to 8192 entries, up to 1000 keys): one launch, sort_wave (one wave, up to 512
+// entries) or sort_small (below).  Otherwise three launches:
 //   sort_count   one wave per unit of SORT_UNIT consecutive entries: per-key counts (LDS)
 //   sort_scan    one workgroup: exclusive scan of the counts in key-major order, which gives
 //                every (key, unit) its first output position; then the segment table
@@ -241,6 +241,83 @@ __global__ __launch_bounds__(1024) void sort_small(const int32_t *__restrict__ k
     }
 }
 
+// One-wave form for the smallest maps (n <= SORT_WAVE_MAX_N): a single wave holds every entry
+// in registers (up to 8 a lane) and the per-key table in LDS, so no step needs a barrier (one
+// wave's LDS operations complete in order).  Counts: the first lane of each ballot-matched group
+// of equal keys adds the group's size; the exclusive scan over the keys, 64 at a time, gives
+// each key its first output position and, compacted with a ballot, the segment table; then the
+// entries are placed in input order, equal keys ranked by lane.  Same output as the kernels
+// above, with a sixteenth of the waves and none of their barriers.
+constexpr int SORT_WAVE_MAX_N = 64 * SORT_SMALL_PER_LANE;
+
+__global__ __launch_bounds__(64) void sort_wave(const int32_t *__restrict__ keys, int32_t n,
+                                                int32_t nkeys, int32_t nbits,
+                                                int32_t *__restrict__ perm,
+                                                int32_t *__restrict__ seg_key,
+                                                int32_t *__restrict__ seg_start,
+                                                int32_t *__restrict__ seg_len,
+                                                int32_t *__restrict__ counts)
+{
+    __shared__ int32_t tab[SORT_SMALL_MAX_KEYS];
+    const int lane = threadIdx.x;
+    const int steps = (n + 63) >> 6;
+    int kk[SORT_SMALL_PER_LANE];
+#pragma unroll
+    for (int i = 0; i < SORT_SMALL_PER_LANE; ++i) {
+        const int p = i * 64 + lane;
+        kk[i] = p < n ? keys[p] : -1;
+    }
+    for (int k = lane; k < nkeys; k += 64)
+        tab[k] = 0;
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < SORT_SMALL_PER_LANE; ++i) {
+        if (i >= steps)
+            break;
+        const int k = kk[i];
+        const uint64_t same = match_key((uint32_t)(k + 1), nbits) & ballot64(k >= 0);
+        if (k >= 0 && __popcll(same & below) == 0)
+            tab[k] += __popcll(same);
+    }
+    int carry = 0, g = 0;
+    for (int k0 = 0; k0 < nkeys; k0 += 64) {
+        const int k = k0 + lane;
+        const int c = k < nkeys ? tab[k] : 0;
+        int tot;
+        const int start = carry + wave_exclusive_scan(c, &tot);
+        const uint64_t used = ballot64(c > 0);
+        if (c > 0) {
+            const int at = g + __popcll(used & below);
+            seg_key[at] = k;
+            seg_start[at] = start;
+            seg_len[at] = c;
+        }
+        if (k < nkeys)
+            tab[k] = start;
+        carry += tot;
+        g += __popcll(used);
+    }
+    if (lane == 0) {
+        counts[0] = g;
+        counts[1] = carry;
+    }
+#pragma unroll
+    for (int i = 0; i < SORT_SMALL_PER_LANE; ++i) {
+        if (i >= steps)
+            break;
+        const int k = kk[i];
+        const bool part = k >= 0;
+        const uint64_t same = match_key((uint32_t)(k + 1), nbits) & ballot64(part);
+        const int rank = __popcll(same & below);
+        if (part) {
+            const int at = tab[k];
+            perm[at + rank] = i * 64 + lane;
+            if (rank == 0)
+                tab[k] = at + __popcll(same);
+        }
+    }
+}
+
 static int key_bits(int32_t nkeys)
 {
     int b = 0;
@@ -259,6 +336,11 @@ hipError_t launch_stable_sort(const int32_t *keys, int64_t n, int32_t nkeys, int
                               int32_t *seg_key, int32_t *seg_start, int32_t *seg_len,
                               int32_t *counts, int32_t *cnt_ws, hipStream_t stream)
 {
+    if (n <= SORT_WAVE_MAX_N && nkeys <= SORT_SMALL_MAX_KEYS) {
+        hipLaunchKernelGGL(sort_wave, dim3(1), dim3(64), 0, stream, keys, (int32_t)n, nkeys,
+                           key_bits(nkeys), perm, seg_key, seg_start, seg_len, counts);
+        return hipGetLastError();
+    }
     if (n <= SORT_SMALL_MAX_N && nkeys <= SORT_SMALL_MAX_KEYS) {
         hipLaunchKernelGGL(sort_small, dim3(1), dim3(1024), 0, stream, keys, (int32_t)n, nkeys,
                            key_bits(nkeys), perm, seg_key, seg_start, seg_len, counts);

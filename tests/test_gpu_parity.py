@@ -737,7 +737,11 @@ def test_t_zero_is_noop():
 PLAN_CASES = [(0, 1, 1, 1), (1, 6, 1, 4), (2, 64, 1, 100), (3, 1000, 3, 7), (4, 16384, 1, 100),
               (5, 8192, 3, 32), (6, 3000, 2, 16384), (7, 0, 1, 5), (8, 5000, 8, 1),
               (9, 8192, 1, 1000), (10, 8193, 1, 1000), (11, 4096, 1, 1001), (12, 1500, 2, 50),
-              (13, 1170, 7, 3), (14, 32768, 1, 1000)]
+              (13, 1170, 7, 3), (14, 32768, 1, 1000),
+              # the one-wave sort (up to 512 pairs): its last size, one past it, 7 slots per
+              # token, a single key, the most keys, and one key too many for it
+              (15, 512, 1, 1000), (16, 513, 1, 1000), (17, 73, 7, 40), (18, 512, 1, 1),
+              (19, 300, 1, 1001)]
 
 
 @pytest.mark.parametrize("case", PLAN_CASES, ids=[f"p{c[0]}" for c in PLAN_CASES])
