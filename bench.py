@@ -313,6 +313,16 @@ class Prepared:
         return sum((L.T + 511) // 512 if self.decode_like else 1 for L in layers)
 
 
+def plan_form(pairs, slots):
+    """The sort the library runs for a map of this size (one wave, one workgroup, or three
+    kernels), by the same limits as its launcher."""
+    if pairs <= 512 and slots <= 1000:
+        return "sort_wave, one launch"
+    if pairs <= 8192 and slots <= 1000:
+        return "sort_small, one launch"
+    return "sort_count + sort_scan + sort_scatter, one region"
+
+
 _SLEEP_CYCLES_PER_US = None
 
 
@@ -605,7 +615,7 @@ def main():
         tot_bytes, tot_flops = k_bytes, 0.0
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                "kernel": "mlora_plan (sort_count + sort_scan + sort_scatter, one region)",
+                "kernel": "mlora_plan (" + plan_form(L0.T * L0.K, L0.S) + ")",
                 "kernel_avg_us": k_avg_ms * 1e3, "algorithmic_bytes_per_launch": k_bytes,
                 "pairs": L0.T * L0.K, "used_pairs": n_used, "segments": n_seg}
     elif args.op == "bgmv":
