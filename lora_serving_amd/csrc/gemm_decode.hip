@@ -353,6 +353,228 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
         }
     }
 }
+// Many more (tile, split) items than CUs in one 64-token chunk (vocabulary-wide outputs): a
+// persistent grid of one workgroup per CU.  Workgroup b keeps split s = b % sk of n_in and walks
+// the row tiles b / sk, b / sk + step, ... (step = grid / sk).  x's slice for s is loaded and
+// moved into the MFMA layout once; each next tile's A rows and W fragments are issued right
+// after the current tile's MFMAs, so they stream in while its 8-wave reduction, partial store
+// and remaining shrink pieces run.  Per tile the arithmetic and its order are those of the
+// kernel above (same output bits).
+template <int TT, bool PW>
+__global__ __launch_bounds__(512) void decode_gemm_ps_kernel(DecodeArgs P)
+{
+    extern __shared__ __attribute__((aligned(16))) float red[];   // [8][4][TT][64] float4
+    __shared__ float sred[DEC_WAVES][16];
+    const uint16_t *__restrict__ W = P.W;
+    const int n_in = P.n_in, n_out = P.n_out, n_tiles = P.n_tiles, K = P.K;
+    const SlotGeom &g = P.g;
+    const int wd = g.n_slices * g.R;
+    const int s = blockIdx.x % P.sk;
+    const int tstep = gridDim.x / P.sk;          // the grid is a multiple of sk
+    int tile = blockIdx.x / P.sk;
+    const int T = P.T, n_pairs = P.n_pairs;
+    const uint16_t *__restrict__ x = P.x;
+    const int32_t *idx = P.idx;
+    float *part = P.part, *upart = P.upart;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15;
+    const int gq = lane >> 4;
+    const int kw = s * P.ks_cols + wave * DEC_WK;
+    const bool wave_on = kw < n_in && wave * DEC_WK < P.ks_cols;
+    auto col = [&](int ks) { return kw + (ks * 4 + gq) * 8; };
+
+    int a0 = -1;
+    if (upart != nullptr && tile < n_pairs)
+        a0 = idx[tile];
+
+    // x: as in the kernel above, once for all the workgroup's tiles
+    uint16_t *xl = (uint16_t *)(red + wave * (4 * TT * 64 * 4));
+    u32x4 xf[TT][4];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int row = tt * 16 + ks * 4 + gq;
+            const int c = kw + r * 8;
+            xf[tt][ks] = dec_ld16(x + (int64_t)min(row, T - 1) * n_in, c,
+                                  wave_on && row < T && c < n_in);
+        }
+    // A rows of a tile's first shrink piece (pair p = tile) and its W fragments
+    u32x4 af[4], wf[4][4];
+    auto load_a = [&](int a) {
+        const int arow = min(r, max(wd, 1) - 1);
+        const uint16_t *ap = upart != nullptr ? g.A + ((int64_t)max(a, 0) * wd + arow) * n_in : x;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int c = col(ks);
+            af[ks] = dec_ld16(ap, c, a >= 0 && wave_on && c < n_in && r < wd);
+        }
+    };
+    auto load_w = [&](int tl) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if constexpr (PW) {
+                    const int rg = tl * 4 + rt, kb = (kw >> 5) + ks;
+                    const bool ok = wave_on && rg < P.n_rg && kb < P.n_kb;
+                    const uint16_t *wp = W + (((int64_t)min(rg, P.n_rg - 1) * P.n_kb + min(kb, P.n_kb - 1)) * 64 + lane) * 8;
+                    wf[rt][ks] = dec_ld16_stream(wp, ok);
+                } else {
+                    const int row = tl * DEC_ROWS + rt * 16 + r;
+                    const uint16_t *wrow = W + (int64_t)min(row, n_out - 1) * n_in;
+                    const int c = col(ks);
+                    wf[rt][ks] = dec_ld16_stream(wrow + c, wave_on && c < n_in && row < n_out);
+                }
+            }
+        }
+    };
+    load_a(a0);
+    load_w(tile);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int row = tt * 16 + ks * 4 + gq;
+            *(u32x4 *)(xl + (row * 16 + (r ^ (row & 15))) * 8) = xf[tt][ks];
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int row = tt * 16 + r;
+            const int c = ks * 4 + gq;
+            xf[tt][ks] = *(const u32x4 *)(xl + (row * 16 + (c ^ (row & 15))) * 8);
+        }
+    // every wave is past its transpose reads before the first tile's sums reuse the LDS
+    lds_barrier();
+
+    while (true) {
+        const int next = tile + tstep;
+        const bool more = next < n_tiles;
+        // the next tile's slot id, early: its A rows wait for it
+        int a0n = -1;
+        if (more && upart != nullptr && next < n_pairs)
+            a0n = idx[next];
+
+        f32x4 acc[4][TT];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+                acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt)
+                    acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, wf[rt][ks]), __builtin_bit_cast(bf16x8, xf[tt][ks]),
+                        acc[rt][tt], 0, 0, 0);
+        const int t0p = tile / K;
+        if (a0 >= 0) {
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < TT; ++q) {
+                if (q == (t0p >> 4)) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, af[ks]), __builtin_bit_cast(bf16x8, xf[q][ks]),
+                            d, 0, 0, 0);
+                }
+            }
+            if (r == (t0p & 15)) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sred[wave][gq * 4 + i] = d[i];
+            }
+        }
+        // the next tile's loads, in flight during this tile's reduction and stores
+        if (more) {
+            load_a(a0n);
+            load_w(next);
+        }
+
+        float4 *red4 = (float4 *)red;
+        constexpr int SLOTS = 4 * TT * 64;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+                red4[wave * SLOTS + (rt * TT + tt) * 64 + lane] =
+                    float4{acc[rt][tt][0], acc[rt][tt][1], acc[rt][tt][2], acc[rt][tt][3]};
+        lds_barrier();
+        if (a0 >= 0 && threadIdx.x < 16 && (int)threadIdx.x < wd) {
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < DEC_WAVES; ++w)
+                sum += sred[w][threadIdx.x];
+            upart[(((int64_t)s * K + (tile - t0p * K)) * T + t0p) * wd + threadIdx.x] = sum;
+        }
+        for (int sl = threadIdx.x; sl < SLOTS; sl += 512) {
+            float4 sum = red4[sl];
+#pragma unroll
+            for (int w = 1; w < DEC_WAVES; ++w) {
+                const float4 v = red4[w * SLOTS + sl];
+                sum.x += v.x;
+                sum.y += v.y;
+                sum.z += v.z;
+                sum.w += v.w;
+            }
+            const int ln = sl & 63;
+            const int rt = sl / (64 * TT);
+            const int tt = (sl / 64) % TT;
+            const int tok = tt * 16 + (ln & 15);
+            const int rloc = rt * 16 + (ln >> 4) * 4;
+            if (tok < T)
+                *(float4 *)(part + (((int64_t)s * n_tiles + tile) * T + tok) * DEC_ROWS + rloc) = sum;
+        }
+
+        // remaining shrink pieces of this tile (as in the kernel above)
+        if (upart != nullptr) {
+            bool synced = false;
+            for (int p = tile; p < n_pairs; p += n_tiles) {
+                const int a = idx[p];
+                if (a < 0)
+                    continue;
+                const int r8 = slot_rank8(g.rank, a, g.R);
+                for (int r0 = (p == tile ? 16 : 0); r0 < wd; r0 += 16) {
+                    if (g.R >= 16 && r0 % g.R >= r8) {
+                        const int t = p / K;
+                        if (threadIdx.x < 16)
+                            upart[(((int64_t)s * K + (p - t * K)) * T + t) * wd + r0 + threadIdx.x] = 0.f;
+                        continue;
+                    }
+                    if (!synced) {
+                        lds_barrier();
+                        synced = true;
+                    }
+                    u32x4 afr[4];
+                    const int arow = r0 + r;
+                    const uint16_t *ap = g.A + ((int64_t)a * wd + min(arow, wd - 1)) * n_in;
+                    const bool rok = arow < wd && arow % g.R < r8;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const int c = col(ks);
+                        afr[ks] = dec_ld16(ap, c, rok && wave_on && c < n_in);
+                    }
+                    decode_shrink_piece<TT>(xf, afr, p, r0, K, T, wd, s, wave, r, gq, sred, upart);
+                }
+            }
+        }
+        if (!more)
+            break;
+        tile = next;
+        a0 = a0n;
+        lds_barrier();   // this tile's reads of red and sred are done before the next one's writes
+    }
+}
+
 DecodeCfg decode_config(int64_t T, int64_t n_in, int64_t n_out)
 {
     DecodeCfg c;
@@ -396,6 +618,17 @@ static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, hipStream_t strea
     if constexpr (TT == 4)   // only full 64-token chunks come before the last one
         if (a.n_chunks > 1)
             return launch_tfm<TT, PW, true>(a, c, stream);
+    // one chunk with at least twice as many (tile, split) items as CUs: the persistent grid
+    const int n_cus = device_cu_count();
+    if ((int64_t)c.n_tiles * c.sk >= 2 * (int64_t)n_cus && c.sk <= n_cus) {
+        const size_t lds = (size_t)DEC_WAVES * 4 * TT * 64 * sizeof(float4);
+        if (hipError_t e = ensure_dynamic_lds((const void *)decode_gemm_ps_kernel<TT, PW>, lds);
+            e != hipSuccess)
+            return e;
+        const dim3 grid((unsigned)((n_cus / c.sk) * c.sk)), block(512);
+        hipLaunchKernelGGL((decode_gemm_ps_kernel<TT, PW>), grid, block, lds, stream, a);
+        return hipGetLastError();
+    }
     return launch_tfm<TT, PW, false>(a, c, stream);
 }
 
