@@ -353,15 +353,17 @@ __global__ __launch_bounds__(512) void decode_gemm_kernel(DecodeArgs P)
         }
     }
 }
-// Many more (tile, split) items than CUs in one 64-token chunk (vocabulary-wide outputs): a
-// persistent grid of one workgroup per CU.  Workgroup b keeps split s = b % sk of n_in and walks
-// the row tiles b / sk, b / sk + step, ... (step = grid / sk).  x's slice for s is loaded and
-// moved into the MFMA layout once; each next tile's A rows and W fragments are issued right
-// after the current tile's MFMAs, so they stream in while its 8-wave reduction, partial store
-// and remaining shrink pieces run.  Per tile the arithmetic and its order are those of the
-// kernel above (same output bits).
-template <int TT, bool PW>
-__global__ __launch_bounds__(512) void decode_gemm_ps_kernel(DecodeArgs P)
+// Many more (chunk, tile, split) items than CUs (vocabulary-wide outputs, or several 64-token
+// chunks): a persistent grid of one workgroup per CU.  A workgroup keeps one (chunk, split s of
+// n_in) and walks row tiles l, l + L, l + 2L, ...: x's slice is loaded and moved into the MFMA
+// layout once, and each next tile's A rows and W fragments are issued right after the current
+// tile's MFMAs, so they stream in while its 8-wave reduction, partial store and remaining
+// shrink pieces run.  With one chunk, workgroup b takes s = b % sk and l = b / sk (L = grid /
+// sk).  With several, the workgroups of one XCD (b mod 8) hold every chunk of the same (s, l)
+// pairs, chunk innermost, so the chunks' copies of a tile's W meet in that XCD's L2.  Per tile
+// the arithmetic and its order are those of the kernel above (same output bits).
+template <int TT, bool PW, bool MC>
+__global__ __launch_bounds__(512) void decode_gemm_ps_kernel(DecodeArgs P, int n_lanes)
 {
     extern __shared__ __attribute__((aligned(16))) float red[];   // [8][4][TT][64] float4
     __shared__ float sred[DEC_WAVES][16];
@@ -369,13 +371,35 @@ __global__ __launch_bounds__(512) void decode_gemm_ps_kernel(DecodeArgs P)
     const int n_in = P.n_in, n_out = P.n_out, n_tiles = P.n_tiles, K = P.K;
     const SlotGeom &g = P.g;
     const int wd = g.n_slices * g.R;
-    const int s = blockIdx.x % P.sk;
-    const int tstep = gridDim.x / P.sk;          // the grid is a multiple of sk
-    int tile = blockIdx.x / P.sk;
-    const int T = P.T, n_pairs = P.n_pairs;
+    int s, tile, tstep, chunk = 0;
+    if constexpr (!MC) {
+        s = blockIdx.x % P.sk;
+        tile = blockIdx.x / P.sk;
+        tstep = gridDim.x / P.sk;                // the grid is a multiple of sk
+    } else {
+        // per XCD: (grid / 8) slots = n_chunks x (its share of the (s, l) pairs)
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        const int per_xcd = (gridDim.x >> 3) / P.n_chunks;
+        chunk = slot % P.n_chunks;
+        const int q = xcd * per_xcd + slot / P.n_chunks;   // (s, l) pair; 8 per_xcd of them
+        s = q % P.sk;
+        tile = q / P.sk;
+        tstep = n_lanes;                          // 8 per_xcd / sk, set by the host
+    }
+    int T = P.T, n_pairs = P.n_pairs;
     const uint16_t *__restrict__ x = P.x;
     const int32_t *idx = P.idx;
     float *part = P.part, *upart = P.upart;
+    if constexpr (MC) {
+        T = min(DEC_CHUNK, P.T - chunk * DEC_CHUNK);
+        n_pairs = T * K;
+        x += (int64_t)chunk * DEC_CHUNK * n_in;
+        if (idx != nullptr)
+            idx += (int64_t)chunk * DEC_CHUNK * K;
+        part += (int64_t)chunk * P.sk * n_tiles * DEC_CHUNK * DEC_ROWS;
+        if (upart != nullptr)
+            upart += (int64_t)chunk * P.sk * K * DEC_CHUNK * wd;
+    }
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;
@@ -613,20 +637,39 @@ static hipError_t launch_tfm(DecodeArgs &a, const DecodeCfg &c, hipStream_t stre
 }
 
 template <int TT, bool PW>
-static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, hipStream_t stream)
+static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, bool shared_cus, hipStream_t stream)
 {
-    if constexpr (TT == 4)   // only full 64-token chunks come before the last one
-        if (a.n_chunks > 1)
+    if constexpr (TT == 4) {   // only full 64-token chunks come before the last one
+        if (a.n_chunks > 1) {
+            // the persistent grid when every XCD can hold all chunks of whole (split, lane)
+            // groups and each workgroup gets at least two tiles
+            const int n_cus = device_cu_count();
+            const int per_xcd = (n_cus / 8) / a.n_chunks;          // (s, l) pairs per XCD
+            const int n_pairs_sl = 8 * per_xcd;
+            if (!shared_cus && per_xcd >= 1 && n_pairs_sl % c.sk == 0 &&
+                c.n_tiles >= 2 * (n_pairs_sl / c.sk)) {
+                const size_t lds = (size_t)DEC_WAVES * 4 * TT * 64 * sizeof(float4);
+                if (hipError_t e =
+                        ensure_dynamic_lds((const void *)decode_gemm_ps_kernel<TT, PW, true>, lds);
+                    e != hipSuccess)
+                    return e;
+                const dim3 grid((unsigned)(8 * per_xcd * a.n_chunks)), block(512);
+                hipLaunchKernelGGL((decode_gemm_ps_kernel<TT, PW, true>), grid, block, lds, stream,
+                                   a, n_pairs_sl / c.sk);
+                return hipGetLastError();
+            }
             return launch_tfm<TT, PW, true>(a, c, stream);
+        }
+    }
     // one chunk with at least twice as many (tile, split) items as CUs: the persistent grid
     const int n_cus = device_cu_count();
-    if ((int64_t)c.n_tiles * c.sk >= 2 * (int64_t)n_cus && c.sk <= n_cus) {
+    if (!shared_cus && (int64_t)c.n_tiles * c.sk >= 2 * (int64_t)n_cus && c.sk <= n_cus) {
         const size_t lds = (size_t)DEC_WAVES * 4 * TT * 64 * sizeof(float4);
-        if (hipError_t e = ensure_dynamic_lds((const void *)decode_gemm_ps_kernel<TT, PW>, lds);
+        if (hipError_t e = ensure_dynamic_lds((const void *)decode_gemm_ps_kernel<TT, PW, false>, lds);
             e != hipSuccess)
             return e;
         const dim3 grid((unsigned)((n_cus / c.sk) * c.sk)), block(512);
-        hipLaunchKernelGGL((decode_gemm_ps_kernel<TT, PW>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((decode_gemm_ps_kernel<TT, PW, false>), grid, block, lds, stream, a, 0);
         return hipGetLastError();
     }
     return launch_tfm<TT, PW, false>(a, c, stream);
@@ -635,7 +678,7 @@ static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, hipStream_t strea
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed, int64_t T,
                               int64_t n_in, int64_t n_out, float *part, const DecodeCfg &c,
                               const SlotGeom *g, const int32_t *idx, int32_t K, float *upart,
-                              hipStream_t stream)
+                              hipStream_t stream, bool shared_cus)
 {
     DecodeArgs a{};
     a.x = x;
@@ -658,12 +701,12 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed,
     a.n_rg = (int)((n_out + 15) / 16);
     a.n_kb = (int)((n_in + 31) / 32);
     switch (c.tt * 2 + (packed ? 1 : 0)) {
-    case 2: return launch_tf<1, false>(a, c, stream);
-    case 3: return launch_tf<1, true>(a, c, stream);
-    case 4: return launch_tf<2, false>(a, c, stream);
-    case 5: return launch_tf<2, true>(a, c, stream);
-    case 8: return launch_tf<4, false>(a, c, stream);
-    case 9: return launch_tf<4, true>(a, c, stream);
+    case 2: return launch_tf<1, false>(a, c, shared_cus, stream);
+    case 3: return launch_tf<1, true>(a, c, shared_cus, stream);
+    case 4: return launch_tf<2, false>(a, c, shared_cus, stream);
+    case 5: return launch_tf<2, true>(a, c, shared_cus, stream);
+    case 8: return launch_tf<4, false>(a, c, shared_cus, stream);
+    case 9: return launch_tf<4, true>(a, c, shared_cus, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -65,11 +65,14 @@ size_t decode_partial_bytes(int64_t T, int64_t n_in, int64_t n_out);
 // the same launch writes the unscaled shrink partials upart[s][j][t][0:n_slices*R] of every
 // pair (-1 pairs skipped).  T above 64: chunks of 64 tokens in one launch, each with its own
 // part and upart blocks (token stride 64; decode_partial_bytes covers them all).
-// W: row-major [n_out][n_in], or the packed layout of pack.hip when `packed`.
+// W: row-major [n_out][n_in], or the packed layout of pack.hip when `packed`.  With many more
+// (chunk, tile, split) items than CUs the launch takes a persistent grid of one workgroup per
+// CU, unless `shared_cus` (other kernels are meant to run beside it: then the workgroups are
+// one per item, so the others' workgroups are dispatched between them).
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed, int64_t T,
                               int64_t n_in, int64_t n_out, float *part, const DecodeCfg &cfg,
                               const SlotGeom *g, const int32_t *idx, int32_t K, float *upart,
-                              hipStream_t stream);
+                              hipStream_t stream, bool shared_cus = false);
 // ---- decode_finish.hip: y = bf16(sum of the split partials + LoRA delta), T <= 64 ----------
 // part: fp32 [sk][n_tiles][T][64] (launch_decode_gemm); upart: fp32 [sk][K][T][wd] unscaled
 // shrink pieces (nullptr: base only, g unused); ysum: fp32 [T][n_out], the same sums before

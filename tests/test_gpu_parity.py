@@ -364,6 +364,29 @@ def test_decode_more_splits_than_loads_in_flight(oracle_mod, path):
         assert tol_ok(y0, y0_ref).all(), f"base: worst {worst(y0, y0_ref):.3e}"
 
 
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_decode_persistent_grid_three_chunks(oracle_mod, path):
+    """150 tokens in one decode launch (chunks of 64, 64 and 22), 4096 rows (64 row tiles) over
+    n_in = 1024 in 4 splits: 768 (chunk, tile, split) items on a persistent grid of 240
+    workgroups (each XCD holding all three chunks of 10 (split, tile-lane) pairs), each walking
+    3 or 4 row tiles.  Decode path with LoRA and the grouped decode (base only in the GEMM)
+    against the oracle."""
+    from lora_serving_amd import mlora
+    L = synth.random_layer(83, T=150, n_in=1024, n_out=4096, S=8, R=16, K=2, p_sentinel=0.2)
+    say(f"[persistent] path={path} T={L.T} n_in={L.n_in} n_out={L.n_out}")
+    flags = mlora.MLORA_PATH_DECODE if path == "decode" else mlora.MLORA_PATH_GROUPED
+    D = DevLayer(L)
+    y = from_dev_bf16(D.linear(flags=flags))
+    y_ref = oracle_mod.linear(L)
+    assert tol_ok(y, y_ref).all(), f"worst {worst(y, y_ref):.3e}"
+    if path == "decode":
+        # the base alone on the same grid (no shrink pieces)
+        import dataclasses
+        y0 = from_dev_bf16(D.linear(flags=flags | mlora.MLORA_NO_ADAPTERS))
+        y0_ref = oracle_mod.linear(dataclasses.replace(L, idx=np.full_like(L.idx, -1)))
+        assert tol_ok(y0, y0_ref).all(), f"base: worst {worst(y0, y0_ref):.3e}"
+
+
 def test_narrow_slots_at_the_limits(oracle_mod):
     """Slot width 32 with the most slots per token (8) and slices (4): the decode finish's v
     block (8 tokens x 4 slices x 32 entries, one quad a thread) and its slot loop, and the
