@@ -21,8 +21,10 @@
 //    keeping the pair's token column;
 //  - the 8 waves' partial tiles are added in LDS in a fixed order (deterministic) and the
 //    split's partial tile goes to fp32 scratch.
-// The finish kernel (decode_finish.hip) then adds the splits in order, adds the LoRA delta and
-// rounds y once.  Partial tiles are stored tile-contiguous ([split][tile][token][64 rows]) so
+// Launches with many more (chunk, tile, split) items than CUs (vocabulary-wide outputs, several
+// chunks) take a persistent variant of the same kernel (below): each workgroup keeps its x and
+// walks W.  The finish kernel (decode_finish.hip) then adds the splits in order, adds the LoRA
+// delta and rounds y once.  Partial tiles are stored tile-contiguous ([split][tile][token][64 rows]) so
 // that the finish kernel reads whole cache lines.
 #include <algorithm>
 
