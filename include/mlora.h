@@ -228,9 +228,11 @@ mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_
  *   idx, scale as in mlora_shrink.  slots may be NULL only with MLORA_NO_ADAPTERS.
  * With flags & MLORA_NO_ADAPTERS no LoRA kernel is launched (y = bf16(W x)); without it, an
  * all-sentinel map gives the same values.  T = 0 is a no-op.  By default the library picks
- * the decode kernels for small batches and the tiled kernels when the batch fills the GPU
- * with 256 x 256 output tiles.  Between them, a decode-sized batch whose per-token adapter
- * reads (each (token, slot) pair's A rows and B columns) would exceed four times W's bytes
+ * the decode kernels or the tiled kernels, whichever a host-side model of their measured
+ * rates estimates faster for the sizes (the tiled kernels from about 1536 tokens at 4096 ->
+ * 4096, 768 at 4096 -> 11008, 256 at vocabulary-wide outputs).  Where the decode kernels
+ * are picked, a batch whose per-token adapter reads (each (token, slot) pair's A rows and B
+ * columns) would exceed four times W's bytes
  * takes the grouped decode ("Multi-LoRA Serving Explained", the segmented method: tokens
  * sorted by adapter so that each adapter is read once per group): the decode kernels' base
  * product, the LoRA terms computed per adapter over its tokens.  MLORA_PATH_DECODE /

@@ -1457,10 +1457,31 @@ bool grouped_decode_worth_it(int64_t T, int32_t K, int64_t n_in, int64_t n_out, 
     return T >= 128 && gather > 4.0 * (double)n_out * n_in;
 }
 
-bool prefill_worth_it(int64_t T, int64_t n_out)
+bool prefill_worth_it(int64_t T, int64_t n_in, int64_t n_out)
 {
+    // Estimated times of the two paths (us), from their rates measured on MI355X:
+    //  decode: launches of up to 512 tokens; each takes about 6 us per round of its (64-token
+    //    chunk, 64-row tile, split) items over the CUs, 5 us more, and the split partials
+    //    written and read (8 bytes per split, token and output at about 6 TB/s);
+    //  tiled: about 125 us per round of 256 x 256 output tiles over the CUs per 4096 columns of
+    //    n_in, times 1.3 for batches whose adapters spread over many tiles (the index map is
+    //    not read here; 1.8 when a tile's fp32 sums exceed the 64 MiB kept for the per-adapter
+    //    expand, so that such tiles take the extra k-steps of all their adapters), and 25 us for
+    //    the plan, shrink and expand kernels.
+    const int64_t n_cus = device_cu_count();
+    double dec = 0.0;
+    for (int64_t t0 = 0; t0 < T; t0 += 512) {
+        const int64_t Tc = std::min<int64_t>(512, T - t0);
+        const DecodeCfg c = decode_config(Tc, n_in, n_out);
+        const int64_t items = (Tc + 63) / 64 * c.n_tiles * c.sk;
+        dec += 6.0 * (double)((items + n_cus - 1) / n_cus) + 5.0 +
+               8.0 * (double)c.sk * (double)Tc * (double)n_out / 6.0e6;
+    }
     const int64_t tiles = ((T + PF_BM - 1) / PF_BM) * ((n_out + PF_BN - 1) / PF_BN);
-    return T >= 512 && tiles >= 128;
+    const double spread = (int64_t)PF_BM * n_out * 4 > (64ll << 20) ? 1.8 : 1.3;
+    const double til =
+        spread * 125.0 * ((double)n_in / 4096.0) * (double)((tiles + n_cus - 1) / n_cus) + 25.0;
+    return til < dec;
 }
 
 // The tiled path's workspace regions of one call.
