@@ -617,12 +617,13 @@ mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in
             void *wpre = wsb + off_pre;
             // the tile plan and the group shrink on the side stream, forked before the GEMM is
             // enqueued and joined before the expand; the GEMM's launch goes in first so that
-            // its workgroups are dispatched from the start (the no-allocation variant creates
-            // nothing and runs all of it on the caller's stream)
+            // its workgroups are dispatched from the start.  When the GEMM takes the persistent
+            // grid (every CU until it ends, nothing to run beside it) all of it goes on the
+            // caller's stream in order, as in the no-allocation variant, which creates nothing
             std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
             SideStream *ss = nullptr;
             hipError_t e = hipSuccess;
-            if (!noalloc) {
+            if (!noalloc && !decode_gemm_persistent(Tc, n_in, n_out)) {
                 lk.lock();
                 e = side_stream(stream, &ss);
                 if (e == hipSuccess && ss != nullptr)

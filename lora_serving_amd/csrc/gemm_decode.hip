@@ -626,6 +626,29 @@ size_t decode_partial_bytes(int64_t T, int64_t n_in, int64_t n_out)
     return (size_t)n_chunks * c.sk * c.n_tiles * (size_t)per * DEC_ROWS * sizeof(float);
 }
 
+// When the launch takes the persistent grid (decode_gemm_ps_kernel): one chunk with at least
+// twice as many (tile, split) items as CUs; several chunks when every XCD can hold all chunks of
+// whole (split, tile-lane) groups and each workgroup walks at least two tiles.
+static bool ps_one_chunk(const DecodeCfg &c)
+{
+    const int n_cus = device_cu_count();
+    return (int64_t)c.n_tiles * c.sk >= 2 * (int64_t)n_cus && c.sk <= n_cus;
+}
+
+static bool ps_several_chunks(int n_chunks, const DecodeCfg &c)
+{
+    const int per_xcd = (device_cu_count() / 8) / n_chunks;
+    const int n_pairs_sl = 8 * per_xcd;
+    return per_xcd >= 1 && n_pairs_sl % c.sk == 0 && c.n_tiles >= 2 * (n_pairs_sl / c.sk);
+}
+
+bool decode_gemm_persistent(int64_t T, int64_t n_in, int64_t n_out)
+{
+    const DecodeCfg c = decode_config(T, n_in, n_out);
+    const int n_chunks = (int)((T + DEC_CHUNK - 1) / DEC_CHUNK);
+    return n_chunks > 1 ? (c.tt == 4 && ps_several_chunks(n_chunks, c)) : ps_one_chunk(c);
+}
+
 template <int TT, bool PW, bool MC>
 static hipError_t launch_tfm(DecodeArgs &a, const DecodeCfg &c, hipStream_t stream)
 {
@@ -648,8 +671,7 @@ static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, bool shared_cus, 
             const int n_cus = device_cu_count();
             const int per_xcd = (n_cus / 8) / a.n_chunks;          // (s, l) pairs per XCD
             const int n_pairs_sl = 8 * per_xcd;
-            if (!shared_cus && per_xcd >= 1 && n_pairs_sl % c.sk == 0 &&
-                c.n_tiles >= 2 * (n_pairs_sl / c.sk)) {
+            if (!shared_cus && ps_several_chunks(a.n_chunks, c)) {
                 const size_t lds = (size_t)DEC_WAVES * 4 * TT * 64 * sizeof(float4);
                 if (hipError_t e =
                         ensure_dynamic_lds((const void *)decode_gemm_ps_kernel<TT, PW, true>, lds);
@@ -665,7 +687,7 @@ static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, bool shared_cus, 
     }
     // one chunk with at least twice as many (tile, split) items as CUs: the persistent grid
     const int n_cus = device_cu_count();
-    if (!shared_cus && (int64_t)c.n_tiles * c.sk >= 2 * (int64_t)n_cus && c.sk <= n_cus) {
+    if (!shared_cus && ps_one_chunk(c)) {
         const size_t lds = (size_t)DEC_WAVES * 4 * TT * 64 * sizeof(float4);
         if (hipError_t e = ensure_dynamic_lds((const void *)decode_gemm_ps_kernel<TT, PW, false>, lds);
             e != hipSuccess)

@@ -73,6 +73,8 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed,
                               int64_t n_in, int64_t n_out, float *part, const DecodeCfg &cfg,
                               const SlotGeom *g, const int32_t *idx, int32_t K, float *upart,
                               hipStream_t stream, bool shared_cus = false);
+// Whether launch_decode_gemm takes the persistent grid for these sizes (without shared_cus).
+bool decode_gemm_persistent(int64_t T, int64_t n_in, int64_t n_out);
 // ---- decode_finish.hip: y = bf16(sum of the split partials + LoRA delta), T <= 64 ----------
 // part: fp32 [sk][n_tiles][T][64] (launch_decode_gemm); upart: fp32 [sk][K][T][wd] unscaled
 // shrink pieces (nullptr: base only, g unused); ysum: fp32 [T][n_out], the same sums before
