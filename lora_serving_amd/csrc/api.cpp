@@ -638,9 +638,8 @@ mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in
                     return hip_status(e, "grouped shrink launch");
             }
             trace_mark(stream, true);
-            // with the side stream, the GEMM leaves room for its kernels between workgroups
             e = launch_decode_gemm(xb + t0 * n_in, (const uint16_t *)W, packed, Tc, n_in, n_out,
-                                   part, cfg, nullptr, nullptr, K, nullptr, stream, ss != nullptr);
+                                   part, cfg, nullptr, nullptr, K, nullptr, stream);
             trace_mark(stream, false);
             if (e != hipSuccess)
                 return hip_status(e, "decode gemm launch");

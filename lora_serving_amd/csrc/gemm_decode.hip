@@ -662,7 +662,7 @@ static hipError_t launch_tfm(DecodeArgs &a, const DecodeCfg &c, hipStream_t stre
 }
 
 template <int TT, bool PW>
-static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, bool shared_cus, hipStream_t stream)
+static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, hipStream_t stream)
 {
     if constexpr (TT == 4) {   // only full 64-token chunks come before the last one
         if (a.n_chunks > 1) {
@@ -671,7 +671,7 @@ static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, bool shared_cus, 
             const int n_cus = device_cu_count();
             const int per_xcd = (n_cus / 8) / a.n_chunks;          // (s, l) pairs per XCD
             const int n_pairs_sl = 8 * per_xcd;
-            if (!shared_cus && ps_several_chunks(a.n_chunks, c)) {
+            if (ps_several_chunks(a.n_chunks, c)) {
                 const size_t lds = (size_t)DEC_WAVES * 4 * TT * 64 * sizeof(float4);
                 if (hipError_t e =
                         ensure_dynamic_lds((const void *)decode_gemm_ps_kernel<TT, PW, true>, lds);
@@ -687,7 +687,7 @@ static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, bool shared_cus, 
     }
     // one chunk with at least twice as many (tile, split) items as CUs: the persistent grid
     const int n_cus = device_cu_count();
-    if (!shared_cus && ps_one_chunk(c)) {
+    if (ps_one_chunk(c)) {
         const size_t lds = (size_t)DEC_WAVES * 4 * TT * 64 * sizeof(float4);
         if (hipError_t e = ensure_dynamic_lds((const void *)decode_gemm_ps_kernel<TT, PW, false>, lds);
             e != hipSuccess)
@@ -702,7 +702,7 @@ static hipError_t launch_tf(DecodeArgs &a, const DecodeCfg &c, bool shared_cus, 
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed, int64_t T,
                               int64_t n_in, int64_t n_out, float *part, const DecodeCfg &c,
                               const SlotGeom *g, const int32_t *idx, int32_t K, float *upart,
-                              hipStream_t stream, bool shared_cus)
+                              hipStream_t stream)
 {
     DecodeArgs a{};
     a.x = x;
@@ -725,12 +725,12 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed,
     a.n_rg = (int)((n_out + 15) / 16);
     a.n_kb = (int)((n_in + 31) / 32);
     switch (c.tt * 2 + (packed ? 1 : 0)) {
-    case 2: return launch_tf<1, false>(a, c, shared_cus, stream);
-    case 3: return launch_tf<1, true>(a, c, shared_cus, stream);
-    case 4: return launch_tf<2, false>(a, c, shared_cus, stream);
-    case 5: return launch_tf<2, true>(a, c, shared_cus, stream);
-    case 8: return launch_tf<4, false>(a, c, shared_cus, stream);
-    case 9: return launch_tf<4, true>(a, c, shared_cus, stream);
+    case 2: return launch_tf<1, false>(a, c, stream);
+    case 3: return launch_tf<1, true>(a, c, stream);
+    case 4: return launch_tf<2, false>(a, c, stream);
+    case 5: return launch_tf<2, true>(a, c, stream);
+    case 8: return launch_tf<4, false>(a, c, stream);
+    case 9: return launch_tf<4, true>(a, c, stream);
     default: return hipErrorInvalidValue;
     }
 }

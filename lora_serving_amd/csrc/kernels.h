@@ -67,13 +67,12 @@ size_t decode_partial_bytes(int64_t T, int64_t n_in, int64_t n_out);
 // part and upart blocks (token stride 64; decode_partial_bytes covers them all).
 // W: row-major [n_out][n_in], or the packed layout of pack.hip when `packed`.  With many more
 // (chunk, tile, split) items than CUs the launch takes a persistent grid of one workgroup per
-// CU, unless `shared_cus` (other kernels are meant to run beside it: then the workgroups are
-// one per item, so the others' workgroups are dispatched between them).
+// CU (decode_gemm_persistent), which holds every CU until it ends.
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed, int64_t T,
                               int64_t n_in, int64_t n_out, float *part, const DecodeCfg &cfg,
                               const SlotGeom *g, const int32_t *idx, int32_t K, float *upart,
-                              hipStream_t stream, bool shared_cus = false);
-// Whether launch_decode_gemm takes the persistent grid for these sizes (without shared_cus).
+                              hipStream_t stream);
+// Whether launch_decode_gemm takes the persistent grid for these sizes.
 bool decode_gemm_persistent(int64_t T, int64_t n_in, int64_t n_out);
 // ---- decode_finish.hip: y = bf16(sum of the split partials + LoRA delta), T <= 64 ----------
 // part: fp32 [sk][n_tiles][T][64] (launch_decode_gemm); upart: fp32 [sk][K][T][wd] unscaled
