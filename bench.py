@@ -413,6 +413,27 @@ def trace_kernel(P: Prepared, steps: int, only_layer=None):
     return ks
 
 
+def decode_gemm_name(T, n_in, n_out, n_cus=256):
+    """Name of the decode GEMM kernel the library launches for one launch of up to 512 tokens:
+    the persistent grid (decode_gemm_ps_kernel) when there are many more (chunk, tile, split)
+    items than CUs, by the same conditions as the library's launcher (label only)."""
+    Tc = min(T, 512)
+    n_tiles = -(-n_out // 64)
+    wblocks = -(-n_in // 128)
+    per = 8
+    while per > 1 and n_tiles * (-(-wblocks // per)) < n_cus:
+        per //= 2
+    sk = -(-n_in // (per * 128))
+    n_chunks = -(-Tc // 64)
+    if n_chunks > 1:
+        per_xcd = (n_cus // 8) // n_chunks
+        pairs = 8 * per_xcd
+        ps = per_xcd >= 1 and pairs % sk == 0 and n_tiles >= 2 * (pairs // sk)
+    else:
+        ps = n_tiles * sk >= 2 * n_cus and sk <= n_cus
+    return "mlora::decode_gemm_ps_kernel" if ps else "mlora::decode_gemm_kernel"
+
+
 def linear_roofline(P: Prepared, kernel_ms, only_layer=None):
     """Roofline object of the main product kernel of mlora_linear: the decode GEMM against HBM
     (algorithmic bytes per launch) or the tiled GEMM against the bf16 MFMA peak (algorithmic
@@ -428,9 +449,12 @@ def linear_roofline(P: Prepared, kernel_ms, only_layer=None):
         achieved = k_bytes / (k_avg_ms * 1e-3) / 1e9
         what = ("base product (grouped decode: the LoRA terms in the group kernels)"
                 if all(p == "grouped" for p in paths) else "base product + LoRA shrink")
+        import torch
+        L0 = P.layers[idxs[0]]
+        n_cus = torch.cuda.get_device_properties(0).multi_processor_count
         return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                "kernel": f"mlora::decode_gemm_kernel ({what})",
+                "kernel": f"{decode_gemm_name(L0.T, L0.n_in, L0.n_out, n_cus)} ({what})",
                 "kernel_avg_us": k_avg_ms * 1e3, "algorithmic_bytes_per_launch": k_bytes}
     k_flops = sum(a["tiled_kernel_flops"] for a in algs) / per_step
     achieved = k_flops / (k_avg_ms * 1e-3) / 1e12
