@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
                 for (int i = 0; i < n; ++i)
                     w[i >> 2] |= (uint32_t)tok[o + i] << ((i & 3) * 8);
                 const int gi = g0 + (o - o0) / 16;
-                grp[2 * gi] = int4{d, lst[d], o, n};
+                grp[2 * gi] = int4{d, lst[d], o, n | (r8[lst[d]] << 8)};
                 grp[2 * gi + 1] = int4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
             }
         }
@@ -541,11 +541,12 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
     const int gidx = local / RB, rb = local - gidx * RB;
     const int D = P.tile_D[m];
     const int4 *rec = P.tile_grp + ((int64_t)m * P.grp_stride + gidx) * 2;
-    const int4 gr = rec[0], gt = rec[1];   // {d, adapter, first entry, tokens}, token bytes
-    const int d = gr.x, a = gr.y, ng = gr.w;
+    // {d, adapter, first entry, tokens | adapter's rank rounded to 8 << 8}, token bytes
+    const int4 gr = rec[0], gt = rec[1];
+    const int d = gr.x, a = gr.y, ng = gr.w & 0xff;
     // rows past the adapter's rank (zero padding) are neither read nor multiplied: their
     // fragments come from the zero block, and a block with no row below the rank skips the loop
-    const int rk = slot_rank8(g.rank, a, R);
+    const int rk = gr.w >> 8;
     const uint16_t *ap[2];
     bool aok[2];
 #pragma unroll
@@ -1224,7 +1225,15 @@ __device__ __forceinline__ int sc_slice(const SlotGeom &g, int n)
     return sg;
 }
 
-__device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int m, int local)
+// The group record of an item: (tile m, group local / n_chunks).
+__device__ __forceinline__ const int4 *sc_record(const ScArgs &P, int m, int local)
+{
+    return P.tile_grp + ((int64_t)m * P.grp_stride + local / P.n_chunks) * 2;
+}
+
+// gr, gt: the item's group record (loaded by the caller, ahead of the item)
+__device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int m, int local,
+                                               const int4 gr, const int4 gt)
 {
     const SlotGeom &g = P.g;
     const int R = g.R;
@@ -1235,9 +1244,8 @@ __device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int m, 
     if (n0 >= P.n_out)
         return;
     const int D = P.tile_D[m];
-    const int4 *rec = P.tile_grp + ((int64_t)m * P.grp_stride + gidx) * 2;
-    const int4 gr = rec[0], gt = rec[1];   // {d, adapter, first entry, tokens}, token bytes
-    const int d = gr.x, a = gr.y, ng = gr.w;
+    // {d, adapter, first entry, tokens | adapter's rank rounded to 8 << 8}, token bytes
+    const int d = gr.x, a = gr.y, ng = gr.w & 0xff;
     const bool tok_ok = r < ng;
     const int tl = tok_ok ? grp_token(gt, r) : 0;
     const int t = m * PF_BM + tl;
@@ -1261,7 +1269,7 @@ __device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int m, 
     }
     const bool act = tok_ok && below == P.pass;
     const bool last = below == n_dist - 1;
-    const int rk = slot_rank8(g.rank, a, R);
+    const int rk = gr.w >> 8;
 
     const int VW = P.tile_w[m];
     const int kxs = ((D * 2 * VW + PF_BK - 1) / PF_BK) * PF_BK;
@@ -1372,8 +1380,9 @@ __global__ __launch_bounds__(256) void sc_expand_kernel(ScArgs P)
         sc_m[o] = P.sc_tiles[o];
     }
     __syncthreads();
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        int lo = 0, hi = n_sc - 1;            // scattered tile: last o with sc_pre[o] <= item
+    // scattered tile of an item: last o with sc_pre[o] <= item
+    auto find = [&](int item) {
+        int lo = 0, hi = n_sc - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (sc_pre[mid] <= item)
@@ -1381,7 +1390,33 @@ __global__ __launch_bounds__(256) void sc_expand_kernel(ScArgs P)
             else
                 hi = mid - 1;
         }
-        sc_expand_item(P, lo, sc_m[lo], item - sc_pre[lo]);
+        return lo;
+    };
+    // each item's group record is loaded one item ahead, so that an item's first dependent
+    // round trip overlaps the previous item
+    int item = blockIdx.x;
+    if (item >= total)
+        return;
+    int o = find(item);
+    const int4 *rec = sc_record(P, sc_m[o], item - sc_pre[o]);
+    int4 gr = rec[0], gt = rec[1];
+    while (true) {
+        const int next = item + gridDim.x;
+        int on = 0;
+        int4 grn = gr, gtn = gt;
+        if (next < total) {
+            on = find(next);
+            const int4 *rn = sc_record(P, sc_m[on], next - sc_pre[on]);
+            grn = rn[0];
+            gtn = rn[1];
+        }
+        sc_expand_item(P, o, sc_m[o], item - sc_pre[o], gr, gt);
+        if (next >= total)
+            break;
+        item = next;
+        o = on;
+        gr = grn;
+        gt = gtn;
     }
 }
 
