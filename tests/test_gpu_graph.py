@@ -1,8 +1,9 @@
 """HIP graph capture of the library's calls.
 
 A serving loop captures its decode steps in a graph so that the host's cost per call is paid
-once per replay.  mlora_linear (decode path; grouped decode; tiled path with stacked and with
-scattered tiles), the mlora_shrink / mlora_expand pair and mlora_plan are captured together on torch's
+once per replay.  mlora_linear (decode path, also on its persistent grid; grouped decode, with
+its side stream and on the caller's stream alone; tiled path with stacked and with scattered
+tiles), the mlora_shrink / mlora_expand pair and mlora_plan are captured together on torch's
 capture stream, then the graph is replayed several times with the program's own eager work
 and synchronizations between the replays; every replay must reproduce the eager results bit
 for bit (the kernels are deterministic, and no call allocates memory or records a memset).
@@ -40,20 +41,27 @@ def test_graph_replays_match_eager():
     # tokens spread over 40 adapters: scattered tiles (per-adapter shrink items, one expand
     # launch per slot after the GEMM)
     Ls = synth.random_layer(83, T=300, n_in=256, n_out=512, S=40, R=16, K=3, p_sentinel=0.2)
-    say(f"[graph] decode T={Ld.T} {Ld.n_in}->{Ld.n_out}, tiled T={Lt.T} {Lt.n_in}->{Lt.n_out}")
-    Dd, Dt, Ds = DevLayer(Ld), DevLayer(Lt), DevLayer(Ls)
+    # three 64-token chunks over 64 row tiles: the decode GEMM's persistent grid, and the
+    # grouped decode with all its kernels on the caller's stream
+    Lp = synth.random_layer(84, T=150, n_in=1024, n_out=4096, S=8, R=16, K=2, p_sentinel=0.2)
+    say(f"[graph] decode T={Ld.T} {Ld.n_in}->{Ld.n_out}, tiled T={Lt.T} {Lt.n_in}->{Lt.n_out}, "
+        f"persistent T={Lp.T} {Lp.n_in}->{Lp.n_out}")
+    Dd, Dt, Ds, Dp = DevLayer(Ld), DevLayer(Lt), DevLayer(Ls), DevLayer(Lp)
     dev = Dd.device
     bf = torch.bfloat16
     yd = torch.empty((Ld.T, Ld.n_out), dtype=bf, device=dev)
     yt = torch.empty((Lt.T, Lt.n_out), dtype=bf, device=dev)
     ys = torch.empty((Ls.T, Ls.n_out), dtype=bf, device=dev)
     yg = torch.empty((Ld.T, Ld.n_out), dtype=bf, device=dev)
+    yp = torch.empty((Lp.T, Lp.n_out), dtype=bf, device=dev)
+    ypg = torch.empty((Lp.T, Lp.n_out), dtype=bf, device=dev)
     v = torch.empty((Ld.K, Ld.T, Ld.n_slices * Ld.R), dtype=torch.float32, device=dev)
     y_base = torch.randn((Ld.T, Ld.n_out), device=dev).to(bf)      # expand accumulates onto it
     ye = torch.empty_like(y_base)
     i32 = lambda n: torch.empty((n,), dtype=torch.int32, device=dev)
     perm, ss, st, sl, cnt = i32(Ld.T * Ld.K), i32(Ld.S), i32(Ld.S), i32(Ld.S), i32(2)
-    outs = [yd, yt, ys, yg, v, ye, perm, ss, st, sl, cnt]
+    outs = [yd, yt, ys, yg, yp, ypg, v, ye, perm, ss, st, sl, cnt]
+    names = ["yd", "yt", "ys", "yg", "yp", "ypg", "v", "ye", "perm", "ss", "st", "sl", "cnt"]
 
     def work():
         mlora.mlora_linear(Dd.x, Dd.W, Dd.slots, Dd.idx, Dd.scale, yd,
@@ -64,6 +72,10 @@ def test_graph_replays_match_eager():
                            flags=mlora.MLORA_PATH_TILED, ws=Ds.ws)
         mlora.mlora_linear(Dd.x, Dd.W, Dd.slots, Dd.idx, Dd.scale, yg,
                            flags=mlora.MLORA_PATH_GROUPED, ws=Dd.ws)
+        mlora.mlora_linear(Dp.x, Dp.W, Dp.slots, Dp.idx, Dp.scale, yp,
+                           flags=mlora.MLORA_PATH_DECODE, ws=Dp.ws)
+        mlora.mlora_linear(Dp.x, Dp.W, Dp.slots, Dp.idx, Dp.scale, ypg,
+                           flags=mlora.MLORA_PATH_GROUPED, ws=Dp.ws)
         mlora.mlora_shrink(Dd.x, Dd.slots, Dd.idx, Dd.scale, v, ws=Dd.ws)
         torch.mul(y_base, 1.0, out=ye)         # a kernel, not a copy or memset node
         mlora.mlora_expand(v, Dd.slots, Dd.idx, ye)
@@ -103,7 +115,7 @@ def test_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         say(f"[graph] replay {rep}")
-        for name, t, r in zip(["yd", "yt", "ys", "v", "ye", "perm", "ss", "st", "sl", "cnt"],
-                              outs, ref):
+        assert len(names) == len(outs) == len(ref)
+        for name, t, r in zip(names, outs, ref):
             assert torch.equal(bits(t), bits(r)), f"replay {rep}: {name} differs from eager"
     assert int(cnt[1].item()) == int(np.count_nonzero(Ld.idx >= 0))
