@@ -4,6 +4,7 @@ Acceptance (floating point): |y - y_ref| <= 2e-2 (1 + |y_ref|) elementwise, on t
 and on the LoRA delta alone (shrink, then expand into a zero y), so a wrong delta cannot hide
 under a large W x.  The mapping plan must match bit-exactly.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -553,6 +554,45 @@ def test_tiled_many_tiles_shrink_stages(oracle_mod, n_tiles, extra):
                               np.int64))
     y_ref = oracle_mod.linear(L, tokens=toks)
     assert tol_ok(y[toks], y_ref).all(), f"worst {worst(y[toks], y_ref):.3e}"
+
+
+DENSE_SPLITS = [
+    # n_tiles, extra tokens, n_in, R: parts of n_in (ks) the dense shrink takes
+    (2, 0, 1024, 16),     # ks 4 (n_in / 256)
+    (3, 0, 256, 8),       # ks 1: V written by the items themselves
+    (100, 0, 512, 16),    # ks 2 (256 items over 100 row blocks, at most n_in / 256)
+    (100, 77, 256, 8),    # ks 1, ragged last tile
+    (180, 0, 512, 16),    # ks 2
+]
+
+
+@pytest.mark.parametrize("n_tiles,extra,n_in,R", DENSE_SPLITS,
+                         ids=[f"{c[0]}x{c[2]}r{c[3]}+{c[1]}" for c in DENSE_SPLITS])
+def test_tiled_dense_shrink_splits(oracle_mod, n_tiles, extra, n_in, R):
+    """The dense shrink splits n_in into ks parts (about 256 items over the tiles' 128-row
+    blocks, at most n_in / 256 parts) and adds the parts' fp32 blocks in order in the reduce;
+    with ks = 1 the items write V themselves.  Every tile here has one row block (at most 6
+    adapters of width 8 or 16), so the tile count and n_in pick ks.  Tokens at the 64-token
+    boundaries of the first, second, middle and last tiles are checked against the oracle, on
+    the layer and on the LoRA delta alone (the same layer with W = 0)."""
+    from lora_serving_amd import mlora
+    T = n_tiles * 256 + extra
+    L = synth.random_layer(1300 + n_tiles + n_in + extra, T=T, n_in=n_in, n_out=96, S=6, R=R,
+                           K=1, p_sentinel=0.25, contiguous=True)
+    say(f"[dense split] T={T} tiles={-(-T // 256)} n_in={n_in} R={R}")
+    D = DevLayer(L)
+    y = from_dev_bf16(D.linear(flags=mlora.MLORA_PATH_TILED))
+    offs = np.array([0, 1, 63, 64, 65, 127, 128, 191, 192, 254, 255], np.int64)
+    tiles = np.array([0, 1, n_tiles // 2, -(-T // 256) - 1], np.int64)
+    toks = np.unique(np.clip((tiles[:, None] * 256 + offs[None, :]).ravel(), 0, T - 1))
+    y_ref = oracle_mod.linear(L, tokens=toks)
+    assert tol_ok(y[toks], y_ref).all(), f"worst {worst(y[toks], y_ref):.3e}"
+    # the same layer with W = 0: the tiled kernels' LoRA delta alone, which a large W x could hide
+    L0 = dataclasses.replace(L, W=np.zeros_like(L.W))
+    d = from_dev_bf16(DevLayer(L0).linear(flags=mlora.MLORA_PATH_TILED))
+    d_ref = oracle_mod.linear(L, tokens=toks, with_base=False)
+    assert tol_ok(d[toks], d_ref).all(), f"delta worst {worst(d[toks], d_ref):.3e}"
+    assert np.any(d_ref != 0)
 
 
 def test_tiled_sentinel_rows_and_k3_invariance():
