@@ -211,6 +211,7 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
         int32_t *toff = tile_toff + (int64_t)m * (list_stride + 1);
         int32_t *gpre = tile_gpre + (int64_t)m * (list_stride + 1);
         int obase = 0, gbase = 0;
+        int my_o0 = 0, my_o1 = 0, my_g0 = 0;     // list range and first group of adapter tid
         for (int d0 = 0; d0 < D; d0 += blockDim.x) {
             const int d = d0 + threadIdx.x;
             const int c = d < D ? cnt[lst[d]] : 0;
@@ -220,6 +221,11 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
                 toff[d] = obase + oex;
                 gpre[d] = gbase + gex;
                 cnt[lst[d]] = obase + oex;        // now the next free place of adapter lst[d]
+                if (d0 == 0) {
+                    my_o0 = obase + oex;
+                    my_o1 = my_o0 + c;
+                    my_g0 = gbase + gex;
+                }
             }
             obase += oall;
             gbase += gall;
@@ -236,7 +242,11 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
         __syncthreads();                          // the lists complete
         int4 *grp = tile_grp + (int64_t)m * grp_stride * 2;
         for (int d = threadIdx.x; d < D; d += blockDim.x) {
-            const int o0 = toff[d], o1 = toff[d + 1], g0 = gpre[d];
+            // the first 256 adapters' ranges are still in registers; the rest are read back
+            // (the stores above are this workgroup's own, ordered by the barrier)
+            const bool mine = d == (int)threadIdx.x;
+            const int o0 = mine ? my_o0 : toff[d], o1 = mine ? my_o1 : toff[d + 1];
+            const int g0 = mine ? my_g0 : gpre[d];
             for (int o = o0; o < o1; o += 16) {
                 const int n = min(16, o1 - o);
                 uint32_t w[4] = {0u, 0u, 0u, 0u};
