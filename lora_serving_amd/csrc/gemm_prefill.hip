@@ -111,10 +111,11 @@ __device__ __forceinline__ void block_scan2(int v1, int v2, int *ws, int &ex1, i
 // One workgroup of 256 threads per tile.  For a scattered tile it also lists, per adapter of
 // the tile (list order), the tile-local tokens that use it (entries toff[d] .. toff[d+1] of the
 // tile's list, built in LDS), in groups of 16 numbered by gpre[d] = sum over d' < d of
-// ceil(count / 16), and writes one record per group: {position d, adapter, first list entry,
-// tokens}, then the group's up to 16 tile-local token numbers as bytes, so that a consumer has
-// the group's tokens after one load.  The order of the tokens inside a list is whatever the
-// atomics give; each token's results do not depend on it.
+// ceil(count / 16), and writes one record per group: {position d, adapter, the tile's V
+// columns per slice, tokens | the adapter's rank rounded to 8 << 8 | log2 of the tile's V width
+// << 20}, then the group's up to 16 tile-local token numbers as bytes, so that a consumer has
+// the group's tokens and where its V goes after one load.  The order of the tokens inside a
+// list is whatever the atomics give; each token's results do not depend on it.
 static_assert(PF_BM == 256, "tile_plan_kernel: one thread per token of a tile");
 __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restrict__ idx, int T,
                                                         int K, int S, int R, int n_slices, int n_in,
@@ -241,6 +242,10 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
                 tok[atomicAdd(&cnt[ids[j]], 1)] = (uint8_t)tl;
         __syncthreads();                          // the lists complete
         int4 *grp = tile_grp + (int64_t)m * grp_stride * 2;
+        // the tile's V block geometry goes into every record, so that a consumer needs no
+        // other load before its V reads: columns per slice, and log2 of the V width
+        const int kxs = ((D * 2 * VW + PF_BK - 1) / PF_BK) * PF_BK;
+        const int lvw = 31 - __clz(VW);
         for (int d = threadIdx.x; d < D; d += blockDim.x) {
             // the first 256 adapters' ranges are still in registers; the rest are read back
             // (the stores above are this workgroup's own, ordered by the barrier)
@@ -253,7 +258,7 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
                 for (int i = 0; i < n; ++i)
                     w[i >> 2] |= (uint32_t)tok[o + i] << ((i & 3) * 8);
                 const int gi = g0 + (o - o0) / 16;
-                grp[2 * gi] = int4{d, lst[d], o, n | (r8[lst[d]] << 8)};
+                grp[2 * gi] = int4{d, lst[d], kxs, n | (r8[lst[d]] << 8) | (lvw << 20)};
                 grp[2 * gi + 1] = int4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
             }
         }
@@ -549,14 +554,14 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
     const int r = lane & 15, gq = lane >> 4;
     const int RB = (wd + SG_ROWS - 1) / SG_ROWS;
     const int gidx = local / RB, rb = local - gidx * RB;
-    const int D = P.tile_D[m];
     const int4 *rec = P.tile_grp + ((int64_t)m * P.grp_stride + gidx) * 2;
-    // {d, adapter, first entry, tokens | adapter's rank rounded to 8 << 8}, token bytes
+    // {d, adapter, V columns per slice, tokens | rank rounded to 8 << 8 | log2 VW << 20},
+    // then the token bytes
     const int4 gr = rec[0], gt = rec[1];
     const int d = gr.x, a = gr.y, ng = gr.w & 0xff;
     // rows past the adapter's rank (zero padding) are neither read nor multiplied: their
     // fragments come from the zero block, and a block with no row below the rank skips the loop
-    const int rk = gr.w >> 8;
+    const int rk = (gr.w >> 8) & 0xfff;
     const uint16_t *ap[2];
     bool aok[2];
 #pragma unroll
@@ -600,8 +605,7 @@ __device__ __forceinline__ void sh_group_item(const ShrinkArgs &P, int m, int lo
     if (j < ng) {
         const int tl = grp_token(gt, j);
         const float cf = sh_coef(P, m * PF_BM + tl, a);
-        const int VW = P.tile_w[m];
-        const int kxs = ((D * 2 * VW + PF_BK - 1) / PF_BK) * PF_BK;
+        const int VW = 1 << (gr.w >> 20), kxs = gr.z;
         uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems + (int64_t)tl * (g.n_slices * kxs) +
                          d * 2 * VW;
 #pragma unroll
@@ -1253,8 +1257,8 @@ __device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int m, 
     const int n0 = nc * SC_ROWS + wave * 64;
     if (n0 >= P.n_out)
         return;
-    const int D = P.tile_D[m];
-    // {d, adapter, first entry, tokens | adapter's rank rounded to 8 << 8}, token bytes
+    // {d, adapter, V columns per slice, tokens | rank rounded to 8 << 8 | log2 VW << 20},
+    // then the token bytes
     const int d = gr.x, a = gr.y, ng = gr.w & 0xff;
     const bool tok_ok = r < ng;
     const int tl = tok_ok ? grp_token(gt, r) : 0;
@@ -1279,10 +1283,8 @@ __device__ __forceinline__ void sc_expand_item(const ScArgs &P, int ord, int m, 
     }
     const bool act = tok_ok && below == P.pass;
     const bool last = below == n_dist - 1;
-    const int rk = gr.w >> 8;
-
-    const int VW = P.tile_w[m];
-    const int kxs = ((D * 2 * VW + PF_BK - 1) / PF_BK) * PF_BK;
+    const int rk = (gr.w >> 8) & 0xfff;
+    const int VW = 1 << (gr.w >> 20), kxs = gr.z;
     const uint16_t *vrow = P.vcat + (int64_t)m * P.vcat_tile_elems + (int64_t)tl * (g.n_slices * kxs) +
                            d * 2 * VW + gq * 8;
     const uint16_t *brow0 = g.B + (int64_t)a * P.n_out * R + gq * 8;
