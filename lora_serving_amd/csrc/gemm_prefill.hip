@@ -1385,9 +1385,11 @@ __global__ __launch_bounds__(256) void sc_expand_kernel(ScArgs P)
     // the scattered tiles and their first items (numbered by sgmv_shrink_kernel), in LDS
     extern __shared__ int sc_pre[];           // [sc_cap] item prefix, then [sc_cap] tiles
     int *sc_m = sc_pre + P.sc_cap;
+    // the tables are read whole (sc_cap entries; those past the scattered tiles' count are
+    // never used), in the same round trip as the counts
     const int n_sc = P.sc_tiles[P.sc_cap];
     const int total = P.sc_pre[P.sc_cap];
-    for (int o = threadIdx.x; o < n_sc; o += 256) {
+    for (int o = threadIdx.x; o < P.sc_cap; o += 256) {
         sc_pre[o] = P.sc_pre[o];
         sc_m[o] = P.sc_tiles[o];
     }
