@@ -517,6 +517,28 @@ def test_limits_rank_slots_slices(oracle_mod, path):
     assert tol_ok(y, y_ref).all(), f"worst {worst(y, y_ref):.3e}"
 
 
+@pytest.mark.parametrize("path", ["decode", "tiled", "grouped"])
+def test_limits_most_slots(oracle_mod, path):
+    """The most resident slots (S = 16384) with K = 8 slots a token: the tile plan then holds a
+    16384-bit adapter map, 16384 counts and ranks and a 2048-entry list in LDS (140 KB of its
+    160).  Slot ids are drawn over the whole range; the layer, and the delta of the standalone
+    shrink/expand pair, are checked against the oracle."""
+    from lora_serving_amd import mlora
+    S = 16384
+    L = synth.random_layer(73, T=64 if path == "decode" else 300, n_in=64, n_out=96, S=S, R=8,
+                           K=8, p_sentinel=0.2, contiguous=(path == "tiled"))
+    assert L.idx.max() > S - 2000   # ids near the top of the range occur
+    say(f"[most slots] path={path} T={L.T} S={S} K={L.K}")
+    flags = {"decode": mlora.MLORA_PATH_DECODE, "tiled": mlora.MLORA_PATH_TILED,
+             "grouped": mlora.MLORA_PATH_GROUPED}[path]
+    D = DevLayer(L)
+    y = from_dev_bf16(D.linear(flags=flags))
+    y_ref = oracle_mod.linear(L)
+    assert tol_ok(y, y_ref).all(), f"worst {worst(y, y_ref):.3e}"
+    if path == "decode":
+        check_delta(oracle_mod, L, D, label="most slots")
+
+
 def test_tiled_path_chunks_past_a_million_tokens(oracle_mod):
     """More tokens than one tiled launch takes (4096 tiles of 256): the batch is cut in chunks;
     tokens on both sides of the cut and the ragged end are checked against the oracle."""
