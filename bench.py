@@ -51,6 +51,10 @@ DESCRIPTIONS = {
                "rank 16 alpha 32, 6 tokens base-only, K=1",
     "mixed_qkv_decode": "mixed_qkv_decode: the mixed batch's 256 one-token requests alone, merged "
                         "QKV 4096->(4096,1024,1024), 64 adapters ranks {8,16,64} padded to 64",
+    "decode_tp8_col": "decode_tp8_col: one GPU's share of the decode layer under 8-way column "
+                      "parallelism, 4096->512 (its rows of W and B), T=64, 100 adapters rank 16",
+    "decode_tp8_row": "decode_tp8_row: one GPU's share of the decode layer under 8-way row "
+                      "parallelism, 512->4096 (its columns of W, A, x), T=64, 100 adapters rank 16",
 }
 # the workloads of the `configs` list, in this order, when the headline is the decode batch
 CONFIG_ORDER = ["tiny", "prefill", "mixed_qkv", "compose"]

@@ -653,7 +653,7 @@ mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in
                 if (e != hipSuccess)
                     return hip_status(e, "grouped shrink launch");
             }
-            e = launch_decode_finish(part, cfg.sk, cfg.n_tiles, nullptr, nullptr, Tc, n_out,
+            e = launch_decode_finish(part, cfg.sk, cfg.n_tiles, nullptr, 0, nullptr, Tc, n_out,
                                      nullptr, nullptr, 1, yb + t0 * n_out,
                                      grouped_base_sums(pc, wpre), stream);
             if (e != hipSuccess)
@@ -668,16 +668,27 @@ mlora_status linear_common(const void *x, const void *W, int64_t T, int64_t n_in
                 return hip_status(e, "grouped expand launch");
             continue;
         }
+        // the shrink inside the GEMM (pieces per split), or apart before a GEMM of the base
+        // alone when the GEMM's workgroups would each chain several pieces
+        const bool apart = lora && decode_shrink_apart(Tc, K, n_out, g.n_slices * g.R);
+        hipError_t e = hipSuccess;
+        if (apart) {
+            e = launch_shrink_pairs(xb + t0 * n_in, Tc, n_in, g, idx_c, K, nullptr, upart, stream,
+                                    true);
+            if (e != hipSuccess)
+                return hip_status(e, "shrink launch");
+        }
+        const bool fused = lora && !apart;
         trace_mark(stream, true);
-        hipError_t e = launch_decode_gemm(xb + t0 * n_in, (const uint16_t *)W, packed, Tc, n_in,
-                                          n_out, part, cfg, lora ? &g : nullptr, idx_c, K,
-                                          lora ? upart : nullptr, stream);
+        e = launch_decode_gemm(xb + t0 * n_in, (const uint16_t *)W, packed, Tc, n_in, n_out, part,
+                               cfg, fused ? &g : nullptr, fused ? idx_c : nullptr, K,
+                               fused ? upart : nullptr, stream);
         trace_mark(stream, false);
         if (e != hipSuccess)
             return hip_status(e, "decode gemm launch");
-        e = launch_decode_finish(part, cfg.sk, cfg.n_tiles, lora ? upart : nullptr, scale_c, Tc,
-                                 n_out, lora ? &g : nullptr, idx_c, K, yb + t0 * n_out, nullptr,
-                                 stream);
+        e = launch_decode_finish(part, cfg.sk, cfg.n_tiles, lora ? upart : nullptr,
+                                 apart ? 1 : cfg.sk, scale_c, Tc, n_out, lora ? &g : nullptr,
+                                 idx_c, K, yb + t0 * n_out, nullptr, stream);
         if (e != hipSuccess)
             return hip_status(e, "decode finish launch");
     }

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void shrink_rows_kernel(const uint16_t *__rest
                                                           const int32_t *__restrict__ idx,
                                                           int32_t K,
                                                           const float *__restrict__ scale,
-                                                          float *__restrict__ v)
+                                                          float *__restrict__ v, int pieces)
 {
     __shared__ float red[4 * RB];
     const u32x4 *zero = (const u32x4 *)vzero;
@@ -101,7 +101,11 @@ __global__ __launch_bounds__(256) void shrink_rows_kernel(const uint16_t *__rest
     const int64_t p = t * K + j;
     const int r0 = (int)blockIdx.y * RB;
     const int nr = min(RB, wd - r0);
-    float *out = v + ((int64_t)j * T + t) * wd + r0;
+    // v [K][T][wd] (scaled), or the decode finish's shrink pieces of one split: per 64-token
+    // chunk c a block [K][Tc][wd] (Tc its tokens), blocks K 64 wd apart, unscaled
+    const int64_t tc = t >> 6, tl = t & 63, Tc = min((int64_t)64, T - (tc << 6));
+    float *out = pieces ? v + (tc * K * 64 + (int64_t)j * Tc + tl) * wd + r0
+                        : v + ((int64_t)j * T + t) * wd + r0;
     const uint16_t *xt = x + t * n_in;
     const int64_t step = (int64_t)blockDim.x * 8;
     const int64_t kt = (int64_t)threadIdx.x * 8;
@@ -170,13 +174,13 @@ __global__ __launch_bounds__(256) void shrink_rows_kernel(const uint16_t *__rest
     if ((int)threadIdx.x < nr) {
         const int rr = threadIdx.x;
         const float tot = ((red[rr] + red[RB + rr]) + red[2 * RB + rr]) + red[3 * RB + rr];
-        out[rr] = (sc * fa) * tot;
+        out[rr] = pieces ? tot : (sc * fa) * tot;
     }
 }
 
 hipError_t launch_shrink_pairs(const uint16_t *x, int64_t T, int64_t n_in, const SlotGeom &g,
                                const int32_t *idx, int32_t K, const float *scale, float *v,
-                               hipStream_t stream)
+                               hipStream_t stream, bool pieces)
 {
     const int64_t P = T * K;
     if (P == 0)
@@ -194,23 +198,23 @@ hipError_t launch_shrink_pairs(const uint16_t *x, int64_t T, int64_t n_in, const
     switch (RB) {
     case 16:
         hipLaunchKernelGGL(shrink_rows_kernel<16>, grid, dim3(256), 0, stream, x, T, n_in, g,
-                           idx, K, scale, v);
+                           idx, K, scale, v, pieces ? 1 : 0);
         break;
     case 8:
         hipLaunchKernelGGL(shrink_rows_kernel<8>, grid, dim3(256), 0, stream, x, T, n_in, g, idx,
-                           K, scale, v);
+                           K, scale, v, pieces ? 1 : 0);
         break;
     case 4:
         hipLaunchKernelGGL(shrink_rows_kernel<4>, grid, dim3(256), 0, stream, x, T, n_in, g, idx,
-                           K, scale, v);
+                           K, scale, v, pieces ? 1 : 0);
         break;
     case 2:
         hipLaunchKernelGGL(shrink_rows_kernel<2>, grid, dim3(256), 0, stream, x, T, n_in, g, idx,
-                           K, scale, v);
+                           K, scale, v, pieces ? 1 : 0);
         break;
     default:
         hipLaunchKernelGGL(shrink_rows_kernel<1>, grid, dim3(256), 0, stream, x, T, n_in, g, idx,
-                           K, scale, v);
+                           K, scale, v, pieces ? 1 : 0);
         break;
     }
     return hipGetLastError();

@@ -67,7 +67,7 @@ __device__ __forceinline__ void df_vload(const float *upart, int sk, int64_t pst
 // adapter's rank (rounded to 8).
 template <bool MC>
 __global__ __launch_bounds__(DF_THREADS) void decode_finish_wide_kernel(
-    const float *__restrict__ part, int sk, int n_tiles, const float *__restrict__ upart,
+    const float *__restrict__ part, int sk, int n_tiles, const float *__restrict__ upart, int usk,
     const float *__restrict__ scale, int T_all, int n_out, SlotGeom g,
     const int32_t *__restrict__ idx, int K, uint16_t *__restrict__ y, float *__restrict__ ysum)
 {
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_wide_kernel(
         const int wd0 = g.n_slices * g.R;
         part += (int64_t)chunk * sk * n_tiles * DF_CHUNK * DF_ROWS;
         if (upart != nullptr)
-            upart += (int64_t)chunk * sk * K * DF_CHUNK * wd0;
+            upart += (int64_t)chunk * usk * K * DF_CHUNK * wd0;
         if (idx != nullptr)
             idx += (int64_t)chunk * DF_CHUNK * K;
         if (scale != nullptr)
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_wide_kernel(
         float4 pv[DF_PQ];
         float sc = 0.f, fa = 0.f;
         if (e0 < nv)
-            df_vload(upart, sk, pstride, K, T, wd, R, t0, 0, 0, e0, sidx, scale, g.factor, pv, sc,
+            df_vload(upart, usk, pstride, K, T, wd, R, t0, 0, 0, e0, sidx, scale, g.factor, pv, sc,
                      fa);
         asm volatile("" ::: "memory");
 
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_wide_kernel(
                     lds_barrier();                 // the previous round's reads are done
                 for (int e = e0; e < nv; e += DF_THREADS * 4) {
                     if (j + sg > 0 || e != e0)
-                        df_vload(upart, sk, pstride, K, T, wd, R, t0, j, sg, e, sidx, scale,
+                        df_vload(upart, usk, pstride, K, T, wd, R, t0, j, sg, e, sidx, scale,
                                  g.factor, pv, sc, fa);
                     const int tt = e / R;
                     const int a = sidx[tt * K + j];
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_wide_kernel(
                         sum.w += pv[sp].w;
                     }
                     // splits past DF_PQ (rare): added in split order after the first ones
-                    for (int sp = DF_PQ; sp < sk; ++sp) {
+                    for (int sp = DF_PQ; sp < usk; ++sp) {
                         const float4 o = *(const float4 *)(a >= 0 ? upart + ((int64_t)j * T + t0 + tt) * wd +
                                                                         sg * R + (e - tt * R) + sp * pstride
                                                                   : df_zero);
@@ -247,7 +247,7 @@ constexpr int DF2_TOK = 8;
 
 template <bool MC, int RC>
 __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
-    const float *__restrict__ part, int sk, int n_tiles, const float *__restrict__ upart,
+    const float *__restrict__ part, int sk, int n_tiles, const float *__restrict__ upart, int usk,
     const float *__restrict__ scale, int T_all, int n_out, SlotGeom g,
     const int32_t *__restrict__ idx, int K, uint16_t *__restrict__ y, float *__restrict__ ysum)
 {
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
         const int wd0 = g.n_slices * RC;
         part += (int64_t)chunk * sk * n_tiles * DF_CHUNK * DF_ROWS;
         if (RC > 0) {
-            upart += (int64_t)chunk * sk * K * DF_CHUNK * wd0;
+            upart += (int64_t)chunk * usk * K * DF_CHUNK * wd0;
             idx += (int64_t)chunk * DF_CHUNK * K;
             if (scale != nullptr)
                 scale += (int64_t)chunk * DF_CHUNK * K;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
             const float *qsrc = upart + ((int64_t)j * T + t0 + tq) * wd + e4;
 #pragma unroll
             for (int sp = 0; sp < DF_PQ; ++sp)
-                pv[sp] = *(const f32x4 *)(has_q && sp < sk ? qsrc + sp * pstride : df_zero);
+                pv[sp] = *(const f32x4 *)(has_q && sp < usk ? qsrc + sp * pstride : df_zero);
             const int aq = has_q ? idx[(int64_t)(t0 + tq) * K + j] : -1;
             const float sc = has_q && scale ? scale[(int64_t)(t0 + tq) * K + j] : 1.f;
             if (j > 0) {
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
 #pragma unroll
                 for (int sp = 0; sp < DF_PQ; ++sp)
                     sum += pv[sp];
-                for (int sp = DF_PQ; sp < sk; ++sp)
+                for (int sp = DF_PQ; sp < usk; ++sp)
                     sum += *(const f32x4 *)(qsrc + sp * pstride);
                 const float cf = aq >= 0 ? (scale ? sc : 1.f) * fa : 0.f;
                 *(f32x4 *)(vl + tq * wd + e4) = sum * cf;
@@ -384,9 +384,9 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
 }
 
 hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, const float *upart,
-                                const float *scale, int64_t T, int64_t n_out, const SlotGeom *g,
-                                const int32_t *idx, int32_t K, uint16_t *y, float *ysum,
-                                hipStream_t stream)
+                                int32_t usk, const float *scale, int64_t T, int64_t n_out,
+                                const SlotGeom *g, const int32_t *idx, int32_t K, uint16_t *y,
+                                float *ysum, hipStream_t stream)
 {
     SlotGeom gg{};
     size_t lds = 0;
@@ -406,7 +406,8 @@ hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, 
                                           ((std::min<int64_t>(T, DF_CHUNK) + DF2_TOK - 1) / DF2_TOK));
 #define DF2_LAUNCH(M, C)                                                                           \
     hipLaunchKernelGGL((decode_finish_kernel<M, C>), dim3(grid2), dim3(DF_THREADS), 0, stream,   \
-                       part, sk, n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y, ysum)
+                       part, sk, n_tiles, upart, usk, scale, (int)T, (int)n_out, gg, idx, K, y, \
+                       ysum)
         switch (rc * 2 + (mc ? 1 : 0)) {
         case 0: DF2_LAUNCH(false, 0); break;
         case 1: DF2_LAUNCH(true, 0); break;
@@ -425,7 +426,8 @@ hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, 
         (unsigned)(n_chunks * n_tiles * ((std::min<int64_t>(T, DF_CHUNK) + DF_TOK - 1) / DF_TOK));
 #define DF_LAUNCH(M)                                                                               \
     hipLaunchKernelGGL((decode_finish_wide_kernel<M>), dim3(grid), dim3(DF_THREADS), lds, stream,   \
-                       part, sk, n_tiles, upart, scale, (int)T, (int)n_out, gg, idx, K, y, ysum)
+                       part, sk, n_tiles, upart, usk, scale, (int)T, (int)n_out, gg, idx, K, y, \
+                       ysum)
     if (mc)
         DF_LAUNCH(true);
     else

@@ -618,6 +618,23 @@ DecodeCfg decode_config(int64_t T, int64_t n_in, int64_t n_out)
     return c;
 }
 
+// The GEMM's workgroups of one row tile share out the shrink pieces of the pairs assigned to
+// that tile (pair p to tile p mod n_tiles), one after another, each a dependent chain (A rows,
+// MFMAs, the 8 waves' sums); the first rides in the main pass.  Where a row tile gets 4 or
+// more pairs (narrow outputs: e.g. 8 pairs a tile at 4096 -> 512 for 64 tokens), the shrink
+// runs apart (the per-pair kernel, in the pieces' layout with one split) before a GEMM of the
+// base alone: measured at 64 tokens, 21.3 against 30.8 us at 4096 -> 512 and 17.6 against
+// 20.1 us at 4096 -> 1024; with 1 to 3 pairs a tile (4096 -> 2048 or 4096, rank 64 slots, 3
+// slots a token) the fused pass stays ahead by 1 to 3 us.
+constexpr int64_t DECODE_APART_PAIRS = 4;
+bool decode_shrink_apart(int64_t T, int32_t K, int64_t n_out, int32_t wd)
+{
+    (void)wd;
+    const int64_t n_tiles = (n_out + DEC_ROWS - 1) / DEC_ROWS;
+    const int64_t pairs = std::min<int64_t>(T, DEC_CHUNK) * K;
+    return (pairs + n_tiles - 1) / n_tiles >= DECODE_APART_PAIRS;
+}
+
 size_t decode_partial_bytes(int64_t T, int64_t n_in, int64_t n_out)
 {
     const DecodeCfg c = decode_config(T, n_in, n_out);

@@ -41,10 +41,12 @@ struct SlotGeom {
 };
 
 // ---- bgmv.hip: per-pair shrink and per-token expand (decode / any T) -----------------------
-// v[j][t][:] = scale*factor * A[a] x[t]  (zeros for -1 pairs)
+// v[j][t][:] = scale*factor * A[a] x[t]  (zeros for -1 pairs); pieces: A[a] x[t] unscaled, in
+// the decode finish's layout of shrink pieces with one split (per 64-token chunk c a block
+// [K][Tc][wd], Tc = the chunk's tokens, the blocks K 64 wd floats apart)
 hipError_t launch_shrink_pairs(const uint16_t *x, int64_t T, int64_t n_in, const SlotGeom &g,
                                const int32_t *idx, int32_t K, const float *scale, float *v,
-                               hipStream_t stream);
+                               hipStream_t stream, bool pieces = false);
 // One workgroup per (token, block of output rows):
 //   y[t][n] = bf16(y[t][n] + sum_j B[a_j][n][:] . v[j][t][slice(n)*R ..]); rows of a token whose
 //   slots are all -1 are left untouched.  hipErrorInvalidValue past the grid's limits
@@ -74,14 +76,17 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed,
                               hipStream_t stream);
 // Whether launch_decode_gemm takes the persistent grid for these sizes.
 bool decode_gemm_persistent(int64_t T, int64_t n_in, int64_t n_out);
+// Whether the decode path's shrink runs apart from the GEMM (launch_shrink_pairs, pieces
+// layout) for a launch of T tokens, K slots and n_out rows (wd, the slots' rows, is not used).
+bool decode_shrink_apart(int64_t T, int32_t K, int64_t n_out, int32_t wd);
 // ---- decode_finish.hip: y = bf16(sum of the split partials + LoRA delta), T <= 64 ----------
-// part: fp32 [sk][n_tiles][T][64] (launch_decode_gemm); upart: fp32 [sk][K][T][wd] unscaled
-// shrink pieces (nullptr: base only, g unused); ysum: fp32 [T][n_out], the same sums before
-// rounding, or nullptr
+// part: fp32 [sk][n_tiles][T][64] (launch_decode_gemm); upart: fp32 [usk][K][T][wd] unscaled
+// shrink pieces, usk = the GEMM's sk or 1 when the shrink ran apart (nullptr: base only, g
+// unused); ysum: fp32 [T][n_out], the same sums before rounding, or nullptr
 hipError_t launch_decode_finish(const float *part, int32_t sk, int32_t n_tiles, const float *upart,
-                                const float *scale, int64_t T, int64_t n_out, const SlotGeom *g,
-                                const int32_t *idx, int32_t K, uint16_t *y, float *ysum,
-                                hipStream_t stream);
+                                int32_t usk, const float *scale, int64_t T, int64_t n_out,
+                                const SlotGeom *g, const int32_t *idx, int32_t K, uint16_t *y,
+                                float *ysum, hipStream_t stream);
 
 // ---- pack.hip: W in the matrix cores' fragment order ------------------------------------------
 // Wp[rg][kb][lane][8] = W[16 rg + lane % 16][32 kb + 8 (lane / 16) + e], zero padded.

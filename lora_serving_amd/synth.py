@@ -262,6 +262,53 @@ def workload_mixed_qkv_decode(seed: int = 1003) -> Layer:
                                segments=L.segments[:nd])
 
 
+def shard_layer(L: Layer, G: int, g: int, kind: str) -> Layer:
+    """Shard g of G of a layer under tensor parallelism (array slicing only).
+
+    kind "col" (column-parallel: q/k/v/gate/up): each slice's output rows split G ways, shard g
+    holding the g-th part of every slice (its rows of W and B); A and x are whole.
+    kind "row" (row-parallel: o/down): the input columns split G ways, shard g holding columns
+    g n_in / G .. of W, A and x, B whole; the shards' outputs add up to the layer's."""
+    if kind == "col":
+        rows, starts = [], [0]
+        for sg in range(L.n_slices):
+            a, b = int(L.slice_start[sg]), int(L.slice_start[sg + 1])
+            if (b - a) % G:
+                raise ValueError("slice sizes must divide by G")
+            part = (b - a) // G
+            rows.append(np.arange(a + g * part, a + (g + 1) * part))
+            starts.append(starts[-1] + part)
+        rows = np.concatenate(rows)
+        return dataclasses.replace(L, name=f"{L.name}_col{g}of{G}", n_out=int(rows.size),
+                                   slice_start=np.asarray(starts, np.int32),
+                                   W=np.ascontiguousarray(L.W[rows]),
+                                   B=np.ascontiguousarray(L.B[:, rows]))
+    if kind == "row":
+        if L.n_in % G:
+            raise ValueError("n_in must divide by G")
+        c = L.n_in // G
+        cols = slice(g * c, (g + 1) * c)
+        return dataclasses.replace(L, name=f"{L.name}_row{g}of{G}", n_in=c,
+                                   x=np.ascontiguousarray(L.x[:, cols]),
+                                   W=np.ascontiguousarray(L.W[:, cols]),
+                                   A=np.ascontiguousarray(L.A[..., cols]))
+    raise ValueError(kind)
+
+
+def workload_decode_tp8_col(seed: int = 1001) -> Layer:
+    """One GPU's share of the decode layer under 8-way column parallelism: 4096 -> 512 (its
+    rows of W and B; A and x whole), the decode mapping."""
+    return dataclasses.replace(shard_layer(workload_decode(seed=seed), 8, 0, "col"),
+                               name="decode_tp8_col")
+
+
+def workload_decode_tp8_row(seed: int = 1001) -> Layer:
+    """One GPU's share of the decode layer under 8-way row parallelism: 512 -> 4096 (its
+    columns of W, A and x; B whole); the GPUs' outputs add up to the layer's."""
+    return dataclasses.replace(shard_layer(workload_decode(seed=seed), 8, 0, "row"),
+                               name="decode_tp8_row")
+
+
 WORKLOADS = {
     "tiny": workload_tiny,
     "decode256": workload_decode256,
@@ -272,6 +319,8 @@ WORKLOADS = {
     "mixed_qkv_prefill_first": workload_mixed_qkv_prefill_first,
     "mixed_qkv_decode": workload_mixed_qkv_decode,
     "compose": workload_compose,
+    "decode_tp8_col": workload_decode_tp8_col,
+    "decode_tp8_row": workload_decode_tp8_row,
 }
 
 

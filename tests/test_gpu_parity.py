@@ -539,6 +539,35 @@ def test_limits_most_slots(oracle_mod, path):
         check_delta(oracle_mod, L, D, label="most slots")
 
 
+@pytest.mark.parametrize("path", ["decode", "tiled"])
+def test_tensor_parallel_shares(oracle_mod, path):
+    """One GPU's share of a layer split 8 ways (merged QKV slices): the library on each column
+    shard (its rows of W and B) and each row shard (its columns of W, A and x) against the
+    oracle of that shard; the row shards' bf16 outputs, added in fp32, against the oracle's
+    whole layer within the sum of their tolerances (the base model's all-reduce would add
+    them)."""
+    from lora_serving_amd import mlora
+    G = 8
+    L = synth.random_layer(74, T=64 if path == "decode" else 300, n_in=1024, n_out=1536, S=9,
+                           R=16, K=2, p_sentinel=0.2, slice_sizes=[1024, 256, 256],
+                           contiguous=(path == "tiled"))
+    flags = mlora.MLORA_PATH_DECODE if path == "decode" else mlora.MLORA_PATH_TILED
+    say(f"[tp shares] path={path} T={L.T} G={G}")
+    total = np.zeros((L.T, L.n_out), np.float64)
+    bound = np.zeros((L.T, L.n_out), np.float64)
+    for g in range(G):
+        for kind in ("col", "row"):
+            Ls = synth.shard_layer(L, G, g, kind)
+            y = from_dev_bf16(DevLayer(Ls).linear(flags=flags))
+            y_ref = oracle_mod.linear(Ls)
+            assert tol_ok(y, y_ref).all(), f"{kind} {g}: worst {worst(y, y_ref):.3e}"
+            if kind == "row":
+                total += y.astype(np.float64)
+                bound += 2e-2 * (1 + np.abs(y_ref))
+    y_full = oracle_mod.linear(L)
+    assert np.all(np.abs(total - y_full) <= bound)
+
+
 def test_tiled_path_chunks_past_a_million_tokens(oracle_mod):
     """More tokens than one tiled launch takes (4096 tiles of 256): the batch is cut in chunks;
     tokens on both sides of the cut and the ragged end are checked against the oracle."""
@@ -892,6 +921,31 @@ def _mlora_kernels_launched(fn):
     return names
 
 
+@pytest.mark.parametrize("n_out,R,K,apart", [(4096, 16, 1, False), (2048, 16, 1, False),
+                                             (1024, 16, 1, True), (512, 16, 1, True),
+                                             (4096, 64, 1, False), (4096, 16, 3, False),
+                                             (4096, 16, 4, True), (1024, 32, 2, True)])
+def test_decode_shrink_route(oracle_mod, n_out, R, K, apart):
+    """Where a 64-row tile of the decode GEMM would get 4 or more (token, slot) pairs of a
+    64-token chunk, whose shrink pieces its workgroups would chain one after another, the shrink
+    runs apart, as the per-pair kernel ahead of a GEMM of the base alone; otherwise it rides in
+    the GEMM pass.  The route is checked from the kernels launched, the output against the
+    oracle."""
+    from lora_serving_amd import mlora
+    L = synth.random_layer(78 + n_out + R + K, T=64, n_in=256, n_out=n_out, S=12, R=R, K=K,
+                           p_sentinel=0.1)
+    D = DevLayer(L)
+    pf = mlora.MLORA_PATH_DECODE
+    D.linear(flags=pf)
+    names = _mlora_kernels_launched(lambda: D.linear(flags=pf))
+    say(f"[shrink route] n_out={n_out} R={R} K={K}: {sorted(names)}")
+    assert ("shrink_rows_kernel" in names) == apart
+    assert "decode_gemm_kernel" in names and any(n.startswith("decode_finish") for n in names)
+    toks = np.arange(0, 64, 3)
+    y = from_dev_bf16(D.linear(flags=pf))
+    assert tol_ok(y[toks], oracle_mod.linear(L, tokens=toks)).all()
+
+
 @pytest.mark.parametrize("path", ["decode", "tiled"])
 def test_no_adapters_flag_launches_base_kernels_only(path):
     """With MLORA_NO_ADAPTERS no LoRA kernel is launched ("Multi-LoRA Serving Explained": the
@@ -909,7 +963,8 @@ def test_no_adapters_flag_launches_base_kernels_only(path):
     say(f"[no-adapters] {path}: with adapters {sorted(with_lora)}, flag {sorted(base_only)}")
     if path == "decode":
         assert base_only == {"decode_gemm_kernel", "decode_finish_kernel"}
-        assert with_lora == base_only            # the shrink rides in the GEMM pass
+        # 12 row tiles for 128 pairs a chunk: the shrink runs apart, ahead of the GEMM
+        assert with_lora == base_only | {"shrink_rows_kernel"}
     else:
         assert base_only == {"prefill_gemm_kernel"}
         assert {"tile_plan_kernel", "sgmv_shrink_kernel"} <= with_lora

@@ -227,6 +227,31 @@ def test_additivity_over_slots(oracle_mod):
     assert np.all(np.abs(total - parts) <= 1e-12 * (mag + 1e-300))
 
 
+@pytest.mark.parametrize("G", [2, 4])
+def test_tensor_parallel_shards(oracle_mod, G):
+    """Tensor-parallel shards (the layer split over G GPUs; every term is linear in x and
+    separate per output row): a column shard's outputs are the layer's rows of its part of
+    every slice, bit for bit; the row shards' outputs add up to the layer's within fp64
+    rounding, the LoRA terms included (each shard's shrink covers its columns of A and x).  A
+    wrong slice offset fails the first, a shrink over the whole of x the second."""
+    L = synth.random_layer(9, T=12, n_in=64, n_out=48, S=5, R=16, K=2, p_sentinel=0.2,
+                           slice_sizes=[24, 12, 12])
+    full = oracle_mod.linear(L)
+    for g in range(G):
+        Lc = synth.shard_layer(L, G, g, "col")
+        rows = np.concatenate([np.arange(a + g * (b - a) // G, a + (g + 1) * (b - a) // G)
+                               for a, b in zip(L.slice_start[:-1], L.slice_start[1:])])
+        assert Lc.n_out == rows.size
+        assert np.array_equal(oracle_mod.linear(Lc), full[:, rows])
+    total = sum(oracle_mod.linear(synth.shard_layer(L, G, g, "row")) for g in range(G))
+    _, mag = cf.merged_linear(L)
+    assert np.all(np.abs(total - full) <= 1e-12 * (mag + 1e-300))
+    # the row shards' deltas alone are each a proper part: none of them is the whole delta
+    d_full = oracle_mod.linear(L, with_base=False)
+    d0 = oracle_mod.linear(synth.shard_layer(L, G, 0, "row"), with_base=False)
+    assert not np.allclose(d0, d_full)
+
+
 def test_cat_merged_virtual_adapter(oracle_mod):
     """K-slot composition equals one adapter whose A stacks the K adapters' rows and whose B
     concatenates c_j B_j (the RFC's exact oracle).  Scales are powers of two so c_j B_j is
