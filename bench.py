@@ -424,11 +424,11 @@ def decode_gemm_name(T, n_in, n_out, n_cus=256):
     Tc = min(T, 512)
     n_tiles = -(-n_out // 64)
     wblocks = -(-n_in // 128)
+    n_chunks = -(-Tc // 64)
     per = 8
-    while per > 1 and n_tiles * (-(-wblocks // per)) < n_cus:
+    while per > 4 and n_chunks * n_tiles * (-(-wblocks // per)) < n_cus:
         per //= 2
     sk = -(-n_in // (per * 128))
-    n_chunks = -(-Tc // 64)
     if n_chunks > 1:
         per_xcd = (n_cus // 8) // n_chunks
         pairs = 8 * per_xcd
@@ -436,6 +436,17 @@ def decode_gemm_name(T, n_in, n_out, n_cus=256):
     else:
         ps = n_tiles * sk >= 2 * n_cus and sk <= n_cus
     return "mlora::decode_gemm_ps_kernel" if ps else "mlora::decode_gemm_kernel"
+
+
+def decode_shrink_apart(T, K, n_out, wd):
+    """Whether the decode path runs the shrink apart from its GEMM (the per-pair kernel ahead of
+    a GEMM of the base alone), by the same condition as the library's decode_shrink_apart: a
+    64-row tile gets 2 or more (token, slot) pairs of a 64-token chunk and 4 or more 16-row
+    pieces of them (8 with several chunks) (label and byte count only)."""
+    n_tiles = -(-n_out // 64)
+    pairs = -(-(min(T, 64) * K) // n_tiles)
+    pieces = pairs * -(-wd // 16)
+    return pairs >= 2 and pieces >= (8 if T > 64 else 4)
 
 
 def linear_roofline(P: Prepared, kernel_ms, only_layer=None):
@@ -448,11 +459,22 @@ def linear_roofline(P: Prepared, kernel_ms, only_layer=None):
     per_step = P.launches_per_step(only_layer)
     if P.decode_like:
         paths = [P.paths[i] for i in idxs]
-        k_bytes = sum(a["grouped_kernel_bytes" if p == "grouped" else "decode_kernel_bytes"]
-                      for a, p in zip(algs, paths)) / per_step
+        # the GEMM reads the adapters' A rows only where the shrink rides in its pass
+        lora = not (P.flags & P.mlora.MLORA_NO_ADAPTERS)
+        base_only = [p == "grouped" or (p == "decode" and lora and
+                                        decode_shrink_apart(P.layers[i].T, P.layers[i].K,
+                                                            P.layers[i].n_out,
+                                                            P.layers[i].n_slices * P.layers[i].R))
+                     for i, p in zip(idxs, paths)]
+        k_bytes = sum(a["grouped_kernel_bytes" if b else "decode_kernel_bytes"]
+                      for a, b in zip(algs, base_only)) / per_step
         achieved = k_bytes / (k_avg_ms * 1e-3) / 1e9
-        what = ("base product (grouped decode: the LoRA terms in the group kernels)"
-                if all(p == "grouped" for p in paths) else "base product + LoRA shrink")
+        if all(p == "grouped" for p in paths):
+            what = "base product (grouped decode: the LoRA terms in the group kernels)"
+        elif all(base_only):
+            what = "base product (the shrink apart, in shrink_rows_kernel)"
+        else:
+            what = "base product + LoRA shrink"
         import torch
         L0 = P.layers[idxs[0]]
         n_cus = torch.cuda.get_device_properties(0).multi_processor_count

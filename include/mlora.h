@@ -235,7 +235,10 @@ mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_
  * columns) would exceed four times W's bytes
  * takes the grouped decode ("Multi-LoRA Serving Explained", the segmented method: tokens
  * sorted by adapter so that each adapter is read once per group): the decode kernels' base
- * product, the LoRA terms computed per adapter over its tokens.  MLORA_PATH_DECODE /
+ * product, the LoRA terms computed per adapter over its tokens.  The decode kernels compute
+ * the shrink inside the GEMM pass, or, where 64 output rows would get 4 or more (token, slot)
+ * pairs of a 64-token chunk (narrow outputs), with the per-pair shrink kernel ahead of a GEMM
+ * of the base alone.  MLORA_PATH_DECODE /
  * MLORA_PATH_TILED / MLORA_PATH_GROUPED force one (more than one set: MLORA_ERR_ARG;
  * MLORA_PATH_GROUPED where the fp32 sums of one launch's up to 512 tokens exceed what the
  * grouped expand keeps, 64 MiB or one 256-token tile: MLORA_ERR_UNSUPPORTED).

@@ -607,11 +607,15 @@ DecodeCfg decode_config(int64_t T, int64_t n_in, int64_t n_out)
     c.tt = T <= 16 ? 1 : T <= 32 ? 2 : 4;   // more than 64 tokens: chunks of 64
     c.n_tiles = (int)((n_out + DEC_ROWS - 1) / DEC_ROWS);
     const int64_t wblocks = (n_in + DEC_WK - 1) / DEC_WK;          // 128-column blocks
-    // each workgroup takes up to 8 blocks (one per wave); split further while the grid is
-    // smaller than the device's CUs
+    // each workgroup takes up to 8 blocks (one per wave); split further, down to 4 blocks a
+    // workgroup, while the grid (all the launch's 64-token chunks) is smaller than the
+    // device's CUs.  Finer splits measured slower: they leave most waves of a workgroup
+    // without columns and make the finish add more partials (64 tokens at 4096 -> 512: 21.3
+    // us at 32 splits, 13.8 at 8; 256 tokens at 512 -> 4096: 31.9 us at 4 splits, 18.6 at 1)
     const int n_cus = device_cu_count();
+    const int64_t n_chunks = (T + DEC_CHUNK - 1) / DEC_CHUNK;
     int per = DEC_WAVES;
-    while (per > 1 && c.n_tiles * ((wblocks + per - 1) / per) < n_cus)
+    while (per > DEC_WAVES / 2 && n_chunks * c.n_tiles * ((wblocks + per - 1) / per) < n_cus)
         per >>= 1;
     c.kr = per * DEC_WK;
     c.sk = (int)((n_in + c.kr - 1) / c.kr);
@@ -619,20 +623,23 @@ DecodeCfg decode_config(int64_t T, int64_t n_in, int64_t n_out)
 }
 
 // The GEMM's workgroups of one row tile share out the shrink pieces of the pairs assigned to
-// that tile (pair p to tile p mod n_tiles), one after another, each a dependent chain (A rows,
-// MFMAs, the 8 waves' sums); the first rides in the main pass.  Where a row tile gets 4 or
-// more pairs (narrow outputs: e.g. 8 pairs a tile at 4096 -> 512 for 64 tokens), the shrink
-// runs apart (the per-pair kernel, in the pieces' layout with one split) before a GEMM of the
-// base alone: measured at 64 tokens, 21.3 against 30.8 us at 4096 -> 512 and 17.6 against
-// 20.1 us at 4096 -> 1024; with 1 to 3 pairs a tile (4096 -> 2048 or 4096, rank 64 slots, 3
-// slots a token) the fused pass stays ahead by 1 to 3 us.
-constexpr int64_t DECODE_APART_PAIRS = 4;
+// that tile (pair p of a 64-token chunk to tile p mod n_tiles), each pair's n_slices R rows in
+// blocks of 16, one piece after another, each a dependent chain (A rows, MFMAs, the 8 waves'
+// sums); the first rides in the main pass.  Where a tile gets 2 or more pairs and 4 or more
+// pieces (8 when the launch has several chunks, whose workgroups take two or more rounds of
+// the CUs and so hide part of the chains), the shrink runs apart (the per-pair kernel, in the
+// pieces' layout with one split) before a GEMM of the base alone.  Measured at 64 tokens:
+// 4096 -> 512 13.3 against 19.8 us, 4096 -> 1024 13.8 against 15.2, merged QKV 4096 -> 1536
+// (3 pairs, 3 blocks a pair) 17.0 against 22.6; kept fused: 4096 -> 2048 (2 pieces) 14.4
+// against 15.6, rank 64 slots at 4096 -> 4096 (1 pair, 4 blocks) 27.7 against 28.8, 512
+// tokens at 4096 -> 1024 (4 pieces, 8 chunks) 35.7 against 40.9.
 bool decode_shrink_apart(int64_t T, int32_t K, int64_t n_out, int32_t wd)
 {
-    (void)wd;
     const int64_t n_tiles = (n_out + DEC_ROWS - 1) / DEC_ROWS;
-    const int64_t pairs = std::min<int64_t>(T, DEC_CHUNK) * K;
-    return (pairs + n_tiles - 1) / n_tiles >= DECODE_APART_PAIRS;
+    const int64_t pairs = (std::min<int64_t>(T, DEC_CHUNK) * K + n_tiles - 1) / n_tiles;
+    const int64_t pieces = pairs * ((wd + 15) / 16);
+    const bool chunks = T > DEC_CHUNK;
+    return pairs >= 2 && pieces >= (chunks ? 8 : 4);
 }
 
 size_t decode_partial_bytes(int64_t T, int64_t n_in, int64_t n_out)

@@ -77,7 +77,7 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, bool packed,
 // Whether launch_decode_gemm takes the persistent grid for these sizes.
 bool decode_gemm_persistent(int64_t T, int64_t n_in, int64_t n_out);
 // Whether the decode path's shrink runs apart from the GEMM (launch_shrink_pairs, pieces
-// layout) for a launch of T tokens, K slots and n_out rows (wd, the slots' rows, is not used).
+// layout) for a launch of T tokens, K slots, n_out rows and slots of wd rows.
 bool decode_shrink_apart(int64_t T, int32_t K, int64_t n_out, int32_t wd);
 // ---- decode_finish.hip: y = bf16(sum of the split partials + LoRA delta), T <= 64 ----------
 // part: fp32 [sk][n_tiles][T][64] (launch_decode_gemm); upart: fp32 [usk][K][T][wd] unscaled

@@ -41,3 +41,12 @@ def test_prefill_flops_match_the_survey_figures():
     assert a["flops"] == base + lora
     assert abs(base / 1e9 - 1477.5) < 0.1 and abs(lora / 1e9 - 31.7) < 0.1
     assert a["tiled_kernel_flops"] == base + 16384 * 2.0 * 64 * 11008
+
+
+def test_decode_shrink_route_label_matches_the_library_cases():
+    """The benchmark's copy of the decode path's shrink route (label and byte count of the GEMM)
+    gives the routes the GPU test checks from the kernels the library launches."""
+    from tests.gpu_util import DECODE_ROUTE_CASES
+    for T, n_out, R, K, slices, apart in DECODE_ROUTE_CASES:
+        wd = (len(slices) if slices else 1) * R
+        assert bench.decode_shrink_apart(T, K, n_out, wd) == apart

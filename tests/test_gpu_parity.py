@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from lora_serving_amd import synth
-from tests.gpu_util import DevLayer, from_dev_bf16, tol_ok, worst
+from tests.gpu_util import DECODE_ROUTE_CASES, DevLayer, from_dev_bf16, tol_ok, worst
 
 pytestmark = pytest.mark.gpu
 
@@ -921,27 +921,25 @@ def _mlora_kernels_launched(fn):
     return names
 
 
-@pytest.mark.parametrize("n_out,R,K,apart", [(4096, 16, 1, False), (2048, 16, 1, False),
-                                             (1024, 16, 1, True), (512, 16, 1, True),
-                                             (4096, 64, 1, False), (4096, 16, 3, False),
-                                             (4096, 16, 4, True), (1024, 32, 2, True)])
-def test_decode_shrink_route(oracle_mod, n_out, R, K, apart):
-    """Where a 64-row tile of the decode GEMM would get 4 or more (token, slot) pairs of a
-    64-token chunk, whose shrink pieces its workgroups would chain one after another, the shrink
-    runs apart, as the per-pair kernel ahead of a GEMM of the base alone; otherwise it rides in
-    the GEMM pass.  The route is checked from the kernels launched, the output against the
-    oracle."""
+@pytest.mark.parametrize("T,n_out,R,K,slices,apart", DECODE_ROUTE_CASES)
+def test_decode_shrink_route(oracle_mod, T, n_out, R, K, slices, apart):
+    """Where a 64-row tile of the decode GEMM would get 2 or more (token, slot) pairs of a
+    64-token chunk and 4 or more 16-row shrink pieces of them (8 with several chunks), which
+    its workgroups would chain one after another, the shrink runs apart, as the per-pair kernel
+    ahead of a GEMM of the base alone; otherwise it rides in the GEMM pass.  The route is
+    checked from the kernels launched, the output against the oracle."""
     from lora_serving_amd import mlora
-    L = synth.random_layer(78 + n_out + R + K, T=64, n_in=256, n_out=n_out, S=12, R=R, K=K,
-                           p_sentinel=0.1)
+    L = synth.random_layer(78 + T + n_out + R + K, T=T, n_in=256, n_out=n_out, S=12, R=R, K=K,
+                           p_sentinel=0.1, slice_sizes=slices)
     D = DevLayer(L)
     pf = mlora.MLORA_PATH_DECODE
     D.linear(flags=pf)
     names = _mlora_kernels_launched(lambda: D.linear(flags=pf))
-    say(f"[shrink route] n_out={n_out} R={R} K={K}: {sorted(names)}")
+    say(f"[shrink route] T={T} n_out={n_out} R={R} K={K}: {sorted(names)}")
     assert ("shrink_rows_kernel" in names) == apart
-    assert "decode_gemm_kernel" in names and any(n.startswith("decode_finish") for n in names)
-    toks = np.arange(0, 64, 3)
+    assert any(n.startswith("decode_gemm") for n in names)
+    assert any(n.startswith("decode_finish") for n in names)
+    toks = np.unique(np.r_[np.arange(0, T, 7), T - 1])
     y = from_dev_bf16(D.linear(flags=pf))
     assert tol_ok(y[toks], oracle_mod.linear(L, tokens=toks)).all()
 
