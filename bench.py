@@ -430,11 +430,10 @@ def decode_gemm_name(T, n_in, n_out, n_cus=256):
         per //= 2
     sk = -(-n_in // (per * 128))
     if n_chunks > 1:
-        per_xcd = (n_cus // 8) // n_chunks
-        pairs = 8 * per_xcd
-        ps = per_xcd >= 1 and pairs % sk == 0 and n_tiles >= 2 * (pairs // sk)
+        n_lanes = 8 * ((n_cus // 8) // n_chunks) // sk
+        ps = n_lanes >= 1 and n_tiles >= 2 * n_lanes
     else:
-        ps = n_tiles * sk >= 2 * n_cus and sk <= n_cus
+        ps = n_tiles * sk > n_cus and sk <= n_cus
     return "mlora::decode_gemm_ps_kernel" if ps else "mlora::decode_gemm_kernel"
 
 
