@@ -139,6 +139,8 @@ def linear(L, tokens=None, with_base: bool = True, acc: str = "f64") -> np.ndarr
     else:
         tok = _c(tokens, np.int64)
         nt = tok.shape[0]
+        if nt and (tok.min() < 0 or tok.max() >= L.T):
+            raise IndexError(f"token indices must lie in [0, {L.T})")
     y = np.zeros((nt, L.n_out), np.float64)
     scale = _c(L.scale, np.float32)
     _load(acc).oracle_linear(_ptr(_c(L.x, np.uint16)), _ptr(_c(L.W, np.uint16)), L.T, L.n_in,

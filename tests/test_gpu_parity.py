@@ -921,6 +921,30 @@ def _mlora_kernels_launched(fn):
     return names
 
 
+@pytest.mark.parametrize("T,n_in,n_out,slices", [(64, 4096, 6144, [4096, 1024, 1024]),
+                                                  (64, 4096, 5120, None),
+                                                  (256, 11008, 1024, None)])
+def test_decode_persistent_grid_between_rounds(oracle_mod, T, n_in, n_out, slices):
+    """The decode GEMM's persistent grid where one workgroup per item would need between one
+    and two rounds of the CUs (one chunk: 384 and 320 items), and for several chunks whose split
+    count (11 for n_in = 11008) does not divide an XCD's 64 (split, lane) slots (the slots past
+    the last whole lane stay idle).  The kernel that ran is read from the launches; sampled
+    tokens of every chunk are checked against the oracle."""
+    from lora_serving_amd import mlora
+    L = synth.random_layer(91 + T + n_in + n_out, T=T, n_in=n_in, n_out=n_out, S=20, R=16, K=1,
+                           p_sentinel=0.1, slice_sizes=slices)
+    D = DevLayer(L)
+    pf = mlora.MLORA_PATH_DECODE
+    D.linear(flags=pf)
+    names = _mlora_kernels_launched(lambda: D.linear(flags=pf))
+    say(f"[persistent] T={T} n_in={n_in} n_out={n_out}: {sorted(names)}")
+    assert "decode_gemm_ps_kernel" in names
+    y = from_dev_bf16(D.linear(flags=pf))
+    toks = np.unique(np.clip(np.r_[np.arange(0, T, 13), 63, 64, T - 1], 0, T - 1))
+    y_ref = oracle_mod.linear(L, tokens=toks)
+    assert tol_ok(y[toks], y_ref).all(), f"worst {worst(y[toks], y_ref):.3e}"
+
+
 @pytest.mark.parametrize("T,n_out,R,K,slices,apart", DECODE_ROUTE_CASES)
 def test_decode_shrink_route(oracle_mod, T, n_out, R, K, slices, apart):
     """Where a 64-row tile of the decode GEMM would get 2 or more (token, slot) pairs of a

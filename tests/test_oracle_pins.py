@@ -384,3 +384,13 @@ def test_fp32_build_within_fp32_rounding_of_fp64(oracle_mod):
     d32 = oracle_mod.linear(L, with_base=False, acc="f32")
     rows = np.where(np.all(L.idx == -1, axis=1))[0]
     assert np.all(d32[rows] == 0)
+
+
+def test_linear_rejects_tokens_out_of_range(oracle_mod):
+    """A sampled-token request past the layer's tokens is an error, not a read past x."""
+    L = synth.random_layer(11, T=8, n_in=16, n_out=8, S=2, R=8, K=1)
+    with pytest.raises(IndexError):
+        oracle_mod.linear(L, tokens=np.array([0, 8]))
+    with pytest.raises(IndexError):
+        oracle_mod.linear(L, tokens=np.array([-1]))
+    assert oracle_mod.linear(L, tokens=np.array([7])).shape == (1, 8)
