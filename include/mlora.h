@@ -231,8 +231,8 @@ mlora_status mlora_expand(const float *v, int64_t T, int64_t n_out, const mlora_
  * the decode kernels or the tiled kernels, whichever a host-side model of their measured
  * rates estimates faster for the sizes (the tiled kernels from about 1536 tokens at 4096 ->
  * 4096, 768 at 4096 -> 11008, 256 at vocabulary-wide outputs).  Where the decode kernels
- * are picked, a batch whose per-token adapter reads (each (token, slot) pair's A rows and B
- * columns) would exceed four times W's bytes
+ * are picked, a batch of 128 or more tokens whose per-token adapter reads (each (token, slot)
+ * pair's A rows and B columns) would exceed both four times W's bytes and 200 MB
  * takes the grouped decode ("Multi-LoRA Serving Explained", the segmented method: tokens
  * sorted by adapter so that each adapter is read once per group): the decode kernels' base
  * product, the LoRA terms computed per adapter over its tokens.  The decode kernels compute

@@ -471,7 +471,8 @@ mlora_status choose_path(int64_t T, int64_t n_in, int64_t n_out, int32_t S, int3
     const bool force_decode = (flags & MLORA_PATH_DECODE) != 0;
     const bool force_tiled = (flags & MLORA_PATH_TILED) != 0;
     const bool force_grouped = (flags & MLORA_PATH_GROUPED) != 0;
-    if (force_tiled || (!force_decode && !force_grouped && prefill_worth_it(T, n_in, n_out))) {
+    if (force_tiled || (!force_decode && !force_grouped &&
+                        prefill_worth_it(T, n_in, n_out, K, lora ? n_slices * R : 0))) {
         *path = MLORA_PATH_TILED;
         return MLORA_OK;
     }

@@ -1496,40 +1496,48 @@ static PrefillLayout prefill_layout(const PrefillCfg &c)
 size_t prefill_workspace_bytes(const PrefillCfg &c) { return prefill_layout(c).total; }
 
 // Grouping pays where the per-(token, slot) reads of the decode kernels (each pair's A rows
-// and B columns, padded slot width) would dwarf the base weight: at least 128 tokens and that
-// gather above four times W's bytes.  Below it the group items (a few tokens each, bound by
-// their latency) lose to the gather, e.g. 256 tokens of rank 16 at 4096 -> 4096.
+// and B columns, padded slot width) would dwarf the base weight and take long in themselves:
+// at least 128 tokens, that gather above four times W's bytes and above 200 MB.  Below it the
+// group kernels (five launches, items of a few tokens bound by their latency) lose to the
+// gather: measured at 256 tokens, rank 16 at 4096 -> 512 (38 MB of gather) 17.8 against 45.1
+// us, rank 32 at 4096 -> 4096 (134 MB) 51.6 against 62.3 us; with 268 MB or more the grouped
+// decode won (rank 64 at 4096 -> 4096: 64.7 against 79.9 us; at 512 tokens 94.6 against 152.9).
 bool grouped_decode_worth_it(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t wd,
                              int32_t R)
 {
     const double gather = (double)T * K * ((double)wd * n_in + (double)n_out * R);
-    return T >= 128 && gather > 4.0 * (double)n_out * n_in;
+    return T >= 128 && gather > 4.0 * (double)n_out * n_in && 2.0 * gather >= 200.0e6;
 }
 
-bool prefill_worth_it(int64_t T, int64_t n_in, int64_t n_out)
+bool prefill_worth_it(int64_t T, int64_t n_in, int64_t n_out, int32_t K, int32_t wd)
 {
-    // Estimated times of the two paths (us), from their rates measured on MI355X:
-    //  decode: launches of up to 512 tokens; each takes about 6 us per round of its (64-token
-    //    chunk, 64-row tile, split) items over the CUs, 5 us more, and the split partials
-    //    written and read (8 bytes per split, token and output at about 6 TB/s);
-    //  tiled: about 125 us per round of 256 x 256 output tiles over the CUs per 4096 columns of
-    //    n_in, times 1.3 for batches whose adapters spread over many tiles (the index map is
-    //    not read here; 1.8 when a tile's fp32 sums exceed the 64 MiB kept for the per-adapter
-    //    expand, so that such tiles take the extra k-steps of all their adapters), and 25 us for
-    //    the plan, shrink and expand kernels.
+    // Estimated times of the two paths (us), fitted to their rates measured on MI355X (64 to
+    // 4096 tokens; 4096 -> 512, 1024, 4096 and 11008, 512 and 11008 -> 4096):
+    //  decode: launches of up to 512 tokens; each takes about 10 us, 6 us per round of its
+    //    (64-token chunk, 64-row tile, split) items over the CUs, 10 us more where the shrink
+    //    runs apart, and the split partials written and read (8 bytes per split, token and
+    //    output at about 6 TB/s);
+    //  tiled: 25 us for the plan, shrink and expand kernels, and per round of 256 x 256 output
+    //    tiles over the CUs about 45 us plus 85 us per 4096 columns of n_in, times 1.15 for
+    //    batches whose adapters spread over many tiles (the index map is not read here; tiles
+    //    of random maps took 1.1 to 1.6 times those of contiguous ones; 1.8 when a tile's fp32
+    //    sums exceed the 64 MiB kept for the per-adapter expand, so that such tiles take the
+    //    extra k-steps of all their adapters).
+    // wd: rows of a slot (n_slices R), 0 for the base alone.
     const int64_t n_cus = device_cu_count();
     double dec = 0.0;
     for (int64_t t0 = 0; t0 < T; t0 += 512) {
         const int64_t Tc = std::min<int64_t>(512, T - t0);
         const DecodeCfg c = decode_config(Tc, n_in, n_out);
         const int64_t items = (Tc + 63) / 64 * c.n_tiles * c.sk;
-        dec += 6.0 * (double)((items + n_cus - 1) / n_cus) + 5.0 +
+        const bool apart = wd > 0 && decode_shrink_apart(Tc, K, n_out, wd);
+        dec += 10.0 + 6.0 * (double)((items + n_cus - 1) / n_cus) + (apart ? 10.0 : 0.0) +
                8.0 * (double)c.sk * (double)Tc * (double)n_out / 6.0e6;
     }
     const int64_t tiles = ((T + PF_BM - 1) / PF_BM) * ((n_out + PF_BN - 1) / PF_BN);
-    const double spread = (int64_t)PF_BM * n_out * 4 > (64ll << 20) ? 1.8 : 1.3;
-    const double til =
-        spread * 125.0 * ((double)n_in / 4096.0) * (double)((tiles + n_cus - 1) / n_cus) + 25.0;
+    const double spread = (int64_t)PF_BM * n_out * 4 > (64ll << 20) ? 1.8 : 1.15;
+    const double til = 25.0 + spread * (double)((tiles + n_cus - 1) / n_cus) *
+                                  (45.0 + 85.0 * (double)n_in / 4096.0);
     return til < dec;
 }
 

@@ -117,7 +117,7 @@ PrefillCfg prefill_config(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int
 size_t prefill_workspace_bytes(const PrefillCfg &c);
 // Whether the tiled kernels are estimated faster than the decode kernels for these sizes
 // (host only: a model of both paths' measured rates).
-bool prefill_worth_it(int64_t T, int64_t n_in, int64_t n_out);
+bool prefill_worth_it(int64_t T, int64_t n_in, int64_t n_out, int32_t K, int32_t wd);
 bool grouped_decode_worth_it(int64_t T, int32_t K, int64_t n_in, int64_t n_out, int32_t wd,
                              int32_t R);
 // y = bf16(x W^T + LoRA delta); g == nullptr: base only.  ws: prefill_workspace_bytes(c).

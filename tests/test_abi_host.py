@@ -121,6 +121,18 @@ def test_linear_path_choice(m):
     assert path(16384, 4096, 11008, slots_struct(m, S=100, R=64)) == til   # prefill
     assert path(2304, 4096, 6144, qkv) == til          # the mixed batch
     assert path(256, 4096, 6144, qkv) == grp           # its 256 one-token requests: ~12x W
+    # the per-pair gather must also be large in itself (200 MB) for the group kernels to pay
+    s64, s32 = slots_struct(m, S=64, R=64), slots_struct(m, S=64, R=32)
+    assert path(256, 4096, 4096, s64) == grp           # 268 MB of gather
+    assert path(128, 4096, 4096, s64) == dec           # 134 MB
+    assert path(256, 4096, 4096, s32) == dec           # 134 MB
+    assert path(256, 4096, 512, s16) == dec            # narrow layer: 38 MB, 9x W
+    assert path(1024, 512, 4096, s16) == dec           # narrow input
+    assert path(2048, 512, 4096, s16) == til
+    assert path(2048, 4096, 512, s16) == dec           # 8 output tiles of 256 rows
+    assert path(4096, 4096, 512, s16) == til
+    assert path(1024, 11008, 4096, s16) == til         # wide input: a round of 64 tiles
+    assert path(512, 11008, 4096, s16) == dec
     assert path(256, 4096, 6144, qkv, flags=dec) == dec
     assert path(256, 4096, 6144, qkv, flags=til) == til
     assert path(64, 4096, 4096, s16, flags=grp) == grp
