@@ -23,4 +23,5 @@ DECODE_ROUTE_CASES = [(64, 4096, 16, 1, None, False), (64, 2048, 16, 1, None, Fa
                       (64, 4096, 64, 1, None, False), (64, 4096, 16, 3, None, False),
                       (64, 4096, 16, 4, None, True), (64, 1024, 32, 2, None, True),
                       (64, 1536, 16, 1, [1024, 256, 256], True), (16, 512, 16, 1, None, False),
-                      (512, 1024, 16, 1, None, False), (256, 512, 16, 1, None, True)]
+                      (512, 1024, 16, 1, None, False), (256, 512, 16, 1, None, True),
+                      (100, 6144, 16, 1, [4096, 1024, 1024], False), (70, 4096, 16, 2, None, False)]
