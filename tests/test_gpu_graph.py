@@ -35,6 +35,8 @@ def say(msg):
 def test_graph_replays_match_eager():
     import torch
     from lora_serving_amd import mlora
+    # 32 row tiles for 128 (token, slot) pairs: the decode path's shrink runs apart, ahead of a
+    # GEMM of the base alone (the 150-token layer below keeps it in the GEMM pass)
     Ld = synth.random_layer(81, T=64, n_in=1024, n_out=2048, S=8, R=16, K=2, p_sentinel=0.2)
     Lt = synth.random_layer(82, T=700, n_in=512, n_out=1024, S=9, R=16, K=2, p_sentinel=0.2,
                             contiguous=True)

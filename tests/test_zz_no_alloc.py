@@ -44,6 +44,16 @@ def test_noalloc_decode_two_calls_second_smaller():
 
 
 @pytest.mark.gpu
+def test_noalloc_fused_shrink_decode_then_smaller():
+    """The decode path with its shrink in the GEMM pass (the calls above take the shrink
+    apart: few row tiles for their pairs), then a smaller call of the same kind."""
+    _check(synth.random_layer(7108, T=64, n_in=1024, n_out=4096, S=12, R=16, K=1,
+                              p_sentinel=0.2))
+    _check(synth.random_layer(7109, T=48, n_in=512, n_out=3072, S=6, R=16, K=1,
+                              p_sentinel=0.3))
+
+
+@pytest.mark.gpu
 def test_noalloc_tiled_then_smaller_decode():
     from lora_serving_amd import mlora
     _check(synth.random_layer(7103, T=600, n_in=256, n_out=512, S=6, R=16, K=2,
