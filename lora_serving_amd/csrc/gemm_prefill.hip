@@ -1123,8 +1123,8 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
         for (int j = 0; j < 8; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // stages past the last k-step repeat it (never read), so every iteration issues the same
-    // number of copies and the wait counts below stay exact
+    // the second prologue stage repeats the first when there is only one (never read), so the
+    // count of the first wait below stays exact
 #pragma unroll
     for (int q = 0; q < PF_STAGES; ++q)
         pf_issue<PW>(P, pf_lds + q * (PF_STAGE_BYTES / 2), min(q, nk - 1), nk_main, nk_extra, m0, n0,
@@ -1149,11 +1149,17 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(GemmArgs P)
     for (; q < nk; ++q) {
         uint16_t *st = pf_lds + (q & 1) * (PF_STAGE_BYTES / 2);
         pf_compute<PW>(st, wn, wm, r, gq, a0, b0, acc);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (q + 1 == nk)
+            break;                                          // nothing left to publish or copy
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stage q+1
         lds_barrier();
         pf_prefetch<PW>(pf_lds + ((q + 1) & 1) * (PF_STAGE_BYTES / 2), wn, wm, r, gq, a0, b0);
-        pf_issue<PW>(P, st, min(q + PF_STAGES, nk - 1), nk_main, nk_extra, m0, n0, vtile, D, kxs,
-                     VW, sg_lo, kb_per_slice, slist, wave, lane);
+        // copies only for stages that exist: the waits in this loop are vmcnt(0), so the
+        // number in flight need not be the same every iteration, and the tile's stores no
+        // longer wait behind copies of a stage nobody reads
+        if (q + PF_STAGES < nk)
+            pf_issue<PW>(P, st, q + PF_STAGES, nk_main, nk_extra, m0, n0, vtile, D, kxs, VW,
+                         sg_lo, kb_per_slice, slist, wave, lane);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no copy outlives the workgroup
 
