@@ -20,7 +20,7 @@ from tests.gpu_util import DevLayer, from_dev_bf16, tol_ok, worst
 pytestmark = pytest.mark.gpu
 
 PATHS = ["decode", "tiled", "grouped", "auto"]
-N_CASES = 160
+N_CASES = 96
 
 
 @pytest.fixture(scope="module", autouse=True)
