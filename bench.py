@@ -514,6 +514,9 @@ def config_entry(name, steps, warmup, cpu_s, with_cpu, graph=False):
     ms, steps_done = time_steps(P, steps, warmup, graph=graph)
     ks = trace_kernel(P, steps_done)
     roof = linear_roofline(P, ks)
+    # HBM bytes per launch from a committed counter summary of this kernel on this workload,
+    # while its sources are unchanged (else null)
+    roof["traffic"] = committed_traffic(roof["kernel"].split()[0].split("::")[-1], name)
     T = P.layers[0].T
     tot_bytes = sum(a["bytes"] for a in P.algs)
     tot_flops = sum(a["flops"] for a in P.algs)
